@@ -1,0 +1,102 @@
+/*
+ * TEST INFRASTRUCTURE ONLY.  fp64 CPU reference ("oracle") for block-quantized
+ * weight-only matmul (MatMulNBits) and the INT3 top-k QMoE layer.
+ *
+ * Only the tests, smoke() and the benchmark's CPU-baseline leg may load this
+ * library.  It shares no code, header or table with the HIP library: the two
+ * are written independently from the same pages so that one can check the
+ * other.
+ *
+ * Sources (page title, then section):
+ *  [PLAN]  "Qwen3 Missing-Kernel Implementation Plan" (onnx-light CPU docs),
+ *          section "PR sequence", steps K01 (contract: FP32 A, UINT8 packed B,
+ *          FP32 scales, bits=4, block_size=32, implicit zero points, scale
+ *          indexing, padding), K02 (M=1 decode GEMV) and K03 (small-M/prefill).
+ *  [P0]    onnxruntime PR "INT3 QMoE CUDA correctness baseline and Qwen
+ *          experimental results", embedded body of the stacked P0/P1 PR,
+ *          section "P0: Portable Format and Numerical References" (row-local
+ *          LSB-first UINT8 packing for widths 1..8, canonical padding, INT3
+ *          offset-4 decoding, tiny predetermined-route SwiGLU MoE).
+ *  [P1]    same body, section "P1: Compatible QMoE v1 Extension" (fused
+ *          interleaved gate/up, activation_type swiglu, block sizes 32/64/128,
+ *          I inferred from the fused FC1 rows).
+ *  [OLIVE] same page, embedded Olive body ("Summary"): INT3 dequantization is
+ *          (code - 4) * scale with implicit zero point 4.
+ *  [ROUTE] pegainfer PR "feat(qwen4): component kernels extracted from the
+ *          brick PRs", section "Description": MoE routing is an fp32 softmax,
+ *          top-k, then renormalization of the selected probabilities
+ *          (norm_topk_prob); combine sums the branch outputs.
+ *
+ * All functions return 0 on success and a negative value on bad arguments.
+ */
+#ifndef MNB_ORACLE_H
+#define MNB_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- bit packing [P0] ---------------------------------------------------- */
+int orc_unpack_bits(const uint8_t* row, int64_t n_codes, int bits, uint8_t* codes);
+int orc_pack_bits(const uint8_t* codes, int64_t n_codes, int bits, uint8_t* row);
+/* 1 if every bit after n_codes*bits in the last byte is zero, else 0. */
+int orc_padding_is_canonical(const uint8_t* row, int64_t n_codes, int bits);
+
+/* ---- IEEE binary16 conversions (RN-even) --------------------------------- */
+double orc_f16_to_f64(uint16_t h);
+uint16_t orc_f64_to_f16(double x);
+int orc_f16_to_f64_array(const uint16_t* h, int64_t n, double* out);
+int orc_f64_to_f16_array(const double* x, int64_t n, uint16_t* out);
+
+/* ---- MatMulNBits [PLAN K01-K03] -------------------------------------------
+ * A fp32 [M,K]; B uint8 [N, nb, bs*bits/8] with nb = ceil(K/bs); scales fp32
+ * [N, nb]; zp NULL (implicit 2^(bits-1)) or uint8 [N, ceil(nb*bits/8)] of
+ * zero points packed like the codes.  Outputs (any may be NULL):
+ *   Y   fp32 [M,N] = fp64 result rounded once;
+ *   Y64 fp64 [M,N];
+ *   S   fp64 [M,N] = sum_k |A[m,k] * w[n,k]|  (the tolerance sum).        */
+int orc_mnb_gemm(int64_t M, int64_t K, int64_t N, int bits, int bs,
+                 const float* A, const uint8_t* B, const float* scales,
+                 const uint8_t* zp, float* Y, double* Y64, double* S,
+                 int nthreads);
+/* Dequantized weights in fp64, W [N,K] = (q - z) * s. */
+int orc_mnb_dequant(int64_t K, int64_t N, int bits, int bs, const uint8_t* B,
+                    const float* scales, const uint8_t* zp, double* W);
+/* Logical codes [N,K] and zero points [N,nb] as bytes. */
+int orc_mnb_codes(int64_t K, int64_t N, int bits, int bs, const uint8_t* B,
+                  const uint8_t* zp, uint8_t* codes, uint8_t* zeros);
+
+/* ---- QMoE routing [ROUTE] -------------------------------------------------
+ * logits fp32 [T,E] -> ids int32 [T,k] (logit descending, lower index first
+ * on ties) and weights fp64 [T,k] = softmax over the selected logits, which
+ * equals softmax over all E followed by renormalization of the top k.     */
+int orc_route(int64_t T, int E, int k, const float* logits, int32_t* ids,
+              double* weights);
+
+/* ---- INT3 QMoE layer [P0][P1][OLIVE] --------------------------------------
+ * x fp16 [T,H]; logits fp32 [T,E];
+ * W1 uint8 [E, 2I, ceil(bits1*H/8)], rows 2i = gate_i and 2i+1 = up_i;
+ * s1 fp16 [E, 2I, H/bs]; W2 uint8 [E, H, ceil(bits2*I/8)]; s2 fp16 [E, H, I/bs];
+ * implicit zero points 2^(bits-1).
+ * Outputs (any may be NULL): out16 fp16 [T,H]; out64 fp64 [T,H]; S fp64 [T,H]
+ * (first-order tolerance sum, see orc_qmoe in oracle.cpp); ids int32 [T,k];
+ * r fp64 [T,k]; g, u, h fp64 [T,k,I]; gs, us fp64 [T,k,I] (sum_k |x*w1| for
+ * the gate and up rows).                                                    */
+int orc_qmoe(int64_t T, int64_t H, int64_t I, int E, int k, int bits1,
+             int bits2, int bs, const uint16_t* x, const float* logits,
+             const uint8_t* W1, const uint16_t* s1, const uint8_t* W2,
+             const uint16_t* s2, uint16_t* out16, double* out64, double* S,
+             int32_t* ids, double* r, double* g, double* u, double* h,
+             double* gs, double* us, int nthreads);
+
+/* FC2 alone on caller-supplied fp64 activations h [T,k,I] for stage checks:
+ * y fp64 [T,k,H] = h . w2[ids]^T and yS = sum_i |h_i * w2[n,i]|.           */
+int orc_qmoe_fc2(int64_t T, int64_t H, int64_t I, int E, int k, int bits2,
+                 int bs, const int32_t* ids, const double* h, const uint8_t* W2,
+                 const uint16_t* s2, double* y, double* yS, int nthreads);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

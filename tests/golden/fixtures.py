@@ -1,0 +1,38 @@
+"""Readers for the hand-derived fixture files in this folder (citations are in
+each file's header)."""
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _lines(name):
+    with open(os.path.join(HERE, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                yield [p.strip() for p in line.split("|")]
+
+
+def _codes(text):
+    out = []
+    for part in text.split(","):
+        part = part.strip()
+        if "x" in part:
+            n, c = part.split("x")
+            out += [int(c)] * int(n)
+        else:
+            out.append(int(part))
+    return out
+
+
+def byte_vectors(name):
+    """[(codes list, bytes)] from int3_byte_vectors.txt / int4_byte_vectors.txt."""
+    return [(_codes(c), bytes.fromhex(b)) for c, b in _lines(name)]
+
+
+def gemv_closed_forms():
+    return {name: (int(K), float(y)) for name, K, y in _lines("gemv_closed_forms.txt")}
+
+
+def tiny_moe():
+    return {k: v for k, v in _lines("tiny_moe.txt")}

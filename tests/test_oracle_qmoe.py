@@ -1,0 +1,148 @@
+"""Pins of the oracle's routing and INT3 QMoE layer (CPU only).
+
+Sources: onnxruntime PR "INT3 QMoE CUDA correctness baseline and Qwen
+experimental results" (embedded P0/P1 body: sections "P0" for the format and
+the tiny predetermined-route SwiGLU MoE, "P1" for fused interleaved gate/up
+and swiglu; embedded Olive body for the (code - 4) * scale decode) and the
+pegainfer PR "component kernels extracted from the brick PRs" (fp32 softmax,
+top-k, renormalized routing weights).
+"""
+import numpy as np
+import pytest
+
+import synth
+from tests.golden import fixtures
+from tests.np_brute import qmoe_all_experts, softmax
+
+
+def _const_rows(code, rows, K):
+    """Rows of K identical INT3 codes, built from the hand-derived byte
+    vectors (64 x code c) of int3_byte_vectors.txt."""
+    vecs = {tuple(c): b for c, b in fixtures.byte_vectors("int3_byte_vectors.txt")}
+    row = np.frombuffer(vecs[tuple([code] * 64)], np.uint8)
+    assert K % 64 == 0
+    return np.tile(row, (rows, K // 64))
+
+
+def test_worked_tiny_moe(orc):
+    f = fixtures.tiny_moe()
+    H = I = 64
+    E, k, bs = 4, 2, 64
+    fc1 = [int(c) for c in f["fc1_codes"].split(",")]
+    fc2 = [int(c) for c in f["fc2_codes"].split(",")]
+    W1 = np.stack([_const_rows(fc1[e], 2 * I, H) for e in range(E)])
+    W2 = np.stack([_const_rows(fc2[e], H, I) for e in range(E)])
+    s = np.float16(float(f["scale"]))
+    s1 = np.full((E, 2 * I, H // bs), s, np.float16)
+    s2 = np.full((E, H, I // bs), s, np.float16)
+    x = np.ones((2, H), np.float16)
+    logits = np.array([[float(v) for v in f["logits_t0"].split(",")],
+                       [float(v) for v in f["logits_t1"].split(",")]], np.float32)
+    o = orc.qmoe(x, logits, W1, s1, W2, s2, k=k, bs=bs)
+    assert o["ids"][0].tolist() == [int(v) for v in f["ids_t0"].split(",")]
+    assert o["ids"][1].tolist() == [int(v) for v in f["ids_t1"].split(",")]
+    np.testing.assert_allclose(o["r"][0], [float(v) for v in f["r_t0"].split(",")], rtol=0, atol=1e-7)
+    np.testing.assert_allclose(o["out64"][0], float(f["out_t0"]), rtol=0, atol=1e-7)
+    assert (o["out16"][0] == int(f["out16_t0"], 16)).all()
+    assert (o["out64"][1] == 0.0).all() and (o["out16"][1] == 0).all()
+    # stage values: expert 0 has g = u = 1, expert 1 has g = u = -1
+    np.testing.assert_allclose(o["g"][0, 0], 1.0, atol=1e-12)
+    np.testing.assert_allclose(o["u"][0, 1], -1.0, atol=1e-12)
+    np.testing.assert_allclose(o["h"][0, 1], 1.0 / (1.0 + np.e), atol=1e-12)
+
+
+def test_route_against_numpy_and_full_softmax(orc):
+    T, E = 64, 16
+    logits = synth.router_logits(5, T, E)
+    for k in (1, 2, 8, E):
+        ids, w = orc.route(logits, k)
+        ref = np.argsort(-logits, axis=1, kind="stable")[:, :k]
+        assert np.array_equal(ids, ref)
+        p = softmax(logits)
+        sel = np.take_along_axis(p, ref, axis=1)
+        np.testing.assert_allclose(w, sel / sel.sum(axis=1, keepdims=True), rtol=1e-13)
+        if k == E:
+            # with k = E the renormalized weights are the full softmax
+            np.testing.assert_allclose(np.take_along_axis(p, ids, axis=1), w, rtol=1e-13)
+        assert np.all(np.diff(w, axis=1) <= 0)
+
+
+def test_route_ties_go_to_lower_index(orc):
+    logits = np.array([[0.5, 1.0, 1.0, 0.25, 1.0, -2.0]], np.float32)
+    ids, w = orc.route(logits, 3)
+    assert ids[0].tolist() == [1, 2, 4]
+    np.testing.assert_allclose(w[0], [1 / 3] * 3, rtol=1e-15)
+
+
+def _random_moe(seed, T, H, I, E, bs):
+    x = synth.activations_f16(seed, T, H)
+    logits = synth.router_logits(seed + 1, T, E)
+    W1 = synth.int3_rows(seed + 2, E * 2 * I, H).reshape(E, 2 * I, -1)
+    s1 = synth.scales_f16(seed + 3, (E, 2 * I, H // bs))
+    W2 = synth.int3_rows(seed + 4, E * H, I).reshape(E, H, -1)
+    s2 = synth.scales_f16(seed + 5, (E, H, I // bs))
+    return x, logits, W1, s1, W2, s2
+
+
+@pytest.mark.parametrize("T,H,I,E,k,bs", [(5, 64, 64, 4, 2, 64), (3, 128, 64, 8, 3, 32),
+                                          (8, 64, 128, 6, 6, 64), (1, 128, 128, 5, 1, 128)])
+def test_qmoe_brute_force_over_all_experts(orc, T, H, I, E, k, bs):
+    x, logits, W1, s1, W2, s2 = _random_moe(T * 100 + E, T, H, I, E, bs)
+    o = orc.qmoe(x, logits, W1, s1, W2, s2, k=k, bs=bs)
+    ref, order, rw = qmoe_all_experts(x, logits, W1, s1, W2, s2, k, bs)
+    assert np.array_equal(o["ids"], order)
+    np.testing.assert_allclose(o["r"], rw, rtol=1e-12)
+    scale = np.abs(ref).max() + 1e-300
+    np.testing.assert_allclose(o["out64"], ref, rtol=1e-10, atol=1e-12 * scale)
+    assert np.array_equal(o["out16"], orc.f64_to_f16(o["out64"]))
+    # the combine is the route-weighted sum of per-expert FC2 outputs
+    y, yS = orc.qmoe_fc2(o["ids"], o["h"], W2, s2, H, I, E, bs=bs)
+    np.testing.assert_allclose((o["r"][:, :, None] * y).sum(axis=1), o["out64"], rtol=1e-12,
+                               atol=1e-14 * scale)
+
+
+def test_qmoe_invariants(orc):
+    T, H, I, E, k, bs = 6, 64, 64, 8, 3, 64
+    x, logits, W1, s1, W2, s2 = _random_moe(901, T, H, I, E, bs)
+    base = orc.qmoe(x, logits, W1, s1, W2, s2, k=k, bs=bs)
+    # permuting tokens permutes the outputs
+    perm = np.array([3, 0, 5, 1, 4, 2])
+    o = orc.qmoe(x[perm], logits[perm], W1, s1, W2, s2, k=k, bs=bs)
+    assert np.array_equal(o["out64"], base["out64"][perm])
+    # relabelling experts together with the logit columns changes nothing
+    rel = np.array([2, 7, 0, 1, 6, 3, 5, 4])
+    o = orc.qmoe(x, logits[:, rel], W1[rel], s1[rel], W2[rel], s2[rel], k=k, bs=bs)
+    assert np.array_equal(o["out64"], base["out64"])
+    # T tokens at once equal T single-token calls
+    for t in range(T):
+        o = orc.qmoe(x[t:t + 1], logits[t:t + 1], W1, s1, W2, s2, k=k, bs=bs)
+        assert np.array_equal(o["out64"][0], base["out64"][t])
+    # all codes equal to the zero point 4 give exactly zero
+    z1 = _const_rows(4, E * 2 * I, H).reshape(E, 2 * I, -1)
+    z2 = _const_rows(4, E * H, I).reshape(E, H, -1)
+    o = orc.qmoe(x, logits, z1, s1, z2, s2, k=k, bs=bs)
+    assert (o["out64"] == 0).all() and (o["S"] == 0).all()
+
+
+def test_qmoe_tolerance_sum_covers_fp16_rounding_chain(orc):
+    """An fp16/fp32 emulation of the GPU rounding chain (weights and h in fp16,
+    fp32 accumulation) must land inside 4e-3 * S + half an fp16 ulp."""
+    T, H, I, E, k, bs = 4, 128, 64, 4, 2, 64
+    x, logits, W1, s1, W2, s2 = _random_moe(555, T, H, I, E, bs)
+    o = orc.qmoe(x, logits, W1, s1, W2, s2, k=k, bs=bs)
+    from tests.np_brute import int3_weights
+    w1 = int3_weights(W1, s1, H, bs).astype(np.float16).astype(np.float32)
+    w2 = int3_weights(W2, s2, I, bs).astype(np.float16).astype(np.float32)
+    out = np.zeros((T, H), np.float32)
+    for t in range(T):
+        for j in range(k):
+            e = o["ids"][t, j]
+            G = x[t].astype(np.float32) @ w1[e, 0::2].T
+            U = x[t].astype(np.float32) @ w1[e, 1::2].T
+            h = (G / (1 + np.exp(-G)) * U).astype(np.float16).astype(np.float32)
+            out[t] += np.float32(o["r"][t, j]) * (h @ w2[e].T)
+    out16 = out.astype(np.float16).astype(np.float64)
+    ulp = np.spacing(np.abs(o["out"]).astype(np.float16)).astype(np.float64)
+    err = np.abs(out16 - o["out64"])
+    assert (err <= 4e-3 * o["S"] + 0.5 * ulp + ulp).all()
+    assert (o["S"] > 0).all()
