@@ -1,0 +1,65 @@
+// Host-side contract of the mnb library: descriptor checks, overflow-checked
+// sizes, content validation and the private prepacked layout.  Plain C++17,
+// no HIP dependency, so all of it runs (and is tested) without a GPU.
+#pragma once
+
+#include <cstdint>
+
+#include "../../include/mnb.h"
+
+namespace mnb {
+
+constexpr uint32_t kPlanMagic = 0x4D4E4250u;  // "MNBP"
+// Version of the private prepacked layout (bumped whenever it changes):
+//  dense INT4: codes [N][nb][bs/2] with every nibble stored as (q - 8) in
+//              4-bit two's complement (byte XOR 0x88) and pad nibbles zero;
+//              scales fp32 [N][nb]; zero points (if explicit) as uint32 words
+//              [ceil(N/8)][nb], nibble r of word (g, b) holding the zero point
+//              of row 8g + r, block b (one load gives a row group's points).
+//  INT3 QMoE:  codes [E*N][3K/8] row-local LSB-first (unchanged);
+//              scales fp16 [E*N][K/bs].
+constexpr uint32_t kLayoutVersion = 2;
+constexpr uint64_t kSectionAlign = 256;
+
+enum Kind : int32_t { kDenseInt4 = 1, kMoeInt3 = 2 };
+
+struct Sizes {
+  Kind kind;
+  int64_t E, N, K, nb, bs, bits;
+  int64_t rows;         // E * N
+  int64_t row_bytes;    // contract bytes per B row
+  uint64_t codes;       // contract (= prepacked) code bytes
+  uint64_t scales;      // scale bytes
+  uint64_t zeros;       // prepacked zero-point bytes (0 if implicit)
+  uint64_t zrow;        // contract zero-point bytes per row (ceil(nb/2))
+  uint64_t off_scales;  // offsets of the sections in the prepacked buffer
+  uint64_t off_zeros;
+  uint64_t total;       // prepacked bytes
+};
+
+// Checks a descriptor and fills every size with overflow-checked arithmetic.
+int32_t check_desc(const mnb_desc* d, Sizes* s);
+
+// Validates the host content of the weights (INT3: finite nonnegative fp16
+// scales and canonical row padding).  Dense INT4 content is not checked.
+int32_t validate_content(const mnb_desc* d, const Sizes& s, const uint8_t* B,
+                         const void* scales, const uint8_t* zp);
+
+// Writes the private layout (s.total bytes) into dst.
+void prepack(const Sizes& s, const uint8_t* B, const void* scales,
+             const uint8_t* zp, uint8_t* dst);
+
+// Fills a plan whose sections start at base (host or device address).
+void fill_plan(const mnb_desc* d, const Sizes& s, void* base, int32_t device,
+               mnb_plan* plan);
+
+// Checks that a plan was produced by this library and rebuilds its sizes.
+int32_t check_plan(const mnb_plan* p, Sizes* s);
+
+// Reads logical codes / zero points / scales back from a host-resident
+// prepacked layout.
+void unpack_host(const Sizes& s, const mnb_plan* p, int64_t expert,
+                 int64_t row0, int64_t nrows, uint8_t* codes, uint8_t* zeros,
+                 void* scales);
+
+}  // namespace mnb

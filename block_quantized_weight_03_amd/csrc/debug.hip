@@ -1,0 +1,105 @@
+// Test-only readers of the prepared device layout: logical codes and the
+// fp16 dequantized weights of the matrix-core paths.  They let the tests
+// check the prepacked bytes and the rounding chain bit-exactly against the
+// oracle (onnxruntime PR "INT3 QMoE CUDA correctness baseline and Qwen
+// experimental results", embedded P0/P1 body, section "P0: Portable Format
+// and Numerical References": row-local LSB-first codes; INT3 decodes as
+// (code - 4) * scale).
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace mnb {
+namespace {
+
+struct Rows {
+  const uint8_t* codes;
+  const void* scales;
+  const uint8_t* zeros;
+  int64_t K, nb, bs, row_bytes, zrow, row_base;  // row_base = expert * N + row0
+  int kind;
+};
+
+__device__ __forceinline__ unsigned code_of(const Rows& r, int64_t row, int64_t k) {
+  const uint8_t* src = r.codes + row * r.row_bytes;
+  if (r.kind == kDenseInt4) {
+    const int64_t b = k / r.bs, j = k % r.bs;
+    const uint8_t byte = src[b * (r.bs / 2) + j / 2];
+    return (((j & 1) ? (byte >> 4) : byte) & 15u) ^ 8u;
+  }
+  unsigned q = 0;
+  for (int t = 0; t < 3; ++t) {
+    const int64_t bit = 3 * k + t;
+    q |= ((src[bit >> 3] >> (bit & 7)) & 1u) << t;
+  }
+  return q;
+}
+
+__global__ void debug_unpack_kernel(Rows r, int64_t nrows, uint8_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nrows * r.K) return;
+  const int64_t row = i / r.K, k = i % r.K;
+  out[i] = (uint8_t)code_of(r, r.row_base + row, k);
+}
+
+__global__ void debug_dequant_kernel(Rows r, int64_t nrows, __half* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nrows * r.K) return;
+  const int64_t row = i / r.K, k = i % r.K;
+  const int64_t grow = r.row_base + row;
+  const unsigned q = code_of(r, grow, k);
+  const int64_t b = k / r.bs;
+  float v;
+  if (r.kind == kDenseInt4) {
+    unsigned z = 8;
+    if (r.zeros) {
+      const uint32_t w = reinterpret_cast<const uint32_t*>(r.zeros)[(grow / 8) * r.nb + b];
+      z = (w >> (4 * (grow % 8))) & 15u;
+    }
+    const float s = static_cast<const float*>(r.scales)[grow * r.nb + b];
+    v = (float)((int)q - (int)z) * s;  // fp32 product, then one fp16 rounding
+  } else {
+    const __half s = static_cast<const __half*>(r.scales)[grow * r.nb + b];
+    v = (float)((int)q - 4) * __half2float(s);  // exact in fp32
+  }
+  out[i] = __float2half_rn(v);
+}
+
+Rows make_rows(const Sizes& s, const mnb_plan& p, int64_t expert, int64_t row0) {
+  Rows r;
+  r.codes = static_cast<const uint8_t*>(p.codes);
+  r.scales = p.scales;
+  r.zeros = static_cast<const uint8_t*>(p.zeros);
+  r.K = s.K;
+  r.nb = s.nb;
+  r.bs = s.bs;
+  r.row_bytes = s.row_bytes;
+  r.zrow = (int64_t)s.zrow;
+  r.row_base = expert * s.N + row0;
+  r.kind = s.kind;
+  return r;
+}
+
+}  // namespace
+
+hipError_t launch_debug_unpack(const Sizes& s, const mnb_plan& p, int64_t expert, int64_t row0,
+                               int64_t nrows, uint8_t* codes, hipStream_t st) {
+  const int64_t n = nrows * s.K;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(debug_unpack_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     make_rows(s, p, expert, row0), nrows, codes);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_dequant_f16(const Sizes& s, const mnb_plan& p, int64_t expert,
+                                    int64_t row0, int64_t nrows, uint16_t* out, hipStream_t st) {
+  const int64_t n = nrows * s.K;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(debug_dequant_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     make_rows(s, p, expert, row0), nrows, reinterpret_cast<__half*>(out));
+  return hipGetLastError();
+}
+
+}  // namespace mnb

@@ -1,0 +1,462 @@
+// M = 1 decode GEMV on packed INT4 weights for gfx950.
+//
+// Operation ("Qwen3 Missing-Kernel Implementation Plan", section "PR
+// sequence", steps K01/K02):
+//   y[n] = sum_{k<K} a[k] * (q[n,k] - z[n,b]) * s[n,b],  b = k / bs,
+// with scales and zero points applied while the packed panel streams by and
+// the float weight matrix never formed.
+//
+// Why integer dot products.  At 8 TB/s an MI355X receives 16e12 INT4 codes
+// per second, while its integer VALU issues about 39e12 lane-ops per second,
+// so a convert + subtract + FMA per code would make the kernel ALU-bound.
+// Instead, the prepared weights store every code as (q - 8) in 4-bit two's
+// complement, and each 32-element sub-block of a is put in block fixed point:
+//   a[k] * 2^e = a_int[k] = sum_{p<8} d[k,p] * 16^p,  d in [-8, 7],
+// with e chosen per sub-block so that max|a| * 2^e < 2^30 (so a_int is exact
+// to 2^-31 of the sub-block maximum).  Then
+//   sum_k (q-8) a_int = sum_p 16^p * dot8(q - 8, d[., p])
+// where dot8 is one v_dot8c_i32_i4 over 8 packed nibbles: the raw 16-byte
+// load of 32 codes feeds the dot products directly, with no unpacking.
+// Explicit zero points add (8 - z) * sum_k a_int per sub-block, from digit
+// sums computed with the digits.  The integer part is exact; the rest is a
+// few fp32 roundings per 32 codes, so the exact special cases stay exact
+// (integer inputs; all codes equal to the zero point give exactly 0).
+//
+// Work mapping.  A K-chunk is 64 sub-blocks (2048 codes).  Lane l of a wave
+// owns sub-block 64c + l of chunk c and keeps that chunk's 32 digit words in
+// registers; the wave walks R rows at a time with one 16-byte coalesced load
+// per lane and row (1 KiB per wave), one scale and optionally one zero-point
+// byte.  When K spans several chunks (up to 4, K <= 8192), the waves of a
+// team each own one chunk and combine in LDS in a fixed order.  The digits
+// are computed inside the kernel by the whole workgroup (so one launch does
+// the whole GEMV), while the first rows' loads are already in flight.  For
+// K > 8192 a separate pre-pass writes the digits to the workspace and each
+// wave reloads them per chunk.  Row partials are reduced across the wave
+// through LDS in a fixed order: the result is deterministic.
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+
+#include "kernels.h"
+
+namespace mnb {
+namespace {
+
+constexpr int kDig = 8;            // balanced base-16 digits per element
+constexpr int kBadExp = INT_MIN;   // marks a sub-block holding NaN/Inf
+constexpr int kMaxTeam = 4;        // chunks held in registers by one team
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// ---- digit planes of a (shared by the in-kernel prologue and the pre-pass) --
+
+// Converts quarter w (8 elements) of sub-block sb.  The 4 quarters of one
+// sub-block must sit in 4 consecutive lanes of one wave (they share a max).
+// Writes plane words to dig[((c*kDig + p)*4 + w)*64 + l] (c = sb/64, l = sb%64),
+// digit sums to sums[(c*4 + j)*64 + l] and -e to nexp[c*64 + l].
+__device__ __forceinline__ void make_digits(const float* __restrict__ A, int64_t K, int64_t sb,
+                                            int w, uint32_t* dig, int32_t* sums,
+                                            int32_t* nexp) {
+  float v[8];
+  const int64_t k0 = sb * 32 + w * 8;
+  float m = 0.0f;
+  int bad = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = (k0 + i < K) ? A[k0 + i] : 0.0f;
+    bad |= !isfinite(v[i]);
+    m = fmaxf(m, fabsf(v[i]));
+  }
+  m = fmaxf(m, __shfl_xor(m, 1, 4));
+  m = fmaxf(m, __shfl_xor(m, 2, 4));
+  bad |= __shfl_xor(bad, 1, 4);
+  bad |= __shfl_xor(bad, 2, 4);
+  int e = 0;
+  if (!bad && m > 0.0f) {
+    int E;
+    frexpf(m, &E);  // m < 2^E
+    e = 30 - E;     // max|a| * 2^e < 2^30
+  }
+  uint32_t u[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float sv = bad ? 0.0f : ldexpf(v[i], e);  // exact power-of-two scaling
+    const int32_t ai = (int32_t)rintf(sv);          // |ai| <= 2^30
+    // adding 8 to every nibble position makes nibble p of u equal d_p + 8
+    u[i] = (uint32_t)ai + 0x88888888u;
+  }
+  const int64_t c = sb >> 6;
+  const int l = (int)(sb & 63);
+  int32_t sd[kDig];
+#pragma unroll
+  for (int p = 0; p < kDig; ++p) {
+    uint32_t d = 0;
+    int32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t nib = (u[i] >> (4 * p)) & 15u;
+      d |= nib << (4 * i);
+      s += (int32_t)nib - 8;
+    }
+    // d_p in 4-bit two's complement is nib ^ 8
+    dig[((c * kDig + p) * 4 + w) * 64 + l] = d ^ 0x88888888u;
+    sd[p] = s;
+  }
+#pragma unroll
+  for (int p = 0; p < kDig; ++p) {
+    sd[p] += __shfl_xor(sd[p], 1, 4);
+    sd[p] += __shfl_xor(sd[p], 2, 4);
+  }
+  if (w == 0) {
+#pragma unroll
+    for (int j = 0; j < kDig / 2; ++j) sums[(c * (kDig / 2) + j) * 64 + l] = sd[2 * j] + 16 * sd[2 * j + 1];
+    nexp[c * 64 + l] = bad ? kBadExp : -e;
+  }
+}
+
+__global__ void __launch_bounds__(256) gemv_prep_a(const float* __restrict__ A, int64_t K,
+                                                   int64_t nsb_pad, uint32_t* __restrict__ dig,
+                                                   int32_t* __restrict__ sums,
+                                                   int32_t* __restrict__ nexp) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if ((t >> 2) >= nsb_pad) return;  // whole groups of 4 lanes leave together
+  make_digits(A, K, t >> 2, (int)(t & 3), dig, sums, nexp);
+}
+
+struct Digits {
+  uint32_t d[kDig][4];
+  int32_t se[kDig / 2];
+  int32_t ne;
+  float poison;
+};
+
+template <class P>
+__device__ __forceinline__ void load_digits(Digits& g, const P* dig, const int32_t* sums,
+                                            const int32_t* nexp, int64_t c, int lane) {
+#pragma unroll
+  for (int p = 0; p < kDig; ++p)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) g.d[p][w] = dig[((c * kDig + p) * 4 + w) * 64 + lane];
+#pragma unroll
+  for (int j = 0; j < kDig / 2; ++j) g.se[j] = sums[(c * (kDig / 2) + j) * 64 + lane];
+  const int32_t ne = nexp[c * 64 + lane];
+  g.poison = ne == kBadExp ? __builtin_nanf("") : 0.0f;
+  g.ne = ne == kBadExp ? 0 : ne;
+}
+
+// Partial of one 32-code sub-block: sum_k (q_k - z) * a_k * s (fp32).
+template <bool HAS_ZP>
+__device__ __forceinline__ float subblock_dot(const u32x4 q, const Digits& g, float s, int z) {
+  int D[kDig];
+#pragma unroll
+  for (int p = 0; p < kDig; ++p) {
+    int acc = __builtin_amdgcn_sdot8((int)q.x, (int)g.d[p][0], 0, false);
+    acc = __builtin_amdgcn_sdot8((int)q.y, (int)g.d[p][1], acc, false);
+    acc = __builtin_amdgcn_sdot8((int)q.z, (int)g.d[p][2], acc, false);
+    acc = __builtin_amdgcn_sdot8((int)q.w, (int)g.d[p][3], acc, false);
+    D[p] = acc;  // |D| <= 32 * 8 * 8
+  }
+  int E0 = D[0] + 16 * D[1], E1 = D[2] + 16 * D[3];
+  int E2 = D[4] + 16 * D[5], E3 = D[6] + 16 * D[7];
+  if (HAS_ZP) {
+    // |8 - z| <= 8 and |digit sums| < 2^13: 24-bit multiplies are exact
+    const int zc = 8 - z;
+    E0 = __mul24(zc, g.se[0]) + E0;
+    E1 = __mul24(zc, g.se[1]) + E1;
+    E2 = __mul24(zc, g.se[2]) + E2;
+    E3 = __mul24(zc, g.se[3]) + E3;
+  }
+  const int F0 = E0 + 256 * E1;  // |E| < 2^16 so |F| < 2^25
+  const int F1 = E2 + 256 * E3;
+  const float f = fmaf((float)F1, 65536.0f, (float)F0);
+  return ldexpf(f * s, g.ne) + g.poison;
+}
+
+template <int R, bool HAS_ZP>
+struct RowTile {
+  u32x4 q[R];
+  float s[R];
+  uint32_t zpk;  // zero point of row r in bits [4r, 4r+4) (R <= 8)
+};
+
+// Loads R rows starting at row n0 for sub-block sb (lane-local).  Rows past N
+// and lanes past the last sub-block load nothing.
+template <int R, bool HAS_ZP>
+__device__ __forceinline__ void load_rows(RowTile<R, HAS_ZP>& t, const uint8_t* __restrict__ codes,
+                                          const float* __restrict__ scales,
+                                          const uint32_t* __restrict__ zeros, int64_t n0, int64_t N,
+                                          int64_t row_bytes, int64_t nb, int64_t zrow, uint32_t qoff,
+                                          uint32_t b, bool act) {
+  t.zpk = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    t.q[r] = u32x4{0, 0, 0, 0};
+    t.s[r] = 0.0f;
+    const int64_t n = n0 + r;
+    if (n < N) {  // wave-uniform
+      const uint8_t* row = codes + n * row_bytes;
+      const float* srow = scales + n * nb;
+      if (act) {
+        // streamed once: nontemporal loads keep them from displacing reused data
+        t.q[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + qoff));
+        t.s[r] = __builtin_nontemporal_load(srow + b);
+      }
+    }
+  }
+  // one word holds the zero points of the 8-row group containing these rows
+  // (R divides 8 and n0 is a multiple of R); it is only shifted at compute time
+  if (HAS_ZP && act && n0 < N)
+    t.zpk = __builtin_nontemporal_load(zeros + (n0 >> 3) * nb + b) >> (4 * (n0 & 7));
+}
+
+// Reduces part[r] over the 64 lanes of the wave in a fixed order and returns,
+// in lane r*(64/R) for each r < R, the total of row r (other lanes: garbage).
+template <int R>
+__device__ __forceinline__ float wave_reduce_rows(float (&part)[R], float* __restrict__ red,
+                                                  int lane) {
+  constexpr int P = 64 / R;  // lanes that share one row after the transpose
+#pragma unroll
+  for (int r = 0; r < R; ++r) red[r * 64 + lane] = part[r];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int r = lane / P, j = lane % P;
+  float acc = 0.0f;
+  const float* src = red + r * 64 + j * R;
+#pragma unroll
+  for (int i = 0; i < R; ++i) acc += src[i];
+#pragma unroll
+  for (int m = P / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, P);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();  // red is reused by the next iteration
+  return acc;
+}
+
+template <int R>
+constexpr int lds_red_floats() {
+  return kMaxTeam * R * 64 + kMaxTeam * R;
+}
+
+// Fused kernel: in-kernel digits, K <= 8192 (team = nchunk waves, one chunk each).
+template <int R, bool HAS_ZP>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) gemv_int4_fused(
+    const float* __restrict__ A, const uint8_t* __restrict__ codes,
+    const float* __restrict__ scales, const uint32_t* __restrict__ zeros, float* __restrict__ Y,
+    int64_t K, int64_t N, int64_t row_bytes, int64_t nb, int32_t nsb, int32_t nchunk,
+    int32_t bs_shift, int64_t zrow) {
+  extern __shared__ __align__(16) uint32_t smem[];
+  float* red_all = reinterpret_cast<float*>(smem);          // [4 waves][R][64]
+  float* tot = red_all + kMaxTeam * R * 64;                  // [4 waves][R]
+  uint32_t* dig = smem + lds_red_floats<R>();                // [nchunk][8][4][64]
+  int32_t* sums = reinterpret_cast<int32_t*>(dig + nchunk * kDig * 4 * 64);  // [nchunk][4][64]
+  int32_t* nexp = sums + nchunk * (kDig / 2) * 64;           // [nchunk][64]
+
+  const int team = nchunk;
+  const int nwaves = (int)(blockDim.x >> 6);
+  const int teams = nwaves / team;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = (int)(threadIdx.x & 63);
+  const int tm = wave / team, wit = wave - tm * team;
+
+  const int32_t sb = wit * 64 + lane;
+  const bool act = sb < nsb;
+  const uint32_t qoff = (uint32_t)sb * 16u;
+  const uint32_t b = (uint32_t)sb >> bs_shift;
+
+  const int64_t nrg = (N + R - 1) / R;
+  const int64_t stride = (int64_t)gridDim.x * teams;
+  const int64_t base0 = (int64_t)blockIdx.x * teams;
+  const int64_t iters = base0 < nrg ? (nrg - base0 + stride - 1) / stride : 0;
+  int64_t rg = base0 + tm;
+
+  RowTile<R, HAS_ZP> t0, t1;
+  if (iters > 0) load_rows<R, HAS_ZP>(t0, codes, scales, zeros, rg * R, rg < nrg ? N : 0, row_bytes, nb, zrow, qoff, b, act);
+
+  // digits of this workgroup's chunks, computed by all threads
+  const int64_t tasks = (int64_t)nchunk * 64 * 4;
+  for (int64_t i = threadIdx.x; i < tasks; i += blockDim.x)
+    make_digits(A, K, i >> 2, (int)(i & 3), dig, sums, nexp);
+  __syncthreads();
+  Digits g;
+  load_digits(g, dig, sums, nexp, wit, lane);
+  float* red = red_all + wave * R * 64;
+
+  auto step = [&](RowTile<R, HAS_ZP>& cur, RowTile<R, HAS_ZP>& nxt, int64_t it) {
+    const int64_t rgn = rg + stride;
+    if (it + 1 < iters)
+      load_rows<R, HAS_ZP>(nxt, codes, scales, zeros, rgn * R, rgn < nrg ? N : 0, row_bytes, nb, zrow, qoff, b, act);
+    float part[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) part[r] = subblock_dot<HAS_ZP>(cur.q[r], g, cur.s[r], (int)((cur.zpk >> (4 * r)) & 15u));
+    const float v = wave_reduce_rows<R>(part, red, lane);
+    constexpr int P = 64 / R;
+    const int r = lane / P;
+    const bool leader = (lane % P) == 0;
+    const int64_t n = rg * R + r;
+    if (team == 1) {
+      if (leader && rg < nrg && n < N) Y[n] = v;
+    } else {
+      if (leader) tot[wave * R + r] = v;
+      __syncthreads();
+      if (wit == 0 && lane < R) {
+        float out = 0.0f;
+        for (int w = 0; w < team; ++w) out += tot[(tm * team + w) * R + lane];
+        const int64_t nn = rg * R + lane;
+        if (rg < nrg && nn < N) Y[nn] = out;
+      }
+      __syncthreads();
+    }
+    rg = rgn;
+  };
+
+  for (int64_t it = 0; it < iters; it += 2) {
+    step(t0, t1, it);
+    if (it + 1 < iters) step(t1, t0, it + 1);
+  }
+}
+
+// K > 8192: digits precomputed in the workspace, each wave walks its chunks.
+template <int R, bool HAS_ZP>
+__global__ void __launch_bounds__(256) gemv_int4_ws(
+    const uint8_t* __restrict__ codes, const float* __restrict__ scales,
+    const uint32_t* __restrict__ zeros, const uint32_t* __restrict__ dig,
+    const int32_t* __restrict__ sums, const int32_t* __restrict__ nexp, float* __restrict__ Y,
+    int64_t N, int64_t row_bytes, int64_t nb, int64_t nsb, int64_t nchunk, int32_t bs_shift,
+    int64_t zrow) {
+  __shared__ __align__(16) float red_all[kMaxTeam * R * 64];
+  __shared__ float tot[kMaxTeam][R];
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = (int)(threadIdx.x & 63);
+  float* red = red_all + wave * R * 64;
+  const int64_t nrg = (N + R - 1) / R;
+  Digits g;
+  for (int64_t rg = blockIdx.x; rg < nrg; rg += gridDim.x) {
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+    for (int64_t c = wave; c < nchunk; c += kMaxTeam) {
+      load_digits(g, dig, sums, nexp, c, lane);
+      const int64_t sb = c * 64 + lane;
+      const bool act = sb < nsb;
+      RowTile<R, HAS_ZP> t;
+      load_rows<R, HAS_ZP>(t, codes, scales, zeros, rg * R, N, row_bytes, nb, zrow,
+                           (uint32_t)(sb * 16), (uint32_t)(sb >> bs_shift), act);
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] += subblock_dot<HAS_ZP>(t.q[r], g, t.s[r], (int)((t.zpk >> (4 * r)) & 15u));
+    }
+    const float v = wave_reduce_rows<R>(acc, red, lane);
+    constexpr int P = 64 / R;
+    if (lane % P == 0) tot[wave][lane / P] = v;
+    __syncthreads();
+    if (wave == 0 && lane < R) {
+      const float out = ((tot[0][lane] + tot[1][lane]) + tot[2][lane]) + tot[3][lane];
+      const int64_t n = rg * R + lane;
+      if (n < N) Y[n] = out;
+    }
+    __syncthreads();
+  }
+}
+
+struct WsLayout {
+  uint64_t dig, sums, nexp, total;
+};
+
+WsLayout ws_layout(int64_t nchunk) {
+  WsLayout w;
+  w.dig = 0;
+  w.sums = align256((uint64_t)nchunk * kDig * 4 * 64 * 4);
+  w.nexp = w.sums + align256((uint64_t)nchunk * (kDig / 2) * 64 * 4);
+  w.total = w.nexp + align256((uint64_t)nchunk * 64 * 4);
+  return w;
+}
+
+int64_t n_subblocks(const Sizes& s) { return s.nb * (s.bs / 32); }
+int bs_shift_of(const Sizes& s) { return s.bs == 32 ? 0 : (s.bs == 64 ? 1 : 2); }
+
+int cu_count() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
+      cus = prop.multiProcessorCount;
+    if (cus <= 0) cus = 256;
+  }
+  return cus;
+}
+
+template <int R, bool HAS_ZP>
+hipError_t launch_fused(const Sizes& s, const mnb_plan& p, const float* A, float* Y, int64_t nsb,
+                        int64_t nchunk, hipStream_t st) {
+  const int team = (int)nchunk;
+  const int teams = kMaxTeam / team;
+  const int threads = 64 * team * teams;
+  const int64_t nrg = (s.N + R - 1) / R;
+  int64_t blocks = (nrg + teams - 1) / teams;
+  // a few resident workgroups per CU; each walks many row groups so that the
+  // digit prologue is amortised
+  const int64_t cap = (int64_t)cu_count() * 4;
+  if (blocks > cap) blocks = cap;
+  const size_t lds = (size_t)lds_red_floats<R>() * 4 + (size_t)nchunk * (kDig * 4 * 64 + (kDig / 2) * 64 + 64) * 4;
+  hipLaunchKernelGGL((gemv_int4_fused<R, HAS_ZP>), dim3((unsigned)blocks), dim3(threads), lds, st,
+                     A, static_cast<const uint8_t*>(p.codes), static_cast<const float*>(p.scales),
+                     static_cast<const uint32_t*>(p.zeros), Y, s.K, s.N, s.row_bytes, s.nb,
+                     (int32_t)nsb, (int32_t)nchunk, bs_shift_of(s), (int64_t)s.zrow);
+  return hipGetLastError();
+}
+
+template <int R, bool HAS_ZP>
+hipError_t launch_ws(const Sizes& s, const mnb_plan& p, const float* A, float* Y, void* ws,
+                     int64_t nsb, int64_t nchunk, hipStream_t st) {
+  const WsLayout L = ws_layout(nchunk);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  const int64_t threads = nchunk * 64 * 4;
+  hipLaunchKernelGGL(gemv_prep_a, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, A,
+                     s.K, nchunk * 64, reinterpret_cast<uint32_t*>(w + L.dig),
+                     reinterpret_cast<int32_t*>(w + L.sums),
+                     reinterpret_cast<int32_t*>(w + L.nexp));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t nrg = (s.N + R - 1) / R;
+  int64_t blocks = nrg;
+  const int64_t cap = (int64_t)cu_count() * 8;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL((gemv_int4_ws<R, HAS_ZP>), dim3((unsigned)blocks), dim3(256), 0, st,
+                     static_cast<const uint8_t*>(p.codes), static_cast<const float*>(p.scales),
+                     static_cast<const uint32_t*>(p.zeros),
+                     reinterpret_cast<const uint32_t*>(w + L.dig),
+                     reinterpret_cast<const int32_t*>(w + L.sums),
+                     reinterpret_cast<const int32_t*>(w + L.nexp), Y, s.N, s.row_bytes, s.nb, nsb,
+                     nchunk, bs_shift_of(s), (int64_t)s.zrow);
+  return hipGetLastError();
+}
+
+template <bool HAS_ZP>
+hipError_t dispatch(const Sizes& s, const mnb_plan& p, const float* A, float* Y, void* ws,
+                    hipStream_t st) {
+  const int64_t nsb = n_subblocks(s);
+  const int64_t nchunk = (nsb + 63) / 64;
+  if (nchunk > kMaxTeam) return launch_ws<8, HAS_ZP>(s, p, A, Y, ws, nsb, nchunk, st);
+  // rows per wave iteration: enough row groups to fill the chip for small N,
+  // deeper load batches for large N
+  const int64_t teams = kMaxTeam / nchunk;
+  const int64_t cap_groups = (int64_t)cu_count() * 4 * teams;
+  if ((s.N + 7) / 8 >= cap_groups) return launch_fused<8, HAS_ZP>(s, p, A, Y, nsb, nchunk, st);
+  if ((s.N + 3) / 4 >= cap_groups / 2) return launch_fused<4, HAS_ZP>(s, p, A, Y, nsb, nchunk, st);
+  return launch_fused<2, HAS_ZP>(s, p, A, Y, nsb, nchunk, st);
+}
+
+}  // namespace
+
+uint64_t gemv_ws_bytes(const Sizes& s) {
+  const int64_t nchunk = (n_subblocks(s) + 63) / 64;
+  return nchunk > kMaxTeam ? ws_layout(nchunk).total : 0;
+}
+
+hipError_t launch_gemv(const Sizes& s, const mnb_plan& p, const float* A, float* Y, void* ws,
+                       hipStream_t st) {
+  return s.zeros ? dispatch<true>(s, p, A, Y, ws, st) : dispatch<false>(s, p, A, Y, ws, st);
+}
+
+}  // namespace mnb

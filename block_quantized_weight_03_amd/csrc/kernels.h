@@ -1,0 +1,44 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "contract.h"
+
+namespace mnb {
+
+// ---- M = 1 GEMV on dense INT4 plans (gemv.hip) ----------------------------
+uint64_t gemv_ws_bytes(const Sizes& s);
+hipError_t launch_gemv(const Sizes& s, const mnb_plan& p, const float* A, float* Y,
+                       void* ws, hipStream_t st);
+
+// ---- small-M / prefill GEMM on dense INT4 plans (gemm.hip) ----------------
+uint64_t gemm_ws_bytes(const Sizes& s, int64_t M);
+hipError_t launch_gemm(const Sizes& s, const mnb_plan& p, int64_t M, const float* A,
+                       float* Y, void* ws, hipStream_t st);
+
+// ---- INT3 QMoE (qmoe.hip) -------------------------------------------------
+struct QmoeDebug {
+  int32_t* ids;
+  float* w;
+  uint16_t* h;
+  float* slot;
+};
+uint64_t qmoe_ws_bytes(const Sizes& s1, const Sizes& s2, int top_k, int64_t T);
+hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2,
+                       const mnb_plan& p2, int top_k, int64_t T, const uint16_t* x,
+                       const float* logits, uint16_t* out, void* ws, hipStream_t st,
+                       const QmoeDebug* dbg);
+
+// ---- test-only readers of the device layout (debug.hip) --------------------
+hipError_t launch_debug_unpack(const Sizes& s, const mnb_plan& p, int64_t expert,
+                               int64_t row0, int64_t nrows, uint8_t* codes, hipStream_t st);
+hipError_t launch_debug_dequant_f16(const Sizes& s, const mnb_plan& p, int64_t expert,
+                                    int64_t row0, int64_t nrows, uint16_t* out,
+                                    hipStream_t st);
+
+inline uint64_t align256(uint64_t v) { return (v + 255) / 256 * 256; }
+
+}  // namespace mnb

@@ -1,0 +1,229 @@
+/*
+ * mnb.h -- C ABI of the block-quantized weight-only matmul library for AMD
+ * Instinct MI355X (gfx950): MatMulNBits GEMV / GEMM on packed INT4 weights and
+ * a top-k routed INT3 QMoE layer.
+ *
+ * Sources (page title, then section):
+ *  [PLAN]  "Qwen3 Missing-Kernel Implementation Plan" (onnx-light CPU docs),
+ *          section "PR sequence": K01 defines the MatMulNBits contract (FP32 A,
+ *          UINT8 packed B, FP32 scales; bits=4, block_size=32,
+ *          accuracy_level=4; implicit zero points; scale indexing; padding;
+ *          prepared storage that reuses constant packed weights; explicit
+ *          rejection of unsupported variants without expanding the weight
+ *          matrix).  K02 is the M=1 decode GEMV (including the vocabulary
+ *          head), K03 the small-M/prefill GEMM on the same compressed weights
+ *          with a bounded workspace.  Section "Common implementation and
+ *          performance gates": unsupported variants never silently run
+ *          another kernel.
+ *  [P0]    onnxruntime PR "INT3 QMoE CUDA correctness baseline and Qwen
+ *          experimental results", embedded body of the stacked P0/P1 PR,
+ *          section "P0: Portable Format and Numerical References": row-local
+ *          LSB-first UINT8 packing, checked size arithmetic, canonical
+ *          padding, INT3 offset-4 decoding.
+ *  [P1]    same body, section "P1: Compatible QMoE v1 Extension": INT3 QMoE
+ *          profile (quant_type int, weights_prepacked 0, activation swiglu,
+ *          fused interleaved gate/up, block sizes 32/64/128, block-aligned K,
+ *          FP16 activations with FP16 scales, H from the activations, I from
+ *          the fused FC1 rows; finite nonnegative scales; overflow-checked
+ *          byte counts).  Sections "Latest Review Fixes" (N need not be
+ *          aligned) and "Review Fixes and Padding Experiment Follow-up"
+ *          (errors are status codes, no exceptions).
+ *  [RUN]   same page, PR summary: CUDA QMoE execution with routing, fused
+ *          gate/up SwiGLU, independent down projection, aggregation and
+ *          bounded activation tiling, without materializing floating weights.
+ *  [ROUTE] pegainfer PR "feat(qwen4): component kernels extracted from the
+ *          brick PRs", section "Description": fp32 softmax, top-k,
+ *          renormalized (norm_topk_prob) routing weights; branch combine.
+ *
+ * Conventions shared by every entry point
+ *  - Return value: MNB_OK (0) or a negative mnb_status.  Nothing is thrown
+ *    across the ABI.  Argument, descriptor and plan checks run on the host
+ *    before any launch; a failed check launches nothing and writes nothing.
+ *  - Device pointers ("_dev") are caller-owned device memory on the device
+ *    that was current when the plan was prepared.  The library never
+ *    allocates device memory and keeps no state between calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every compute call only enqueues work on `stream` and returns; only
+ *    mnb_prepare waits (for its own upload).
+ *  - Sizes are bytes (uint64_t); shapes are element counts (int64_t) and are
+ *    overflow-checked.
+ */
+#ifndef MNB_H
+#define MNB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MNB_ABI_VERSION 1
+
+typedef enum mnb_status {
+  MNB_OK = 0,
+  MNB_ERR_INVALID_ARG = -1,         /* NULL pointer, bad shape or enum value   */
+  MNB_ERR_UNSUPPORTED = -2,         /* valid request outside what is built     */
+  MNB_ERR_SIZE_OVERFLOW = -3,       /* a byte count does not fit 64 bits      */
+  MNB_ERR_CONTENT = -4,             /* malformed weight content [P1]           */
+  MNB_ERR_WORKSPACE_TOO_SMALL = -5, /* ws or dst smaller than required         */
+  MNB_ERR_DEVICE = -6,              /* a HIP call or kernel launch failed      */
+  MNB_ERR_STALE_PLAN = -7,          /* plan not made by this library version   */
+  MNB_ERR_HOST_MEMORY = -8          /* host staging allocation failed          */
+} mnb_status;
+
+enum { MNB_DTYPE_F32 = 0, MNB_DTYPE_F16 = 1 };
+
+/* Row layouts of B.  BLOCKED: each row is ceil(K/bs) blocks of bs*bits/8
+ * bytes, the K tail padded to a whole block [PLAN K01].  ROW_LOCAL: each row
+ * is one LSB-first bit stream of ceil(K*bits/8) bytes [P0].  The two are
+ * byte-identical when K is a multiple of the block size. */
+enum { MNB_ROWS_BLOCKED = 0, MNB_ROWS_ROW_LOCAL = 1 };
+
+/* Weight descriptor.  Supported profiles (anything else: UNSUPPORTED):
+ *  dense MatMulNBits [PLAN K01]: bits 4, block_size 32/64/128, scale_dtype
+ *    F32, row_layout BLOCKED, num_experts 1, zero points optional, any
+ *    K >= 1 and N >= 1;
+ *  QMoE projection [P1]: bits 3, block_size 32/64/128, scale_dtype F16,
+ *    row_layout ROW_LOCAL, num_experts >= 1, no explicit zero points,
+ *    K a multiple of block_size, any N >= 1 (per-expert matrix [N, K]).
+ * accuracy_level must be 0..4; it is recorded, and the numerics are fixed by
+ * the kernels (fp32 GEMV, fp16-input MFMA GEMM with fp32 accumulation). */
+typedef struct mnb_desc {
+  int32_t abi_version;     /* MNB_ABI_VERSION                               */
+  int32_t bits;            /* 4 (dense) or 3 (QMoE)                          */
+  int32_t block_size;      /* codes per scale along K: 32, 64 or 128         */
+  int32_t accuracy_level;  /* 0..4                                            */
+  int64_t K;               /* reduction length (columns of the logical W)    */
+  int64_t N;               /* output features (rows of W, per expert)        */
+  int32_t scale_dtype;     /* MNB_DTYPE_F32 (dense) / MNB_DTYPE_F16 (QMoE)   */
+  int32_t has_zero_points; /* 0 = implicit 2^(bits-1), 1 = explicit          */
+  int32_t row_layout;      /* MNB_ROWS_BLOCKED / MNB_ROWS_ROW_LOCAL          */
+  int32_t num_experts;     /* 1 for dense; E for a stacked QMoE projection   */
+} mnb_desc;
+
+/* Prepared constant weights [PLAN K01 "prepared storage", K02 "repeated
+ * calls do not repack"].  Caller-owned POD filled by mnb_prepare; read-only
+ * afterwards; valid while the dst buffer given to mnb_prepare lives; may be
+ * used concurrently from several streams. */
+typedef struct mnb_plan {
+  mnb_desc desc;
+  uint32_t magic;          /* identifies a plan made by this library        */
+  uint32_t layout_version; /* version of the private prepacked layout       */
+  int64_t n_blocks;        /* ceil(K / block_size)                          */
+  int64_t row_bytes;       /* contract bytes of one B row                   */
+  uint64_t codes_bytes;    /* prepacked codes                               */
+  uint64_t scales_bytes;   /* prepacked scales                              */
+  uint64_t zeros_bytes;    /* prepacked zero points (0 if implicit)         */
+  uint64_t total_bytes;    /* bytes of dst used (<= dst_bytes)              */
+  void* codes;             /* device pointers into dst                      */
+  void* scales;
+  void* zeros;
+  int32_t device;          /* HIP device ordinal the plan lives on          */
+  int32_t reserved;
+} mnb_plan;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* mnb_status_string(int32_t status);
+
+/* Bytes of device memory mnb_prepare needs for `desc`.  The prepacked layout
+ * holds as many code and scale bytes as the contract's B and scales; explicit
+ * zero points take 4 bytes per (group of 8 rows, block), which is no more
+ * than the contract's N * ceil(nb/2) when N is a multiple of 8; on top come
+ * at most 768 bytes of section alignment. */
+int32_t mnb_prepacked_size(const mnb_desc* desc, uint64_t* bytes);
+
+/* One-time preparation of constant weights [PLAN K01]:
+ *  1. checks the descriptor and computes every byte count with overflow
+ *     checks [P0];
+ *  2. validates content: for bits 3, scales must be finite and >= 0 and the
+ *     pad bits after K*3 in each row must be zero [P1]; dense INT4 content
+ *     is not value-checked (non-finite scales propagate to the outputs);
+ *  3. repacks on the host into the private layout and uploads it to dst_dev
+ *     with an asynchronous copy on `stream`, then waits for that stream.
+ * Host inputs (read only; any alignment):
+ *  B_host           uint8, [E*N, nb, bs*bits/8] (BLOCKED) or
+ *                   [E*N, ceil(K*bits/8)] (ROW_LOCAL), E = num_experts;
+ *  scales_host      fp32 or fp16 (per scale_dtype), [E*N, nb], index n*nb + b;
+ *  zero_points_host NULL when has_zero_points == 0, else uint8
+ *                   [N, ceil(nb/2)]: block b of row n in byte b/2, low
+ *                   nibble for even b.
+ * dst_dev must hold mnb_prepacked_size(desc) bytes and be 256-byte aligned.
+ * On success *plan describes the prepared weights; on failure *plan is
+ * zeroed.  Errors: INVALID_ARG, UNSUPPORTED, SIZE_OVERFLOW, CONTENT,
+ * WORKSPACE_TOO_SMALL (dst_bytes), HOST_MEMORY, DEVICE. */
+int32_t mnb_prepare(const mnb_desc* desc, const uint8_t* B_host,
+                    const void* scales_host, const uint8_t* zero_points_host,
+                    void* dst_dev, uint64_t dst_bytes, void* stream,
+                    mnb_plan* plan);
+
+/* Workspace bytes mnb_gemv needs for this plan (grows with K only). */
+int32_t mnb_gemv_workspace_size(const mnb_plan* plan, uint64_t* bytes);
+
+/* M = 1 decode GEMV [PLAN K02], dense INT4 plans only:
+ *   Y[n] = sum_{k<K} A[k] * (q[n,k] - z[n,k/bs]) * s[n,k/bs],  n < N.
+ * A_dev fp32 [K] (contiguous); Y_dev fp32 [N] (contiguous, written once per
+ * element, nothing else is touched); ws_dev >= mnb_gemv_workspace_size bytes,
+ * 256-byte aligned, scratch for the call (contents need not be initialised
+ * and are clobbered).  Deterministic: the same inputs give the same bits.
+ * Errors: INVALID_ARG, UNSUPPORTED (non-dense plan), STALE_PLAN,
+ * WORKSPACE_TOO_SMALL, DEVICE. */
+int32_t mnb_gemv(const mnb_plan* plan, const float* A_dev, float* Y_dev,
+                 void* ws_dev, uint64_t ws_bytes, void* stream);
+
+/* Workspace bytes mnb_gemm needs for this plan and M (may be 0). */
+int32_t mnb_gemm_workspace_size(const mnb_plan* plan, int64_t M, uint64_t* bytes);
+
+/* Small-M / prefill GEMM on the same compressed weights [PLAN K03]:
+ *   Y[m,n] = sum_{k<K} A[m,k] * (q[n,k] - z) * s,  m < M, n < N.
+ * A_dev fp32 [M, K] row-major (lda = K); Y_dev fp32 [M, N] row-major.  A and
+ * the dequantized weights are rounded to fp16 at the matrix-core inputs and
+ * accumulated in fp32.  M = 0 is a no-op.  ws_dev as for mnb_gemv (may be
+ * NULL when the required size is 0).  Errors as for mnb_gemv. */
+int32_t mnb_gemm(const mnb_plan* plan, int64_t M, const float* A_dev,
+                 float* Y_dev, void* ws_dev, uint64_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Top-k routed INT3 QMoE layer [P1][RUN][ROUTE].
+ */
+enum { QMOE_ACT_SWIGLU = 1 };
+enum { QMOE_GATE_UP_INTERLEAVED = 1 };
+enum { QMOE_QUANT_INT = 0 };
+
+typedef struct qmoe_desc {
+  int32_t abi_version;               /* MNB_ABI_VERSION                      */
+  int32_t top_k;                     /* 1..num_experts (8 for the configs)   */
+  int32_t normalize_routing_weights; /* must be 1 (renormalized top-k)       */
+  int32_t activation;                /* must be QMOE_ACT_SWIGLU              */
+  int32_t gate_up;                   /* must be QMOE_GATE_UP_INTERLEAVED     */
+  int32_t weights_prepacked;         /* must be 0                            */
+  int32_t quant_type;                /* must be QMOE_QUANT_INT               */
+  int32_t reserved;                  /* must be 0                            */
+} qmoe_desc;
+
+/* Workspace bytes for qmoe_forward with T tokens. */
+int32_t qmoe_workspace_size(const mnb_plan* fc1, const mnb_plan* fc2,
+                            const qmoe_desc* q, int64_t T, uint64_t* bytes);
+
+/* One QMoE layer on T tokens.
+ *  fc1: QMoE plan with N = 2I, K = H (rows 2i = gate_i, 2i+1 = up_i);
+ *  fc2: QMoE plan with N = H, K = I; both with the same num_experts E and
+ *       block size.
+ *  x_dev      fp16 [T, H] activations;
+ *  logits_dev fp32 [T, E] router logits;
+ *  out_dev    fp16 [T, H].
+ * Computes, per token: top_k experts by logit (ties: lower index), weights
+ * r_j = softmax over the selected logits (= fp32 softmax over all E then
+ * renormalization); h = silu(x.W1g^T) * (x.W1u^T) rounded to fp16;
+ * out = fp16(sum_j r_j * h_j.W2^T) summed in rank order.
+ * T = 0 is a no-op.  No host synchronisation (graph-capturable).
+ * Errors: INVALID_ARG, UNSUPPORTED, STALE_PLAN, WORKSPACE_TOO_SMALL, DEVICE. */
+int32_t qmoe_forward(const mnb_plan* fc1, const mnb_plan* fc2,
+                     const qmoe_desc* q, int64_t T, const uint16_t* x_dev,
+                     const float* logits_dev, uint16_t* out_dev, void* ws_dev,
+                     uint64_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MNB_H */

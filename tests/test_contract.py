@@ -1,0 +1,257 @@
+"""Host contract of the C ABI, exercised without a GPU through the host-only
+twin mnb_prepare_host and through argument checks that fail before any HIP
+call.
+
+Contract sources: "Qwen3 Missing-Kernel Implementation Plan", section "PR
+sequence", step K01 (FP32/UINT8/FP32 contract, bits=4, block_size=32,
+accuracy_level=4, implicit zero points, padding, explicit rejection of
+unsupported variants); onnxruntime PR "INT3 QMoE CUDA correctness baseline and
+Qwen experimental results", embedded P0/P1 body, sections "P0" (checked size
+arithmetic, canonical padding), "P1" (INT3 profile, finite nonnegative FP16
+scales, block-aligned K) and "Latest Review Fixes" (N = 127 accepted).
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import block_quantized_weight_03_amd as mnb
+import synth
+
+OK, INVALID, UNSUP, OVERFLOW, CONTENT, SMALL, DEVICE, STALE = 0, -1, -2, -3, -4, -5, -6, -7
+
+
+def status_of(fn, *args):
+    try:
+        fn(*args)
+        return OK
+    except mnb.MnbError as e:
+        return e.status
+
+
+def size_status(desc):
+    return status_of(mnb.mnb_prepacked_size, desc)
+
+
+def dense_inputs(N, K, bs=32, zp=False, seed=1):
+    nb = -(-K // bs)
+    B = synth.int4_blocked_weights(seed, N, K, bs)
+    s = synth.scales_f32(seed + 1, (N, nb))
+    Z = synth.int4_zero_points(seed + 2, N, nb) if zp else None
+    return B, s, Z
+
+
+def host_prepare(desc, B, s, Z):
+    dst = np.zeros(mnb.mnb_prepacked_size(desc) + 512, np.uint8)
+    off = (-dst.ctypes.data) % 256
+    view = dst[off:off + mnb.mnb_prepacked_size(desc)]
+    plan = mnb.mnb_prepare_host(desc, B, s, Z, view)
+    return plan, view, dst
+
+
+def test_descriptor_rejections():
+    good = mnb.dense_desc(64, 16)
+    assert size_status(good) == OK
+
+    def with_(**kw):
+        d = mnb.dense_desc(64, 16)
+        for k, v in kw.items():
+            setattr(d, k, v)
+        return d
+
+    assert size_status(with_(abi_version=2)) == INVALID
+    for bits in (1, 2, 5, 8):
+        assert size_status(with_(bits=bits)) == UNSUP
+    for bits in (0, 9, -1):
+        assert size_status(with_(bits=bits)) == INVALID
+    for bs in (16, 256, 48):
+        assert size_status(with_(block_size=bs)) == UNSUP
+    assert size_status(with_(block_size=0)) == INVALID
+    for lvl in (-1, 5):
+        assert size_status(with_(accuracy_level=lvl)) == INVALID
+    for lvl in range(5):
+        assert size_status(with_(accuracy_level=lvl)) == OK
+    assert size_status(with_(K=0)) == INVALID
+    assert size_status(with_(N=0)) == INVALID
+    assert size_status(with_(N=-3)) == INVALID
+    assert size_status(with_(num_experts=0)) == INVALID
+    assert size_status(with_(scale_dtype=mnb.MNB_DTYPE_F16)) == UNSUP
+    assert size_status(with_(row_layout=mnb.MNB_ROWS_ROW_LOCAL)) == UNSUP
+    assert size_status(with_(num_experts=2)) == UNSUP
+    assert size_status(with_(has_zero_points=2)) == INVALID
+    assert size_status(with_(scale_dtype=7)) == INVALID
+    # INT3 QMoE profile
+    q = mnb.qmoe_proj_desc(2048, 1536, 128, 64)
+    assert size_status(q) == OK
+    q.has_zero_points = 1
+    assert size_status(q) == UNSUP
+    assert size_status(mnb.qmoe_proj_desc(100, 8, 2, 64)) == UNSUP  # K not block aligned
+    q = mnb.qmoe_proj_desc(128, 8, 2, 64)
+    q.scale_dtype = mnb.MNB_DTYPE_F32
+    assert size_status(q) == UNSUP
+
+
+def test_size_overflow_is_detected():
+    d = mnb.dense_desc(2 ** 40, 2 ** 40)
+    assert size_status(d) == OVERFLOW
+    d = mnb.dense_desc(2 ** 62, 8)
+    assert size_status(d) == OVERFLOW
+    q = mnb.qmoe_proj_desc(2 ** 61, 2 ** 10, 4, 64)
+    assert size_status(q) == OVERFLOW
+
+
+@pytest.mark.parametrize("K,N,bs,zp", [(2048, 2048, 32, False), (2050, 1024, 32, False),
+                                       (2048, 151936, 32, True), (6144, 2048, 64, False),
+                                       (33, 127, 128, True)])
+def test_prepacked_size_never_inflates(K, N, bs, zp):
+    nb = -(-K // bs)
+    contract = N * nb * bs // 2 + N * nb * 4 + (N * ((nb + 1) // 2) if zp else 0)
+    size = mnb.mnb_prepacked_size(mnb.dense_desc(K, N, bs, zp))
+    assert contract <= size <= contract + 768
+
+
+@pytest.mark.parametrize("K,N,bs,zp", [(64, 16, 32, False), (2050, 33, 32, True), (34, 5, 32, False),
+                                       (200, 127, 64, True), (130, 3, 128, False)])
+def test_dense_host_prepack_round_trip(orc, K, N, bs, zp):
+    B, s, Z = dense_inputs(N, K, bs, zp, seed=K + N)
+    desc = mnb.dense_desc(K, N, bs, zp)
+    plan, _, _keep = host_prepare(desc, B, s, Z)
+    assert plan.device == -1 and plan.layout_version >= 1
+    codes, zeros, scales = mnb.mnb_debug_unpack_host(plan, 0, 0, N)
+    ocodes, ozeros = orc.mnb_codes(B, Z, K, N, bs=bs)
+    assert np.array_equal(codes, ocodes)
+    assert np.array_equal(zeros, ozeros)
+    assert np.array_equal(scales, s)
+    # a sub-range of rows
+    c2, _, _ = mnb.mnb_debug_unpack_host(plan, 0, 1, N - 1)
+    assert np.array_equal(c2, ocodes[1:])
+
+
+def test_pad_codes_do_not_change_the_prepared_codes(orc):
+    K, N, bs = 2050, 4, 32
+    Bz = synth.int4_blocked_weights(9, N, K, bs, pad="zero")
+    Br = synth.int4_blocked_weights(9, N, K, bs, pad="random")
+    s = synth.scales_f32(10, (N, 65))
+    pz, vz, _a = host_prepare(mnb.dense_desc(K, N, bs), Bz, s, None)
+    pr, vr, _b = host_prepare(mnb.dense_desc(K, N, bs), Br, s, None)
+    assert not np.array_equal(Bz, Br)
+    assert np.array_equal(vz, vr)  # pad nibbles are normalised by the prepack
+
+
+def test_int3_host_prepack_round_trip_and_n127(orc):
+    E, N, K, bs = 3, 127, 256, 64
+    W = synth.int3_rows(4, E * N, K)
+    s = synth.scales_f16(5, (E * N, K // bs))
+    desc = mnb.qmoe_proj_desc(K, N, E, bs)
+    plan, _, _keep = host_prepare(desc, W, s, None)
+    for e in range(E):
+        codes, zeros, sc = mnb.mnb_debug_unpack_host(plan, e, 0, N)
+        ref = np.stack([orc.unpack_bits(W[e * N + r], K, 3) for r in range(N)])
+        assert np.array_equal(codes, ref)
+        assert (zeros == 4).all()
+        assert np.array_equal(sc.view(np.uint16), s[e * N:(e + 1) * N].view(np.uint16))
+
+
+@pytest.mark.parametrize("bad", [np.inf, -np.inf, np.nan, -0.5, -65504.0])
+def test_int3_scale_content_rejected(bad):
+    E, N, K, bs = 2, 4, 128, 64
+    W = synth.int3_rows(4, E * N, K)
+    s = synth.scales_f16(5, (E * N, K // bs))
+    s[3, 1] = np.float16(bad)
+    desc = mnb.qmoe_proj_desc(K, N, E, bs)
+    with pytest.raises(mnb.MnbError) as ei:
+        host_prepare(desc, W, s, None)
+    assert ei.value.status == CONTENT
+
+
+def test_int3_negative_zero_and_zero_scales_accepted():
+    E, N, K, bs = 1, 2, 64, 64
+    W = synth.int3_rows(4, E * N, K)
+    s = np.array([[-0.0], [0.0]], np.float16)
+    host_prepare(mnb.qmoe_proj_desc(K, N, E, bs), W, s, None)
+
+
+def test_prepare_argument_errors():
+    K, N = 64, 8
+    B, s, Z = dense_inputs(N, K)
+    desc = mnb.dense_desc(K, N)
+    need = mnb.mnb_prepacked_size(desc)
+    buf = np.zeros(need + 512, np.uint8)
+    off = (-buf.ctypes.data) % 256
+    ok_view = buf[off:off + need]
+    assert status_of(mnb.mnb_prepare_host, desc, B, s, None, ok_view) == OK
+    assert status_of(mnb.mnb_prepare_host, desc, B, s, None, buf[off:off + need - 1]) == SMALL
+    assert status_of(mnb.mnb_prepare_host, desc, B, s, None, buf[off + 1:off + 1 + need]) == INVALID
+    zdesc = mnb.dense_desc(K, N, has_zero_points=True)
+    zneed = mnb.mnb_prepacked_size(zdesc)
+    assert status_of(mnb.mnb_prepare_host, zdesc, B, s, None, buf[off:off + zneed]) == INVALID
+    lib = mnb.lib()
+    plan = mnb.mnb_plan()
+    assert lib.mnb_prepare_host(ctypes.byref(desc), None, s.ctypes.data, None,
+                                ok_view.ctypes.data, need, ctypes.byref(plan)) == INVALID
+    assert lib.mnb_prepare_host(ctypes.byref(desc), B.ctypes.data, s.ctypes.data, None,
+                                ok_view.ctypes.data, need, None) == INVALID
+    # a failed prepare leaves a zeroed plan
+    plan.magic = 123
+    assert lib.mnb_prepare_host(ctypes.byref(desc), B.ctypes.data, s.ctypes.data, None,
+                                ok_view.ctypes.data, 1, ctypes.byref(plan)) == SMALL
+    assert plan.magic == 0
+
+
+def test_stale_and_mismatched_plans_rejected_before_any_launch():
+    K, N = 64, 8
+    B, s, _ = dense_inputs(N, K)
+    plan, _, _keep = host_prepare(mnb.dense_desc(K, N), B, s, None)
+    assert mnb.mnb_gemv_workspace_size(plan) == 0  # K <= 8192: one fused launch
+    Kl = 8192 + 32
+    Bl, sl, _ = dense_inputs(N, Kl)
+    plan_l, _, _keep_l = host_prepare(mnb.dense_desc(Kl, N), Bl, sl, None)
+    assert mnb.mnb_gemv_workspace_size(plan_l) > 0  # longer K: digit pre-pass in ws
+    lib = mnb.lib()
+    out = ctypes.c_uint64()
+    for field, val in (("magic", 1), ("layout_version", 999), ("codes_bytes", 7)):
+        bad = mnb.mnb_plan.from_buffer_copy(plan)
+        setattr(bad, field, val)
+        assert lib.mnb_gemv_workspace_size(ctypes.byref(bad), ctypes.byref(out)) == STALE
+        assert lib.mnb_gemv(ctypes.byref(bad), 1, 1, 1, 1 << 20, None) == STALE
+    bad = mnb.mnb_plan.from_buffer_copy(plan)
+    bad.desc.K = 65
+    assert lib.mnb_gemv_workspace_size(ctypes.byref(bad), ctypes.byref(out)) == STALE
+    # argument errors are found before any HIP call
+    assert lib.mnb_gemv(ctypes.byref(plan), None, 1, 1, 1 << 20, None) == INVALID
+    assert lib.mnb_gemv(ctypes.byref(plan_l), 1, 1, None, 0, None) == SMALL
+    assert lib.mnb_gemv(ctypes.byref(plan_l), 1, 1, 256, 1, None) == SMALL
+    assert lib.mnb_gemm(ctypes.byref(plan), -1, 1, 1, None, 0, None) == INVALID
+    assert lib.mnb_gemm(ctypes.byref(plan), 0, None, None, None, 0, None) == OK  # M = 0: no-op
+    assert lib.mnb_gemm(ctypes.byref(plan), 2 ** 62, 1, 1, None, 0, None) == OVERFLOW
+    assert lib.mnb_debug_unpack_host(ctypes.byref(plan), 1, 0, 1, None, None, None) == INVALID
+    assert lib.mnb_debug_unpack_host(ctypes.byref(plan), 0, 5, 4, None, None, None) == INVALID
+
+
+def test_qmoe_descriptor_and_shape_checks():
+    E, H, I, bs = 4, 128, 64, 64
+    W1 = synth.int3_rows(1, E * 2 * I, H)
+    s1 = synth.scales_f16(2, (E * 2 * I, H // bs))
+    W2 = synth.int3_rows(3, E * H, I)
+    s2 = synth.scales_f16(4, (E * H, I // bs))
+    p1, _, _k1 = host_prepare(mnb.qmoe_proj_desc(H, 2 * I, E, bs), W1, s1, None)
+    p2, _, _k2 = host_prepare(mnb.qmoe_proj_desc(I, H, E, bs), W2, s2, None)
+    q = mnb.make_qmoe_desc(2)
+    assert mnb.qmoe_workspace_size(p1, p2, q, 16) >= 0
+    assert status_of(mnb.qmoe_workspace_size, p2, p1, q, 16) == INVALID  # swapped projections
+    assert status_of(mnb.qmoe_workspace_size, p1, p2, q, -1) == INVALID
+    for field, val, want in (("top_k", 0, INVALID), ("top_k", E + 1, INVALID),
+                             ("normalize_routing_weights", 0, UNSUP), ("activation", 0, UNSUP),
+                             ("gate_up", 0, UNSUP), ("weights_prepacked", 1, UNSUP),
+                             ("quant_type", 1, UNSUP), ("abi_version", 0, INVALID)):
+        bad = mnb.make_qmoe_desc(2)
+        setattr(bad, field, val)
+        assert status_of(mnb.qmoe_workspace_size, p1, p2, bad, 16) == want, field
+    lib = mnb.lib()
+    assert lib.qmoe_forward(ctypes.byref(p1), ctypes.byref(p2), ctypes.byref(q), 0, None, None,
+                            None, None, 0, None) == OK  # T = 0: no-op
+    # a dense plan is not a QMoE projection
+    B, s, _ = dense_inputs(8, 64)
+    pd, _, _k3 = host_prepare(mnb.dense_desc(64, 8), B, s, None)
+    assert status_of(mnb.qmoe_workspace_size, pd, p2, q, 4) == UNSUP
+    assert lib.mnb_gemv(ctypes.byref(p1), 1, 1, 256, 1 << 20, None) == UNSUP

@@ -1,0 +1,205 @@
+"""GPU parity of the M = 1 GEMV against the fp64 oracle, through the C ABI.
+
+Operation: "Qwen3 Missing-Kernel Implementation Plan", section "PR sequence",
+step K02 (packed INT4 decode GEMV for every projection including the
+vocabulary head; exact packing and tail tests; repeated calls do not repack).
+Bar: |y - y_oracle| <= 2e-5 * sum_k |a_k w_k| per element; exact cases
+bit-exact.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import block_quantized_weight_03_amd as mnb  # noqa: E402
+
+TOL = 2e-5
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def prepare(K, N, bs=32, zp=False, seed=0, pad="zero"):
+    nb = -(-K // bs)
+    B = synth.int4_blocked_weights(synth.seed_for(seed, 1), N, K, bs, pad=pad)
+    s = synth.scales_f32(synth.seed_for(seed, 2), (N, nb))
+    Z = synth.int4_zero_points(synth.seed_for(seed, 3), N, nb) if zp else None
+    w = mnb.PreparedWeight(mnb.dense_desc(K, N, bs, zp), B, s, Z)
+    return w, B, s, Z
+
+
+def run_gemv(w, a_np, guard=64):
+    """Runs mnb_gemv with NaN guard bands around Y; returns Y and checks the bands."""
+    N = w.desc.N
+    A = torch.from_numpy(a_np.reshape(-1)).cuda()
+    Yg = torch.full((N + 2 * guard,), float("nan"), dtype=torch.float32, device="cuda")
+    Y = Yg[guard:guard + N]
+    ws = torch.empty(mnb.mnb_gemv_workspace_size(w.plan) + 256, dtype=torch.uint8, device="cuda")
+    mnb.mnb_gemv(w.plan, A, Y, ws, ws.numel())
+    torch.cuda.synchronize()
+    g = Yg.cpu().numpy()
+    assert np.isnan(g[:guard]).all() and np.isnan(g[guard + N:]).all(), "guard band written"
+    return g[guard:guard + N].copy()
+
+
+def check(orc, y, a, B, s, Z, K, N, bs, rows=None):
+    if rows is None:
+        _, y64, S = orc.mnb_gemm(a.reshape(1, -1), B, s, Z, K, N, bs=bs, nthreads=8)
+        y64, S, yy = y64[0], S[0], y
+    else:
+        _, y64, S = orc.mnb_gemm(a.reshape(1, -1), B[rows], s[rows],
+                                 None if Z is None else Z[rows], K, len(rows), bs=bs, nthreads=8)
+        y64, S, yy = y64[0], S[0], y[rows]
+    err = np.abs(yy.astype(np.float64) - y64)
+    bad = err > TOL * S
+    assert not bad.any(), (f"{bad.sum()} elements over 2e-5*S; worst ratio "
+                           f"{(err / np.maximum(S, 1e-300)).max():.3e}")
+    return (err / np.maximum(S, 1e-300)).max()
+
+
+@pytest.mark.parametrize("K,N,bs,zp", [
+    (32, 1, 32, False), (34, 7, 32, False), (100, 127, 32, True), (2048, 129, 64, False),
+    (4096, 300, 128, True), (6144, 64, 32, False), (8192, 33, 32, True), (10000, 40, 32, False),
+    (2050, 1024, 32, False), (1, 5, 32, False), (4160, 17, 64, True)])
+def test_gemv_small_shapes_elementwise(orc, K, N, bs, zp):
+    say(f"gemv small K={K} N={N} bs={bs} zp={zp}")
+    w, B, s, Z = prepare(K, N, bs, zp, seed=K * 7 + N)
+    a = synth.activations_f32(synth.seed_for(K + N, 9), 1, K)
+    y = run_gemv(w, a)
+    check(orc, y, a, B, s, Z, K, N, bs)
+
+
+def test_gemv_config_one_full(orc):
+    """M=1, K=2048, N=2048, block 32, implicit zero point 8."""
+    say("gemv cfg K=2048 N=2048")
+    K = N = 2048
+    w, B, s, Z = prepare(K, N, seed=1)
+    a = synth.activations_f32(synth.seed_for(1, 0), 1, K)
+    y = run_gemv(w, a)
+    worst = check(orc, y, a, B, s, Z, K, N, 32)
+    say(f"  worst err/S = {worst:.3e}")
+
+
+@pytest.mark.parametrize("name,K,N", [("qkv", 2048, 4096), ("o_proj", 2048, 2048),
+                                      ("gate", 2048, 6144), ("up", 2048, 6144),
+                                      ("down", 6144, 2048), ("tail", 2050, 1024)])
+def test_gemv_decoder_layer(orc, name, K, N):
+    say(f"gemv layer {name} K={K} N={N}")
+    w, B, s, Z = prepare(K, N, seed=2 * 100 + K % 97 + N % 89)
+    a = synth.activations_f32(synth.seed_for(2, K % 251), 1, K)
+    y = run_gemv(w, a)
+    check(orc, y, a, B, s, Z, K, N, 32)
+    if name == "qkv":
+        # the [2048, 1024, 1024] split is a view of the fused output
+        q, k, v = np.split(y, [2048, 3072])
+        assert q.shape == (2048,) and k.shape == (1024,) and v.shape == (1024,)
+
+
+def test_gemv_tail_random_pad_gives_identical_output():
+    say("gemv tail random pad")
+    K, N = 2050, 1024
+    wz, *_ = prepare(K, N, seed=5, pad="zero")
+    wr, *_ = prepare(K, N, seed=5, pad="random")
+    a = synth.activations_f32(synth.seed_for(5, 0), 1, K)
+    assert np.array_equal(run_gemv(wz, a), run_gemv(wr, a))
+
+
+def test_gemv_vocabulary_head_sampled(orc):
+    """K=2048, N=151936, explicit packed 4-bit zero points; oracle on sampled rows."""
+    say("gemv vocab head K=2048 N=151936 zp")
+    K, N = 2048, 151936
+    w, B, s, Z = prepare(K, N, zp=True, seed=3)
+    a = synth.activations_f32(synth.seed_for(3, 0), 1, K)
+    y = run_gemv(w, a)
+    assert np.isfinite(y).all()
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(N - 64, N),
+                                     rng.choice(N, 4096, replace=False)]))
+    check(orc, y, a, B, s, Z, K, N, 32, rows=rows)
+
+
+def test_gemv_exact_integer_case_bit_exact(orc):
+    say("gemv exact integer")
+    K, N = 4096, 256
+    w, B, _, Z = prepare(K, N, seed=11)
+    s1 = np.ones((N, K // 32), np.float32)
+    w = mnb.PreparedWeight(mnb.dense_desc(K, N), B, s1, None)
+    a = synth.small_int_activations(synth.seed_for(11, 0), 1, K)
+    y = run_gemv(w, a)
+    _, y64, _ = orc.mnb_gemm(a, B, s1, None, K, N)
+    assert np.array_equal(y.astype(np.float64), y64[0])
+
+
+def test_gemv_all_codes_at_zero_point_give_zero():
+    say("gemv zero invariant")
+    K, N = 2048, 512
+    nb = K // 32
+    s = synth.scales_f32(7, (N, nb))
+    a = synth.activations_f32(8, 1, K)
+    B = np.full((N, nb, 16), 0x88, np.uint8)
+    w = mnb.PreparedWeight(mnb.dense_desc(K, N), B, s, None)
+    assert (run_gemv(w, a) == 0).all()
+    Z = synth.int4_zero_points(9, N, nb)
+    zfull = np.empty((N, nb), np.uint8)
+    zfull[:, 0::2] = Z & 15
+    zfull[:, 1::2] = Z >> 4
+    codes = np.repeat(zfull, 32, axis=1).reshape(N, nb, 32)
+    B2 = (codes[:, :, 0::2] | (codes[:, :, 1::2] << 4)).astype(np.uint8)
+    w2 = mnb.PreparedWeight(mnb.dense_desc(K, N, has_zero_points=True), B2, s, Z)
+    assert (run_gemv(w2, a) == 0).all()
+
+
+def test_gemv_deterministic_and_no_repack():
+    say("gemv determinism")
+    K, N = 6144, 2048
+    w, *_ = prepare(K, N, seed=13)
+    a = synth.activations_f32(14, 1, K)
+    before = w.buffer.clone()
+    y1 = run_gemv(w, a)
+    y2 = run_gemv(w, a)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    assert torch.equal(before, w.buffer)  # compute calls never touch the prepared weights
+
+
+def test_gemv_scale_invariance_power_of_two():
+    say("gemv power-of-two scaling")
+    K, N = 2048, 256
+    w, *_ = prepare(K, N, seed=15)
+    a = synth.activations_f32(16, 1, K)
+    y = run_gemv(w, a)
+    for p in (-40, -3, 5, 60):
+        ys = run_gemv(w, (a * np.float32(2.0 ** p)).astype(np.float32))
+        assert np.array_equal(ys, (y.astype(np.float64) * 2.0 ** p).astype(np.float32))
+
+
+def test_gemv_non_finite_activation_poisons_output():
+    say("gemv non-finite A")
+    K, N = 256, 64
+    w, *_ = prepare(K, N, seed=17)
+    a = synth.activations_f32(18, 1, K)
+    a[0, 77] = np.inf
+    assert np.isnan(run_gemv(w, a)).all()
+
+
+def test_debug_unpack_and_dequant_bit_exact(orc):
+    say("debug unpack / dequant")
+    for K, N, bs, zp in ((2050, 37, 32, True), (256, 9, 128, False)):
+        w, B, s, Z = prepare(K, N, bs, zp, seed=19 + K)
+        codes = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+        mnb.mnb_debug_unpack(w.plan, 0, 0, N, codes)
+        deq = torch.empty((N, K), dtype=torch.float16, device="cuda")
+        mnb.mnb_debug_dequant_f16(w.plan, 0, 0, N, deq)
+        torch.cuda.synchronize()
+        ocodes, _ = orc.mnb_codes(B, Z, K, N, bs=bs)
+        assert np.array_equal(codes.cpu().numpy(), ocodes)
+        # exact fp64 dequant -> fp32 (RN) -> fp16 (RN), as documented for the MFMA path
+        W = orc.mnb_dequant(B, s, Z, K, N, bs=bs)
+        ref = orc.f64_to_f16(W.astype(np.float32).astype(np.float64))
+        assert np.array_equal(deq.cpu().numpy().view(np.uint16), ref)
