@@ -1,0 +1,127 @@
+"""GPU parity of the small-M / prefill GEMM against the fp64 oracle, through
+the C ABI.
+
+Operation: "Qwen3 Missing-Kernel Implementation Plan", section "PR sequence",
+step K03 (small-M and prefill GEMM on the same compressed weights; partial
+blocks and output tails).  Bar: |y - y_oracle| <= 4e-3 * sum_k |a_k w_k| per
+element (fp16 matrix-core inputs, fp32 accumulation); exact cases bit-exact.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import block_quantized_weight_03_amd as mnb  # noqa: E402
+
+TOL = 4e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def prepare(K, N, bs=32, zp=False, seed=0):
+    nb = -(-K // bs)
+    B = synth.int4_blocked_weights(synth.seed_for(seed, 1), N, K, bs)
+    s = synth.scales_f32(synth.seed_for(seed, 2), (N, nb))
+    Z = synth.int4_zero_points(synth.seed_for(seed, 3), N, nb) if zp else None
+    return mnb.PreparedWeight(mnb.dense_desc(K, N, bs, zp), B, s, Z), B, s, Z
+
+
+def run_gemm(w, a_np, guard=256):
+    M, N = a_np.shape[0], w.desc.N
+    A = torch.from_numpy(np.ascontiguousarray(a_np)).cuda()
+    Yg = torch.full((M * N + 2 * guard,), float("nan"), dtype=torch.float32, device="cuda")
+    Y = Yg[guard:guard + M * N]
+    need = mnb.mnb_gemm_workspace_size(w.plan, M)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    mnb.mnb_gemm(w.plan, M, A, Y, ws, ws.numel())
+    torch.cuda.synchronize()
+    g = Yg.cpu().numpy()
+    assert np.isnan(g[:guard]).all() and np.isnan(g[guard + M * N:]).all(), "guard band written"
+    return g[guard:guard + M * N].reshape(M, N).copy()
+
+
+def check(orc, y, a, B, s, Z, K, N, bs):
+    _, y64, S = orc.mnb_gemm(a, B, s, Z, K, N, bs=bs, nthreads=8)
+    err = np.abs(y.astype(np.float64) - y64)
+    ratio = err / np.maximum(S, 1e-300)
+    assert (err <= TOL * S).all(), f"{(err > TOL * S).sum()} over 4e-3*S, worst {ratio.max():.3e}"
+    return ratio.max()
+
+
+@pytest.mark.parametrize("M,K,N,bs,zp", [
+    (1, 32, 1, 32, False), (3, 34, 7, 32, False), (17, 100, 127, 32, True),
+    (33, 2050, 300, 32, False), (64, 4096, 256, 128, True), (65, 64, 129, 64, False),
+    (130, 6144, 129, 64, False), (257, 96, 513, 32, True), (5, 33, 1000, 32, True),
+    (300, 2048, 260, 32, False), (2, 1, 3, 32, False)])
+def test_gemm_small_shapes_elementwise(orc, M, K, N, bs, zp):
+    say(f"gemm small M={M} K={K} N={N} bs={bs} zp={zp}")
+    w, B, s, Z = prepare(K, N, bs, zp, seed=M * 31 + K + N)
+    a = synth.activations_f32(synth.seed_for(M + K, N % 255), M, K)
+    y = run_gemm(w, a)
+    check(orc, y, a, B, s, Z, K, N, bs)
+
+
+@pytest.mark.parametrize("K,N", [(2048, 6144), (6144, 2048)])
+@pytest.mark.parametrize("M", [16, 128, 512, 2048, 4096])
+def test_gemm_prefill_configs_sampled_rows(orc, M, K, N):
+    """The prefill configurations at full size; the oracle recomputes a sample
+    of output rows (every column of each)."""
+    say(f"gemm prefill M={M} K={K} N={N}")
+    w, B, s, Z = prepare(K, N, seed=4 * 1000 + K % 997)
+    a = synth.activations_f32(synth.seed_for(4, M % 251), M, K)
+    y = run_gemm(w, a)
+    assert np.isfinite(y).all()
+    rng = np.random.default_rng(M)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(M, 14), replace=False)]))
+    check(orc, y[rows], a[rows], B, s, Z, K, N, 32)
+
+
+def test_gemm_exact_integer_case_bit_exact(orc):
+    say("gemm exact integer")
+    M, K, N = 70, 1024, 300
+    _, B, _, _ = prepare(K, N, seed=21)
+    s = np.full((N, K // 32), 0.25, np.float32)
+    w = mnb.PreparedWeight(mnb.dense_desc(K, N), B, s, None)
+    a = synth.small_int_activations(22, M, K)
+    y = run_gemm(w, a)
+    _, y64, _ = orc.mnb_gemm(a, B, s, None, K, N)
+    assert np.array_equal(y.astype(np.float64), y64)
+
+
+def test_gemm_all_codes_at_zero_point_give_zero():
+    say("gemm zero invariant")
+    M, K, N = 40, 256, 256
+    nb = K // 32
+    B = np.full((N, nb, 16), 0x88, np.uint8)
+    s = synth.scales_f32(23, (N, nb))
+    w = mnb.PreparedWeight(mnb.dense_desc(K, N), B, s, None)
+    assert (run_gemm(w, synth.activations_f32(24, M, K)) == 0).all()
+
+
+def test_gemm_deterministic():
+    say("gemm determinism")
+    M, K, N = 512, 2048, 1024
+    w, *_ = prepare(K, N, seed=25)
+    a = synth.activations_f32(26, M, K)
+    y1, y2 = run_gemm(w, a), run_gemm(w, a)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+def test_gemm_rows_are_independent():
+    """Row m of the output depends only on row m of A (no cross-row mixing in
+    the tiling): a sub-batch gives the same bits."""
+    say("gemm row independence")
+    M, K, N = 300, 512, 384
+    w, *_ = prepare(K, N, seed=27)
+    a = synth.activations_f32(28, M, K)
+    y = run_gemm(w, a)
+    y_sub = run_gemm(w, a[100:117])
+    assert np.array_equal(y[100:117], y_sub)
