@@ -1,0 +1,327 @@
+#!/usr/bin/env python3
+"""Benchmark: packed-weight HBM GB/s of the M = 1 INT4 decode GEMVs of one
+Qwen3-shaped decoder layer on one MI355X, with the prefill GEMM TFLOP/s, the
+vocabulary-head GEMV and the INT3 QMoE layer reported alongside.
+
+A step is one pass over the layer's projections (fused QKV 2048->4096, o_proj
+2048->2048, gate and up 2048->6144, down 6144->2048, and the K-tail case
+2050->1024), each an mnb_gemv call on the library's prepared INT4 weights.
+Weights rotate over enough distinct copies (>= 1 GiB) that every step streams
+them from HBM rather than from the 256 MB Infinity Cache.  The timed steps are
+replayed from a HIP graph (launch overhead of the Python binding excluded) and
+bracketed by torch.cuda.synchronize() on both sides.
+
+Per-kernel durations for the roofline come from HIP events recorded on the
+launch stream around each launch of one eager pass over the same steps, queued
+behind a GPU sleep so that every event pair brackets only its kernel.
+
+Prints one JSON line.  Everything is synthetic (seeded, synth.py).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
+PEAK_FP16_TFLOPS = 2500.0    # MI355X dense fp16 matrix, published (no sparsity)
+ROTATE_BYTES = 1 << 30       # >= 4x the 256 MB MALL
+
+LAYER = [  # name, K, N (M = 1, block 32, implicit zero point 8)
+    ("qkv", 2048, 4096), ("o_proj", 2048, 2048), ("gate", 2048, 6144), ("up", 2048, 6144),
+    ("down", 6144, 2048), ("tail", 2050, 1024)]
+
+
+def gemv_bytes(K, N, bs=32, zp=False):
+    """Algorithmic bytes of one GEMV: packed codes + scales (+ zero points)."""
+    nb = -(-K // bs)
+    return N * nb * bs // 2 + N * nb * 4 + (N * ((nb + 1) // 2) if zp else 0)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Graph:
+    """A captured sequence of library calls, replayed on the current stream."""
+
+    def __init__(self, torch, fn):
+        self.torch = torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()  # warm-up outside capture
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        self.g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g):
+            fn()
+        torch.cuda.synchronize()
+
+    def replay(self):
+        self.g.replay()
+
+
+def timed_launches(torch, calls, sleep_cycles=80_000_000):
+    """Runs each call once behind a GPU sleep, with an event pair around each
+    launch; returns per-call durations in ms."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in calls]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(sleep_cycles)
+    for (a, b), c in zip(evs, calls):
+        a.record()
+        c()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "block_quantized_weight_03_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key, src_hash):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(layer_host, budget_s):
+    """The oracle on the layer's GEMVs, repeated for about budget_s seconds."""
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    done_bytes, passes = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        for (name, K, N), (B, s, a) in zip(LAYER, layer_host):
+            oracle.mnb_gemm(a, B, s, None, K, N, bs=32, nthreads=threads)
+            done_bytes += gemv_bytes(K, N)
+        passes += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{passes} pass(es) of the decoder-layer GEMVs (6 projections, "
+                      f"{sum(gemv_bytes(K, N) for _, K, N in LAYER)} B each) in {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=330)
+    ap.add_argument("--warmup", type=int, default=33)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-extras", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        sys.exit(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are "
+                 "not part of this build")
+
+    import torch
+    import block_quantized_weight_03_amd as mnb
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    # ---- decoder-layer weights, rotated over >= 1 GiB ------------------------
+    step_bytes = sum(gemv_bytes(K, N) for _, K, N in LAYER)
+    copies = max(1, -(-ROTATE_BYTES // step_bytes))
+    log(f"preparing {copies} copies of the layer ({step_bytes} B each)")
+    acts = []
+    for i, (name, K, N) in enumerate(LAYER):
+        a = synth.activations_f32(synth.seed_for(2, 100 + i), 1, K)
+        acts.append((a, torch.from_numpy(a[0]).to(dev)))
+    layers, layer_host = [], None
+    for c in range(copies):
+        ws = []
+        host = []
+        for i, (name, K, N) in enumerate(LAYER):
+            nb = -(-K // 32)
+            B = synth.int4_blocked_weights(synth.seed_for(2, 1000 * c + 10 * i + 1), N, K, 32)
+            s = synth.scales_f32(synth.seed_for(2, 1000 * c + 10 * i + 2), (N, nb))
+            ws.append(mnb.PreparedWeight(mnb.dense_desc(K, N), B, s, None))
+            if c == 0:
+                host.append((B, s, acts[i][0]))
+        if c == 0:
+            layer_host = host
+        layers.append(ws)
+    outs = [torch.empty(N, dtype=torch.float32, device=dev) for _, K, N in LAYER]
+    gemv_ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    for ws in layers[0]:
+        assert mnb.mnb_gemv_workspace_size(ws.plan) == 0
+
+    def step(c):
+        for i, w in enumerate(layers[c]):
+            mnb.mnb_gemv(w.plan, acts[i][1], outs[i], gemv_ws, gemv_ws.numel())
+
+    full = Graph(torch, lambda: [step(c) for c in range(copies)])
+    rem = args.steps % copies
+    part = Graph(torch, lambda: [step(c) for c in range(rem)]) if rem else None
+
+    # ---- warm-up, then exactly K timed steps -------------------------------
+    for _ in range(max(1, args.warmup // copies)):
+        full.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps // copies):
+        full.replay()
+    if part:
+        part.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = step_bytes * args.steps / elapsed / 1e9
+
+    # ---- per-launch durations of the GEMV kernel (roofline) -----------------
+    calls, byts = [], []
+    for c in range(copies):
+        for i, (name, K, N) in enumerate(LAYER):
+            w = layers[c][i]
+            calls.append(lambda w=w, i=i: mnb.mnb_gemv(w.plan, acts[i][1], outs[i], gemv_ws,
+                                                       gemv_ws.numel()))
+            byts.append(gemv_bytes(K, N))
+    durs = timed_launches(torch, calls)
+    avg_ms = sum(durs) / len(durs)
+    avg_bytes = sum(byts) / len(byts)
+    achieved = avg_bytes / (avg_ms * 1e-3) / 1e9
+    gemv_hash = source_hash("gemv.hip")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": load_traffic("gemv_int4_fused/decoder_layer", gemv_hash),
+                "kernel": "gemv_int4_fused", "launches": len(durs),
+                "avg_launch_us": round(avg_ms * 1e3, 3),
+                "algorithmic_bytes_per_launch": round(avg_bytes, 1)}
+    per_proj = {}
+    for i, (name, K, N) in enumerate(LAYER):
+        d = [durs[c * len(LAYER) + i] for c in range(copies)]
+        us = 1e3 * sum(d) / len(d)
+        per_proj[name] = {"us": round(us, 3), "GB/s": round(gemv_bytes(K, N) / us / 1e3, 1)}
+
+    del full, part
+    torch.cuda.synchronize()
+
+    extra = {"per_projection": per_proj}
+    if not args.no_extras:
+        extra.update(bench_extras(torch, mnb, dev))
+
+    base = cpu_baseline(layer_host, args.cpu_seconds)
+
+    rec = {"metric": "packed-weight HBM GB/s at M=1; prefill TFLOP/s; % of MI355X roofline",
+           "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "i4xi4->i32,f32", "data": "synthetic",
+           "config": {"workload": "Qwen3-shaped decoder layer of INT4 decode GEMVs, M=1, block 32, "
+                                  "implicit zero point 8: QKV 2048->4096, o 2048->2048, gate and up "
+                                  "2048->6144, down 6144->2048, tail 2050->1024",
+                      "bytes_per_step": step_bytes, "rotation_copies": copies,
+                      "timing": "HIP graph replay, wall clock between synchronizes"},
+           "roofline": roofline, "cpu_baseline": base, "extra": extra}
+    print(json.dumps(rec), flush=True)
+
+
+def bench_extras(torch, mnb, dev):
+    """Vocabulary head GEMV, prefill GEMM and INT3 QMoE, each timed per launch
+    with HIP events (weights rotated where the working set would fit in the
+    Infinity Cache)."""
+    out = {}
+    # vocabulary head: K=2048, N=151936, explicit zero points
+    K, N = 2048, 151936
+    nb = K // 32
+    copies = 6
+    vw = []
+    for c in range(copies):
+        B = synth.int4_blocked_weights(synth.seed_for(3, 10 * c + 1), N, K, 32)
+        s = synth.scales_f32(synth.seed_for(3, 10 * c + 2), (N, nb))
+        Z = synth.int4_zero_points(synth.seed_for(3, 10 * c + 3), N, nb)
+        vw.append(mnb.PreparedWeight(mnb.dense_desc(K, N, 32, True), B, s, Z))
+    A = torch.from_numpy(synth.activations_f32(synth.seed_for(3, 0), 1, K)[0]).to(dev)
+    Y = torch.empty(N, dtype=torch.float32, device=dev)
+    ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    calls = [lambda w=w: mnb.mnb_gemv(w.plan, A, Y, ws, 256) for w in vw] * 5
+    timed_launches(torch, calls[:copies])
+    d = timed_launches(torch, calls)
+    us = 1e3 * sum(d) / len(d)
+    vb = gemv_bytes(K, N, zp=True)
+    out["vocab_head_gemv"] = {"K": K, "N": N, "zero_points": True, "us": round(us, 3),
+                              "GB/s": round(vb / us / 1e3, 1),
+                              "frac_of_hbm_peak": round(vb / us / 1e3 / PEAK_HBM_GBS, 4)}
+    del vw
+    # prefill GEMM at M = 16 .. 4096 on both shapes
+    pre = {}
+    for (K, N) in ((2048, 6144), (6144, 2048)):
+        nb = K // 32
+        w = mnb.PreparedWeight(mnb.dense_desc(K, N), synth.int4_blocked_weights(synth.seed_for(4, K), N, K, 32),
+                               synth.scales_f32(synth.seed_for(4, K + 1), (N, nb)))
+        for M in (16, 128, 512, 2048, 4096):
+            a = torch.from_numpy(synth.activations_f32(synth.seed_for(4, M), M, K)).to(dev)
+            y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            need = mnb.mnb_gemm_workspace_size(w.plan, M)
+            gws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+            call = lambda w=w, M=M, a=a, y=y, gws=gws: mnb.mnb_gemm(w.plan, M, a, y, gws, gws.numel())
+            timed_launches(torch, [call])
+            d = timed_launches(torch, [call] * 10)
+            us = 1e3 * sum(d) / len(d)
+            tf = 2.0 * M * N * K / us / 1e6
+            pre[f"M{M}_K{K}_N{N}"] = {"us": round(us, 2), "TFLOP/s": round(tf, 1),
+                                       "frac_of_fp16_peak": round(tf / PEAK_FP16_TFLOPS, 4)}
+        del w
+    out["prefill_gemm"] = pre
+    # INT3 QMoE layer
+    H, I, E, k, bs = 2048, 768, 128, 8, 64
+    W1 = synth.int3_rows(synth.seed_for(5, 3), E * 2 * I, H)
+    s1 = synth.scales_f16(synth.seed_for(5, 4), (E * 2 * I, H // bs))
+    W2 = synth.int3_rows(synth.seed_for(5, 5), E * H, I)
+    s2 = synth.scales_f16(synth.seed_for(5, 6), (E * H, I // bs))
+    copies = 4
+    experts = []
+    for c in range(copies):  # distinct device copies of the same expert bytes
+        experts.append((mnb.PreparedWeight(mnb.qmoe_proj_desc(H, 2 * I, E, bs), W1, s1),
+                        mnb.PreparedWeight(mnb.qmoe_proj_desc(I, H, E, bs), W2, s2)))
+    q = mnb.make_qmoe_desc(k)
+    per_expert = 2 * I * (3 * H // 8) + 2 * I * (H // bs) * 2 + H * (3 * I // 8) + H * (I // bs) * 2
+    moe = {}
+    for T in (1, 128, 512):
+        x = torch.from_numpy(synth.activations_f16(synth.seed_for(5, 1), T, H)).to(dev)
+        lg = torch.from_numpy(synth.router_logits(synth.seed_for(5, 2), T, E)).to(dev)
+        o = torch.empty((T, H), dtype=torch.float16, device=dev)
+        need = mnb.qmoe_workspace_size(experts[0][0].plan, experts[0][1].plan, q, T)
+        qws = torch.empty(need, dtype=torch.uint8, device=dev)
+        calls = [lambda p=p, x=x, lg=lg, o=o, qws=qws, T=T: mnb.qmoe_forward(
+            p[0].plan, p[1].plan, q, T, x, lg, o, qws, qws.numel()) for p in experts] * 3
+        timed_launches(torch, calls[:copies])
+        d = timed_launches(torch, calls)
+        us = 1e3 * sum(d) / len(d)
+        ids = torch.topk(lg.float(), k, dim=1).indices.unique().numel()  # distinct experts routed
+        byts = ids * per_expert
+        moe[f"T{T}"] = {"us": round(us, 2), "distinct_experts": ids,
+                        "weight_GB/s": round(byts / us / 1e3, 1),
+                        "frac_of_hbm_peak": round(byts / us / 1e3 / PEAK_HBM_GBS, 4),
+                        "TFLOP/s": round(2.0 * T * k * (2 * I * H + H * I) / us / 1e6, 2)}
+    out["qmoe_int3_layer"] = moe
+    return out
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,100 @@
+"""The library's compute calls enqueue only kernels on the caller's stream (no
+host synchronisation, no memset nodes), so they can be captured in a HIP graph.
+Each test replays a captured graph several times, with eager work and
+synchronisations in between, and checks every replay bit for bit against the
+eager result."""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import block_quantized_weight_03_amd as mnb  # noqa: E402
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def capture(fn):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def replay_and_check(g, out, ref, eager):
+    for _ in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        eager()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_graph_gemv_and_gemm():
+    say("graph gemv + gemm")
+    K, N, M = 2050, 700, 37
+    nb = -(-K // 32)
+    w = mnb.PreparedWeight(mnb.dense_desc(K, N, 32, True), synth.int4_blocked_weights(1, N, K, 32),
+                           synth.scales_f32(2, (N, nb)), synth.int4_zero_points(3, N, nb))
+    a1 = torch.from_numpy(synth.activations_f32(4, 1, K)[0]).cuda()
+    aM = torch.from_numpy(synth.activations_f32(5, M, K)).cuda()
+    y1 = torch.empty(N, device="cuda")
+    yM = torch.empty((M, N), device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+
+    def run():
+        mnb.mnb_gemv(w.plan, a1, y1, ws, 256)
+        mnb.mnb_gemm(w.plan, M, aM, yM, ws, 256)
+
+    run()
+    torch.cuda.synchronize()
+    ref1, refM = y1.clone(), yM.clone()
+    g = capture(run)
+    for _ in range(3):
+        y1.fill_(float("nan"))
+        yM.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y1, ref1) and torch.equal(yM, refM)
+        (aM * 2).sum().item()
+        torch.cuda.synchronize()
+
+
+def test_graph_qmoe():
+    say("graph qmoe")
+    T, H, I, E, k, bs = 48, 256, 128, 16, 4, 64
+    W1 = synth.int3_rows(1, E * 2 * I, H)
+    s1 = synth.scales_f16(2, (E * 2 * I, H // bs))
+    W2 = synth.int3_rows(3, E * H, I)
+    s2 = synth.scales_f16(4, (E * H, I // bs))
+    p1 = mnb.PreparedWeight(mnb.qmoe_proj_desc(H, 2 * I, E, bs), W1, s1)
+    p2 = mnb.PreparedWeight(mnb.qmoe_proj_desc(I, H, E, bs), W2, s2)
+    q = mnb.make_qmoe_desc(k)
+    x = torch.from_numpy(synth.activations_f16(5, T, H)).cuda()
+    lg = torch.from_numpy(synth.router_logits(6, T, E)).cuda()
+    out = torch.empty((T, H), dtype=torch.float16, device="cuda")
+    ws = torch.empty(mnb.qmoe_workspace_size(p1.plan, p2.plan, q, T), dtype=torch.uint8, device="cuda")
+
+    def run():
+        mnb.qmoe_forward(p1.plan, p2.plan, q, T, x, lg, out, ws, ws.numel())
+
+    run()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    g = capture(run)
+    replay_and_check(g, out, ref, lambda: (x.float() * 3).sum().item())
