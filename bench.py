@@ -11,9 +11,11 @@ them from HBM rather than from the 256 MB Infinity Cache.  The timed steps are
 replayed from a HIP graph (launch overhead of the Python binding excluded) and
 bracketed by torch.cuda.synchronize() on both sides.
 
-Per-kernel durations for the roofline come from HIP events recorded on the
-launch stream around each launch of one eager pass over the same steps, queued
-behind a GPU sleep so that every event pair brackets only its kernel.
+The roofline's average launch duration comes from HIP events recorded on the
+launch stream around the same timed graph replays (one GEMV kernel per
+launch, launches back to back, so the average includes the short gaps between
+kernels).  The other figures are measured the same way, each from a graph of
+its own launches.
 
 Prints one JSON line.  Everything is synthetic (seeded, synth.py).
 """
@@ -70,19 +72,19 @@ class Graph:
         self.g.replay()
 
 
-def timed_launches(torch, calls, sleep_cycles=80_000_000):
-    """Runs each call once behind a GPU sleep, with an event pair around each
-    launch; returns per-call durations in ms."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in calls]
+def graph_time(torch, calls, reps):
+    """Captures `calls` in one graph and returns the average per call in ms
+    over `reps` replays, timed with an event pair on the launch stream."""
+    g = Graph(torch, lambda: [c() for c in calls])
+    g.replay()
     torch.cuda.synchronize()
-    torch.cuda._sleep(sleep_cycles)
-    for (a, b), c in zip(evs, calls):
-        a.record()
-        c()
-        b.record()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
     torch.cuda.synchronize()
-    return [a.elapsed_time(b) for a, b in evs]
+    return e0.elapsed_time(e1) / (reps * len(calls))
 
 
 def source_hash(*names):
@@ -183,39 +185,36 @@ def main():
     for _ in range(max(1, args.warmup // copies)):
         full.replay()
     torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record()
     for _ in range(args.steps // copies):
         full.replay()
     if part:
         part.replay()
+    e1.record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
     value = step_bytes * args.steps / elapsed / 1e9
 
-    # ---- per-launch durations of the GEMV kernel (roofline) -----------------
-    calls, byts = [], []
-    for c in range(copies):
-        for i, (name, K, N) in enumerate(LAYER):
-            w = layers[c][i]
-            calls.append(lambda w=w, i=i: mnb.mnb_gemv(w.plan, acts[i][1], outs[i], gemv_ws,
-                                                       gemv_ws.numel()))
-            byts.append(gemv_bytes(K, N))
-    durs = timed_launches(torch, calls)
-    avg_ms = sum(durs) / len(durs)
-    avg_bytes = sum(byts) / len(byts)
+    # ---- roofline of the GEMV kernel over the same timed region --------------
+    launches = args.steps * len(LAYER)
+    avg_ms = e0.elapsed_time(e1) / launches
+    avg_bytes = step_bytes / len(LAYER)
     achieved = avg_bytes / (avg_ms * 1e-3) / 1e9
     gemv_hash = source_hash("gemv.hip")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": load_traffic("gemv_int4_fused/decoder_layer", gemv_hash),
-                "kernel": "gemv_int4_fused", "launches": len(durs),
+                "kernel": "gemv_int4_fused", "launches": launches,
                 "avg_launch_us": round(avg_ms * 1e3, 3),
                 "algorithmic_bytes_per_launch": round(avg_bytes, 1)}
     per_proj = {}
     for i, (name, K, N) in enumerate(LAYER):
-        d = [durs[c * len(LAYER) + i] for c in range(copies)]
-        us = 1e3 * sum(d) / len(d)
+        calls = [lambda w=layers[c][i], i=i: mnb.mnb_gemv(w.plan, acts[i][1], outs[i], gemv_ws,
+                                                          gemv_ws.numel()) for c in range(copies)]
+        us = 1e3 * graph_time(torch, calls, 10)
         per_proj[name] = {"us": round(us, 3), "GB/s": round(gemv_bytes(K, N) / us / 1e3, 1)}
 
     del full, part
@@ -242,9 +241,9 @@ def main():
 
 
 def bench_extras(torch, mnb, dev):
-    """Vocabulary head GEMV, prefill GEMM and INT3 QMoE, each timed per launch
-    with HIP events (weights rotated where the working set would fit in the
-    Infinity Cache)."""
+    """Vocabulary head GEMV, prefill GEMM and INT3 QMoE, each timed from graph
+    replays of its own launches (weights rotated where the working set would
+    fit in the Infinity Cache)."""
     out = {}
     # vocabulary head: K=2048, N=151936, explicit zero points
     K, N = 2048, 151936
@@ -259,10 +258,8 @@ def bench_extras(torch, mnb, dev):
     A = torch.from_numpy(synth.activations_f32(synth.seed_for(3, 0), 1, K)[0]).to(dev)
     Y = torch.empty(N, dtype=torch.float32, device=dev)
     ws = torch.empty(256, dtype=torch.uint8, device=dev)
-    calls = [lambda w=w: mnb.mnb_gemv(w.plan, A, Y, ws, 256) for w in vw] * 5
-    timed_launches(torch, calls[:copies])
-    d = timed_launches(torch, calls)
-    us = 1e3 * sum(d) / len(d)
+    calls = [lambda w=w: mnb.mnb_gemv(w.plan, A, Y, ws, 256) for w in vw]
+    us = 1e3 * graph_time(torch, calls, 10)
     vb = gemv_bytes(K, N, zp=True)
     out["vocab_head_gemv"] = {"K": K, "N": N, "zero_points": True, "us": round(us, 3),
                               "GB/s": round(vb / us / 1e3, 1),
@@ -280,9 +277,7 @@ def bench_extras(torch, mnb, dev):
             need = mnb.mnb_gemm_workspace_size(w.plan, M)
             gws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
             call = lambda w=w, M=M, a=a, y=y, gws=gws: mnb.mnb_gemm(w.plan, M, a, y, gws, gws.numel())
-            timed_launches(torch, [call])
-            d = timed_launches(torch, [call] * 10)
-            us = 1e3 * sum(d) / len(d)
+            us = 1e3 * graph_time(torch, [call] * 4, 5)
             tf = 2.0 * M * N * K / us / 1e6
             pre[f"M{M}_K{K}_N{N}"] = {"us": round(us, 2), "TFLOP/s": round(tf, 1),
                                        "frac_of_fp16_peak": round(tf / PEAK_FP16_TFLOPS, 4)}
@@ -309,10 +304,8 @@ def bench_extras(torch, mnb, dev):
         need = mnb.qmoe_workspace_size(experts[0][0].plan, experts[0][1].plan, q, T)
         qws = torch.empty(need, dtype=torch.uint8, device=dev)
         calls = [lambda p=p, x=x, lg=lg, o=o, qws=qws, T=T: mnb.qmoe_forward(
-            p[0].plan, p[1].plan, q, T, x, lg, o, qws, qws.numel()) for p in experts] * 3
-        timed_launches(torch, calls[:copies])
-        d = timed_launches(torch, calls)
-        us = 1e3 * sum(d) / len(d)
+            p[0].plan, p[1].plan, q, T, x, lg, o, qws, qws.numel()) for p in experts]
+        us = 1e3 * graph_time(torch, calls, 5)
         ids = torch.topk(lg.float(), k, dim=1).indices.unique().numel()  # distinct experts routed
         byts = ids * per_expert
         moe[f"T{T}"] = {"us": round(us, 2), "distinct_experts": ids,

@@ -51,8 +51,17 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // ---- digit planes of a (shared by the in-kernel prologue and the pre-pass) --
 
+// DPP move within groups of 4 lanes (quad_perm), used for the 4-lane
+// reductions of a sub-block's quarters.
+template <int CTRL>
+__device__ __forceinline__ int quad_mov(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
+
 // Converts quarter w (8 elements) of sub-block sb.  The 4 quarters of one
-// sub-block must sit in 4 consecutive lanes of one wave (they share a max).
+// sub-block must sit in the 4 lanes of one DPP quad (they share a maximum).
 // Writes plane words to dig[((c*kDig + p)*4 + w)*64 + l] (c = sb/64, l = sb%64),
 // digit sums to sums[(c*4 + j)*64 + l] and -e to nexp[c*64 + l].
 __device__ __forceinline__ void make_digits(const float* __restrict__ A, int64_t K, int64_t sb,
@@ -68,10 +77,10 @@ __device__ __forceinline__ void make_digits(const float* __restrict__ A, int64_t
     bad |= !isfinite(v[i]);
     m = fmaxf(m, fabsf(v[i]));
   }
-  m = fmaxf(m, __shfl_xor(m, 1, 4));
-  m = fmaxf(m, __shfl_xor(m, 2, 4));
-  bad |= __shfl_xor(bad, 1, 4);
-  bad |= __shfl_xor(bad, 2, 4);
+  m = fmaxf(m, __int_as_float(quad_mov<kQuadSwap1>(__float_as_int(m))));
+  m = fmaxf(m, __int_as_float(quad_mov<kQuadSwap2>(__float_as_int(m))));
+  bad |= quad_mov<kQuadSwap1>(bad);
+  bad |= quad_mov<kQuadSwap2>(bad);
   int e = 0;
   if (!bad && m > 0.0f) {
     int E;
@@ -86,27 +95,38 @@ __device__ __forceinline__ void make_digits(const float* __restrict__ A, int64_t
     // adding 8 to every nibble position makes nibble p of u equal d_p + 8
     u[i] = (uint32_t)ai + 0x88888888u;
   }
+  // 8 x 8 nibble transpose (word i holds value i's digits -> word p holds
+  // plane p's digits of values 0..7) in three butterfly stages: 16-bit and
+  // 8-bit blocks with byte permutes, 4-bit blocks with bitfield inserts.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a = u[i], b = u[i + 4];
+    u[i] = __builtin_amdgcn_perm(b, a, 0x05040100u);
+    u[i + 4] = __builtin_amdgcn_perm(b, a, 0x07060302u);
+  }
+#pragma unroll
+  for (int i : {0, 1, 4, 5}) {
+    const uint32_t a = u[i], b = u[i + 2];
+    u[i] = __builtin_amdgcn_perm(b, a, 0x06020400u);
+    u[i + 2] = __builtin_amdgcn_perm(b, a, 0x07030501u);
+  }
+#pragma unroll
+  for (int i : {0, 2, 4, 6}) {
+    const uint32_t a = u[i], b = u[i + 1];
+    u[i] = (a & 0x0F0F0F0Fu) | ((b << 4) & 0xF0F0F0F0u);
+    u[i + 1] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+  }
   const int64_t c = sb >> 6;
   const int l = (int)(sb & 63);
   int32_t sd[kDig];
 #pragma unroll
   for (int p = 0; p < kDig; ++p) {
-    uint32_t d = 0;
-    int32_t s = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t nib = (u[i] >> (4 * p)) & 15u;
-      d |= nib << (4 * i);
-      s += (int32_t)nib - 8;
-    }
     // d_p in 4-bit two's complement is nib ^ 8
-    dig[((c * kDig + p) * 4 + w) * 64 + l] = d ^ 0x88888888u;
-    sd[p] = s;
-  }
-#pragma unroll
-  for (int p = 0; p < kDig; ++p) {
-    sd[p] += __shfl_xor(sd[p], 1, 4);
-    sd[p] += __shfl_xor(sd[p], 2, 4);
+    dig[((c * kDig + p) * 4 + w) * 64 + l] = u[p] ^ 0x88888888u;
+    // sum over the 8 values of d_p = (sum of the biased nibbles) - 64
+    sd[p] = (int32_t)__builtin_amdgcn_udot8(u[p], 0x11111111u, 0u, false) - 64;
+    sd[p] += quad_mov<kQuadSwap1>(sd[p]);
+    sd[p] += quad_mov<kQuadSwap2>(sd[p]);
   }
   if (w == 0) {
 #pragma unroll
