@@ -59,7 +59,9 @@ __global__ void debug_dequant_kernel(Rows r, int64_t nrows, __half* __restrict__
       z = (w >> (4 * (grow % 8))) & 15u;
     }
     const float s = static_cast<const float*>(r.scales)[grow * r.nb + b];
-    v = (float)((int)q - (int)z) * s;  // fp32 product, then one fp16 rounding
+    // the matrix-core chain: fp32 fma(q, s, -(z*s)), then one fp16 rounding
+    // (for z = 8, -(z*s) is exact and this is fp32((q - 8) * s))
+    v = fmaf((float)q, s, -((float)z * s));
   } else {
     const __half s = static_cast<const __half*>(r.scales)[grow * r.nb + b];
     v = (float)((int)q - 4) * __half2float(s);  // exact in fp32

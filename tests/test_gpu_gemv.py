@@ -197,9 +197,17 @@ def test_debug_unpack_and_dequant_bit_exact(orc):
         deq = torch.empty((N, K), dtype=torch.float16, device="cuda")
         mnb.mnb_debug_dequant_f16(w.plan, 0, 0, N, deq)
         torch.cuda.synchronize()
-        ocodes, _ = orc.mnb_codes(B, Z, K, N, bs=bs)
+        ocodes, oz = orc.mnb_codes(B, Z, K, N, bs=bs)
         assert np.array_equal(codes.cpu().numpy(), ocodes)
-        # exact fp64 dequant -> fp32 (RN) -> fp16 (RN), as documented for the MFMA path
-        W = orc.mnb_dequant(B, s, Z, K, N, bs=bs)
-        ref = orc.f64_to_f16(W.astype(np.float32).astype(np.float64))
+        # the documented matrix-core chain: fp32 fma(q, s, -(z*s)), then fp16 (RN);
+        # fp64 of q*s - zs32 is exact here, so one fp32 rounding reproduces the fma
+        codes64 = ocodes.astype(np.float64)
+        zeros64 = np.repeat(oz, bs, axis=1)[:, :K].astype(np.float64)
+        s64 = np.repeat(s.astype(np.float64), bs, axis=1)[:, :K]
+        zs32 = (zeros64 * s64).astype(np.float32).astype(np.float64)
+        w32 = (codes64 * s64 - zs32).astype(np.float32)
+        ref = orc.f64_to_f16(w32.astype(np.float64))
         assert np.array_equal(deq.cpu().numpy().view(np.uint16), ref)
+        if Z is None:  # implicit zero point 8: the chain is fp32((q - 8) * s)
+            W = orc.mnb_dequant(B, s, Z, K, N, bs=bs)
+            assert np.array_equal(ref, orc.f64_to_f16(W.astype(np.float32).astype(np.float64)))

@@ -55,11 +55,12 @@ def test_graph_gemv_and_gemm():
     aM = torch.from_numpy(synth.activations_f32(5, M, K)).cuda()
     y1 = torch.empty(N, device="cuda")
     yM = torch.empty((M, N), device="cuda")
-    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    need = max(mnb.mnb_gemv_workspace_size(w.plan), mnb.mnb_gemm_workspace_size(w.plan, M), 256)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
 
     def run():
-        mnb.mnb_gemv(w.plan, a1, y1, ws, 256)
-        mnb.mnb_gemm(w.plan, M, aM, yM, ws, 256)
+        mnb.mnb_gemv(w.plan, a1, y1, ws, need)
+        mnb.mnb_gemm(w.plan, M, aM, yM, ws, need)
 
     run()
     torch.cuda.synchronize()
