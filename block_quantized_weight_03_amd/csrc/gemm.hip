@@ -429,10 +429,11 @@ bool fast_ok(const Sizes& s, int64_t M, const void* A) {
 }
 
 struct Plan {
-  int cfg;          // index into the configuration table below
+  bool lds;         // the 256 x 256 LDS-streaming kernel (gemm_lds.hip)
+  int cfg;          // else: index into the configuration table below
   int64_t tiles_n, tiles;
   int32_t splits;
-  int64_t kc;       // K per split (multiple of 32)
+  int64_t kc;       // K per split (multiple of the kernel's K step)
 };
 
 struct CfgDesc {
@@ -443,8 +444,37 @@ constexpr CfgDesc kCfgs[] = {{256, 256}, {128, 256}, {128, 128}, {64, 256}, {32,
 constexpr int64_t kTargetWork = 256;                 // workgroups wanted (one per CU)
 constexpr uint64_t kMaxPartialBytes = 64ull << 20;  // split-K workspace bound
 
+// Splits K so that tiles * splits reaches about one workgroup per CU, with at
+// least 8 steps of `step` codes per split and a bounded partial workspace.
+void split_k(Plan& p, const Sizes& s, int64_t M, int64_t step) {
+  const int64_t ksteps = (s.K + step - 1) / step;
+  int64_t S = 1;
+  if (p.tiles < kTargetWork * 3 / 4) {
+    S = (kTargetWork + p.tiles - 1) / p.tiles;
+    const int64_t max_by_k = ksteps / 8 > 1 ? ksteps / 8 : 1;
+    if (S > max_by_k) S = max_by_k;
+    while (S > 1 && (uint64_t)S * (uint64_t)M * (uint64_t)s.N * 4 > kMaxPartialBytes) --S;
+  }
+  const int64_t steps_per = (ksteps + S - 1) / S;
+  p.splits = (int32_t)((ksteps + steps_per - 1) / steps_per);  // no empty split
+  p.kc = steps_per * step;
+}
+
+// rows of A from which the LDS-streaming kernel is used
+constexpr int64_t kLdsMinM = 1024;
+
 Plan choose(const Sizes& s, int64_t M, bool fast) {
   const int64_t N = s.N, K = s.K;
+  (void)K;
+  if (fast && M >= kLdsMinM && gemm_lds_supported(s, M)) {
+    Plan p;
+    p.lds = true;
+    p.cfg = -1;
+    p.tiles_n = (N + 255) / 256;
+    p.tiles = ((M + 255) / 256) * p.tiles_n;
+    split_k(p, s, M, 64);
+    return p;
+  }
   auto tiles_of = [&](int c) {
     return ((M + kCfgs[c].bm - 1) / kCfgs[c].bm) * ((N + kCfgs[c].bn - 1) / kCfgs[c].bn);
   };
@@ -464,21 +494,18 @@ Plan choose(const Sizes& s, int64_t M, bool fast) {
       }
   }
   Plan p;
+  p.lds = false;
   p.cfg = c;
   p.tiles_n = (N + kCfgs[c].bn - 1) / kCfgs[c].bn;
   p.tiles = tiles_of(c);
-  const int64_t ksteps = (K + kBK - 1) / kBK;
-  int64_t S = 1;
-  if (p.tiles < kTargetWork * 3 / 4) {
-    S = (kTargetWork + p.tiles - 1) / p.tiles;
-    const int64_t max_by_k = ksteps / 8 > 1 ? ksteps / 8 : 1;  // >= 8 steps per split
-    if (S > max_by_k) S = max_by_k;
-    while (S > 1 && (uint64_t)S * (uint64_t)M * (uint64_t)N * 4 > kMaxPartialBytes) --S;
-  }
-  const int64_t steps_per = (ksteps + S - 1) / S;
-  p.splits = (int32_t)((ksteps + steps_per - 1) / steps_per);  // no empty split
-  p.kc = steps_per * kBK;
+  split_k(p, s, M, kBK);
   return p;
+}
+
+uint64_t plan_ws_bytes(const Plan& p, const Sizes& s, int64_t M) {
+  uint64_t b = p.splits > 1 ? align256((uint64_t)p.splits * (uint64_t)M * (uint64_t)s.N * 4) : 0;
+  if (p.lds) b += gemm_lds_a16_bytes(s, M);
+  return b;
 }
 
 template <int BM, int BN, int WAVES_M>
@@ -523,16 +550,29 @@ hipError_t launch_cfg(const Sizes& s, const mnb_plan& p, const Plan& pl, int64_t
 uint64_t gemm_ws_bytes(const Sizes& s, int64_t M) {
   if (M <= 0) return 0;
   // the plan may differ between the fast and the general kernel: size for both
-  const Plan pf = choose(s, M, true), pg = choose(s, M, false);
-  const int64_t splits = pf.splits > pg.splits ? pf.splits : pg.splits;
-  return splits > 1 ? align256((uint64_t)splits * (uint64_t)M * (uint64_t)s.N * 4) : 0;
+  const uint64_t bf = plan_ws_bytes(choose(s, M, true), s, M);
+  const uint64_t bg = plan_ws_bytes(choose(s, M, false), s, M);
+  return bf > bg ? bf : bg;
 }
 
 hipError_t launch_gemm(const Sizes& s, const mnb_plan& p, int64_t M, const float* A, float* Y,
                        void* ws, hipStream_t st) {
   const Plan pl = choose(s, M, fast_ok(s, M, A));
-  float* part = pl.splits > 1 ? static_cast<float*>(ws) : nullptr;
   hipError_t e;
+  if (pl.lds) {
+    // workspace: [fp16 copy of A][split partials]
+    float* part = pl.splits > 1
+                      ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
+                                                 gemm_lds_a16_bytes(s, M))
+                      : nullptr;
+    e = launch_gemm_lds(s, p, M, A, ws, Y, part, pl.splits, pl.kc, st);
+    if (e != hipSuccess || pl.splits == 1) return e;
+    const int64_t MN = M * s.N;
+    hipLaunchKernelGGL(gemm_splitk_reduce, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, st,
+                       static_cast<const float*>(part), Y, MN, pl.splits);
+    return hipGetLastError();
+  }
+  float* part = pl.splits > 1 ? static_cast<float*>(ws) : nullptr;
   switch (pl.cfg) {
     case 0: e = launch_cfg<256, 256, 2>(s, p, pl, M, A, Y, part, st); break;
     case 1: e = launch_cfg<128, 256, 2>(s, p, pl, M, A, Y, part, st); break;

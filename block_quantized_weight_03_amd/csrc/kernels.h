@@ -19,6 +19,14 @@ uint64_t gemm_ws_bytes(const Sizes& s, int64_t M);
 hipError_t launch_gemm(const Sizes& s, const mnb_plan& p, int64_t M, const float* A,
                        float* Y, void* ws, hipStream_t st);
 
+// large-M kernel streaming fp16 A and the codes through LDS (gemm_lds.hip);
+// its workspace starts with an fp16 copy of A, then the split partials
+bool gemm_lds_supported(const Sizes& s, int64_t M);
+uint64_t gemm_lds_a16_bytes(const Sizes& s, int64_t M);
+hipError_t launch_gemm_lds(const Sizes& s, const mnb_plan& p, int64_t M, const float* A,
+                           void* ws, float* Y, float* part, int32_t splits, int64_t kc,
+                           hipStream_t st);
+
 // ---- INT3 QMoE (qmoe.hip) -------------------------------------------------
 struct QmoeDebug {
   int32_t* ids;

@@ -125,3 +125,26 @@ def test_gemm_rows_are_independent():
     y = run_gemm(w, a)
     y_sub = run_gemm(w, a[100:117])
     assert np.array_equal(y[100:117], y_sub)
+
+
+# M >= 1024 with K a multiple of 64 takes the 256 x 256 LDS-streaming kernel:
+# ragged M and N tails, one-stage K, every block size, zero points, split K.
+@pytest.mark.parametrize("M,K,N,bs,zp", [
+    (1100, 320, 700, 64, True), (1025, 64, 33, 32, False), (1030, 384, 257, 128, True),
+    (1300, 192, 1000, 32, False), (1040, 4096, 300, 128, True), (600, 320, 700, 64, True)])
+def test_gemm_large_m_ragged_elementwise(orc, M, K, N, bs, zp):
+    say(f"gemm large-M M={M} K={K} N={N} bs={bs} zp={zp}")
+    w, B, s, Z = prepare(K, N, bs, zp, seed=M * 7 + K + N)
+    a = synth.activations_f32(synth.seed_for(M + K, N % 251), M, K)
+    y = run_gemm(w, a)
+    check(orc, y, a, B, s, Z, K, N, bs)
+
+
+def test_gemm_large_m_rows_are_independent():
+    say("gemm large-M row independence")
+    M, K, N = 1500, 512, 2048
+    w, *_ = prepare(K, N, seed=29)
+    a = synth.activations_f32(30, M, K)
+    y = run_gemm(w, a)
+    y_sub = run_gemm(w, a[100:1300])
+    assert np.array_equal(y[100:1300], y_sub)
