@@ -206,8 +206,8 @@ def main():
     gemv_hash = source_hash("gemv.hip")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": load_traffic("gemv_int4_fused/decoder_layer", gemv_hash),
-                "kernel": "gemv_int4_fused", "launches": launches,
+                "traffic": load_traffic("gemv_int4_f32/decoder_layer", gemv_hash),
+                "kernel": "gemv_int4_f32", "launches": launches,
                 "avg_launch_us": round(avg_ms * 1e3, 3),
                 "algorithmic_bytes_per_launch": round(avg_bytes, 1)}
     per_proj = {}

@@ -22,6 +22,9 @@
 // few fp32 roundings per 32 codes, so the exact special cases stay exact
 // (integer inputs; all codes equal to the zero point give exactly 0).
 //
+// Short row streams (N up to 32768) use a plain fp32 variant of the same
+// mapping instead (below), which needs no digit planes.
+//
 // Work mapping.  A K-chunk is 64 sub-blocks (2048 codes).  Lane l of a wave
 // owns sub-block 64c + l of chunk c and keeps that chunk's 32 digit words in
 // registers; the wave walks R rows at a time with one 16-byte coalesced load
@@ -46,6 +49,7 @@ namespace {
 constexpr int kDig = 8;            // balanced base-16 digits per element
 constexpr int kBadExp = INT_MIN;   // marks a sub-block holding NaN/Inf
 constexpr int kMaxTeam = 4;        // chunks held in registers by one team
+constexpr int64_t kF32MaxRows = 32768;  // N up to which the plain fp32 path is used
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -336,6 +340,130 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) g
   }
 }
 
+// ---- plain fp32 path for small N ----------------------------------------
+//
+// When each wave only sees a few rows, building the digit planes costs more
+// than it saves.  Lane l instead keeps the 32 activations of its sub-block in
+// registers and takes every code as a sign-extended nibble: (q - z) is an
+// exact small integer, and four fp32 FMA chains per row (one per 8-code word)
+// add (q - z) * a in a fixed order; the sub-block partial is then scaled by
+// s.  Rounding: at most ~32 ulp of fp32 relative to sum |(q - z) a| per
+// sub-block; codes equal to the zero point contribute exactly 0.  A
+// non-finite activation makes every output NaN, as in the digit path.
+//
+// These launches are short, and every dispatch starts with cold instruction
+// caches, so the code is kept compact: activations come in through
+// bounds-checked buffer loads (reads past K return 0, no tail branch) and the
+// row loop is not unrolled.
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct Acts {
+  float a[32];
+  float poison;
+};
+
+__device__ __forceinline__ void load_acts(Acts& x, const float* __restrict__ A, int64_t K,
+                                          int32_t sb) {
+  // raw buffer over exactly K floats: out-of-range dwords read as 0
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(A), (short)0, (int)(K * 4), 0x00020000);
+  const uint32_t off = (uint32_t)sb * 128u;
+  float p = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const f32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u * i, 0, 0);
+    x.a[4 * i] = v.x;
+    x.a[4 * i + 1] = v.y;
+    x.a[4 * i + 2] = v.z;
+    x.a[4 * i + 3] = v.w;
+  }
+  // a * 0 is 0 for finite a and NaN otherwise
+#pragma unroll
+  for (int i = 0; i < 32; ++i) p = fmaf(x.a[i], 0.0f, p);
+  x.poison = p;
+}
+
+template <bool HAS_ZP>
+__device__ __forceinline__ float subblock_dot_f32(const u32x4 q, const Acts& x, float s, int z) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  float acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc[i] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      int v = (int)(w[i] << (28 - 4 * e)) >> 28;  // stored nibble = q - 8, sign-extended
+      if (HAS_ZP) v += 8 - z;
+      acc[i] = fmaf((float)v, x.a[8 * i + e], acc[i]);
+    }
+  }
+  return ((acc[0] + acc[1]) + (acc[2] + acc[3])) * s + x.poison;
+}
+
+template <int R, bool HAS_ZP>
+__global__ void __launch_bounds__(256) gemv_int4_f32(
+    const float* __restrict__ A, const uint8_t* __restrict__ codes,
+    const float* __restrict__ scales, const uint32_t* __restrict__ zeros, float* __restrict__ Y,
+    int64_t K, int64_t N, int64_t row_bytes, int64_t nb, int32_t nsb, int32_t nchunk,
+    int32_t bs_shift, int64_t zrow) {
+  __shared__ __align__(16) float red_all[kMaxTeam * R * 64];
+  __shared__ float tot[kMaxTeam * R];
+
+  const int team = nchunk;
+  const int nwaves = (int)(blockDim.x >> 6);
+  const int teams = nwaves / team;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = (int)(threadIdx.x & 63);
+  const int tm = wave / team, wit = wave - tm * team;
+
+  const int32_t sb = wit * 64 + lane;
+  const bool act = sb < nsb;
+  const uint32_t qoff = (uint32_t)sb * 16u;
+  const uint32_t b = (uint32_t)sb >> bs_shift;
+
+  const int64_t nrg = (N + R - 1) / R;
+  const int64_t stride = (int64_t)gridDim.x * teams;
+  const int64_t base0 = (int64_t)blockIdx.x * teams;
+  const int64_t iters = base0 < nrg ? (nrg - base0 + stride - 1) / stride : 0;
+  int64_t rg = base0 + tm;
+
+  RowTile<R, HAS_ZP> cur, nxt;
+  if (iters > 0) load_rows<R, HAS_ZP>(cur, codes, scales, zeros, rg * R, rg < nrg ? N : 0, row_bytes, nb, zrow, qoff, b, act);
+  Acts x;
+  load_acts(x, A, K, sb);
+  float* red = red_all + wave * R * 64;
+  constexpr int P = 64 / R;
+
+#pragma unroll 1
+  for (int64_t it = 0; it < iters; ++it) {
+    const int64_t rgn = rg + stride;
+    if (it + 1 < iters)
+      load_rows<R, HAS_ZP>(nxt, codes, scales, zeros, rgn * R, rgn < nrg ? N : 0, row_bytes, nb, zrow, qoff, b, act);
+    float part[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) part[r] = subblock_dot_f32<HAS_ZP>(cur.q[r], x, cur.s[r], (int)((cur.zpk >> (4 * r)) & 15u));
+    const float v = wave_reduce_rows<R>(part, red, lane);
+    const int r = lane / P;
+    if (team == 1) {
+      const int64_t n = rg * R + r;
+      if ((lane % P) == 0 && rg < nrg && n < N) Y[n] = v;
+    } else {
+      if ((lane % P) == 0) tot[wave * R + r] = v;
+      __syncthreads();
+      if (wit == 0 && lane < R) {
+        float out = 0.0f;
+        for (int w = 0; w < team; ++w) out += tot[(tm * team + w) * R + lane];
+        const int64_t nn = rg * R + lane;
+        if (rg < nrg && nn < N) Y[nn] = out;
+      }
+      __syncthreads();
+    }
+    cur = nxt;
+    rg = rgn;
+  }
+}
+
 // K > 8192: digits precomputed in the workspace, each wave walks its chunks.
 template <int R, bool HAS_ZP>
 __global__ void __launch_bounds__(256) gemv_int4_ws(
@@ -427,6 +555,23 @@ hipError_t launch_fused(const Sizes& s, const mnb_plan& p, const float* A, float
 }
 
 template <int R, bool HAS_ZP>
+hipError_t launch_f32(const Sizes& s, const mnb_plan& p, const float* A, float* Y, int64_t nsb,
+                      int64_t nchunk, hipStream_t st) {
+  const int team = (int)nchunk;
+  const int teams = kMaxTeam / team;
+  const int64_t nrg = (s.N + R - 1) / R;
+  int64_t blocks = (nrg + teams - 1) / teams;
+  const int64_t cap = (int64_t)cu_count() * 8;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL((gemv_int4_f32<R, HAS_ZP>), dim3((unsigned)blocks), dim3(64 * team * teams),
+                     0, st, A, static_cast<const uint8_t*>(p.codes),
+                     static_cast<const float*>(p.scales), static_cast<const uint32_t*>(p.zeros), Y,
+                     s.K, s.N, s.row_bytes, s.nb, (int32_t)nsb, (int32_t)nchunk, bs_shift_of(s),
+                     (int64_t)s.zrow);
+  return hipGetLastError();
+}
+
+template <int R, bool HAS_ZP>
 hipError_t launch_ws(const Sizes& s, const mnb_plan& p, const float* A, float* Y, void* ws,
                      int64_t nsb, int64_t nchunk, hipStream_t st) {
   const WsLayout L = ws_layout(nchunk);
@@ -458,6 +603,11 @@ hipError_t dispatch(const Sizes& s, const mnb_plan& p, const float* A, float* Y,
   const int64_t nsb = n_subblocks(s);
   const int64_t nchunk = (nsb + 63) / 64;
   if (nchunk > kMaxTeam) return launch_ws<8, HAS_ZP>(s, p, A, Y, ws, nsb, nchunk, st);
+  // few rows per wave: the plain fp32 path (measured faster up to tens of
+  // thousands of rows; the digit planes pay off on long row streams)
+  if (s.N <= kF32MaxRows)
+    return s.N <= 2048 ? launch_f32<2, HAS_ZP>(s, p, A, Y, nsb, nchunk, st)
+                       : launch_f32<4, HAS_ZP>(s, p, A, Y, nsb, nchunk, st);
   // rows per wave iteration: enough row groups to fill the chip for small N,
   // deeper load batches for large N
   const int64_t teams = kMaxTeam / nchunk;
