@@ -605,9 +605,10 @@ hipError_t dispatch(const Sizes& s, const mnb_plan& p, const float* A, float* Y,
   if (nchunk > kMaxTeam) return launch_ws<8, HAS_ZP>(s, p, A, Y, ws, nsb, nchunk, st);
   // few rows per wave: the plain fp32 path (measured faster up to tens of
   // thousands of rows; the digit planes pay off on long row streams)
+  // (two rows per wave step while that keeps about 1024 waves busy, else four)
   if (s.N <= kF32MaxRows)
-    return s.N <= 2048 ? launch_f32<2, HAS_ZP>(s, p, A, Y, nsb, nchunk, st)
-                       : launch_f32<4, HAS_ZP>(s, p, A, Y, nsb, nchunk, st);
+    return s.N * nchunk <= 2048 ? launch_f32<2, HAS_ZP>(s, p, A, Y, nsb, nchunk, st)
+                                : launch_f32<4, HAS_ZP>(s, p, A, Y, nsb, nchunk, st);
   // rows per wave iteration: enough row groups to fill the chip for small N,
   // deeper load batches for large N
   const int64_t teams = kMaxTeam / nchunk;
