@@ -154,7 +154,28 @@ void prepack(const Sizes& s, const uint8_t* B, const void* scales,
       }
     }
   } else {
-    std::memcpy(codes, B, s.codes);
+    // contract rows are LSB-first 3-bit streams; regroup every 32 codes into
+    // the pair-interleaved words (same byte count per row)
+    for (int64_t row = 0; row < s.rows; ++row) {
+      const uint8_t* src = B + (uint64_t)row * (uint64_t)s.row_bytes;
+      uint8_t* out = codes + (uint64_t)row * (uint64_t)s.row_bytes;
+      for (int64_t G = 0; G < s.K / 32; ++G) {
+        uint32_t w[3] = {0, 0, 0};
+        for (int i = 0; i < 32; ++i) {
+          uint32_t q = 0;
+          for (int t = 0; t < 3; ++t) {
+            const int64_t bit = 3 * (32 * G + i) + t;
+            q |= (uint32_t)((src[bit >> 3] >> (bit & 7)) & 1u) << t;
+          }
+          if (i < 30) {
+            w[int3_word(i)] |= q << int3_bit(i);
+          } else {
+            for (int t = 0; t < 3; ++t) w[t] |= ((q >> t) & 1u) << (i == 30 ? 15 : 31);
+          }
+        }
+        std::memcpy(out + 12 * G, w, 12);
+      }
+    }
   }
   std::memcpy(dst + s.off_scales, scales, s.scales);
   if (s.zeros) {
@@ -225,10 +246,14 @@ void unpack_host(const Sizes& s, const mnb_plan* p, int64_t expert,
           const uint8_t byte = src[b * (s.bs / 2) + j / 2];
           q = ((j & 1) ? (byte >> 4) : (byte & 15u)) ^ 8u;
         } else {
-          q = 0;
-          for (int t = 0; t < 3; ++t) {
-            const int64_t bit = 3 * k + t;
-            q |= ((src[bit >> 3] >> (bit & 7)) & 1u) << t;
+          uint32_t w[3];
+          std::memcpy(w, src + 12 * (k / 32), 12);
+          const int i = (int)(k % 32);
+          if (i < 30) {
+            q = (w[int3_word(i)] >> int3_bit(i)) & 7u;
+          } else {
+            q = 0;
+            for (int t = 0; t < 3; ++t) q |= ((w[t] >> (i == 30 ? 15 : 31)) & 1u) << t;
           }
         }
         codes[(uint64_t)r * (uint64_t)s.K + (uint64_t)k] = (uint8_t)q;

@@ -16,12 +16,22 @@ constexpr uint32_t kPlanMagic = 0x4D4E4250u;  // "MNBP"
 //              scales fp32 [N][nb]; zero points (if explicit) as uint32 words
 //              [ceil(N/8)][nb], nibble r of word (g, b) holding the zero point
 //              of row 8g + r, block b (one load gives a row group's points).
-//  INT3 QMoE:  codes [E*N][3K/8] row-local LSB-first (unchanged);
-//              scales fp16 [E*N][K/bs].
-constexpr uint32_t kLayoutVersion = 2;
+//  INT3 QMoE:  codes [E*N][3K/8], the same bytes per row as the contract,
+//              regrouped for the matrix-core dequantization: each group of 32
+//              codes c0..c31 (k = 32G + i) is three 32-bit words w0, w1, w2;
+//              word m holds the pairs (c[10m+2p], c[10m+2p+1]) for p = 0..4 at
+//              bits [3p, 3p+3) and [16+3p, 16+3p+3), so (w >> 3p) & 0x00070007
+//              puts a pair in the two 16-bit halves; bit t of c30 is bit 15 of
+//              w_t and bit t of c31 is bit 31 of w_t.  Scales fp16 [E*N][K/bs].
+constexpr uint32_t kLayoutVersion = 3;
 constexpr uint64_t kSectionAlign = 256;
 
 enum Kind : int32_t { kDenseInt4 = 1, kMoeInt3 = 2 };
+
+// Word (within its group of three) and bit offset of INT3 code i (0..31) of a
+// group, for the codes stored in one 3-bit field (i < 30).
+constexpr int int3_word(int i) { return i / 10; }
+constexpr int int3_bit(int i) { return 3 * ((i % 10) / 2) + 16 * (i % 2); }
 
 struct Sizes {
   Kind kind;

@@ -3,8 +3,8 @@
 // check the prepacked bytes and the rounding chain bit-exactly against the
 // oracle (onnxruntime PR "INT3 QMoE CUDA correctness baseline and Qwen
 // experimental results", embedded P0/P1 body, section "P0: Portable Format
-// and Numerical References": row-local LSB-first codes; INT3 decodes as
-// (code - 4) * scale).
+// and Numerical References": INT3 decodes as (code - 4) * scale); the INT3
+// codes are read from the private pair-interleaved groups.
 
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
@@ -29,12 +29,12 @@ __device__ __forceinline__ unsigned code_of(const Rows& r, int64_t row, int64_t 
     const uint8_t byte = src[b * (r.bs / 2) + j / 2];
     return (((j & 1) ? (byte >> 4) : byte) & 15u) ^ 8u;
   }
-  unsigned q = 0;
-  for (int t = 0; t < 3; ++t) {
-    const int64_t bit = 3 * k + t;
-    q |= ((src[bit >> 3] >> (bit & 7)) & 1u) << t;
-  }
-  return q;
+  // INT3: pair-interleaved groups of three words per 32 codes
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(src + 12 * (k / 32));
+  const int i = (int)(k % 32);
+  if (i < 30) return (w[int3_word(i)] >> int3_bit(i)) & 7u;
+  const int b = i == 30 ? 15 : 31;
+  return ((w[0] >> b) & 1u) | (((w[1] >> b) & 1u) << 1) | (((w[2] >> b) & 1u) << 2);
 }
 
 __global__ void debug_unpack_kernel(Rows r, int64_t nrows, uint8_t* __restrict__ out) {

@@ -19,9 +19,10 @@
 //              T*k slots into expert-grouped order that is stable in (token,
 //              rank) order, and the list of (expert, row-tile) work items.
 //  3. fc1:     per work item, G = X_e W1_e^T on the matrix cores (gathered
-//              token rows; INT3 tiles dequantized into LDS as
-//              fp16((q - 4) * s)); epilogue h_i = silu(g_i) * u_i from the
-//              interleaved gate/up columns, rounded to fp16.
+//              token rows in LDS; INT3 weights dequantized in registers as
+//              fp16((q - 4) * s), once per item); epilogue
+//              h_i = silu(g_i) * u_i from the interleaved gate/up columns,
+//              rounded to fp16.
 //  4. fc2:     per work item, Y_e = h_e W2_e^T; epilogue multiplies by the
 //              slot's routing weight and writes an fp32 slot row.
 //  5. combine: out[t] = fp16(sum_j slot[t, j]) in rank order (deterministic).
@@ -42,20 +43,43 @@ typedef unsigned int u32x3 __attribute__((ext_vector_type(3), aligned(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTokTile = 512;   // tokens per pass (bounds the workspace)
+constexpr int kDecodeSlots = 32; // T * k up to which the per-slot decode path runs
 constexpr int kMaxE = 1024;     // experts supported by the grouping kernel
-constexpr int kBM = 32;         // token rows per work item
-constexpr int kBN = 64;         // weight rows per workgroup
-constexpr int kBK = 128;        // K per step
-constexpr int kPitch = kBK + 8; // LDS pitch (halves): conflict-free fragment reads
 constexpr int kGroupThreads = 1024;
 
 // ---------------------------------------------------------------------------
 // 1. routing
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
-  return v1 > v2 || (v1 == v2 && i1 < i2);
+// Order-preserving key of a logit: larger logit -> larger unsigned key; NaN
+// ranks with -inf; key 0 marks an expert that is taken or absent.
+__device__ __forceinline__ uint32_t logit_key(float x) {
+  if (x != x) x = -INFINITY;
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_logit(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+// Wave-wide reductions with DPP moves (no LDS round trips): after the row
+// steps every lane of a 16-lane row holds the row result, the two broadcasts
+// fold the rows into lane 63, which is read back as a uniform value.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
+  auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// One wave per token: k rounds of "largest logit, lower expert on ties" over
+// the E <= 1024 experts (lane l holds experts 64i + l), then
+// r_j = exp(l_j - l_max) / sum_sel exp(l_i - l_max) in fp32, which equals an
+// fp32 softmax over all experts renormalized over the selected ones.
 __global__ void __launch_bounds__(256) qmoe_route(const float* __restrict__ logits, int64_t T,
                                                   int E, int k, int32_t* __restrict__ ids,
                                                   float* __restrict__ wts) {
@@ -63,50 +87,44 @@ __global__ void __launch_bounds__(256) qmoe_route(const float* __restrict__ logi
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (t >= T) return;  // whole waves leave together
+  const int nper = (E + 63) >> 6;
   const float* l = logits + t * E;
-  float v[kPer];
-  uint32_t taken = 0;
+  uint32_t key[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int e = i * 64 + lane;
-    const float x = e < E ? l[e] : 0.0f;
-    v[i] = x != x ? -INFINITY : x;  // NaN ranks last, so k <= E picks are always valid
+    key[i] = (i < nper && e < E) ? logit_key(l[e]) : 0u;
   }
-  float lmax = 0.0f, den = 0.0f;
-  float sel_v[16];
+  float lmax = 0.0f, den = 0.0f, sel_v[16];
   int sel_i[16];
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+  for (int j = 0; j < k; ++j) {  // k <= 16 (checked by the launcher)
+    // this lane's best: largest key, lowest i on ties (= lowest expert)
+    uint32_t bk = 0;
+    int bi = 0;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int e = i * 64 + lane;
-      if (e < E && !((taken >> i) & 1u) && better(v[i], e, bv, bi)) {
-        bv = v[i];
-        bi = e;
+    for (int i = 0; i < kPer; ++i)
+      if (i < nper && key[i] > bk) {
+        bk = key[i];
+        bi = i;
       }
-    }
+    const uint32_t mk = wave_reduce_u32<true>(bk);
+    // lowest expert index among the lanes holding the maximum
+    const uint32_t cand = (bk == mk) ? (uint32_t)(bi * 64 + lane) : 0xFFFFFFFFu;
+    const int win = (int)wave_reduce_u32<false>(cand);
+    if ((win & 63) == lane) {
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float ov = __shfl_xor(bv, m);
-      const int oi = __shfl_xor(bi, m);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
+      for (int i = 0; i < kPer; ++i)
+        if (i == (win >> 6)) key[i] = 0u;
     }
-    // every lane now holds the same winner
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (j == 0) lmax = bv;
-    const float ex = expf(bv - lmax);
+    const float v = key_logit(mk);
+    if (j == 0) lmax = v;
+    const float ex = expf(v - lmax);
     den += ex;
-    if (j < 16) {
-      sel_v[j] = ex;
-      sel_i[j] = bi;
-    }
+    sel_v[j] = ex;
+    sel_i[j] = win;
   }
   if (lane == 0) {
-    for (int j = 0; j < k && j < 16; ++j) {
+    for (int j = 0; j < k; ++j) {
       ids[t * k + j] = sel_i[j];
       wts[t * k + j] = sel_v[j] / den;
     }
@@ -129,7 +147,7 @@ struct GroupOut {
 
 __global__ void __launch_bounds__(kGroupThreads) qmoe_group(const int32_t* __restrict__ ids,
                                                             int64_t T, int k, int E, int64_t max_items,
-                                                            GroupOut o) {
+                                                            int bm, GroupOut o) {
   extern __shared__ __align__(16) int32_t gsm[];
   int32_t* cnt = gsm;                 // [E]
   int32_t* off = cnt + E;             // [E + 1]
@@ -153,7 +171,7 @@ __global__ void __launch_bounds__(kGroupThreads) qmoe_group(const int32_t* __res
     for (int e = 0; e < E; ++e) {
       off[e] = acc;
       acc += cnt[e];
-      for (int32_t m0 = 0; m0 < cnt[e] && items < max_items; m0 += kBM, ++items) {
+      for (int32_t m0 = 0; m0 < cnt[e] && items < max_items; m0 += bm, ++items) {
         o.items[2 * items] = e;
         o.items[2 * items + 1] = m0;
       }
@@ -213,41 +231,55 @@ __global__ void __launch_bounds__(kGroupThreads) qmoe_group(const int32_t* __res
 // ---------------------------------------------------------------------------
 // 3./4. grouped INT3 GEMM (FC1 with SwiGLU epilogue, FC2 with route weights)
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t cvt_pk_rn(float a, float b) {
-  const half2v h = half2v{(_Float16)a, (_Float16)b};
+//
+// A workgroup takes one work item (expert e, up to BM of its tokens) and 64
+// weight rows; wave w owns rows [16w, 16w + 16) and computes them for all of
+// the item's tokens with v_mfma_f32_16x16x32_f16 (C tiles of 16 tokens x 16
+// rows).  The weights never go through LDS: lane (n, g) = (lane & 15,
+// lane >> 4) loads the 12-byte group g (32 codes, k = 32g .. 32g + 31 of a
+// 128-wide K chunk) of its row straight into registers and dequantizes it once
+// for every token of the item.  K order inside an MFMA is free when both
+// operands share it: MFMA t of a chunk takes k = 32g + 8t + [0, 8) in lane
+// group g, on both sides.  The token rows of the chunk (gathered by route for
+// FC1, contiguous grouped rows for FC2) are staged in LDS (pitch 136 halves:
+// the 16 rows of an operand read fall on distinct banks), double-buffered.
+//
+// Dequantization of a pair of codes from the private layout: one shift and one
+// and-or give the fp16 values 1024 + q in both halves, v_pk_add_f16 makes the
+// exact q - 4, v_pk_mul_f16 by the fp16 scale rounds once: fp16((q - 4) * s),
+// the same value as the exact fp32 product rounded to fp16.
+
+typedef _Float16 half2t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t int3_pair_scale(uint32_t bits, half2t s2) {
+  half2t h = __builtin_bit_cast(half2t, bits | 0x64006400u);  // 1024 + q
+  h = (h + half2t{(_Float16)-1028.0f, (_Float16)-1028.0f}) * s2;  // (q - 4) * s
   return __builtin_bit_cast(uint32_t, h);
 }
 
-// 3-bit code j (0..31) of a 96-bit little-endian stream held in d0, d1, d2.
-template <int J>
-__device__ __forceinline__ uint32_t code3(uint32_t d0, uint32_t d1, uint32_t d2) {
-  constexpr int bit = 3 * J;
-  if constexpr (bit + 3 <= 32) return (d0 >> bit) & 7u;
-  else if constexpr (bit < 32) return __builtin_amdgcn_alignbit(d1, d0, bit) & 7u;
-  else if constexpr (bit + 3 <= 64) return (d1 >> (bit - 32)) & 7u;
-  else if constexpr (bit < 64) return __builtin_amdgcn_alignbit(d2, d1, bit - 32) & 7u;
-  else return (d2 >> (bit - 64)) & 7u;
-}
-
-template <int J>
-__device__ __forceinline__ void dequant_pairs(uint32_t d0, uint32_t d1, uint32_t d2, float s,
-                                              uint32_t* out) {
-  if constexpr (J < 32) {
-    // (q - 4) * s is exact in fp32 (3-bit integer times an fp16 value), so the
-    // packed conversion rounds once: fp16((q - 4) * s)
-    const float a = ((float)code3<J>(d0, d1, d2) - 4.0f) * s;
-    const float b = ((float)code3<J + 1>(d0, d1, d2) - 4.0f) * s;
-    out[J / 2] = cvt_pk_rn(a, b);
-    dequant_pairs<J + 2>(d0, d1, d2, s, out);
+// the 32 codes of one group as four MFMA operands (8 consecutive k each)
+__device__ __forceinline__ void dequant_group(const u32x3 w, _Float16 s, half8 (&out)[4]) {
+  const half2t s2 = half2t{s, s};
+  uint32_t p[16];
+#pragma unroll
+  for (int m = 0; m < 3; ++m) {
+    const uint32_t x = m == 0 ? w.x : (m == 1 ? w.y : w.z);
+#pragma unroll
+    for (int q = 0; q < 5; ++q) p[5 * m + q] = int3_pair_scale((x >> (3 * q)) & 0x00070007u, s2);
   }
+  p[15] = int3_pair_scale(((w.x >> 15) & 0x00010001u) | ((w.y >> 14) & 0x00020002u) |
+                              ((w.z >> 13) & 0x00040004u), s2);
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    out[t] = __builtin_bit_cast(half8, u32x4{p[4 * t], p[4 * t + 1], p[4 * t + 2], p[4 * t + 3]});
 }
 
 struct MoeGemmArgs {
-  const uint8_t* codes;    // [E][N][row_bytes]
+  const uint8_t* codes;    // [E][N][row_bytes], pair-interleaved groups
   const __half* scales;    // [E][N][K/bs]
   const void* act;         // FC1: x fp16 [T][K]; FC2: h fp16 [T*k][K] (grouped order)
   int64_t N, K, row_bytes, nblk, bs;
-  int top_k;
+  int top_k, E;
   const int32_t* counts;
   const int32_t* offsets;
   const int32_t* perm;
@@ -258,102 +290,128 @@ struct MoeGemmArgs {
   float* slot_out;         // FC2 output [T*k][N] (slot order)
 };
 
-template <bool FC1>
+constexpr int kQBN = 64;         // weight rows per workgroup
+constexpr int kQBK = 128;        // K per chunk
+constexpr int kQPitch = kQBK + 8;
+
+template <bool FC1, int BM>
 __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t tiles_n) {
-  __shared__ __align__(16) _Float16 As[kBM * kPitch];
-  __shared__ __align__(16) _Float16 Ws[kBN * kPitch];
-  __shared__ int32_t arow[kBM];  // activation row index of each tile row (-1: none)
+  constexpr int TM = BM / 16;          // 16-token MFMA tiles
+  constexpr int AP = BM * 16 / 256;    // 16-byte activation chunks per thread and chunk
+  __shared__ __align__(16) _Float16 As[2][BM * kQPitch];
+  __shared__ int32_t arow[BM];  // activation row of each tile row (-1: none)
 
   const int64_t item = blockIdx.x / tiles_n;
   const int64_t nt = blockIdx.x % tiles_n;
   if (item >= *g.nitems) return;  // uniform for the workgroup
   const int e = g.items[2 * item];
   const int m0 = g.items[2 * item + 1];
-  const int rows = min(kBM, g.counts[e] - m0);
+  const int rows = min(BM, g.counts[e] - m0);
+  const int vt = (rows + 15) >> 4;       // valid token tiles
   const int64_t seg0 = g.offsets[e] + m0;  // grouped position of tile row 0
-  const int64_t n0 = nt * kBN;
+  const int64_t n0 = nt * kQBN;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (tid < kBM) {
+  for (int i = tid; i < BM; i += 256) {
     int32_t r = -1;
-    if (tid < rows) r = FC1 ? g.perm[seg0 + tid] / g.top_k : (int32_t)(seg0 + tid);
-    arow[tid] = r;
+    if (i < rows) r = FC1 ? g.perm[seg0 + i] / g.top_k : (int32_t)(seg0 + i);
+    arow[i] = r;
   }
   __syncthreads();
 
-  // staging: activations 32 rows x 128 halves (8 threads per row, 32 B each),
-  // weights 64 rows x 48 bytes (4 threads per row, 12 B = 32 codes each)
-  const int a_r = tid >> 3, a_c = (tid & 7) * 16;
-  const int w_r = tid >> 2, w_q = tid & 3;
-  const int32_t my_arow = arow[a_r];
-  const int64_t wrow = n0 + w_r;
-  const uint8_t* wsrc = g.codes + ((int64_t)e * g.N + wrow) * g.row_bytes;
-  const __half* ssrc = g.scales + ((int64_t)e * g.N + wrow) * g.nblk;
+  // activation staging: thread -> chunk (tid & 15) of rows (tid >> 4) + 16 j
+  const int a_c = (tid & 15) * 8, a_r0 = tid >> 4;
+  int32_t my_arow[AP];
+#pragma unroll
+  for (int j = 0; j < AP; ++j) my_arow[j] = arow[a_r0 + 16 * j];
   const _Float16* act = static_cast<const _Float16*>(g.act);
+  // weights: lane (n, gi) = (lane & 15, lane >> 4), row n0 + 16 wave + n
+  const int wn = lane & 15, wg = lane >> 4;
+  const int64_t wrow = n0 + wave * 16 + wn;
+  const bool wvalid = wrow < g.N;
+  const uint8_t* wsrc = g.codes + ((int64_t)e * g.N + (wvalid ? wrow : 0)) * g.row_bytes;
+  const __half* ssrc = g.scales + ((int64_t)e * g.N + (wvalid ? wrow : 0)) * g.nblk;
 
-  u32x4 ra0, ra1;
-  u32x3 rw;
-  float rs;
-  auto load_step = [&](int64_t k0) {
-    ra0 = u32x4{0, 0, 0, 0};
-    ra1 = u32x4{0, 0, 0, 0};
-    if (my_arow >= 0 && k0 + a_c < g.K) {  // K is a multiple of 32: chunks are whole
-      const u32x4* src = reinterpret_cast<const u32x4*>(act + (int64_t)my_arow * g.K + k0 + a_c);
-      ra0 = src[0];
-      ra1 = src[1];
+  // Register staging is double-buffered: the loads of chunk c + 1 are issued
+  // one chunk ahead and land in LDS (activations) or are dequantized
+  // (weights) while chunk c computes.
+  struct Stage {
+    u32x4 ra[AP];
+    u32x3 rw;
+    _Float16 rs;
+  };
+  auto load_chunk = [&](Stage& st, int64_t k0) {
+#pragma unroll
+    for (int j = 0; j < AP; ++j) {
+      st.ra[j] = u32x4{0, 0, 0, 0};
+      if (my_arow[j] >= 0 && k0 + a_c < g.K)  // K is a multiple of 32: chunks are whole
+        st.ra[j] = *reinterpret_cast<const u32x4*>(act + (int64_t)my_arow[j] * g.K + k0 + a_c);
     }
-    rw = u32x3{0, 0, 0};
-    rs = 0.0f;
-    if (wrow < g.N && k0 + w_q * 32 < g.K) {
-      rw = *reinterpret_cast<const u32x3*>(wsrc + (k0 / 8) * 3 + w_q * 12);
-      rs = __half2float(ssrc[(k0 + w_q * 32) / g.bs]);
+    st.rw = u32x3{0, 0, 0};
+    st.rs = (_Float16)0.0f;
+    const int64_t kg = k0 + 32 * wg;  // first code of this lane's group
+    if (wvalid && kg < g.K) {
+      st.rw = *reinterpret_cast<const u32x3*>(wsrc + (kg / 32) * 12);
+      st.rs = __builtin_bit_cast(_Float16, ssrc[kg / g.bs]);
     }
   };
-  auto store_step = [&]() {
-    *reinterpret_cast<u32x4*>(&As[a_r * kPitch + a_c]) = ra0;
-    *reinterpret_cast<u32x4*>(&As[a_r * kPitch + a_c + 8]) = ra1;
-    uint32_t out[16];
-    dequant_pairs<0>(rw.x, rw.y, rw.z, rs, out);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(&Ws[w_r * kPitch + w_q * 32]);
+  auto store_chunk = [&](const Stage& st, int b) {
 #pragma unroll
-    for (int i = 0; i < 16; i += 4) *reinterpret_cast<u32x4*>(dst + i) = u32x4{out[i], out[i + 1], out[i + 2], out[i + 3]};
+    for (int j = 0; j < AP; ++j)
+      *reinterpret_cast<u32x4*>(&As[b][(a_r0 + 16 * j) * kQPitch + a_c]) = st.ra[j];
   };
 
-  f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-  const int fr = lane & 15, fk = (lane >> 4) * 8;
-  load_step(0);
-  store_step();
-  __syncthreads();
-  for (int64_t k0 = 0; k0 < g.K; k0 += kBK) {
-    const bool more = k0 + kBK < g.K;
-    if (more) load_step(k0 + kBK);
+  f32x4 acc[TM];
 #pragma unroll
-    for (int kk = 0; kk < kBK; kk += 32) {
-      const half8 b = *reinterpret_cast<const half8*>(&Ws[(wave * 16 + fr) * kPitch + kk + fk]);
-      const half8 a0 = *reinterpret_cast<const half8*>(&As[fr * kPitch + kk + fk]);
-      const half8 a1 = *reinterpret_cast<const half8*>(&As[(16 + fr) * kPitch + kk + fk]);
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b, acc1, 0, 0, 0);
+  for (int i = 0; i < TM; ++i) acc[i] = f32x4{0, 0, 0, 0};
+  const int fr = lane & 15;
+
+  // chunk c: dequantize its weights (stage cur), let its activations (LDS
+  // buffer b) feed the MFMAs, then move chunk c + 1 (stage nxt, loaded one
+  // chunk ago) into the other buffer and start the loads of chunk c + 2
+  auto step = [&](Stage& cur, Stage& nxt, int b, int64_t k0) {
+    half8 wf[4];
+    dequant_group(cur.rw, cur.rs, wf);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int kk = 32 * wg + 8 * t;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        if (i < vt) {
+          const half8 a = *reinterpret_cast<const half8*>(&As[b][(i * 16 + fr) * kQPitch + kk]);
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, wf[t], acc[i], 0, 0, 0);
+        }
+      }
     }
-    __syncthreads();
-    if (more) {
-      store_step();
+    if (k0 + kQBK < g.K) {
+      store_chunk(nxt, b ^ 1);
+      if (k0 + 2 * kQBK < g.K) load_chunk(cur, k0 + 2 * kQBK);
       __syncthreads();
     }
+  };
+
+  Stage s0, s1;
+  load_chunk(s0, 0);
+  if (kQBK < g.K) load_chunk(s1, kQBK);
+  store_chunk(s0, 0);
+  __syncthreads();
+  for (int64_t k0 = 0; k0 < g.K; k0 += 2 * kQBK) {
+    step(s0, s1, 0, k0);
+    if (k0 + kQBK >= g.K) break;
+    step(s1, s0, 1, k0 + kQBK);
   }
 
-  // lane l holds rows 4(l/16) + r of each 16-row tile, column l%16
+  // lane l holds tokens 16i + 4(l/16) + r of tile i, weight row l%16
   const int64_t col = n0 + wave * 16 + (lane & 15);
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const f32x4 a = mt ? acc1 : acc0;
+  for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = mt * 16 + 4 * (lane >> 4) + r;
-      const float v = a[r];
+      const int row = i * 16 + 4 * (lane >> 4) + r;
+      const float v = acc[i][r];
       if (FC1) {
-        // interleaved gate/up: even column = gate_i, odd column = up_i
+        // interleaved gate/up: even row = gate_i, odd row = up_i
         const float partner = __shfl_xor(v, 1);
         if ((lane & 1) == 0 && row < rows && col < g.N) {
           const float gt = v, up = partner;
@@ -367,6 +425,113 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t tiles_n)
         }
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode path (a few tokens): no grouping, no slot buffer.  Each selected
+// (token, rank) pair is its own GEMV: with T * k small every pair reads its
+// expert's weights once, which is what the grouped path would read as well.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x140, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Reinterprets a 32-bit word as two halves.  The word is taken by value: this
+// compiler folds __builtin_bit_cast of a vector element (v.y, v.z, v.w) to a
+// read of element .x, so elements are always copied into a scalar first.
+__device__ __forceinline__ half2t as_half2(uint32_t v) { return __builtin_bit_cast(half2t, v); }
+
+// sum_k w_k a_k over one 32-code group: w = fp16((q - 4) s), a fp16 (16 B x 4)
+__device__ __forceinline__ float group_dot(const u32x3 w, _Float16 s, const u32x4* a16) {
+  half8 wf[4];
+  dequant_group(w, s, wf);
+  float acc = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const u32x4 av = a16[t];
+    const u32x4 wv = __builtin_bit_cast(u32x4, wf[t]);
+    acc = __builtin_amdgcn_fdot2(as_half2(wv.x), as_half2(av.x), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_half2(wv.y), as_half2(av.y), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_half2(wv.z), as_half2(av.z), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_half2(wv.w), as_half2(av.w), acc, false);
+  }
+  return acc;
+}
+
+// FC1 + SwiGLU: one wave per (token t, rank j, i): rows 2i (gate) and 2i + 1
+// (up) of expert ids[t, j]; lane l takes the 32-code groups l, l + 64, ...
+// h[(t k + j) I + i] = fp16(silu(g) u).
+__global__ void __launch_bounds__(256) qmoe_fc1_decode(MoeGemmArgs g, int64_t T) {
+  const int lane = threadIdx.x & 63;
+  const int64_t I = g.N / 2, pairs = T * g.top_k * I;
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  const int ng = (int)(g.K / 32);
+  const _Float16* x = static_cast<const _Float16*>(g.act);
+  for (int64_t p = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); p < pairs;
+       p += nwaves) {
+    const int64_t slot = p / I, i = p % I, t = slot / g.top_k;
+    const int e = clamp_id(g.perm[slot], g.E);  // perm holds the routed ids here
+    const int64_t row = (int64_t)e * g.N + 2 * i;
+    float gs = 0.0f, us = 0.0f;
+    for (int gi = lane; gi < ng; gi += 64) {
+      const u32x4* a = reinterpret_cast<const u32x4*>(x + t * g.K + 32 * gi);
+      const u32x4 av[4] = {a[0], a[1], a[2], a[3]};
+      const u32x3 wg = *reinterpret_cast<const u32x3*>(g.codes + row * g.row_bytes + 12 * gi);
+      const u32x3 wu = *reinterpret_cast<const u32x3*>(g.codes + (row + 1) * g.row_bytes + 12 * gi);
+      const int b = (32 * gi) / (int)g.bs;
+      gs += group_dot(wg, __builtin_bit_cast(_Float16, g.scales[row * g.nblk + b]), av);
+      us += group_dot(wu, __builtin_bit_cast(_Float16, g.scales[(row + 1) * g.nblk + b]), av);
+    }
+    gs = wave_sum_f32(gs);
+    us = wave_sum_f32(us);
+    if (lane == 0) g.h_out[slot * I + i] = __float2half_rn(gs / (1.0f + expf(-gs)) * us);
+  }
+}
+
+// FC2 + combine: a workgroup per output row n of token t; thread L takes rank
+// j = L / G and group gi = L % G (G = I / 32) of expert ids[t, j]; the rank
+// sums y_j are formed in LDS in a fixed order, then
+// out[t, n] = fp16(sum_j r_j y_j) in rank order.
+__global__ void __launch_bounds__(256) qmoe_fc2_decode(MoeGemmArgs g, int64_t T, __half* out,
+                                                       float* slot_dbg) {
+  __shared__ float red[1024];
+  __shared__ float yj[16];
+  const int64_t H = g.N, I = g.K;
+  const int G = (int)(I / 32), k = g.top_k;
+  const int64_t t = blockIdx.x / H, n = blockIdx.x % H;
+  const __half* h = static_cast<const __half*>(g.act);
+  for (int L = threadIdx.x; L < k * G; L += blockDim.x) {
+    const int j = L / G, gi = L % G;
+    const int64_t slot = t * k + j;
+    const int e = clamp_id(g.perm[slot], g.E);  // perm holds the routed ids here
+    const int64_t row = (int64_t)e * H + n;
+    const u32x4* a = reinterpret_cast<const u32x4*>(h + slot * I + 32 * gi);
+    const u32x4 av[4] = {a[0], a[1], a[2], a[3]};
+    const u32x3 w = *reinterpret_cast<const u32x3*>(g.codes + row * g.row_bytes + 12 * gi);
+    red[L] = group_dot(w, __builtin_bit_cast(_Float16, g.scales[row * g.nblk + (32 * gi) / g.bs]), av);
+  }
+  __syncthreads();
+  if (threadIdx.x < k) {
+    const int j = threadIdx.x;
+    float y = 0.0f;
+    for (int gi = 0; gi < G; ++gi) y += red[j * G + gi];
+    const float r = g.wts[t * k + j];
+    yj[j] = r * y;
+    if (slot_dbg) slot_dbg[(t * k + j) * H + n] = r * y;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float o = 0.0f;
+    for (int j = 0; j < k; ++j) o += yj[j];
+    out[t * H + n] = __float2half_rn(o);
   }
 }
 
@@ -396,10 +561,16 @@ struct Ws {
   uint64_t ids, wts, counts, offsets, perm, inv, items, nitems, h, slots, total;
 };
 
-int64_t max_items(int64_t Tt, int k, int64_t E) {
+constexpr int kMaxBM = 64;  // largest token tile of a work item
+
+int64_t max_items(int64_t Tt, int k, int64_t E, int bm) {
   const int64_t S = Tt * k;
-  return (S < E ? S : E) + (S + kBM - 1) / kBM;
+  return (S < E ? S : E) + (S + bm - 1) / bm;
 }
+
+// Token tile of the work items: about the expected tokens per expert, so a
+// weight tile is dequantized once for all of an expert's tokens.
+int pick_bm(int64_t Tt, int k, int64_t E) { return Tt * k <= 24 * E ? 32 : kMaxBM; }
 
 Ws ws_layout(const Sizes& s1, const Sizes& s2, int k, int64_t T) {
   const int64_t Tt = T < kTokTile ? T : kTokTile;
@@ -417,7 +588,7 @@ Ws ws_layout(const Sizes& s1, const Sizes& s2, int k, int64_t T) {
   w.offsets = take((E + 1) * 4);
   w.perm = take(S * 4);
   w.inv = take(S * 4);
-  w.items = take(max_items(Tt, k, E) * 8);
+  w.items = take(max_items(Tt, k, E, 32) * 8);  // the smallest tile has the most items
   w.nitems = take(4);
   w.h = take(S * I * 2);
   w.slots = take(S * H * 4);
@@ -452,24 +623,56 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
   const int rows = (int)((16384 / E) < kTokTile ? (16384 / E) : kTokTile);
   const size_t group_lds = (size_t)(E + E + 1 + E + segs * E) * 4 + (size_t)rows * E * 2;
 
+  // few tokens: per-slot GEMVs, no grouping (every slot reads its expert once)
+  if (T * k <= kDecodeSlots && k * (I / 32) <= 1024) {
+    const int64_t S = T * k;
+    hipLaunchKernelGGL(qmoe_route, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, logits, T,
+                       (int)E, k, ids, wts);
+    MoeGemmArgs a1{static_cast<const uint8_t*>(p1.codes), static_cast<const __half*>(p1.scales),
+                   x, s1.N, s1.K, s1.row_bytes, s1.nb, s1.bs, k, (int)E,
+                   nullptr, nullptr, ids, nullptr, nullptr, wts, hbuf, nullptr};
+    const int64_t pairs = S * I;
+    int64_t b1 = (pairs + 3) / 4;
+    if (b1 > 8192) b1 = 8192;
+    hipLaunchKernelGGL(qmoe_fc1_decode, dim3((unsigned)b1), dim3(256), 0, st, a1, T);
+    MoeGemmArgs a2{static_cast<const uint8_t*>(p2.codes), static_cast<const __half*>(p2.scales),
+                   hbuf, s2.N, s2.K, s2.row_bytes, s2.nb, s2.bs, k, (int)E,
+                   nullptr, nullptr, ids, nullptr, nullptr, wts, nullptr, nullptr};
+    hipLaunchKernelGGL(qmoe_fc2_decode, dim3((unsigned)(T * H)), dim3(256), 0, st, a2, T,
+                       reinterpret_cast<__half*>(out), dbg ? dbg->slot : nullptr);
+    if (dbg) {
+      if (dbg->ids) (void)hipMemcpyAsync(dbg->ids, ids, S * 4, hipMemcpyDeviceToDevice, st);
+      if (dbg->w) (void)hipMemcpyAsync(dbg->w, wts, S * 4, hipMemcpyDeviceToDevice, st);
+      if (dbg->h) (void)hipMemcpyAsync(dbg->h, hbuf, S * I * 2, hipMemcpyDeviceToDevice, st);
+    }
+    return hipGetLastError();
+  }
+
   for (int64_t t0 = 0; t0 < T; t0 += kTokTile) {
     const int64_t Tt = (T - t0) < kTokTile ? (T - t0) : kTokTile;
     const int64_t S = Tt * k;
-    const int64_t items = max_items(Tt, k, E);
+    const int bm = pick_bm(Tt, k, E);
+    const int64_t items = max_items(Tt, k, E, bm);
     hipLaunchKernelGGL(qmoe_route, dim3((unsigned)((Tt + 3) / 4)), dim3(256), 0, st,
                        logits + t0 * E, Tt, (int)E, k, ids, wts);
     hipLaunchKernelGGL(qmoe_group, dim3(1), dim3(kGroupThreads), group_lds, st, ids, Tt, k, (int)E,
-                       items, go);
+                       items, bm, go);
     MoeGemmArgs a1{static_cast<const uint8_t*>(p1.codes), static_cast<const __half*>(p1.scales),
-                   x + t0 * H, s1.N, s1.K, s1.row_bytes, s1.nb, s1.bs, k,
+                   x + t0 * H, s1.N, s1.K, s1.row_bytes, s1.nb, s1.bs, k, (int)E,
                    go.counts, go.offsets, go.perm, go.items, go.nitems, wts, hbuf, nullptr};
-    const int64_t nt1 = (s1.N + kBN - 1) / kBN;
-    hipLaunchKernelGGL(qmoe_gemm<true>, dim3((unsigned)(items * nt1)), dim3(256), 0, st, a1, nt1);
+    const int64_t nt1 = (s1.N + kQBN - 1) / kQBN;
+    if (bm == 32)
+      hipLaunchKernelGGL((qmoe_gemm<true, 32>), dim3((unsigned)(items * nt1)), dim3(256), 0, st, a1, nt1);
+    else
+      hipLaunchKernelGGL((qmoe_gemm<true, kMaxBM>), dim3((unsigned)(items * nt1)), dim3(256), 0, st, a1, nt1);
     MoeGemmArgs a2{static_cast<const uint8_t*>(p2.codes), static_cast<const __half*>(p2.scales),
-                   hbuf, s2.N, s2.K, s2.row_bytes, s2.nb, s2.bs, k,
+                   hbuf, s2.N, s2.K, s2.row_bytes, s2.nb, s2.bs, k, (int)E,
                    go.counts, go.offsets, go.perm, go.items, go.nitems, wts, nullptr, slots};
-    const int64_t nt2 = (s2.N + kBN - 1) / kBN;
-    hipLaunchKernelGGL(qmoe_gemm<false>, dim3((unsigned)(items * nt2)), dim3(256), 0, st, a2, nt2);
+    const int64_t nt2 = (s2.N + kQBN - 1) / kQBN;
+    if (bm == 32)
+      hipLaunchKernelGGL((qmoe_gemm<false, 32>), dim3((unsigned)(items * nt2)), dim3(256), 0, st, a2, nt2);
+    else
+      hipLaunchKernelGGL((qmoe_gemm<false, kMaxBM>), dim3((unsigned)(items * nt2)), dim3(256), 0, st, a2, nt2);
     hipLaunchKernelGGL(qmoe_combine, dim3((unsigned)((Tt * H + 255) / 256)), dim3(256), 0, st,
                        slots, Tt, k, H, reinterpret_cast<__half*>(out + t0 * H));
     if (dbg) {

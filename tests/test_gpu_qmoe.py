@@ -189,10 +189,16 @@ def test_qmoe_invariants():
     base = m.run(x, logits)["out"]
     # determinism
     assert np.array_equal(base.view(np.uint16), m.run(x, logits)["out"].view(np.uint16))
-    # a token's result does not depend on the other tokens
+    # a token's result does not depend on the other tokens: bit for bit among
+    # batches that take the same path (grouped: T * k > 32; per-slot decode
+    # GEMVs: T * k <= 32, whose sums run in another order)
     for t in (0, 17, T - 1):
+        lo = min(t, T - 12)
+        sub = m.run(x[lo:lo + 12], logits[lo:lo + 12])["out"][t - lo]
+        assert np.array_equal(sub.view(np.uint16), base[t].view(np.uint16))
         one = m.run(x[t:t + 1], logits[t:t + 1])["out"][0]
-        assert np.array_equal(one.view(np.uint16), base[t].view(np.uint16))
+        two = m.run(x[[t, (t + 5) % T]], logits[[t, (t + 5) % T]])["out"][0]
+        assert np.array_equal(one.view(np.uint16), two.view(np.uint16))
     # permuting tokens permutes the outputs
     perm = np.random.default_rng(1).permutation(T)
     assert np.array_equal(m.run(x[perm], logits[perm])["out"].view(np.uint16),
@@ -211,3 +217,28 @@ def test_qmoe_all_codes_at_zero_point_give_zero():
     s2 = synth.scales_f16(95, (E, H, I // bs))
     m = Moe(x, logits, W1, s1, W2, s2, k, bs)
     assert (m.run(x, logits)["out"] == 0).all()
+
+
+@pytest.mark.parametrize("T,E,k", [(5, 4, 2), (37, 128, 8), (9, 1000, 16), (64, 64, 1), (3, 7, 7)])
+def test_qmoe_routing_matches_oracle_with_ties(orc, T, E, k):
+    """Selected experts are exact and in rank order (ties: lower expert first);
+    routing weights within 1e-6 of the fp64 renormalized softmax."""
+    say(f"qmoe routing T={T} E={E} k={k}")
+    H, I, bs = 64, 32, 32
+    x, logits, m = random_moe(T + E + k, T, H, I, E, k, bs)
+    # coarse logits: many exact ties inside each row
+    logits = (np.round(logits * 2) / 2).astype(np.float32)
+    res = m.run(x, logits, debug=True)
+    ids, w = orc.route(logits, k)
+    assert np.array_equal(res["ids"], ids)
+    assert np.abs(res["w"].astype(np.float64) - w).max() <= 1e-6
+
+
+def test_qmoe_routing_nan_logits_rank_last():
+    say("qmoe routing NaN logits")
+    T, H, I, E, k, bs = 4, 64, 32, 16, 4, 32
+    x, logits, m = random_moe(91, T, H, I, E, k, bs)
+    logits[0, [1, 5, 9]] = np.nan
+    res = m.run(x, logits, debug=True)
+    assert not np.isin(res["ids"][0], [1, 5, 9]).any()
+    assert ((res["ids"] >= 0) & (res["ids"] < E)).all()
