@@ -145,86 +145,106 @@ struct GroupOut {
   int32_t* nitems;   // [1]
 };
 
+// One workgroup of 16 waves; every step is parallel:
+//  counts:   LDS atomics, also per wave over a contiguous range of slots;
+//  offsets:  block-wide exclusive scans over the experts of the counts and of
+//            the work items per expert (ceil(count / bm)); each expert's
+//            thread writes its own work items;
+//  ranks:    the base of wave w in expert e is offsets[e] plus the counts of
+//            waves 0 .. w-1; a wave walks its slots in order, 64 at a time,
+//            and a slot's rank inside the batch is the number of lower lanes
+//            with the same expert.  The permutation is therefore stable in
+//            slot (token, rank) order.
 __global__ void __launch_bounds__(kGroupThreads) qmoe_group(const int32_t* __restrict__ ids,
                                                             int64_t T, int k, int E, int64_t max_items,
                                                             int bm, GroupOut o) {
   extern __shared__ __align__(16) int32_t gsm[];
-  int32_t* cnt = gsm;                 // [E]
-  int32_t* off = cnt + E;             // [E + 1]
-  int32_t* carry = off + E + 1;       // [E]
-  int32_t* segpre = carry + E;        // [segs][E]
-  const int tid = threadIdx.x;
-  const int segs = E >= kGroupThreads ? 1 : kGroupThreads / E;
-  uint16_t* mx = reinterpret_cast<uint16_t*>(segpre + segs * E);  // [rows][E]
-  const int rows = (int)((16384 / E) < kTokTile ? (16384 / E) : kTokTile);  // tokens per sub-tile
+  constexpr int kWaves = kGroupThreads / 64;
+  int32_t* cnt = gsm;              // [E]
+  int32_t* off = cnt + E;          // [E] exclusive offsets (scanned in place)
+  int32_t* ioff = off + E;         // [E] exclusive item offsets
+  int32_t* tmp = ioff + E;         // [2 E] scan double buffer
+  int32_t* hist = tmp + 2 * E;     // [kWaves][E]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t S = T * k;
 
+  for (int e = tid; e < E; e += kGroupThreads) cnt[e] = 0;
+  for (int i = tid; i < kWaves * E; i += kGroupThreads) hist[i] = 0;
+  __syncthreads();
+  const int64_t per = (S + kWaves - 1) / kWaves;
+  const int64_t s_lo = wave * per, s_hi = (s_lo + per) < S ? (s_lo + per) : S;
+  for (int64_t sl = s_lo + lane; sl < s_hi; sl += 64) {
+    const int e = clamp_id(ids[sl], E);
+    atomicAdd(&hist[wave * E + e], 1);
+    atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+
+  // inclusive Hillis-Steele scans of counts and of items per expert
   for (int e = tid; e < E; e += kGroupThreads) {
-    cnt[e] = 0;
-    carry[e] = 0;
+    off[e] = cnt[e];
+    ioff[e] = (cnt[e] + bm - 1) / bm;
   }
   __syncthreads();
-  for (int64_t s = tid; s < S; s += kGroupThreads) atomicAdd(&cnt[clamp_id(ids[s], E)], 1);
-  __syncthreads();
-  if (tid == 0) {
-    int32_t acc = 0, items = 0;
-    for (int e = 0; e < E; ++e) {
-      off[e] = acc;
-      acc += cnt[e];
-      for (int32_t m0 = 0; m0 < cnt[e] && items < max_items; m0 += bm, ++items) {
-        o.items[2 * items] = e;
-        o.items[2 * items + 1] = m0;
-      }
+  for (int d = 1; d < E; d <<= 1) {
+    for (int e = tid; e < E; e += kGroupThreads) {
+      tmp[e] = off[e] + (e >= d ? off[e - d] : 0);
+      tmp[E + e] = ioff[e] + (e >= d ? ioff[e - d] : 0);
     }
-    off[E] = acc;
-    *o.nitems = items;
+    __syncthreads();
+    for (int e = tid; e < E; e += kGroupThreads) {
+      off[e] = tmp[e];
+      ioff[e] = tmp[E + e];
+    }
+    __syncthreads();
+  }
+  // to exclusive, outputs, work items
+  for (int e = tid; e < E; e += kGroupThreads) {
+    const int32_t c = cnt[e];
+    const int32_t ex = off[e] - c;
+    const int32_t iex = ioff[e] - (c + bm - 1) / bm;
+    o.counts[e] = c;
+    o.offsets[e] = ex;
+    if (e == E - 1) {
+      o.offsets[E] = off[e];
+      *o.nitems = (int32_t)(ioff[e] < max_items ? ioff[e] : max_items);
+    }
+    for (int32_t m0 = 0, it = iex; m0 < c && it < max_items; m0 += bm, ++it) {
+      o.items[2 * it] = e;
+      o.items[2 * it + 1] = m0;
+    }
+    tmp[e] = ex;  // keep the exclusive offset for the bases below
   }
   __syncthreads();
-  for (int e = tid; e <= E; e += kGroupThreads) {
-    o.offsets[e] = off[e];
-    if (e < E) o.counts[e] = cnt[e];
+  // per-wave bases: offsets[e] + counts of the earlier waves
+  for (int e = tid; e < E; e += kGroupThreads) {
+    int32_t run = tmp[e];
+    for (int w = 0; w < kWaves; ++w) {
+      const int32_t v = hist[w * E + e];
+      hist[w * E + e] = run;
+      run += v;
+    }
   }
-  // position of slot (t, j) inside its expert's segment = number of earlier
-  // tokens that chose the same expert: a column-wise exclusive scan of the
-  // token x expert incidence matrix, one sub-tile of `rows` tokens at a time
-  const int seg_rows = (rows + segs - 1) / segs;
-  for (int64_t t0 = 0; t0 < T; t0 += rows) {
-    const int nt = (int)((T - t0) < rows ? (T - t0) : rows);
-    for (int i = tid; i < rows * E; i += kGroupThreads) mx[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < nt * k; i += kGroupThreads) mx[(i / k) * E + clamp_id(ids[(t0 * k) + i], E)] = 1;
-    __syncthreads();
-    if (tid < segs * E) {
-      const int e = tid % E, sg = tid / E;
-      int32_t run = 0;
-      const int r1 = (sg + 1) * seg_rows < nt ? (sg + 1) * seg_rows : nt;
-      for (int r = sg * seg_rows; r < r1; ++r) {
-        const int32_t v = mx[r * E + e];
-        mx[r * E + e] = (uint16_t)run;
-        run += v;
-      }
-      segpre[sg * E + e] = run;
+  __syncthreads();
+  int32_t* base = hist + wave * E;
+  for (int64_t b0 = s_lo; b0 < s_hi; b0 += 64) {
+    const int64_t sl = b0 + lane;
+    const bool valid = sl < s_hi;
+    const int e = valid ? clamp_id(ids[sl], E) : -1;
+    int32_t r = 0;
+    for (int j = 0; j < 64; ++j) {
+      const int ej = __builtin_amdgcn_readlane(e, j);
+      r += (j < lane && ej == e) ? 1 : 0;
     }
-    __syncthreads();
-    if (tid < E) {  // exclusive prefix of the segment totals, plus the carry
-      int32_t acc = carry[tid];
-      for (int sg = 0; sg < segs; ++sg) {
-        const int32_t v = segpre[sg * E + tid];
-        segpre[sg * E + tid] = acc;
-        acc += v;
-      }
-      carry[tid] = acc;
+    int32_t pos = 0;
+    if (valid) {
+      pos = base[e] + r;
+      o.perm[pos] = (int32_t)sl;
+      o.inv[sl] = pos;
     }
-    __syncthreads();
-    for (int i = tid; i < nt * k; i += kGroupThreads) {
-      const int r = i / k;
-      const int64_t slot = t0 * k + i;
-      const int e = clamp_id(ids[slot], E);
-      const int32_t pos = off[e] + segpre[(r / seg_rows) * E + e] + mx[r * E + e];
-      o.perm[pos] = (int32_t)slot;
-      o.inv[slot] = pos;
-    }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
+    if (valid) atomicMax(&base[e], pos + 1);
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -251,27 +271,41 @@ __global__ void __launch_bounds__(kGroupThreads) qmoe_group(const int32_t* __res
 
 typedef _Float16 half2t __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t int3_pair_scale(uint32_t bits, half2t s2) {
-  half2t h = __builtin_bit_cast(half2t, bits | 0x64006400u);  // 1024 + q
-  h = (h + half2t{(_Float16)-1028.0f, (_Float16)-1028.0f}) * s2;  // (q - 4) * s
+// (a & m) | (b & ~m): one v_bfi_b32
+__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); }
+
+// fp16 (q - 4) * s for the two codes in bits [0, 3) and [16, 19) of v;
+// magic holds 0x64006400 (1024.0 in both halves), in a register the compiler
+// cannot fold, so that the insert stays a single v_bfi_b32
+__device__ __forceinline__ uint32_t int3_pair(uint32_t v, uint32_t magic, half2t s2) {
+  half2t h = __builtin_bit_cast(half2t, bfi(0x00070007u, v, magic));  // 1024 + q
+  h = (h + half2t{(_Float16)-1028.0f, (_Float16)-1028.0f}) * s2;        // (q - 4) * s
   return __builtin_bit_cast(uint32_t, h);
 }
 
 // the 32 codes of one group as four MFMA operands (8 consecutive k each)
-__device__ __forceinline__ void dequant_group(const u32x3 w, _Float16 s, half8 (&out)[4]) {
+__device__ __forceinline__ void dequant_group(const u32x3 w, _Float16 s, uint32_t magic,
+                                              half8 (&out)[4]) {
   const half2t s2 = half2t{s, s};
   uint32_t p[16];
 #pragma unroll
   for (int m = 0; m < 3; ++m) {
     const uint32_t x = m == 0 ? w.x : (m == 1 ? w.y : w.z);
 #pragma unroll
-    for (int q = 0; q < 5; ++q) p[5 * m + q] = int3_pair_scale((x >> (3 * q)) & 0x00070007u, s2);
+    for (int q = 0; q < 5; ++q) p[5 * m + q] = int3_pair(x >> (3 * q), magic, s2);
   }
-  p[15] = int3_pair_scale(((w.x >> 15) & 0x00010001u) | ((w.y >> 14) & 0x00020002u) |
-                              ((w.z >> 13) & 0x00040004u), s2);
+  const uint32_t c3031 = bfi(0x00010001u, w.x >> 15, bfi(0x00020002u, w.y >> 14, bfi(0x00040004u, w.z >> 13, magic)));
+  p[15] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2t, c3031) +
+                                        half2t{(_Float16)-1028.0f, (_Float16)-1028.0f}) * s2);
 #pragma unroll
   for (int t = 0; t < 4; ++t)
     out[t] = __builtin_bit_cast(half8, u32x4{p[4 * t], p[4 * t + 1], p[4 * t + 2], p[4 * t + 3]});
+}
+
+__device__ __forceinline__ uint32_t opaque_magic() {
+  uint32_t m = 0x64006400u;
+  asm volatile("" : "+v"(m));
+  return m;
 }
 
 struct MoeGemmArgs {
@@ -293,23 +327,26 @@ struct MoeGemmArgs {
 constexpr int kQBN = 64;         // weight rows per workgroup
 constexpr int kQBK = 128;        // K per chunk
 constexpr int kQPitch = kQBK + 8;
+constexpr int kNTG = 4;          // 64-row weight tiles per workgroup
 
 template <bool FC1, int BM>
-__global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t tiles_n) {
+__global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n, int64_t tiles_n) {
   constexpr int TM = BM / 16;          // 16-token MFMA tiles
   constexpr int AP = BM * 16 / 256;    // 16-byte activation chunks per thread and chunk
   __shared__ __align__(16) _Float16 As[2][BM * kQPitch];
   __shared__ int32_t arow[BM];  // activation row of each tile row (-1: none)
 
-  const int64_t item = blockIdx.x / tiles_n;
-  const int64_t nt = blockIdx.x % tiles_n;
+  // work unit: item (expert, first token) x a group of kNTG 64-row weight tiles,
+  // walked as one sequence of (tile, K chunk) steps
+  const int64_t item = blockIdx.x / groups_n;
+  const int nt0 = (int)(blockIdx.x % groups_n) * kNTG;
   if (item >= *g.nitems) return;  // uniform for the workgroup
   const int e = g.items[2 * item];
   const int m0 = g.items[2 * item + 1];
   const int rows = min(BM, g.counts[e] - m0);
   const int vt = (rows + 15) >> 4;       // valid token tiles
   const int64_t seg0 = g.offsets[e] + m0;  // grouped position of tile row 0
-  const int64_t n0 = nt * kQBN;
+  const int ntc = (int)(tiles_n - nt0 < kNTG ? tiles_n - nt0 : kNTG);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -320,46 +357,74 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t tiles_n)
   }
   __syncthreads();
 
-  // activation staging: thread -> chunk (tid & 15) of rows (tid >> 4) + 16 j
+  // activation staging: thread -> chunk (tid & 15) of rows (tid >> 4) + 16 j;
+  // rows without a token read row 0 of the item instead (their results are
+  // never stored: an MFMA output row depends on its own A row only)
   const int a_c = (tid & 15) * 8, a_r0 = tid >> 4;
-  int32_t my_arow[AP];
-#pragma unroll
-  for (int j = 0; j < AP; ++j) my_arow[j] = arow[a_r0 + 16 * j];
   const _Float16* act = static_cast<const _Float16*>(g.act);
-  // weights: lane (n, gi) = (lane & 15, lane >> 4), row n0 + 16 wave + n
+  const _Float16* a_src[AP];
+#pragma unroll
+  for (int j = 0; j < AP; ++j) {
+    const int32_t r = arow[a_r0 + 16 * j];
+    a_src[j] = act + (int64_t)(r >= 0 ? r : arow[0]) * g.K + a_c;
+  }
+  // weights: lane (n, gi) = (lane & 15, lane >> 4), row 64 t + 16 wave + n of
+  // weight tile t.  Rows past N and groups past K read a valid group and get
+  // scale 0.
   const int wn = lane & 15, wg = lane >> 4;
-  const int64_t wrow = n0 + wave * 16 + wn;
-  const bool wvalid = wrow < g.N;
-  const uint8_t* wsrc = g.codes + ((int64_t)e * g.N + (wvalid ? wrow : 0)) * g.row_bytes;
-  const __half* ssrc = g.scales + ((int64_t)e * g.N + (wvalid ? wrow : 0)) * g.nblk;
+  const int Kc = (int)g.K;
+  const int nch = (Kc + kQBK - 1) / kQBK;
+  const int nsteps = ntc * nch;
+  const int bshift = g.bs == 32 ? 5 : (g.bs == 64 ? 6 : 7);
+  const uint32_t magic = opaque_magic();
+  const uint8_t* wbase = g.codes + (int64_t)e * g.N * g.row_bytes + 12 * wg;
+  const uint16_t* sbase = reinterpret_cast<const uint16_t*>(g.scales) + (int64_t)e * g.N * g.nblk;
 
-  // Register staging is double-buffered: the loads of chunk c + 1 are issued
-  // one chunk ahead and land in LDS (activations) or are dequantized
-  // (weights) while chunk c computes.
-  struct Stage {
-    u32x4 ra[AP];
+  // All loads are unconditional (clamped addresses, validity applied where
+  // the data is used), so the compiler keeps them in flight: weights four
+  // steps ahead (a ring of register stages; the HBM stream), activations
+  // (L2-resident) one step ahead through registers into the other LDS buffer.
+  struct WStage {
     u32x3 rw;
-    _Float16 rs;
+    uint32_t rs;
+    bool ok;
   };
-  auto load_chunk = [&](Stage& st, int64_t k0) {
-#pragma unroll
-    for (int j = 0; j < AP; ++j) {
-      st.ra[j] = u32x4{0, 0, 0, 0};
-      if (my_arow[j] >= 0 && k0 + a_c < g.K)  // K is a multiple of 32: chunks are whole
-        st.ra[j] = *reinterpret_cast<const u32x4*>(act + (int64_t)my_arow[j] * g.K + k0 + a_c);
-    }
-    st.rw = u32x3{0, 0, 0};
-    st.rs = (_Float16)0.0f;
-    const int64_t kg = k0 + 32 * wg;  // first code of this lane's group
-    if (wvalid && kg < g.K) {
-      st.rw = *reinterpret_cast<const u32x3*>(wsrc + (kg / 32) * 12);
-      st.rs = __builtin_bit_cast(_Float16, ssrc[kg / g.bs]);
-    }
+  auto load_w = [&](WStage& st, int sidx) {
+    sidx = sidx < nsteps ? sidx : nsteps - 1;
+    const int t = sidx / nch, c = sidx - t * nch;
+    const int64_t row = (int64_t)(nt0 + t) * kQBN + wave * 16 + wn;
+    const bool rok = row < g.N;
+    const int64_t rowc = rok ? row : 0;
+    const int kg = c * kQBK + 32 * wg;  // first code of this lane's group
+    st.ok = rok && kg < Kc;
+    const int kc = kg < Kc ? c * kQBK : 0;
+    st.rw = *reinterpret_cast<const u32x3*>(wbase + rowc * g.row_bytes + (uint32_t)(kc >> 5) * 12u);
+    st.rs = sbase[rowc * g.nblk + ((uint32_t)(kc + 32 * wg) >> bshift)];
   };
-  auto store_chunk = [&](const Stage& st, int b) {
+  // (a_src already includes this thread's column a_c)
+  u32x4 ra[AP];
+  auto load_a = [&](int sidx) {
+    sidx = sidx < nsteps ? sidx : nsteps - 1;
+    const int c = sidx % nch;
+    const int k0 = c * kQBK;
+    // columns past K (only in a last, partial chunk) read a valid column of
+    // the same row; they are zeroed when stored
+    const int kk = k0 + a_c < Kc ? k0 : Kc - 8 - a_c;
 #pragma unroll
-    for (int j = 0; j < AP; ++j)
-      *reinterpret_cast<u32x4*>(&As[b][(a_r0 + 16 * j) * kQPitch + a_c]) = st.ra[j];
+    for (int j = 0; j < AP; ++j) ra[j] = *reinterpret_cast<const u32x4*>(a_src[j] + kk);
+  };
+  const bool ktail = nch * kQBK > Kc;
+  const bool a_tail = ktail && (nch - 1) * kQBK + a_c >= Kc;  // this thread's column in a last chunk is past K
+  auto store_a = [&](int b, int c) {
+    if (ktail && c == nch - 1) {  // uniform: the last, partial chunk
+#pragma unroll
+      for (int j = 0; j < AP; ++j)
+        *reinterpret_cast<u32x4*>(&As[b][(a_r0 + 16 * j) * kQPitch + a_c]) = a_tail ? u32x4{0, 0, 0, 0} : ra[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < AP; ++j)
+        *reinterpret_cast<u32x4*>(&As[b][(a_r0 + 16 * j) * kQPitch + a_c]) = ra[j];
+    }
   };
 
   f32x4 acc[TM];
@@ -367,12 +432,44 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t tiles_n)
   for (int i = 0; i < TM; ++i) acc[i] = f32x4{0, 0, 0, 0};
   const int fr = lane & 15;
 
-  // chunk c: dequantize its weights (stage cur), let its activations (LDS
-  // buffer b) feed the MFMAs, then move chunk c + 1 (stage nxt, loaded one
-  // chunk ago) into the other buffer and start the loads of chunk c + 2
-  auto step = [&](Stage& cur, Stage& nxt, int b, int64_t k0) {
+  // epilogue of weight tile t: lane l holds tokens 16i + 4(l/16) + r of
+  // token tile i, weight row l%16 of this wave's 16
+  auto epilogue = [&](int t) {
+    const int64_t col = (int64_t)(nt0 + t) * kQBN + wave * 16 + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = i * 16 + 4 * (lane >> 4) + r;
+        const float v = acc[i][r];
+        if (FC1) {
+          // interleaved gate/up: even row = gate_i, odd row = up_i
+          const float partner = __shfl_xor(v, 1);
+          if ((lane & 1) == 0 && row < rows && col < g.N) {
+            const float gt = v, up = partner;
+            const float hv = gt / (1.0f + expf(-gt)) * up;
+            g.h_out[(seg0 + row) * (g.N / 2) + col / 2] = __float2half_rn(hv);
+          }
+        } else {
+          if (row < rows && col < g.N) {
+            const int32_t slot = g.perm[seg0 + row];
+            g.slot_out[(int64_t)slot * g.N + col] = g.wts[slot] * v;
+          }
+        }
+      }
+      acc[i] = f32x4{0, 0, 0, 0};
+    }
+  };
+
+  // step s = (tile t, chunk c): dequantize the weights (ring stage s mod 4)
+  // and refill that stage with step s + 4; MFMAs on LDS buffer s mod 2;
+  // after a tile's last chunk, its outputs; then move step s + 1's
+  // activations into the other buffer and fetch step s + 2's
+  auto step = [&](WStage& ws, int sidx) {
     half8 wf[4];
-    dequant_group(cur.rw, cur.rs, wf);
+    dequant_group(ws.rw, __builtin_bit_cast(_Float16, (uint16_t)(ws.ok ? ws.rs : 0u)), magic, wf);
+    load_w(ws, sidx + 4);
+    const int b = sidx & 1;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int kk = 32 * wg + 8 * t;
@@ -384,47 +481,32 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t tiles_n)
         }
       }
     }
-    if (k0 + kQBK < g.K) {
-      store_chunk(nxt, b ^ 1);
-      if (k0 + 2 * kQBK < g.K) load_chunk(cur, k0 + 2 * kQBK);
+    const int t = sidx / nch, c = sidx - t * nch;
+    if (c == nch - 1) epilogue(t);
+    if (sidx + 1 < nsteps) {
+      store_a(b ^ 1, c + 1 == nch ? 0 : c + 1);
+      load_a(sidx + 2);
       __syncthreads();
     }
   };
 
-  Stage s0, s1;
-  load_chunk(s0, 0);
-  if (kQBK < g.K) load_chunk(s1, kQBK);
-  store_chunk(s0, 0);
+  WStage w0, w1, w2, w3;
+  load_w(w0, 0);
+  load_w(w1, 1);
+  load_w(w2, 2);
+  load_w(w3, 3);
+  load_a(0);
+  store_a(0, 0);
+  load_a(1);
   __syncthreads();
-  for (int64_t k0 = 0; k0 < g.K; k0 += 2 * kQBK) {
-    step(s0, s1, 0, k0);
-    if (k0 + kQBK >= g.K) break;
-    step(s1, s0, 1, k0 + kQBK);
-  }
-
-  // lane l holds tokens 16i + 4(l/16) + r of tile i, weight row l%16
-  const int64_t col = n0 + wave * 16 + (lane & 15);
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = i * 16 + 4 * (lane >> 4) + r;
-      const float v = acc[i][r];
-      if (FC1) {
-        // interleaved gate/up: even row = gate_i, odd row = up_i
-        const float partner = __shfl_xor(v, 1);
-        if ((lane & 1) == 0 && row < rows && col < g.N) {
-          const float gt = v, up = partner;
-          const float hv = gt / (1.0f + expf(-gt)) * up;
-          g.h_out[(seg0 + row) * (g.N / 2) + col / 2] = __float2half_rn(hv);
-        }
-      } else {
-        if (row < rows && col < g.N) {
-          const int32_t slot = g.perm[seg0 + row];
-          g.slot_out[(int64_t)slot * g.N + col] = g.wts[slot] * v;
-        }
-      }
-    }
+  for (int sidx = 0; sidx < nsteps; sidx += 4) {
+    step(w0, sidx);
+    if (sidx + 1 >= nsteps) break;
+    step(w1, sidx + 1);
+    if (sidx + 2 >= nsteps) break;
+    step(w2, sidx + 2);
+    if (sidx + 3 >= nsteps) break;
+    step(w3, sidx + 3);
   }
 }
 
@@ -450,9 +532,10 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 __device__ __forceinline__ half2t as_half2(uint32_t v) { return __builtin_bit_cast(half2t, v); }
 
 // sum_k w_k a_k over one 32-code group: w = fp16((q - 4) s), a fp16 (16 B x 4)
-__device__ __forceinline__ float group_dot(const u32x3 w, _Float16 s, const u32x4* a16) {
+__device__ __forceinline__ float group_dot(const u32x3 w, _Float16 s, uint32_t magic,
+                                           const u32x4* a16) {
   half8 wf[4];
-  dequant_group(w, s, wf);
+  dequant_group(w, s, magic, wf);
   float acc = 0.0f;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -475,6 +558,7 @@ __global__ void __launch_bounds__(256) qmoe_fc1_decode(MoeGemmArgs g, int64_t T)
   const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
   const int ng = (int)(g.K / 32);
   const _Float16* x = static_cast<const _Float16*>(g.act);
+  const uint32_t magic = opaque_magic();
   for (int64_t p = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); p < pairs;
        p += nwaves) {
     const int64_t slot = p / I, i = p % I, t = slot / g.top_k;
@@ -487,8 +571,8 @@ __global__ void __launch_bounds__(256) qmoe_fc1_decode(MoeGemmArgs g, int64_t T)
       const u32x3 wg = *reinterpret_cast<const u32x3*>(g.codes + row * g.row_bytes + 12 * gi);
       const u32x3 wu = *reinterpret_cast<const u32x3*>(g.codes + (row + 1) * g.row_bytes + 12 * gi);
       const int b = (32 * gi) / (int)g.bs;
-      gs += group_dot(wg, __builtin_bit_cast(_Float16, g.scales[row * g.nblk + b]), av);
-      us += group_dot(wu, __builtin_bit_cast(_Float16, g.scales[(row + 1) * g.nblk + b]), av);
+      gs += group_dot(wg, __builtin_bit_cast(_Float16, g.scales[row * g.nblk + b]), magic, av);
+      us += group_dot(wu, __builtin_bit_cast(_Float16, g.scales[(row + 1) * g.nblk + b]), magic, av);
     }
     gs = wave_sum_f32(gs);
     us = wave_sum_f32(us);
@@ -508,6 +592,7 @@ __global__ void __launch_bounds__(256) qmoe_fc2_decode(MoeGemmArgs g, int64_t T,
   const int G = (int)(I / 32), k = g.top_k;
   const int64_t t = blockIdx.x / H, n = blockIdx.x % H;
   const __half* h = static_cast<const __half*>(g.act);
+  const uint32_t magic = opaque_magic();
   for (int L = threadIdx.x; L < k * G; L += blockDim.x) {
     const int j = L / G, gi = L % G;
     const int64_t slot = t * k + j;
@@ -516,7 +601,8 @@ __global__ void __launch_bounds__(256) qmoe_fc2_decode(MoeGemmArgs g, int64_t T,
     const u32x4* a = reinterpret_cast<const u32x4*>(h + slot * I + 32 * gi);
     const u32x4 av[4] = {a[0], a[1], a[2], a[3]};
     const u32x3 w = *reinterpret_cast<const u32x3*>(g.codes + row * g.row_bytes + 12 * gi);
-    red[L] = group_dot(w, __builtin_bit_cast(_Float16, g.scales[row * g.nblk + (32 * gi) / g.bs]), av);
+    red[L] = group_dot(w, __builtin_bit_cast(_Float16, g.scales[row * g.nblk + (32 * gi) / g.bs]),
+                       magic, av);
   }
   __syncthreads();
   if (threadIdx.x < k) {
@@ -619,9 +705,7 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
               reinterpret_cast<int32_t*>(w + L.items), reinterpret_cast<int32_t*>(w + L.nitems)};
   __half* hbuf = reinterpret_cast<__half*>(w + L.h);
   float* slots = reinterpret_cast<float*>(w + L.slots);
-  const int segs = E >= kGroupThreads ? 1 : kGroupThreads / (int)E;
-  const int rows = (int)((16384 / E) < kTokTile ? (16384 / E) : kTokTile);
-  const size_t group_lds = (size_t)(E + E + 1 + E + segs * E) * 4 + (size_t)rows * E * 2;
+  const size_t group_lds = (size_t)(5 + kGroupThreads / 64) * E * 4;
 
   // few tokens: per-slot GEMVs, no grouping (every slot reads its expert once)
   if (T * k <= kDecodeSlots && k * (I / 32) <= 1024) {
@@ -660,19 +744,19 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
     MoeGemmArgs a1{static_cast<const uint8_t*>(p1.codes), static_cast<const __half*>(p1.scales),
                    x + t0 * H, s1.N, s1.K, s1.row_bytes, s1.nb, s1.bs, k, (int)E,
                    go.counts, go.offsets, go.perm, go.items, go.nitems, wts, hbuf, nullptr};
-    const int64_t nt1 = (s1.N + kQBN - 1) / kQBN;
+    const int64_t nt1 = (s1.N + kQBN - 1) / kQBN, ng1 = (nt1 + kNTG - 1) / kNTG;
     if (bm == 32)
-      hipLaunchKernelGGL((qmoe_gemm<true, 32>), dim3((unsigned)(items * nt1)), dim3(256), 0, st, a1, nt1);
+      hipLaunchKernelGGL((qmoe_gemm<true, 32>), dim3((unsigned)(items * ng1)), dim3(256), 0, st, a1, ng1, nt1);
     else
-      hipLaunchKernelGGL((qmoe_gemm<true, kMaxBM>), dim3((unsigned)(items * nt1)), dim3(256), 0, st, a1, nt1);
+      hipLaunchKernelGGL((qmoe_gemm<true, kMaxBM>), dim3((unsigned)(items * ng1)), dim3(256), 0, st, a1, ng1, nt1);
     MoeGemmArgs a2{static_cast<const uint8_t*>(p2.codes), static_cast<const __half*>(p2.scales),
                    hbuf, s2.N, s2.K, s2.row_bytes, s2.nb, s2.bs, k, (int)E,
                    go.counts, go.offsets, go.perm, go.items, go.nitems, wts, nullptr, slots};
-    const int64_t nt2 = (s2.N + kQBN - 1) / kQBN;
+    const int64_t nt2 = (s2.N + kQBN - 1) / kQBN, ng2 = (nt2 + kNTG - 1) / kNTG;
     if (bm == 32)
-      hipLaunchKernelGGL((qmoe_gemm<false, 32>), dim3((unsigned)(items * nt2)), dim3(256), 0, st, a2, nt2);
+      hipLaunchKernelGGL((qmoe_gemm<false, 32>), dim3((unsigned)(items * ng2)), dim3(256), 0, st, a2, ng2, nt2);
     else
-      hipLaunchKernelGGL((qmoe_gemm<false, kMaxBM>), dim3((unsigned)(items * nt2)), dim3(256), 0, st, a2, nt2);
+      hipLaunchKernelGGL((qmoe_gemm<false, kMaxBM>), dim3((unsigned)(items * ng2)), dim3(256), 0, st, a2, ng2, nt2);
     hipLaunchKernelGGL(qmoe_combine, dim3((unsigned)((Tt * H + 255) / 256)), dim3(256), 0, st,
                        slots, Tt, k, H, reinterpret_cast<__half*>(out + t0 * H));
     if (dbg) {
