@@ -72,13 +72,24 @@ class Graph:
         self.g.replay()
 
 
-def graph_time(torch, calls, reps):
-    """Captures `calls` in one graph and returns the average per call in ms
-    over `reps` replays, timed with an event pair on the launch stream."""
+def graph_time(torch, calls, reps, min_calls=24):
+    """Captures `calls` (repeated to at least `min_calls` launches, so that the
+    graph launch itself is amortised) in one graph and returns the average per
+    call in ms over `reps` replays, timed with an event pair on the launch
+    stream."""
+    calls = list(calls) * max(1, -(-min_calls // len(calls)))
     g = Graph(torch, lambda: [c() for c in calls])
-    g.replay()
-    torch.cuda.synchronize()
+    # warm-up: about 20 ms of replays, so that clocks are at their sustained
+    # level when the timed replays start
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g.replay()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    for _ in range(max(2, int(20.0 / max(e0.elapsed_time(e1), 1e-3)))):
+        g.replay()
+    torch.cuda.synchronize()
     e0.record()
     for _ in range(reps):
         g.replay()
@@ -132,8 +143,8 @@ def cpu_baseline(layer_host, budget_s):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=330)
-    ap.add_argument("--warmup", type=int, default=33)
+    ap.add_argument("--steps", type=int, default=1980)
+    ap.add_argument("--warmup", type=int, default=660)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-extras", action="store_true")
     args = ap.parse_args()
