@@ -155,10 +155,10 @@ void prepack(const Sizes& s, const uint8_t* B, const void* scales,
     }
   } else {
     // contract rows are LSB-first 3-bit streams; regroup every 32 codes into
-    // the pair-interleaved words (same byte count per row)
+    // the pair-interleaved words, stored tile-major (same byte count)
     for (int64_t row = 0; row < s.rows; ++row) {
       const uint8_t* src = B + (uint64_t)row * (uint64_t)s.row_bytes;
-      uint8_t* out = codes + (uint64_t)row * (uint64_t)s.row_bytes;
+      const int64_t e = row / s.N, n = row % s.N;
       for (int64_t G = 0; G < s.K / 32; ++G) {
         uint32_t w[3] = {0, 0, 0};
         for (int i = 0; i < 32; ++i) {
@@ -173,7 +173,7 @@ void prepack(const Sizes& s, const uint8_t* B, const void* scales,
             for (int t = 0; t < 3; ++t) w[t] |= ((q >> t) & 1u) << (i == 30 ? 15 : 31);
           }
         }
-        std::memcpy(out + 12 * G, w, 12);
+        std::memcpy(codes + int3_group_offset(s.N, s.K, e, n, G), w, 12);
       }
     }
   }
@@ -247,7 +247,7 @@ void unpack_host(const Sizes& s, const mnb_plan* p, int64_t expert,
           q = ((j & 1) ? (byte >> 4) : (byte & 15u)) ^ 8u;
         } else {
           uint32_t w[3];
-          std::memcpy(w, src + 12 * (k / 32), 12);
+          std::memcpy(w, base + int3_group_offset(s.N, s.K, row / s.N, row % s.N, k / 32), 12);
           const int i = (int)(k % 32);
           if (i < 30) {
             q = (w[int3_word(i)] >> int3_bit(i)) & 7u;

@@ -16,14 +16,19 @@ constexpr uint32_t kPlanMagic = 0x4D4E4250u;  // "MNBP"
 //              scales fp32 [N][nb]; zero points (if explicit) as uint32 words
 //              [ceil(N/8)][nb], nibble r of word (g, b) holding the zero point
 //              of row 8g + r, block b (one load gives a row group's points).
-//  INT3 QMoE:  codes [E*N][3K/8], the same bytes per row as the contract,
-//              regrouped for the matrix-core dequantization: each group of 32
-//              codes c0..c31 (k = 32G + i) is three 32-bit words w0, w1, w2;
-//              word m holds the pairs (c[10m+2p], c[10m+2p+1]) for p = 0..4 at
-//              bits [3p, 3p+3) and [16+3p, 16+3p+3), so (w >> 3p) & 0x00070007
-//              puts a pair in the two 16-bit halves; bit t of c30 is bit 15 of
-//              w_t and bit t of c31 is bit 31 of w_t.  Scales fp16 [E*N][K/bs].
-constexpr uint32_t kLayoutVersion = 3;
+//  INT3 QMoE:  codes: the same bytes per row as the contract, 3K/8, regrouped
+//              for the matrix-core dequantization.  Each group of 32 codes
+//              c0..c31 (k = 32G + i) of a row is three 32-bit words w0, w1,
+//              w2; word m holds the pairs (c[10m+2p], c[10m+2p+1]) for
+//              p = 0..4 at bits [3p, 3p+3) and [16+3p, 16+3p+3), so
+//              (w >> 3p) & 0x00070007 puts a pair in the two 16-bit halves;
+//              bit t of c30 is bit 15 of w_t and bit t of c31 is bit 31 of w_t.
+//              The groups are stored tile-major: the rows of an expert in
+//              tiles of 16 (the last may hold fewer), each tile as a sequence
+//              of K chunks of 4 groups (128 codes; the last may hold fewer),
+//              each chunk as its rows' groups row by row; so one chunk of one
+//              tile is 16 x 48 contiguous bytes.  Scales fp16 [E*N][K/bs].
+constexpr uint32_t kLayoutVersion = 4;
 constexpr uint64_t kSectionAlign = 256;
 
 enum Kind : int32_t { kDenseInt4 = 1, kMoeInt3 = 2 };
@@ -32,6 +37,16 @@ enum Kind : int32_t { kDenseInt4 = 1, kMoeInt3 = 2 };
 // group, for the codes stored in one 3-bit field (i < 30).
 constexpr int int3_word(int i) { return i / 10; }
 constexpr int int3_bit(int i) { return 3 * ((i % 10) / 2) + 16 * (i % 2); }
+
+// Byte offset, inside the code section, of 32-code group G of row n_local of
+// expert e (tile-major INT3 layout; K is a multiple of 32).
+inline uint64_t int3_group_offset(int64_t N, int64_t K, int64_t e, int64_t n_local, int64_t G) {
+  const int64_t ng = K / 32, rt = n_local / 16, r = n_local % 16;
+  const int64_t rcnt = (N - 16 * rt) < 16 ? (N - 16 * rt) : 16;
+  const int64_t c = G / 4, g = G % 4;
+  const int64_t gic = (ng - 4 * c) < 4 ? (ng - 4 * c) : 4;
+  return (uint64_t)(e * N + 16 * rt) * (uint64_t)(ng * 12) + (uint64_t)(rcnt * 48 * c + r * gic * 12 + g * 12);
+}
 
 struct Sizes {
   Kind kind;

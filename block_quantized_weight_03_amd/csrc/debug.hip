@@ -18,9 +18,19 @@ struct Rows {
   const uint8_t* codes;
   const void* scales;
   const uint8_t* zeros;
-  int64_t K, nb, bs, row_bytes, zrow, row_base;  // row_base = expert * N + row0
+  int64_t N, K, nb, bs, row_bytes, zrow, row_base;  // row_base = expert * N + row0
   int kind;
 };
+
+// byte offset of 32-code group G of row n of expert e in the tile-major INT3
+// layout (rows in tiles of 16, each tile as chunks of 4 groups, row by row)
+__device__ __forceinline__ int64_t int3_goff(int64_t N, int64_t K, int64_t e, int64_t n, int64_t G) {
+  const int64_t ng = K / 32, rt = n / 16, r = n % 16;
+  const int64_t rcnt = (N - 16 * rt) < 16 ? (N - 16 * rt) : 16;
+  const int64_t c = G / 4, g = G % 4;
+  const int64_t gic = (ng - 4 * c) < 4 ? (ng - 4 * c) : 4;
+  return (e * N + 16 * rt) * (ng * 12) + rcnt * 48 * c + r * gic * 12 + g * 12;
+}
 
 __device__ __forceinline__ unsigned code_of(const Rows& r, int64_t row, int64_t k) {
   const uint8_t* src = r.codes + row * r.row_bytes;
@@ -29,8 +39,9 @@ __device__ __forceinline__ unsigned code_of(const Rows& r, int64_t row, int64_t 
     const uint8_t byte = src[b * (r.bs / 2) + j / 2];
     return (((j & 1) ? (byte >> 4) : byte) & 15u) ^ 8u;
   }
-  // INT3: pair-interleaved groups of three words per 32 codes
-  const uint32_t* w = reinterpret_cast<const uint32_t*>(src + 12 * (k / 32));
+  // INT3: pair-interleaved groups of three words per 32 codes, tile-major
+  const uint32_t* w =
+      reinterpret_cast<const uint32_t*>(r.codes + int3_goff(r.N, r.K, row / r.N, row % r.N, k / 32));
   const int i = (int)(k % 32);
   if (i < 30) return (w[int3_word(i)] >> int3_bit(i)) & 7u;
   const int b = i == 30 ? 15 : 31;
@@ -74,6 +85,7 @@ Rows make_rows(const Sizes& s, const mnb_plan& p, int64_t expert, int64_t row0) 
   r.codes = static_cast<const uint8_t*>(p.codes);
   r.scales = p.scales;
   r.zeros = static_cast<const uint8_t*>(p.zeros);
+  r.N = s.N;
   r.K = s.K;
   r.nb = s.nb;
   r.bs = s.bs;

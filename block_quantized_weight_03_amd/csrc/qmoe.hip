@@ -308,6 +308,18 @@ __device__ __forceinline__ uint32_t opaque_magic() {
   return m;
 }
 
+// Byte offset, within one expert's codes, of 32-code group G of row n in the
+// tile-major INT3 layout: rows in tiles of 16 (the last may hold fewer), each
+// tile as K chunks of 4 groups (the last may hold fewer), each chunk row by
+// row; a full tile's chunk is 16 x 48 contiguous bytes.
+__device__ __forceinline__ uint32_t int3_goff(int N, int K, int n, int G) {
+  const int ng = K >> 5, rt = n >> 4, r = n & 15;
+  const int rcnt = min(16, N - 16 * rt);
+  const int c = G >> 2, gg = G & 3;
+  const int gic = min(4, ng - 4 * c);
+  return (uint32_t)(16 * rt * ng * 12 + rcnt * 48 * c + r * gic * 12 + gg * 12);
+}
+
 struct MoeGemmArgs {
   const uint8_t* codes;    // [E][N][row_bytes], pair-interleaved groups
   const __half* scales;    // [E][N][K/bs]
@@ -337,9 +349,13 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
   __shared__ int32_t arow[BM];  // activation row of each tile row (-1: none)
 
   // work unit: item (expert, first token) x a group of kNTG 64-row weight tiles,
-  // walked as one sequence of (tile, K chunk) steps
-  const int64_t item = blockIdx.x / groups_n;
-  const int nt0 = (int)(blockIdx.x % groups_n) * kNTG;
+  // walked as one sequence of (tile, K chunk) steps.  Workgroups go to the 8
+  // XCDs round-robin by index; all weight-tile groups of an item run on one XCD
+  // (XCD b % 8 takes items 8 q + b % 8), so its activation rows come from HBM
+  // into that XCD's L2 once.  The grid covers the item count rounded up to 8.
+  const int bj = (int)(blockIdx.x >> 3);
+  const int64_t item = (int64_t)(bj / groups_n) * 8 + (blockIdx.x & 7);
+  const int nt0 = (int)(bj % groups_n) * kNTG;
   if (item >= *g.nitems) return;  // uniform for the workgroup
   const int e = g.items[2 * item];
   const int m0 = g.items[2 * item + 1];
@@ -377,7 +393,8 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
   const int nsteps = ntc * nch;
   const int bshift = g.bs == 32 ? 5 : (g.bs == 64 ? 6 : 7);
   const uint32_t magic = opaque_magic();
-  const uint8_t* wbase = g.codes + (int64_t)e * g.N * g.row_bytes + 12 * wg;
+  const uint8_t* wbase = g.codes + (int64_t)e * g.N * g.row_bytes;  // this expert's codes
+  const int Nc = (int)g.N;
   const uint16_t* sbase = reinterpret_cast<const uint16_t*>(g.scales) + (int64_t)e * g.N * g.nblk;
 
   // All loads are unconditional (clamped addresses, validity applied where
@@ -392,14 +409,14 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
   auto load_w = [&](WStage& st, int sidx) {
     sidx = sidx < nsteps ? sidx : nsteps - 1;
     const int t = sidx / nch, c = sidx - t * nch;
-    const int64_t row = (int64_t)(nt0 + t) * kQBN + wave * 16 + wn;
-    const bool rok = row < g.N;
-    const int64_t rowc = rok ? row : 0;
+    const int row = (nt0 + t) * kQBN + wave * 16 + wn;
+    const bool rok = row < Nc;
     const int kg = c * kQBK + 32 * wg;  // first code of this lane's group
     st.ok = rok && kg < Kc;
-    const int kc = kg < Kc ? c * kQBK : 0;
-    st.rw = *reinterpret_cast<const u32x3*>(wbase + rowc * g.row_bytes + (uint32_t)(kc >> 5) * 12u);
-    st.rs = sbase[rowc * g.nblk + ((uint32_t)(kc + 32 * wg) >> bshift)];
+    const int rowc = rok ? row : 0;
+    const int G = kg < Kc ? (kg >> 5) : 0;
+    st.rw = *reinterpret_cast<const u32x3*>(wbase + int3_goff(Nc, Kc, rowc, G));
+    st.rs = sbase[(int64_t)rowc * g.nblk + ((uint32_t)(G * 32) >> bshift)];
   };
   // (a_src already includes this thread's column a_c)
   u32x4 ra[AP];
@@ -564,12 +581,13 @@ __global__ void __launch_bounds__(256) qmoe_fc1_decode(MoeGemmArgs g, int64_t T)
     const int64_t slot = p / I, i = p % I, t = slot / g.top_k;
     const int e = clamp_id(g.perm[slot], g.E);  // perm holds the routed ids here
     const int64_t row = (int64_t)e * g.N + 2 * i;
+    const uint8_t* ebase = g.codes + (int64_t)e * g.N * g.row_bytes;
     float gs = 0.0f, us = 0.0f;
     for (int gi = lane; gi < ng; gi += 64) {
       const u32x4* a = reinterpret_cast<const u32x4*>(x + t * g.K + 32 * gi);
       const u32x4 av[4] = {a[0], a[1], a[2], a[3]};
-      const u32x3 wg = *reinterpret_cast<const u32x3*>(g.codes + row * g.row_bytes + 12 * gi);
-      const u32x3 wu = *reinterpret_cast<const u32x3*>(g.codes + (row + 1) * g.row_bytes + 12 * gi);
+      const u32x3 wg = *reinterpret_cast<const u32x3*>(ebase + int3_goff((int)g.N, (int)g.K, (int)(2 * i), gi));
+      const u32x3 wu = *reinterpret_cast<const u32x3*>(ebase + int3_goff((int)g.N, (int)g.K, (int)(2 * i + 1), gi));
       const int b = (32 * gi) / (int)g.bs;
       gs += group_dot(wg, __builtin_bit_cast(_Float16, g.scales[row * g.nblk + b]), magic, av);
       us += group_dot(wu, __builtin_bit_cast(_Float16, g.scales[(row + 1) * g.nblk + b]), magic, av);
@@ -600,7 +618,8 @@ __global__ void __launch_bounds__(256) qmoe_fc2_decode(MoeGemmArgs g, int64_t T,
     const int64_t row = (int64_t)e * H + n;
     const u32x4* a = reinterpret_cast<const u32x4*>(h + slot * I + 32 * gi);
     const u32x4 av[4] = {a[0], a[1], a[2], a[3]};
-    const u32x3 w = *reinterpret_cast<const u32x3*>(g.codes + row * g.row_bytes + 12 * gi);
+    const u32x3 w = *reinterpret_cast<const u32x3*>(g.codes + (int64_t)e * H * g.row_bytes +
+                                                    int3_goff((int)H, (int)I, (int)n, gi));
     red[L] = group_dot(w, __builtin_bit_cast(_Float16, g.scales[row * g.nblk + (32 * gi) / g.bs]),
                        magic, av);
   }
@@ -696,6 +715,9 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
   const int k = top_k;
   // limits of these kernels (checked before any launch)
   if (E > kMaxE || k > 16 || H % 32 || I % 32) return hipErrorNotSupported;
+  // in-expert code offsets are 32-bit
+  if (s1.N * s1.row_bytes >= (int64_t(1) << 31) || s2.N * s2.row_bytes >= (int64_t(1) << 31))
+    return hipErrorNotSupported;
   const Ws L = ws_layout(s1, s2, k, T);
   uint8_t* w = static_cast<uint8_t*>(ws);
   int32_t* ids = reinterpret_cast<int32_t*>(w + L.ids);
@@ -746,17 +768,17 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
                    go.counts, go.offsets, go.perm, go.items, go.nitems, wts, hbuf, nullptr};
     const int64_t nt1 = (s1.N + kQBN - 1) / kQBN, ng1 = (nt1 + kNTG - 1) / kNTG;
     if (bm == 32)
-      hipLaunchKernelGGL((qmoe_gemm<true, 32>), dim3((unsigned)(items * ng1)), dim3(256), 0, st, a1, ng1, nt1);
+      hipLaunchKernelGGL((qmoe_gemm<true, 32>), dim3((unsigned)((items + 7) / 8 * 8 * ng1)), dim3(256), 0, st, a1, ng1, nt1);
     else
-      hipLaunchKernelGGL((qmoe_gemm<true, kMaxBM>), dim3((unsigned)(items * ng1)), dim3(256), 0, st, a1, ng1, nt1);
+      hipLaunchKernelGGL((qmoe_gemm<true, kMaxBM>), dim3((unsigned)((items + 7) / 8 * 8 * ng1)), dim3(256), 0, st, a1, ng1, nt1);
     MoeGemmArgs a2{static_cast<const uint8_t*>(p2.codes), static_cast<const __half*>(p2.scales),
                    hbuf, s2.N, s2.K, s2.row_bytes, s2.nb, s2.bs, k, (int)E,
                    go.counts, go.offsets, go.perm, go.items, go.nitems, wts, nullptr, slots};
     const int64_t nt2 = (s2.N + kQBN - 1) / kQBN, ng2 = (nt2 + kNTG - 1) / kNTG;
     if (bm == 32)
-      hipLaunchKernelGGL((qmoe_gemm<false, 32>), dim3((unsigned)(items * ng2)), dim3(256), 0, st, a2, ng2, nt2);
+      hipLaunchKernelGGL((qmoe_gemm<false, 32>), dim3((unsigned)((items + 7) / 8 * 8 * ng2)), dim3(256), 0, st, a2, ng2, nt2);
     else
-      hipLaunchKernelGGL((qmoe_gemm<false, kMaxBM>), dim3((unsigned)(items * ng2)), dim3(256), 0, st, a2, ng2, nt2);
+      hipLaunchKernelGGL((qmoe_gemm<false, kMaxBM>), dim3((unsigned)((items + 7) / 8 * 8 * ng2)), dim3(256), 0, st, a2, ng2, nt2);
     hipLaunchKernelGGL(qmoe_combine, dim3((unsigned)((Tt * H + 255) / 256)), dim3(256), 0, st,
                        slots, Tt, k, H, reinterpret_cast<__half*>(out + t0 * H));
     if (dbg) {
