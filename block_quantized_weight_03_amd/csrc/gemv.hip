@@ -363,27 +363,6 @@ struct Acts {
   float poison;
 };
 
-__device__ __forceinline__ void load_acts(Acts& x, const float* __restrict__ A, int64_t K,
-                                          int32_t sb) {
-  // raw buffer over exactly K floats: out-of-range dwords read as 0
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(A), (short)0, (int)(K * 4), 0x00020000);
-  const uint32_t off = (uint32_t)sb * 128u;
-  float p = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const f32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u * i, 0, 0);
-    x.a[4 * i] = v.x;
-    x.a[4 * i + 1] = v.y;
-    x.a[4 * i + 2] = v.z;
-    x.a[4 * i + 3] = v.w;
-  }
-  // a * 0 is 0 for finite a and NaN otherwise
-#pragma unroll
-  for (int i = 0; i < 32; ++i) p = fmaf(x.a[i], 0.0f, p);
-  x.poison = p;
-}
-
 template <bool HAS_ZP>
 __device__ __forceinline__ float subblock_dot_f32(const u32x4 q, const Acts& x, float s, int z) {
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
@@ -401,66 +380,141 @@ __device__ __forceinline__ float subblock_dot_f32(const u32x4 q, const Acts& x, 
   return ((acc[0] + acc[1]) + (acc[2] + acc[3])) * s + x.poison;
 }
 
+// Raw buffer resource over `bytes` bytes at p: a load whose dwords lie past
+// the end returns 0 for them, so clamps and tail branches are not needed.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past every resource used here
+constexpr int kNT = 2;                          // cache policy: nontemporal (streamed once)
+
+// Sum over the 64 lanes of a wave with DPP moves (no LDS round trip); the
+// total lands in lane 63.  Fixed order, so the result is deterministic.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_mov<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141, 0xF>(v);  // row_half_mirror: 8-lane sums
+  v += dpp_mov<0x140, 0xF>(v);  // row_mirror: 16-lane sums
+  v += dpp_mov<0x142, 0xA>(v);  // row_bcast15: rows 1, 3 add rows 0, 2
+  v += dpp_mov<0x143, 0xC>(v);  // row_bcast31: rows 2, 3 add lane 31
+  return v;
+}
+
+constexpr int kTeams = 4;  // row groups (teams of waves) per workgroup of the fp32 path
+constexpr int kNPT = 8 / kTeams;  // 16-byte pieces of A per thread
+
+// One-shot: every wave takes R consecutive rows of one K chunk, with 32-bit
+// index math throughout (the launcher checks that the codes of the matrix
+// span less than 2^31 bytes).  Inactive lanes and rows past N read through
+// an out-of-range buffer offset and so contribute exact zeros.  The
+// workgroup stages A once in LDS (each teams' waves read it from there, so
+// global A traffic is one copy per workgroup instead of one per wave):
+// 16-byte chunk j of sub-block i sits at chunk j ^ ((i >> 1) & 7) of the
+// sub-block's 128 bytes, so the 16 lanes served per LDS cycle hit 64
+// distinct banks.  The A loads are issued before the weight loads; loads
+// complete in order, so waiting for A does not wait for the weights.
 template <int R, bool HAS_ZP>
-__global__ void __launch_bounds__(256) gemv_int4_f32(
+__global__ void __launch_bounds__(1024) gemv_int4_f32(
     const float* __restrict__ A, const uint8_t* __restrict__ codes,
     const float* __restrict__ scales, const uint32_t* __restrict__ zeros, float* __restrict__ Y,
-    int64_t K, int64_t N, int64_t row_bytes, int64_t nb, int32_t nsb, int32_t nchunk,
-    int32_t bs_shift, int64_t zrow) {
-  __shared__ __align__(16) float red_all[kMaxTeam * R * 64];
-  __shared__ float tot[kMaxTeam * R];
+    int32_t K, int32_t N, int32_t row_bytes, int32_t nb, int32_t nsb, int32_t team,
+    int32_t bs_shift) {
+  // A: 64 * team sub-blocks of 128 bytes (the launcher sizes it), then the
+  // team partials
+  extern __shared__ __align__(16) u32x4 as[];
+  float* tot = reinterpret_cast<float*>(as + 512 * team);
 
-  const int team = nchunk;
-  const int nwaves = (int)(blockDim.x >> 6);
-  const int teams = nwaves / team;
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int lane = (int)(threadIdx.x & 63);
-  const int tm = wave / team, wit = wave - tm * team;
+  const int tid = (int)threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  // kTeams teams of `team` waves (one K chunk each), one row group per team
+  const int tm = (wave >= team) + (wave >= 2 * team) + (wave >= 3 * team);
+  const int wit = wave - tm * team;
+  const int n0 = ((int)blockIdx.x * kTeams + tm) * R;
 
-  const int32_t sb = wit * 64 + lane;
-  const bool act = sb < nsb;
-  const uint32_t qoff = (uint32_t)sb * 16u;
-  const uint32_t b = (uint32_t)sb >> bs_shift;
-
-  const int64_t nrg = (N + R - 1) / R;
-  const int64_t stride = (int64_t)gridDim.x * teams;
-  const int64_t base0 = (int64_t)blockIdx.x * teams;
-  const int64_t iters = base0 < nrg ? (nrg - base0 + stride - 1) / stride : 0;
-  int64_t rg = base0 + tm;
-
-  RowTile<R, HAS_ZP> cur, nxt;
-  if (iters > 0) load_rows<R, HAS_ZP>(cur, codes, scales, zeros, rg * R, rg < nrg ? N : 0, row_bytes, nb, zrow, qoff, b, act);
-  Acts x;
-  load_acts(x, A, K, sb);
-  float* red = red_all + wave * R * 64;
-  constexpr int P = 64 / R;
-
-#pragma unroll 1
-  for (int64_t it = 0; it < iters; ++it) {
-    const int64_t rgn = rg + stride;
-    if (it + 1 < iters)
-      load_rows<R, HAS_ZP>(nxt, codes, scales, zeros, rgn * R, rgn < nrg ? N : 0, row_bytes, nb, zrow, qoff, b, act);
-    float part[R];
+  // A pieces of this thread: tid + nt * u (past K: zeros); the workgroup's
+  // nt = 256 team threads hold all 8 * 64 * team pieces of its K chunks
+  const int nt = 64 * kTeams * team;
+  const __amdgpu_buffer_rsrc_t ra = buffer_over(A, (uint32_t)K * 4u);
+  u32x4 ap[kNPT];
 #pragma unroll
-    for (int r = 0; r < R; ++r) part[r] = subblock_dot_f32<HAS_ZP>(cur.q[r], x, cur.s[r], (int)((cur.zpk >> (4 * r)) & 15u));
-    const float v = wave_reduce_rows<R>(part, red, lane);
-    const int r = lane / P;
-    if (team == 1) {
-      const int64_t n = rg * R + r;
-      if ((lane % P) == 0 && rg < nrg && n < N) Y[n] = v;
-    } else {
-      if ((lane % P) == 0) tot[wave * R + r] = v;
-      __syncthreads();
-      if (wit == 0 && lane < R) {
-        float out = 0.0f;
-        for (int w = 0; w < team; ++w) out += tot[(tm * team + w) * R + lane];
-        const int64_t nn = rg * R + lane;
-        if (rg < nrg && nn < N) Y[nn] = out;
-      }
-      __syncthreads();
+  for (int u = 0; u < kNPT; ++u)
+    ap[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, 16u * (uint32_t)(tid + nt * u), 0, 0));
+
+  const int sb = wit * 64 + lane;
+  const bool act = sb < nsb;
+  const uint32_t b = (uint32_t)sb >> bs_shift;
+  const __amdgpu_buffer_rsrc_t rc = buffer_over(codes, (uint32_t)N * (uint32_t)row_bytes);
+  const __amdgpu_buffer_rsrc_t rs = buffer_over(scales, (uint32_t)N * (uint32_t)nb * 4u);
+  u32x4 q[R];
+  float s[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t row = (uint32_t)(n0 + r);
+    q[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         rc, act ? row * row_bytes + 16u * sb : kOutOfRange, 0, kNT));
+    s[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                         rs, act ? (row * nb + b) * 4u : kOutOfRange, 0, kNT));
+  }
+  uint32_t zpk = 0;  // zero point of row n0 + r in bits [4r, 4r + 4)
+  if (HAS_ZP) {
+    const uint32_t zbytes = (uint32_t)((N + 7) >> 3) * (uint32_t)nb * 4u;
+    zpk = __builtin_amdgcn_raw_buffer_load_b32(buffer_over(zeros, zbytes),
+                                               act ? ((n0 >> 3) * nb + b) * 4u : kOutOfRange, 0, kNT) >>
+          (4 * (n0 & 7));
+  }
+
+#pragma unroll
+  for (int u = 0; u < kNPT; ++u) {
+    const int pc = tid + nt * u, i = pc >> 3, j = pc & 7;
+    as[(i << 3) | (j ^ ((i >> 1) & 7))] = ap[u];
+  }
+  __syncthreads();
+  Acts x;
+  {
+    float p = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const u32x4 v = as[(sb << 3) | (j ^ ((sb >> 1) & 7))];
+      x.a[4 * j] = __uint_as_float(v.x);
+      x.a[4 * j + 1] = __uint_as_float(v.y);
+      x.a[4 * j + 2] = __uint_as_float(v.z);
+      x.a[4 * j + 3] = __uint_as_float(v.w);
     }
-    cur = nxt;
-    rg = rgn;
+    // a * 0 is 0 for finite a and NaN otherwise (four short chains)
+    float pc[4] = {p, p, p, p};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) pc[i & 3] = fmaf(x.a[i], 0.0f, pc[i & 3]);
+    x.poison = (pc[0] + pc[1]) + (pc[2] + pc[3]);
+  }
+
+  float v[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    v[r] = wave_sum_dpp(subblock_dot_f32<HAS_ZP>(q[r], x, s[r], (int)((zpk >> (4 * r)) & 15u)));
+  if (team == 1) {
+    if (lane == 63) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (n0 + r < N) Y[n0 + r] = v[r];
+    }
+  } else {
+    if (lane == 63) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) tot[wave * R + r] = v[r];
+    }
+    __syncthreads();
+    if (wit == 0 && lane < R) {
+      float out = 0.0f;
+      for (int w = 0; w < team; ++w) out += tot[(tm * team + w) * R + lane];
+      if (n0 + lane < N) Y[n0 + lane] = out;
+    }
   }
 }
 
@@ -558,16 +612,14 @@ template <int R, bool HAS_ZP>
 hipError_t launch_f32(const Sizes& s, const mnb_plan& p, const float* A, float* Y, int64_t nsb,
                       int64_t nchunk, hipStream_t st) {
   const int team = (int)nchunk;
-  const int teams = kMaxTeam / team;
   const int64_t nrg = (s.N + R - 1) / R;
-  int64_t blocks = (nrg + teams - 1) / teams;
-  const int64_t cap = (int64_t)cu_count() * 8;
-  if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL((gemv_int4_f32<R, HAS_ZP>), dim3((unsigned)blocks), dim3(64 * team * teams),
-                     0, st, A, static_cast<const uint8_t*>(p.codes),
+  const int64_t blocks = (nrg + kTeams - 1) / kTeams;
+  const size_t lds = (size_t)team * 8192 + (size_t)kTeams * team * R * 4;
+  hipLaunchKernelGGL((gemv_int4_f32<R, HAS_ZP>), dim3((unsigned)blocks), dim3(64 * kTeams * team),
+                     lds, st, A, static_cast<const uint8_t*>(p.codes),
                      static_cast<const float*>(p.scales), static_cast<const uint32_t*>(p.zeros), Y,
-                     s.K, s.N, s.row_bytes, s.nb, (int32_t)nsb, (int32_t)nchunk, bs_shift_of(s),
-                     (int64_t)s.zrow);
+                     (int32_t)s.K, (int32_t)s.N, (int32_t)s.row_bytes, (int32_t)s.nb, (int32_t)nsb,
+                     team, bs_shift_of(s));
   return hipGetLastError();
 }
 
@@ -603,12 +655,11 @@ hipError_t dispatch(const Sizes& s, const mnb_plan& p, const float* A, float* Y,
   const int64_t nsb = n_subblocks(s);
   const int64_t nchunk = (nsb + 63) / 64;
   if (nchunk > kMaxTeam) return launch_ws<8, HAS_ZP>(s, p, A, Y, ws, nsb, nchunk, st);
-  // few rows per wave: the plain fp32 path (measured faster up to tens of
-  // thousands of rows; the digit planes pay off on long row streams)
-  // (two rows per wave step while that keeps about 1024 waves busy, else four)
-  if (s.N <= kF32MaxRows)
-    return s.N * nchunk <= 2048 ? launch_f32<2, HAS_ZP>(s, p, A, Y, nsb, nchunk, st)
-                                : launch_f32<4, HAS_ZP>(s, p, A, Y, nsb, nchunk, st);
+  // up to tens of thousands of rows: the plain fp32 path, two rows per wave
+  // (measured faster there; the digit planes pay off on long row streams);
+  // 32-bit offsets: rows of at most 4 KiB of codes, N <= 32768
+  if (s.N <= kF32MaxRows && s.row_bytes * s.N < (int64_t(1) << 31))
+    return launch_f32<2, HAS_ZP>(s, p, A, Y, nsb, nchunk, st);
   // rows per wave iteration: enough row groups to fill the chip for small N,
   // deeper load batches for large N
   const int64_t teams = kMaxTeam / nchunk;
