@@ -429,7 +429,8 @@ bool fast_ok(const Sizes& s, int64_t M, const void* A) {
 }
 
 struct Plan {
-  bool lds;         // the 256 x 256 LDS-streaming kernel (gemm_lds.hip)
+  bool lds;         // the LDS-streaming kernel (gemm_lds.hip), bm x bm tiles
+  int bm;
   int cfg;          // else: index into the configuration table below
   int64_t tiles_n, tiles;
   int32_t splits;
@@ -460,18 +461,21 @@ void split_k(Plan& p, const Sizes& s, int64_t M, int64_t step) {
   p.kc = steps_per * step;
 }
 
-// rows of A from which the LDS-streaming kernel is used
+// rows of A from which the LDS-streaming kernel is used, with 128 x 128
+// tiles, and from which with 256 x 256 tiles
+constexpr int64_t kLdsSmallMinM = 128;
 constexpr int64_t kLdsMinM = 1024;
 
 Plan choose(const Sizes& s, int64_t M, bool fast) {
   const int64_t N = s.N, K = s.K;
   (void)K;
-  if (fast && M >= kLdsMinM && gemm_lds_supported(s, M)) {
+  if (fast && M >= kLdsSmallMinM && gemm_lds_supported(s, M)) {
     Plan p;
     p.lds = true;
+    p.bm = M >= kLdsMinM ? 256 : 128;
     p.cfg = -1;
-    p.tiles_n = (N + 255) / 256;
-    p.tiles = ((M + 255) / 256) * p.tiles_n;
+    p.tiles_n = (N + p.bm - 1) / p.bm;
+    p.tiles = ((M + p.bm - 1) / p.bm) * p.tiles_n;
     split_k(p, s, M, 64);
     return p;
   }
@@ -495,6 +499,7 @@ Plan choose(const Sizes& s, int64_t M, bool fast) {
   }
   Plan p;
   p.lds = false;
+  p.bm = 0;
   p.cfg = c;
   p.tiles_n = (N + kCfgs[c].bn - 1) / kCfgs[c].bn;
   p.tiles = tiles_of(c);
@@ -565,7 +570,7 @@ hipError_t launch_gemm(const Sizes& s, const mnb_plan& p, int64_t M, const float
                       ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
                                                  gemm_lds_a16_bytes(s, M))
                       : nullptr;
-    e = launch_gemm_lds(s, p, M, A, ws, Y, part, pl.splits, pl.kc, st);
+    e = launch_gemm_lds(s, p, M, A, ws, Y, part, pl.splits, pl.kc, pl.bm, st);
     if (e != hipSuccess || pl.splits == 1) return e;
     const int64_t MN = M * s.N;
     hipLaunchKernelGGL(gemm_splitk_reduce, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, st,

@@ -44,13 +44,25 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kTM = 8, kTN = 2;                  // 32 x 32 tiles per wave (256 x 64)
-constexpr int kABytes = kBM * kBK * 2;           // fp16 A per stage: 32 KiB
-constexpr int kWBytes = kBN * kBK / 2;           // packed codes per stage: 8 KiB
-constexpr int kSBytes = 4 * kTN * 64 * 4;        // one scale per lane and weight tile: 2 KiB
-constexpr int kStages = 3;
+constexpr int kBK = 64;
 constexpr int kXcds = 8;
+
+// Tile BM x BM: wave w computes all BM rows of columns [w BM/4, (w+1) BM/4)
+// as TM x TN tiles of 32 x 32.  BM = 256 (TM 8, TN 2) for large M, 128 (TM 4,
+// TN 1) below.
+template <int BM>
+struct Tile {
+  static constexpr int TM = BM / 32, TN = BM / 128, BN = BM;
+  static constexpr int ABytes = BM * kBK * 2;     // fp16 A per stage (32 / 16 KiB)
+  static constexpr int WBytes = BN * kBK / 2;     // packed codes per stage (8 / 4 KiB)
+  static constexpr int SBytes = 4 * TN * 64 * 4;  // one scale per lane and weight tile
+  static constexpr int ACopies = BM / 32;         // 1 KiB A copies per wave and stage
+  // LDS stages in flight (for 128-row tiles, 4 and 6 stages measured no
+  // faster than 3, which leaves room for two workgroups per CU)
+  static constexpr int Stages = 3;
+  template <bool HAS_ZP>
+  static constexpr int stage_bytes() { return ABytes + WBytes + (HAS_ZP ? 2 : 1) * SBytes; }
+};
 
 __device__ __forceinline__ uint32_t cvt_pk_rn(float a, float b) {
   const half2v h = half2v{(_Float16)a, (_Float16)b};  // v_cvt_pk_f16_f32, RN
@@ -98,16 +110,20 @@ __global__ void __launch_bounds__(256) round_a_f16(const float* __restrict__ A,
       u32x4{cvt_pk_rn(a.x, a.y), cvt_pk_rn(a.z, a.w), cvt_pk_rn(b.x, b.y), cvt_pk_rn(b.z, b.w)};
 }
 
-template <bool HAS_ZP>
+template <bool HAS_ZP, int BM>
 __global__ void __launch_bounds__(256) gemm_int4_lds(
     const _Float16* __restrict__ A16, const uint8_t* __restrict__ codes,
     const float* __restrict__ scales, const uint32_t* __restrict__ zeros, float* __restrict__ Y,
     float* __restrict__ part, int64_t M, int64_t N, int64_t K, int64_t row_bytes, int64_t nb,
     int32_t bs_shift, int64_t tiles_n, int64_t work, int32_t splits, int64_t kc) {
   extern __shared__ __align__(16) uint8_t smem[];
-  // per stage: [A 32 KiB][codes 8 KiB][scales 2 KiB][zero-point words 2 KiB]
-  constexpr int kStageBytes = kABytes + kWBytes + (HAS_ZP ? 2 : 1) * kSBytes;
-  constexpr int kGroup = 8 + kTN * (HAS_ZP ? 3 : 2);  // vector-memory ops per stage and wave
+  using T_ = Tile<BM>;
+  constexpr int kBM = BM, kBN = T_::BN, kTM = T_::TM, kTN = T_::TN;
+  constexpr int kABytes = T_::ABytes, kWBytes = T_::WBytes, kSBytes = T_::SBytes;
+  constexpr int kAC = T_::ACopies;
+  // per stage: [A][codes][scales][zero-point words]
+  constexpr int kStageBytes = T_::template stage_bytes<HAS_ZP>();
+  constexpr int kGroup = kAC + kTN * (HAS_ZP ? 3 : 2);  // vector-memory ops per stage and wave
 
   // XCD x (= blockIdx % 8) takes work items [x * per, (x + 1) * per)
   const int64_t per = (work + kXcds - 1) / kXcds;
@@ -124,20 +140,20 @@ __global__ void __launch_bounds__(256) gemm_int4_lds(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  // A copies: this wave fills rows [64 * wave, 64 * wave + 64) of a stage, 8
-  // rows (1 KiB) per instruction; lane l writes physical chunk l & 7 of row
-  // 8u + (l >> 3), which holds logical chunk (l & 7) ^ ((row >> 1) & 7).
+  // A copies: this wave fills rows [BM/4 * wave, BM/4 * (wave + 1)) of a
+  // stage, 8 rows (1 KiB) per instruction; lane l writes physical chunk l & 7
+  // of row 8u + (l >> 3), which holds logical chunk (l & 7) ^ ((row >> 1) & 7).
   // Rows past M are clamped (their results are never stored).
-  uint32_t a_off[8];  // element offsets into A16; the launcher checks M * K < 2^31
+  uint32_t a_off[kAC];  // element offsets into A16; the launcher checks M * K < 2^31
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int u = 0; u < kAC; ++u) {
     const int r = u * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
-    int64_t m = m0 + wave * 64 + r;
+    int64_t m = m0 + wave * (kBM / 4) + r;
     m = m < M ? m : M - 1;
     a_off[u] = (uint32_t)(m * K + 8 * c);
   }
-  // Codes, scales and zero points of this wave's own 64 weight rows (rows past
+  // Codes, scales and zero points of this wave's own BM/4 weight rows (rows past
   // N clamped).  Codes: two instructions of 32 rows x 32 bytes, stored
   // chunk-major (lane l: row l & 31, 16-byte half l >> 5), the order of the
   // operand reads; scale and zero-point word: one dword per lane, for the
@@ -149,7 +165,7 @@ __global__ void __launch_bounds__(256) gemm_int4_lds(
   int z_sh[kTN];
 #pragma unroll
   for (int j = 0; j < kTN; ++j) {
-    int64_t n = n0 + wave * 64 + j * 32 + wl_n;
+    int64_t n = n0 + wave * (kBN / 4) + j * 32 + wl_n;
     n = n < N ? n : N - 1;
     w_src[j] = codes + n * row_bytes + 16 * wl_g;
     s_row[j] = scales + n * nb;
@@ -164,7 +180,7 @@ __global__ void __launch_bounds__(256) gemm_int4_lds(
     const int64_t k0 = kbeg + (int64_t)st * kBK;
     uint8_t* base = smem + b * kStageBytes;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) copy16(A16 + a_off[u] + k0, base + (wave * 8 + u) * 1024);
+    for (int u = 0; u < kAC; ++u) copy16(A16 + a_off[u] + k0, base + (wave * kAC + u) * 1024);
     base += kABytes;
 #pragma unroll
     for (int j = 0; j < kTN; ++j) copy16(w_src[j] + (k0 >> 1), base + (wave * kTN + j) * 1024);
@@ -239,30 +255,32 @@ __global__ void __launch_bounds__(256) gemm_int4_lds(
 #pragma unroll
         for (int q = 0; q < kTM * kTN; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
-          if ((q & 1) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+          __builtin_amdgcn_sched_group_barrier(0x002, 24 / kTM, 0);  // VALU
+          if ((q % kTN) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Per stage s (buffer b = s mod 3): wait for this wave's copies of stage s
-  // (the newest group, of stage s + 1, may stay in flight) and for its LDS
-  // reads of stage s - 1; publish with a barrier; refill the buffer of stage
-  // s - 1 with stage s + 2; compute stage s.
-  issue(0, 0);
-  issue(1, 1);
+  // Per stage s (buffer b = s mod S for S stages): wait for this wave's
+  // copies of stage s (the newer groups, of stages s + 1 .. s + S - 2, may stay
+  // in flight) and for its LDS reads of stage s - 1; publish with a barrier;
+  // refill the buffer of stage s - 1 with stage s + S - 1; compute stage s.
+  constexpr int S = T_::Stages;
+  static_assert((S - 2) * kGroup < 64, "vmcnt range");
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i) issue(i, i);
   int b = 0;
   for (int s = 0; s < steps; ++s) {
-    wait_vm_lgkm0<kGroup>();
+    wait_vm_lgkm0<(S - 2) * kGroup>();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    issue(s + 2, b == 0 ? 2 : b - 1);
+    issue(s + S - 1, b == 0 ? S - 1 : b - 1);
     compute(b);
-    b = b == 2 ? 0 : b + 1;
+    b = b == S - 1 ? 0 : b + 1;
   }
   // drain the copies still in flight before the workgroup's LDS is released
   wait_vm_lgkm0<0>();
@@ -272,7 +290,7 @@ __global__ void __launch_bounds__(256) gemm_int4_lds(
   for (int i = 0; i < kTM; ++i)
 #pragma unroll
     for (int j = 0; j < kTN; ++j) {
-      const int64_t col = n0 + wave * 64 + j * 32 + (lane & 31);
+      const int64_t col = n0 + wave * (kBN / 4) + j * 32 + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t row = m0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -291,29 +309,34 @@ uint64_t gemm_lds_a16_bytes(const Sizes& s, int64_t M) {
   return align256((uint64_t)M * (uint64_t)s.K * 2);
 }
 
+template <bool HAS_ZP, int BM>
+hipError_t launch_tile(const Sizes& s, const mnb_plan& p, int64_t M, const _Float16* A16, float* Y,
+                       float* part, int32_t splits, int64_t kc, hipStream_t st) {
+  using T_ = Tile<BM>;
+  const int64_t tiles_n = (s.N + T_::BN - 1) / T_::BN;
+  const int64_t work = ((M + BM - 1) / BM) * tiles_n * splits;
+  const int64_t blocks = (work + kXcds - 1) / kXcds * kXcds;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const size_t lds = (size_t)T_::Stages * T_::template stage_bytes<HAS_ZP>();
+  hipLaunchKernelGGL((gemm_int4_lds<HAS_ZP, BM>), dim3((unsigned)blocks), dim3(256), lds, st, A16,
+                     static_cast<const uint8_t*>(p.codes), static_cast<const float*>(p.scales),
+                     static_cast<const uint32_t*>(p.zeros), Y, part, M, s.N, s.K, s.row_bytes, s.nb,
+                     s.bs == 32 ? 0 : (s.bs == 64 ? 1 : 2), tiles_n, work, splits, kc);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_lds(const Sizes& s, const mnb_plan& p, int64_t M, const float* A,
-                           void* ws, float* Y, float* part, int32_t splits, int64_t kc,
+                           void* ws, float* Y, float* part, int32_t splits, int64_t kc, int bm,
                            hipStream_t st) {
   _Float16* A16 = static_cast<_Float16*>(ws);
   const int64_t n8 = M * s.K / 8;
   hipLaunchKernelGGL(round_a_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, A, A16,
                      n8);
-  const int64_t tiles_n = (s.N + kBN - 1) / kBN;
-  const int64_t work = ((M + kBM - 1) / kBM) * tiles_n * splits;
-  const int64_t blocks = (work + kXcds - 1) / kXcds * kXcds;
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const size_t lds = (size_t)kStages * (kABytes + kWBytes + (s.zeros ? 2 : 1) * kSBytes);
-  if (s.zeros)
-    hipLaunchKernelGGL(gemm_int4_lds<true>, dim3((unsigned)blocks), dim3(256), lds, st, A16,
-                       static_cast<const uint8_t*>(p.codes), static_cast<const float*>(p.scales),
-                       static_cast<const uint32_t*>(p.zeros), Y, part, M, s.N, s.K, s.row_bytes,
-                       s.nb, s.bs == 32 ? 0 : (s.bs == 64 ? 1 : 2), tiles_n, work, splits, kc);
-  else
-    hipLaunchKernelGGL(gemm_int4_lds<false>, dim3((unsigned)blocks), dim3(256), lds, st, A16,
-                       static_cast<const uint8_t*>(p.codes), static_cast<const float*>(p.scales),
-                       nullptr, Y, part, M, s.N, s.K, s.row_bytes, s.nb,
-                       s.bs == 32 ? 0 : (s.bs == 64 ? 1 : 2), tiles_n, work, splits, kc);
-  return hipGetLastError();
+  if (bm == 128)
+    return s.zeros ? launch_tile<true, 128>(s, p, M, A16, Y, part, splits, kc, st)
+                   : launch_tile<false, 128>(s, p, M, A16, Y, part, splits, kc, st);
+  return s.zeros ? launch_tile<true, 256>(s, p, M, A16, Y, part, splits, kc, st)
+                 : launch_tile<false, 256>(s, p, M, A16, Y, part, splits, kc, st);
 }
 
 }  // namespace mnb

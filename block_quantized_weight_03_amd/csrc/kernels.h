@@ -23,8 +23,9 @@ hipError_t launch_gemm(const Sizes& s, const mnb_plan& p, int64_t M, const float
 // its workspace starts with an fp16 copy of A, then the split partials
 bool gemm_lds_supported(const Sizes& s, int64_t M);
 uint64_t gemm_lds_a16_bytes(const Sizes& s, int64_t M);
+// (bm: square tile, 256 or 128)
 hipError_t launch_gemm_lds(const Sizes& s, const mnb_plan& p, int64_t M, const float* A,
-                           void* ws, float* Y, float* part, int32_t splits, int64_t kc,
+                           void* ws, float* Y, float* part, int32_t splits, int64_t kc, int bm,
                            hipStream_t st);
 
 // ---- INT3 QMoE (qmoe.hip) -------------------------------------------------

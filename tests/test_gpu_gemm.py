@@ -115,20 +115,24 @@ def test_gemm_deterministic():
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
 
 
-def test_gemm_rows_are_independent():
+@pytest.mark.parametrize("M,lo,hi", [(100, 20, 37), (700, 100, 400)])
+def test_gemm_rows_are_independent(M, lo, hi):
     """Row m of the output depends only on row m of A (no cross-row mixing in
-    the tiling): a sub-batch gives the same bits."""
-    say("gemm row independence")
-    M, K, N = 300, 512, 384
+    the tiling): a sub-batch that takes the same kernel (the register-staged
+    one below 128 rows, the 128 x 128 LDS-streaming one from 128 to 1023)
+    gives the same bits.  Different kernels sum K in different orders."""
+    say(f"gemm row independence M={M}")
+    K, N = 512, 384
     w, *_ = prepare(K, N, seed=27)
     a = synth.activations_f32(28, M, K)
     y = run_gemm(w, a)
-    y_sub = run_gemm(w, a[100:117])
-    assert np.array_equal(y[100:117], y_sub)
+    y_sub = run_gemm(w, a[lo:hi])
+    assert np.array_equal(y[lo:hi], y_sub)
 
 
-# M >= 1024 with K a multiple of 64 takes the 256 x 256 LDS-streaming kernel:
-# ragged M and N tails, one-stage K, every block size, zero points, split K.
+# M >= 128 with K a multiple of 64 takes the LDS-streaming kernel (128 x 128
+# tiles below M = 1024, 256 x 256 from there): ragged M and N tails, one-stage
+# K, every block size, zero points, split K.
 @pytest.mark.parametrize("M,K,N,bs,zp", [
     (1100, 320, 700, 64, True), (1025, 64, 33, 32, False), (1030, 384, 257, 128, True),
     (1300, 192, 1000, 32, False), (1040, 4096, 300, 128, True), (600, 320, 700, 64, True)])
