@@ -44,6 +44,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTokTile = 512;   // tokens per pass (bounds the workspace)
 constexpr int kDecodeSlots = 32; // T * k up to which the per-slot decode path runs
+constexpr int kFusedRouteSlots = 8;  // T * k up to which FC1 also routes (one launch less)
 constexpr int kMaxE = 1024;     // experts supported by the grouping kernel
 constexpr int kGroupThreads = 1024;
 
@@ -66,13 +67,16 @@ __device__ __forceinline__ float key_logit(uint32_t k) {
 // fold the rows into lane 63, which is read back as a uniform value.
 template <bool MAX>
 __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
+  // the moved-in value defaults to the identity of the operation, so each
+  // step compiles to one v_max_u32_dpp / v_min_u32_dpp
+  constexpr int id = MAX ? 0 : -1;
   auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
@@ -80,15 +84,14 @@ __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
 // the E <= 1024 experts (lane l holds experts 64i + l), then
 // r_j = exp(l_j - l_max) / sum_sel exp(l_i - l_max) in fp32, which equals an
 // fp32 softmax over all experts renormalized over the selected ones.
-__global__ void __launch_bounds__(256) qmoe_route(const float* __restrict__ logits, int64_t T,
-                                                  int E, int k, int32_t* __restrict__ ids,
-                                                  float* __restrict__ wts) {
-  constexpr int kPer = kMaxE / 64;
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (t >= T) return;  // whole waves leave together
+// (kPer: experts per lane, E <= 64 kPer; instantiated for 2, 4 and 16)
+// Top-k of one token's E logits by one wave (lane l holds experts 64i + l);
+// lane 0 writes ids[j] and the renormalized weights wts[j], j < k <= 16.
+// (kPer: experts per lane, E <= 64 kPer; instantiated for 2, 4 and 16)
+template <int kPer>
+__device__ __forceinline__ void route_token(const float* __restrict__ l, int E, int k, int lane,
+                                            int32_t* ids, float* wts) {
   const int nper = (E + 63) >> 6;
-  const float* l = logits + t * E;
   uint32_t key[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
@@ -125,10 +128,20 @@ __global__ void __launch_bounds__(256) qmoe_route(const float* __restrict__ logi
   }
   if (lane == 0) {
     for (int j = 0; j < k; ++j) {
-      ids[t * k + j] = sel_i[j];
-      wts[t * k + j] = sel_v[j] / den;
+      ids[j] = sel_i[j];
+      wts[j] = sel_v[j] / den;
     }
   }
+}
+
+template <int kPer>
+__global__ void __launch_bounds__(256) qmoe_route(const float* __restrict__ logits, int64_t T,
+                                                  int E, int k, int32_t* __restrict__ ids,
+                                                  float* __restrict__ wts) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole waves leave together
+  route_token<kPer>(logits + t * E, E, k, lane, ids + t * k, wts + t * k);
 }
 
 // ---------------------------------------------------------------------------
@@ -533,110 +546,234 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
 // expert's weights once, which is what the grouped path would read as well.
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ float wave_sum_f32(float v) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0xB1, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x4E, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x141, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x140, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-
 // Reinterprets a 32-bit word as two halves.  The word is taken by value: this
 // compiler folds __builtin_bit_cast of a vector element (v.y, v.z, v.w) to a
 // read of element .x, so elements are always copied into a scalar first.
 __device__ __forceinline__ half2t as_half2(uint32_t v) { return __builtin_bit_cast(half2t, v); }
 
-// sum_k w_k a_k over one 32-code group: w = fp16((q - 4) s), a fp16 (16 B x 4)
-__device__ __forceinline__ float group_dot(const u32x3 w, _Float16 s, uint32_t magic,
-                                           const u32x4* a16) {
-  half8 wf[4];
-  dequant_group(w, s, magic, wf);
+// s * sum_k (q_k - 4) a_k over one 32-code group, for the decode GEMVs: the
+// codes become exact fp16 (q - 4) (no per-code scale multiply), v_dot2 sums
+// the exact products in fp32 and the group's scale is applied once.
+__device__ __forceinline__ float group_dot_unscaled(const u32x3 w, float s, uint32_t magic,
+                                                    const u32x4* a16) {
+  const half2t m4 = half2t{(_Float16)-1028.0f, (_Float16)-1028.0f};
+  uint32_t p[16];
+#pragma unroll
+  for (int m = 0; m < 3; ++m) {
+    const uint32_t x = m == 0 ? w.x : (m == 1 ? w.y : w.z);
+#pragma unroll
+    for (int q = 0; q < 5; ++q)
+      p[5 * m + q] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2t, bfi(0x00070007u, x >> (3 * q), magic)) + m4);
+  }
+  const uint32_t c3031 = bfi(0x00010001u, w.x >> 15, bfi(0x00020002u, w.y >> 14, bfi(0x00040004u, w.z >> 13, magic)));
+  p[15] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2t, c3031) + m4);
   float acc = 0.0f;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const u32x4 av = a16[t];
-    const u32x4 wv = __builtin_bit_cast(u32x4, wf[t]);
-    acc = __builtin_amdgcn_fdot2(as_half2(wv.x), as_half2(av.x), acc, false);
-    acc = __builtin_amdgcn_fdot2(as_half2(wv.y), as_half2(av.y), acc, false);
-    acc = __builtin_amdgcn_fdot2(as_half2(wv.z), as_half2(av.z), acc, false);
-    acc = __builtin_amdgcn_fdot2(as_half2(wv.w), as_half2(av.w), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_half2(p[4 * t]), as_half2(av.x), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_half2(p[4 * t + 1]), as_half2(av.y), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_half2(p[4 * t + 2]), as_half2(av.z), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_half2(p[4 * t + 3]), as_half2(av.w), acc, false);
   }
-  return acc;
+  return acc * s;
 }
 
-// FC1 + SwiGLU: one wave per (token t, rank j, i): rows 2i (gate) and 2i + 1
-// (up) of expert ids[t, j]; lane l takes the 32-code groups l, l + 64, ...
-// h[(t k + j) I + i] = fp16(silu(g) u).
-__global__ void __launch_bounds__(256) qmoe_fc1_decode(MoeGemmArgs g, int64_t T) {
-  const int lane = threadIdx.x & 63;
-  const int64_t I = g.N / 2, pairs = T * g.top_k * I;
-  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
-  const int ng = (int)(g.K / 32);
-  const _Float16* x = static_cast<const _Float16*>(g.act);
-  const uint32_t magic = opaque_magic();
-  for (int64_t p = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); p < pairs;
-       p += nwaves) {
-    const int64_t slot = p / I, i = p % I, t = slot / g.top_k;
-    const int e = clamp_id(g.perm[slot], g.E);  // perm holds the routed ids here
-    const int64_t row = (int64_t)e * g.N + 2 * i;
-    const uint8_t* ebase = g.codes + (int64_t)e * g.N * g.row_bytes;
-    float gs = 0.0f, us = 0.0f;
-    for (int gi = lane; gi < ng; gi += 64) {
-      const u32x4* a = reinterpret_cast<const u32x4*>(x + t * g.K + 32 * gi);
-      const u32x4 av[4] = {a[0], a[1], a[2], a[3]};
-      const u32x3 wg = *reinterpret_cast<const u32x3*>(ebase + int3_goff((int)g.N, (int)g.K, (int)(2 * i), gi));
-      const u32x3 wu = *reinterpret_cast<const u32x3*>(ebase + int3_goff((int)g.N, (int)g.K, (int)(2 * i + 1), gi));
-      const int b = (32 * gi) / (int)g.bs;
-      gs += group_dot(wg, __builtin_bit_cast(_Float16, g.scales[row * g.nblk + b]), magic, av);
-      us += group_dot(wu, __builtin_bit_cast(_Float16, g.scales[(row + 1) * g.nblk + b]), magic, av);
+// Partial dot products of the 16-row weight tile at row0 of one expert with
+// an fp16 activation row held in LDS: lane (n, g) = (lane & 15, lane >> 4)
+// takes group 4c + g of row row0 + n for the chunks c = c0, c0 + cstep, ...
+// (one 768-byte load per wave and chunk in the tile-major layout).  Loads
+// are issued in batches of kDecBatch chunks before any is used, the first
+// batch before the activations are staged; groups past K read a valid group
+// with scale 0.
+constexpr int kDecBatch = 8;
+
+struct TileRef {
+  const uint8_t* codes;     // this expert's codes
+  const uint16_t* scales;   // this expert's fp16 scales
+  int N, K, nblk, bshift, row, ng, nch, g;
+};
+
+struct TileBatch {
+  u32x3 w[kDecBatch];
+  uint16_t s[kDecBatch];
+  int G[kDecBatch];
+  uint32_t ok;  // bit u: group G[u] lies inside K (the loaded scale is used as is)
+  int cnt;      // chunks of this batch inside K (wave-uniform)
+
+  // (the loaded words are not touched here, so no wait is needed before the
+  // caller's next steps)
+  __device__ __forceinline__ void load(const TileRef& t, int c0, int cstep) {
+    cnt = c0 < t.nch ? (t.nch - c0 + cstep - 1) / cstep : 0;
+    ok = 0;
+#pragma unroll
+    for (int u = 0; u < kDecBatch; ++u) {
+      const int Gr = 4 * (c0 + u * cstep) + t.g;
+      ok |= (Gr < t.ng ? 1u : 0u) << u;
+      G[u] = Gr < t.ng ? Gr : t.ng - 1;
+      w[u] = *reinterpret_cast<const u32x3*>(t.codes + int3_goff(t.N, t.K, t.row, G[u]));
+      s[u] = t.scales[t.row * t.nblk + ((32 * G[u]) >> t.bshift)];
     }
-    gs = wave_sum_f32(gs);
-    us = wave_sum_f32(us);
-    if (lane == 0) g.h_out[slot * I + i] = __float2half_rn(gs / (1.0f + expf(-gs)) * us);
+  }
+  __device__ __forceinline__ float dot(const _Float16* xs, uint32_t magic) const {
+    float acc = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kDecBatch; ++u)
+      if (u < cnt) {
+        const uint16_t sc = (ok >> u) & 1u ? s[u] : (uint16_t)0;
+        acc += group_dot_unscaled(w[u], (float)__builtin_bit_cast(_Float16, sc), magic,
+                                  reinterpret_cast<const u32x4*>(xs + 32 * G[u]));
+      }
+    return acc;
+  }
+};
+
+// Stages n 16-byte pieces of src into LDS dst with nt threads: the first two
+// pieces per thread are loaded by stage_first (before the caller issues its
+// weight loads: loads complete in order, so waiting for these does not wait
+// for the weights) and stored by stage_rest, which also copies any further
+// pieces.
+struct Stage2 {
+  u32x4 v[2];
+  __device__ __forceinline__ void first(const u32x4* src, int n, int tid, int nt) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = tid + u * nt;
+      v[u] = src[i < n ? i : n - 1];
+    }
+  }
+  __device__ __forceinline__ void rest(const u32x4* src, u32x4* dst, int n, int tid, int nt) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if (tid + u * nt < n) dst[tid + u * nt] = v[u];
+    for (int i = tid + 2 * nt; i < n; i += nt) dst[i] = src[i];
+  }
+};
+
+__device__ __forceinline__ TileRef tile_ref(const MoeGemmArgs& g, int e, int row0, int lane) {
+  TileRef t;
+  t.N = (int)g.N;
+  t.K = (int)g.K;
+  t.codes = g.codes + (int64_t)e * t.N * g.row_bytes;
+  t.scales = reinterpret_cast<const uint16_t*>(g.scales) + (int64_t)e * t.N * g.nblk;
+  t.nblk = (int)g.nblk;
+  t.bshift = g.bs == 32 ? 5 : (g.bs == 64 ? 6 : 7);
+  t.row = row0 + (lane & 15);
+  t.ng = t.K >> 5;
+  t.nch = (t.ng + 3) >> 2;
+  t.g = lane >> 4;
+  return t;
+}
+
+// (Routing +) FC1 + SwiGLU: a workgroup per (slot, 16-row tile = 8 gate/up
+// pairs).  With ROUTE (used for very few slots, where a separate routing
+// launch costs more than the repeated work), wave 0 routes the slot's token
+// (every workgroup recomputes the same top-k; the tile-0 workgroup of rank 0
+// also writes it out for FC2) while the token's row of x is loading into
+// LDS; otherwise the ids come from the routing kernel.  Wave w then takes the K
+// chunks w, w + 4, ... of expert ids[t, j]'s tile; partials are summed in a
+// fixed order and h[slot I + 8 tile + m] = fp16(silu(g_m) u_m) for gate row
+// 2m, up row 2m + 1.
+template <int kPer, bool ROUTE>
+__global__ void __launch_bounds__(256) qmoe_fc1_decode(MoeGemmArgs g, int64_t T,
+                                                       const float* __restrict__ logits,
+                                                       int32_t* __restrict__ ids,
+                                                       float* __restrict__ wts) {
+  extern __shared__ __align__(16) uint8_t sm[];
+  const int K = (int)g.K, N = (int)g.N, I = N / 2, ntile = N >> 4, k = g.top_k;
+  _Float16* xs = reinterpret_cast<_Float16*>(sm);
+  float* red = reinterpret_cast<float*>(sm + 2 * K);  // K % 32 == 0: 16-byte aligned
+  int32_t* rid = reinterpret_cast<int32_t*>(red + 256);
+  float* rw = reinterpret_cast<float*>(rid + 16);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = (int)blockIdx.x / ntile, tile = (int)blockIdx.x % ntile;
+  const int t = slot / k, j = slot % k;
+  const u32x4* xr = reinterpret_cast<const u32x4*>(static_cast<const _Float16*>(g.act) + (int64_t)t * K);
+  Stage2 xst;
+  xst.first(xr, K / 8, tid, 256);
+  __builtin_amdgcn_sched_barrier(0);
+  int e;
+  if constexpr (ROUTE) {
+    if (wave == 0) route_token<kPer>(logits + (int64_t)t * g.E, g.E, k, lane, rid, rw);
+    __syncthreads();
+    if (tile == 0 && j == 0 && tid < k) {
+      ids[t * k + tid] = rid[tid];
+      wts[t * k + tid] = rw[tid];
+    }
+    e = clamp_id(rid[j], g.E);
+  } else {
+    e = clamp_id(ids[slot], g.E);
+  }
+  const TileRef tr = tile_ref(g, e, 16 * tile, lane);
+  TileBatch b;
+  b.load(tr, wave, 4);
+  __builtin_amdgcn_sched_barrier(0);
+  xst.rest(xr, reinterpret_cast<u32x4*>(xs), K / 8, tid, 256);
+  __syncthreads();
+  const uint32_t magic = opaque_magic();
+  float acc = b.dot(xs, magic);
+  for (int c = wave + 4 * kDecBatch; c < tr.nch; c += 4 * kDecBatch) {
+    b.load(tr, c, 4);
+    acc += b.dot(xs, magic);
+  }
+  red[wave * 64 + lane] = acc;
+  __syncthreads();
+  if (tid < 8) {
+    float gs = 0.0f, us = 0.0f;
+    for (int w = 0; w < 4; ++w)
+      for (int q = 0; q < 4; ++q) {
+        gs += red[w * 64 + q * 16 + 2 * tid];
+        us += red[w * 64 + q * 16 + 2 * tid + 1];
+      }
+    g.h_out[(int64_t)slot * I + 8 * tile + tid] = __float2half_rn(gs / (1.0f + expf(-gs)) * us);
   }
 }
 
-// FC2 + combine: a workgroup per output row n of token t; thread L takes rank
-// j = L / G and group gi = L % G (G = I / 32) of expert ids[t, j]; the rank
-// sums y_j are formed in LDS in a fixed order, then
-// out[t, n] = fp16(sum_j r_j y_j) in rank order.
-__global__ void __launch_bounds__(256) qmoe_fc2_decode(MoeGemmArgs g, int64_t T, __half* out,
-                                                       float* slot_dbg) {
-  __shared__ float red[1024];
-  __shared__ float yj[16];
-  const int64_t H = g.N, I = g.K;
-  const int G = (int)(I / 32), k = g.top_k;
-  const int64_t t = blockIdx.x / H, n = blockIdx.x % H;
-  const __half* h = static_cast<const __half*>(g.act);
+// FC2 + combine: a workgroup per (token t, 16-row tile) with one wave per rank
+// j; the token's k rows of h are staged in LDS; wave j forms the partials of
+// expert ids[t, j]'s tile rows, then out[t, n] = fp16(sum_j r_j y_j[n]) with
+// y_j and the rank sum in fixed orders.
+__global__ void __launch_bounds__(1024) qmoe_fc2_decode(MoeGemmArgs g, int64_t T, __half* out,
+                                                        float* slot_dbg) {
+  extern __shared__ __align__(16) uint8_t sm[];
+  const int H = (int)g.N, I = (int)g.K, k = g.top_k, ntile = H >> 4;
+  _Float16* hs = reinterpret_cast<_Float16*>(sm);
+  float* red = reinterpret_cast<float*>(sm + 2 * k * I);  // I % 32 == 0: 16-byte aligned
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int j = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t = (int)blockIdx.x / ntile, tile = (int)blockIdx.x % ntile;
+  const int e = clamp_id(g.perm[t * k + j], g.E);  // perm holds the routed ids here
+  const TileRef tr = tile_ref(g, e, 16 * tile, lane);
+  const u32x4* hr = reinterpret_cast<const u32x4*>(static_cast<const _Float16*>(g.act) + (int64_t)t * k * I);
+  Stage2 hst;
+  hst.first(hr, k * I / 8, tid, 64 * k);
+  __builtin_amdgcn_sched_barrier(0);
+  TileBatch b;
+  b.load(tr, 0, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  hst.rest(hr, reinterpret_cast<u32x4*>(hs), k * I / 8, tid, 64 * k);
+  __syncthreads();
   const uint32_t magic = opaque_magic();
-  for (int L = threadIdx.x; L < k * G; L += blockDim.x) {
-    const int j = L / G, gi = L % G;
-    const int64_t slot = t * k + j;
-    const int e = clamp_id(g.perm[slot], g.E);  // perm holds the routed ids here
-    const int64_t row = (int64_t)e * H + n;
-    const u32x4* a = reinterpret_cast<const u32x4*>(h + slot * I + 32 * gi);
-    const u32x4 av[4] = {a[0], a[1], a[2], a[3]};
-    const u32x3 w = *reinterpret_cast<const u32x3*>(g.codes + (int64_t)e * H * g.row_bytes +
-                                                    int3_goff((int)H, (int)I, (int)n, gi));
-    red[L] = group_dot(w, __builtin_bit_cast(_Float16, g.scales[row * g.nblk + (32 * gi) / g.bs]),
-                       magic, av);
+  const _Float16* hj = hs + j * I;
+  float acc = b.dot(hj, magic);
+  for (int c = kDecBatch; c < tr.nch; c += kDecBatch) {
+    b.load(tr, c, 1);
+    acc += b.dot(hj, magic);
   }
+  red[j * 64 + lane] = acc;
   __syncthreads();
-  if (threadIdx.x < k) {
-    const int j = threadIdx.x;
-    float y = 0.0f;
-    for (int gi = 0; gi < G; ++gi) y += red[j * G + gi];
-    const float r = g.wts[t * k + j];
-    yj[j] = r * y;
-    if (slot_dbg) slot_dbg[(t * k + j) * H + n] = r * y;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid < 16) {
+    const int n = 16 * tile + tid;
     float o = 0.0f;
-    for (int j = 0; j < k; ++j) o += yj[j];
-    out[t * H + n] = __float2half_rn(o);
+    for (int r = 0; r < k; ++r) {
+      float y = 0.0f;
+      for (int q = 0; q < 4; ++q) y += red[r * 64 + q * 16 + tid];
+      const float ry = g.wts[t * k + r] * y;
+      if (slot_dbg) slot_dbg[((int64_t)t * k + r) * H + n] = ry;
+      o += ry;
+    }
+    out[(int64_t)t * H + n] = __float2half_rn(o);
   }
 }
 
@@ -701,6 +838,18 @@ Ws ws_layout(const Sizes& s1, const Sizes& s2, int k, int64_t T) {
   return w;
 }
 
+void launch_route(const float* logits, int64_t T, int E, int k, int32_t* ids, float* wts,
+                  hipStream_t st) {
+  const dim3 grid((unsigned)((T + 3) / 4)), block(256);
+  if (E <= 128)
+    hipLaunchKernelGGL(qmoe_route<2>, grid, block, 0, st, logits, T, E, k, ids, wts);
+  else if (E <= 256)
+    hipLaunchKernelGGL(qmoe_route<4>, grid, block, 0, st, logits, T, E, k, ids, wts);
+  else
+    hipLaunchKernelGGL(qmoe_route<kMaxE / 64>, grid, block, 0, st, logits, T, E, k, ids, wts);
+}
+
+
 }  // namespace
 
 uint64_t qmoe_ws_bytes(const Sizes& s1, const Sizes& s2, int top_k, int64_t T) {
@@ -729,22 +878,30 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
   float* slots = reinterpret_cast<float*>(w + L.slots);
   const size_t group_lds = (size_t)(5 + kGroupThreads / 64) * E * 4;
 
-  // few tokens: per-slot GEMVs, no grouping (every slot reads its expert once)
-  if (T * k <= kDecodeSlots && k * (I / 32) <= 1024) {
+  // few tokens: per-slot GEMVs, no grouping (every slot reads its expert once);
+  // the activation rows they stage in LDS bound H and k * I
+  if (T * k <= kDecodeSlots && H <= 16384 && k * I <= 16384) {
     const int64_t S = T * k;
-    hipLaunchKernelGGL(qmoe_route, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, logits, T,
-                       (int)E, k, ids, wts);
     MoeGemmArgs a1{static_cast<const uint8_t*>(p1.codes), static_cast<const __half*>(p1.scales),
                    x, s1.N, s1.K, s1.row_bytes, s1.nb, s1.bs, k, (int)E,
                    nullptr, nullptr, ids, nullptr, nullptr, wts, hbuf, nullptr};
-    const int64_t pairs = S * I;
-    int64_t b1 = (pairs + 3) / 4;
-    if (b1 > 8192) b1 = 8192;
-    hipLaunchKernelGGL(qmoe_fc1_decode, dim3((unsigned)b1), dim3(256), 0, st, a1, T);
+    const dim3 g1((unsigned)(S * (s1.N / 16))), b1(256);
+    const size_t l1 = (size_t)(2 * H + 4 * 256 + 128);
+    if (S > kFusedRouteSlots) {
+      launch_route(logits, T, (int)E, k, ids, wts, st);
+      hipLaunchKernelGGL((qmoe_fc1_decode<2, false>), g1, b1, l1, st, a1, T, logits, ids, wts);
+    } else if (E <= 128) {
+      hipLaunchKernelGGL((qmoe_fc1_decode<2, true>), g1, b1, l1, st, a1, T, logits, ids, wts);
+    } else if (E <= 256) {
+      hipLaunchKernelGGL((qmoe_fc1_decode<4, true>), g1, b1, l1, st, a1, T, logits, ids, wts);
+    } else {
+      hipLaunchKernelGGL((qmoe_fc1_decode<kMaxE / 64, true>), g1, b1, l1, st, a1, T, logits, ids, wts);
+    }
     MoeGemmArgs a2{static_cast<const uint8_t*>(p2.codes), static_cast<const __half*>(p2.scales),
                    hbuf, s2.N, s2.K, s2.row_bytes, s2.nb, s2.bs, k, (int)E,
                    nullptr, nullptr, ids, nullptr, nullptr, wts, nullptr, nullptr};
-    hipLaunchKernelGGL(qmoe_fc2_decode, dim3((unsigned)(T * H)), dim3(256), 0, st, a2, T,
+    hipLaunchKernelGGL(qmoe_fc2_decode, dim3((unsigned)(T * (H / 16))), dim3(64 * k),
+                       (size_t)(2 * k * I + 4 * 64 * k), st, a2, T,
                        reinterpret_cast<__half*>(out), dbg ? dbg->slot : nullptr);
     if (dbg) {
       if (dbg->ids) (void)hipMemcpyAsync(dbg->ids, ids, S * 4, hipMemcpyDeviceToDevice, st);
@@ -759,8 +916,7 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
     const int64_t S = Tt * k;
     const int bm = pick_bm(Tt, k, E);
     const int64_t items = max_items(Tt, k, E, bm);
-    hipLaunchKernelGGL(qmoe_route, dim3((unsigned)((Tt + 3) / 4)), dim3(256), 0, st,
-                       logits + t0 * E, Tt, (int)E, k, ids, wts);
+    launch_route(logits + t0 * E, Tt, (int)E, k, ids, wts, st);
     hipLaunchKernelGGL(qmoe_group, dim3(1), dim3(kGroupThreads), group_lds, st, ids, Tt, k, (int)E,
                        items, bm, go);
     MoeGemmArgs a1{static_cast<const uint8_t*>(p1.codes), static_cast<const __half*>(p1.scales),
