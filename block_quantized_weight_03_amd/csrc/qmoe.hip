@@ -352,10 +352,14 @@ struct MoeGemmArgs {
 constexpr int kQBN = 64;         // weight rows per workgroup
 constexpr int kQBK = 128;        // K per chunk
 constexpr int kQPitch = kQBK + 8;
-constexpr int kNTG = 4;          // 64-row weight tiles per workgroup
+// 64-row weight tiles per workgroup: 4 with 32-token tiles, 2 with 64 (their
+// accumulators would otherwise cost occupancy)
+template <int BM>
+constexpr int ntg_of() { return BM == 32 ? 4 : 2; }
 
 template <bool FC1, int BM>
 __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n, int64_t tiles_n) {
+  constexpr int kNTG = ntg_of<BM>();
   constexpr int TM = BM / 16;          // 16-token MFMA tiles
   constexpr int AP = BM * 16 / 256;    // 16-byte activation chunks per thread and chunk
   __shared__ __align__(16) _Float16 As[2][BM * kQPitch];
@@ -403,7 +407,6 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
   const int wn = lane & 15, wg = lane >> 4;
   const int Kc = (int)g.K;
   const int nch = (Kc + kQBK - 1) / kQBK;
-  const int nsteps = ntc * nch;
   const int bshift = g.bs == 32 ? 5 : (g.bs == 64 ? 6 : 7);
   const uint32_t magic = opaque_magic();
   const uint8_t* wbase = g.codes + (int64_t)e * g.N * g.row_bytes;  // this expert's codes
@@ -411,17 +414,21 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
   const uint16_t* sbase = reinterpret_cast<const uint16_t*>(g.scales) + (int64_t)e * g.N * g.nblk;
 
   // All loads are unconditional (clamped addresses, validity applied where
-  // the data is used), so the compiler keeps them in flight: weights four
-  // steps ahead (a ring of register stages; the HBM stream), activations
-  // (L2-resident) one step ahead through registers into the other LDS buffer.
+  // the data is used), so the compiler keeps them in flight.  The steps walk
+  // the K chunks; in chunk c all kNTG weight tiles use the same staged
+  // activations (staged once per chunk, not once per tile): the wave
+  // dequantizes its group of tile t, loaded during chunk c - 1, and refills
+  // that register stage with chunk c + 1 (the HBM stream); the activations
+  // (L2-resident) move one chunk ahead through registers into the other LDS
+  // buffer.  Tiles past ntc repeat the last tile and are never stored.
   struct WStage {
     u32x3 rw;
     uint32_t rs;
     bool ok;
   };
-  auto load_w = [&](WStage& st, int sidx) {
-    sidx = sidx < nsteps ? sidx : nsteps - 1;
-    const int t = sidx / nch, c = sidx - t * nch;
+  auto load_w = [&](WStage& st, int t, int c) {
+    c = c < nch ? c : nch - 1;
+    t = t < ntc ? t : ntc - 1;
     const int row = (nt0 + t) * kQBN + wave * 16 + wn;
     const bool rok = row < Nc;
     const int kg = c * kQBK + 32 * wg;  // first code of this lane's group
@@ -433,9 +440,8 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
   };
   // (a_src already includes this thread's column a_c)
   u32x4 ra[AP];
-  auto load_a = [&](int sidx) {
-    sidx = sidx < nsteps ? sidx : nsteps - 1;
-    const int c = sidx % nch;
+  auto load_a = [&](int c) {
+    c = c < nch ? c : nch - 1;
     const int k0 = c * kQBK;
     // columns past K (only in a last, partial chunk) read a valid column of
     // the same row; they are zeroed when stored
@@ -457,13 +463,15 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
     }
   };
 
-  f32x4 acc[TM];
+  f32x4 acc[kNTG][TM];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) acc[i] = f32x4{0, 0, 0, 0};
+  for (int t = 0; t < kNTG; ++t)
+#pragma unroll
+    for (int i = 0; i < TM; ++i) acc[t][i] = f32x4{0, 0, 0, 0};
   const int fr = lane & 15;
 
-  // epilogue of weight tile t: lane l holds tokens 16i + 4(l/16) + r of
-  // token tile i, weight row l%16 of this wave's 16
+  // outputs of weight tile t: lane l holds tokens 16i + 4(l/16) + r of token
+  // tile i, weight row l%16 of this wave's 16
   auto epilogue = [&](int t) {
     const int64_t col = (int64_t)(nt0 + t) * kQBN + wave * 16 + (lane & 15);
 #pragma unroll
@@ -471,7 +479,7 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = i * 16 + 4 * (lane >> 4) + r;
-        const float v = acc[i][r];
+        const float v = acc[t][i][r];
         if (FC1) {
           // interleaved gate/up: even row = gate_i, odd row = up_i
           const float partner = __shfl_xor(v, 1);
@@ -487,57 +495,46 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
           }
         }
       }
-      acc[i] = f32x4{0, 0, 0, 0};
     }
   };
 
-  // step s = (tile t, chunk c): dequantize the weights (ring stage s mod 4)
-  // and refill that stage with step s + 4; MFMAs on LDS buffer s mod 2;
-  // after a tile's last chunk, its outputs; then move step s + 1's
-  // activations into the other buffer and fetch step s + 2's
-  auto step = [&](WStage& ws, int sidx) {
-    half8 wf[4];
-    dequant_group(ws.rw, __builtin_bit_cast(_Float16, (uint16_t)(ws.ok ? ws.rs : 0u)), magic, wf);
-    load_w(ws, sidx + 4);
-    const int b = sidx & 1;
+  WStage ws[kNTG];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int kk = 32 * wg + 8 * t;
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        if (i < vt) {
-          const half8 a = *reinterpret_cast<const half8*>(&As[b][(i * 16 + fr) * kQPitch + kk]);
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, wf[t], acc[i], 0, 0, 0);
-        }
-      }
-    }
-    const int t = sidx / nch, c = sidx - t * nch;
-    if (c == nch - 1) epilogue(t);
-    if (sidx + 1 < nsteps) {
-      store_a(b ^ 1, c + 1 == nch ? 0 : c + 1);
-      load_a(sidx + 2);
-      __syncthreads();
-    }
-  };
-
-  WStage w0, w1, w2, w3;
-  load_w(w0, 0);
-  load_w(w1, 1);
-  load_w(w2, 2);
-  load_w(w3, 3);
+  for (int t = 0; t < kNTG; ++t) load_w(ws[t], t, 0);
   load_a(0);
   store_a(0, 0);
   load_a(1);
   __syncthreads();
-  for (int sidx = 0; sidx < nsteps; sidx += 4) {
-    step(w0, sidx);
-    if (sidx + 1 >= nsteps) break;
-    step(w1, sidx + 1);
-    if (sidx + 2 >= nsteps) break;
-    step(w2, sidx + 2);
-    if (sidx + 3 >= nsteps) break;
-    step(w3, sidx + 3);
+  for (int c = 0; c < nch; ++c) {
+    const int b = c & 1;
+#pragma unroll
+    for (int t = 0; t < kNTG; ++t) {
+      half8 wf[4];
+      dequant_group(ws[t].rw, __builtin_bit_cast(_Float16, (uint16_t)(ws[t].ok ? ws[t].rs : 0u)), magic, wf);
+      load_w(ws[t], t, c + 1);
+      if (t < ntc) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int kk = 32 * wg + 8 * q;
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            if (i < vt) {
+              const half8 a = *reinterpret_cast<const half8*>(&As[b][(i * 16 + fr) * kQPitch + kk]);
+              acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, wf[q], acc[t][i], 0, 0, 0);
+            }
+          }
+        }
+      }
+    }
+    if (c + 1 < nch) {
+      store_a(b ^ 1, c + 1);
+      load_a(c + 2);
+      __syncthreads();
+    }
   }
+#pragma unroll
+  for (int t = 0; t < kNTG; ++t)
+    if (t < ntc) epilogue(t);
 }
 
 // ---------------------------------------------------------------------------
@@ -922,7 +919,8 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
     MoeGemmArgs a1{static_cast<const uint8_t*>(p1.codes), static_cast<const __half*>(p1.scales),
                    x + t0 * H, s1.N, s1.K, s1.row_bytes, s1.nb, s1.bs, k, (int)E,
                    go.counts, go.offsets, go.perm, go.items, go.nitems, wts, hbuf, nullptr};
-    const int64_t nt1 = (s1.N + kQBN - 1) / kQBN, ng1 = (nt1 + kNTG - 1) / kNTG;
+    const int ntg = bm == 32 ? ntg_of<32>() : ntg_of<kMaxBM>();
+    const int64_t nt1 = (s1.N + kQBN - 1) / kQBN, ng1 = (nt1 + ntg - 1) / ntg;
     if (bm == 32)
       hipLaunchKernelGGL((qmoe_gemm<true, 32>), dim3((unsigned)((items + 7) / 8 * 8 * ng1)), dim3(256), 0, st, a1, ng1, nt1);
     else
@@ -930,7 +928,7 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
     MoeGemmArgs a2{static_cast<const uint8_t*>(p2.codes), static_cast<const __half*>(p2.scales),
                    hbuf, s2.N, s2.K, s2.row_bytes, s2.nb, s2.bs, k, (int)E,
                    go.counts, go.offsets, go.perm, go.items, go.nitems, wts, nullptr, slots};
-    const int64_t nt2 = (s2.N + kQBN - 1) / kQBN, ng2 = (nt2 + kNTG - 1) / kNTG;
+    const int64_t nt2 = (s2.N + kQBN - 1) / kQBN, ng2 = (nt2 + ntg - 1) / ntg;
     if (bm == 32)
       hipLaunchKernelGGL((qmoe_gemm<false, 32>), dim3((unsigned)((items + 7) / 8 * 8 * ng2)), dim3(256), 0, st, a2, ng2, nt2);
     else
