@@ -5,15 +5,17 @@ vocabulary-head GEMV and the INT3 QMoE layer reported alongside.
 
 A step is one pass over the layer's projections (fused QKV 2048->4096, o_proj
 2048->2048, gate and up 2048->6144, down 6144->2048, and the K-tail case
-2050->1024), each an mnb_gemv call on the library's prepared INT4 weights.
+2050->1024) on the library's prepared INT4 weights: an mnb_gemv call each,
+except gate and up, which read the same input vector (as in a SwiGLU MLP) and
+go through one mnb_gemv_multi call (one launch for both).
 Weights rotate over enough distinct copies (>= 1 GiB) that every step streams
 them from HBM rather than from the 256 MB Infinity Cache.  The timed steps are
 replayed from a HIP graph (launch overhead of the Python binding excluded) and
 bracketed by torch.cuda.synchronize() on both sides.
 
 The roofline's average launch duration comes from HIP events recorded on the
-launch stream around the same timed graph replays (one GEMV kernel per
-launch, launches back to back, so the average includes the short gaps between
+launch stream around the same timed graph replays (five GEMV kernel launches
+per step, back to back, so the average includes the short gaps between
 kernels).  The other figures are measured the same way, each from a graph of
 its own launches.
 
@@ -163,8 +165,12 @@ def main():
     log(f"preparing {copies} copies of the layer ({step_bytes} B each)")
     acts = []
     for i, (name, K, N) in enumerate(LAYER):
+        if name == "up":  # gate and up read the same input
+            acts.append(acts[-1])
+            continue
         a = synth.activations_f32(synth.seed_for(2, 100 + i), 1, K)
         acts.append((a, torch.from_numpy(a[0]).to(dev)))
+    gate, up = [n for n, _, _ in LAYER].index("gate"), [n for n, _, _ in LAYER].index("up")
     layers, layer_host = [], None
     for c in range(copies):
         ws = []
@@ -186,7 +192,13 @@ def main():
 
     def step(c):
         for i, w in enumerate(layers[c]):
-            mnb.mnb_gemv(w.plan, acts[i][1], outs[i], gemv_ws, gemv_ws.numel())
+            if i == up:
+                continue
+            if i == gate:
+                mnb.mnb_gemv_multi([w.plan, layers[c][up].plan], acts[i][1], [outs[gate], outs[up]],
+                                   gemv_ws, gemv_ws.numel())
+            else:
+                mnb.mnb_gemv(w.plan, acts[i][1], outs[i], gemv_ws, gemv_ws.numel())
 
     full = Graph(torch, lambda: [step(c) for c in range(copies)])
     rem = args.steps % copies
@@ -210,9 +222,10 @@ def main():
     value = step_bytes * args.steps / elapsed / 1e9
 
     # ---- roofline of the GEMV kernel over the same timed region --------------
-    launches = args.steps * len(LAYER)
+    launches_per_step = len(LAYER) - 1  # gate and up share one launch
+    launches = args.steps * launches_per_step
     avg_ms = e0.elapsed_time(e1) / launches
-    avg_bytes = step_bytes / len(LAYER)
+    avg_bytes = step_bytes / launches_per_step
     achieved = avg_bytes / (avg_ms * 1e-3) / 1e9
     gemv_hash = source_hash("gemv.hip")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
@@ -227,6 +240,12 @@ def main():
                                                           gemv_ws.numel()) for c in range(copies)]
         us = 1e3 * graph_time(torch, calls, 10)
         per_proj[name] = {"us": round(us, 3), "GB/s": round(gemv_bytes(K, N) / us / 1e3, 1)}
+    calls = [lambda c=c: mnb.mnb_gemv_multi([layers[c][gate].plan, layers[c][up].plan], acts[gate][1],
+                                            [outs[gate], outs[up]], gemv_ws, gemv_ws.numel())
+             for c in range(copies)]
+    us = 1e3 * graph_time(torch, calls, 10)
+    gu = gemv_bytes(LAYER[gate][1], LAYER[gate][2]) + gemv_bytes(LAYER[up][1], LAYER[up][2])
+    per_proj["gate+up (one launch)"] = {"us": round(us, 3), "GB/s": round(gu / us / 1e3, 1)}
 
     del full, part
     torch.cuda.synchronize()

@@ -72,6 +72,7 @@ SIGNATURES = {
     "mnb_prepare": [_PD, _P, _P, _P, _P, _U64, _P, _PPLAN],
     "mnb_gemv_workspace_size": [_PPLAN, _PU64],
     "mnb_gemv": [_PPLAN, _P, _P, _P, _U64, _P],
+    "mnb_gemv_multi": [_P, _I32, _P, _P, _P, _U64, _P],
     "mnb_gemm_workspace_size": [_PPLAN, _I64, _PU64],
     "mnb_gemm": [_PPLAN, _I64, _P, _P, _P, _U64, _P],
     "qmoe_workspace_size": [_PPLAN, _PPLAN, _PQ, _I64, _PU64],
@@ -194,6 +195,18 @@ def mnb_gemv_workspace_size(plan: mnb_plan) -> int:
 def mnb_gemv(plan: mnb_plan, A_dev, Y_dev, ws_dev, ws_bytes: int, stream=None):
     _check(lib().mnb_gemv(ctypes.byref(plan), _ptr(A_dev), _ptr(Y_dev), _ptr(ws_dev), ws_bytes,
                           _stream(stream)), "mnb_gemv")
+
+
+def mnb_gemv_multi(plans, A_dev, Y_devs, ws_dev, ws_bytes: int, stream=None):
+    """plans: sequence of mnb_plan; Y_devs: one output per plan."""
+    n = len(plans)
+    if n != len(Y_devs):
+        raise ValueError("one output per plan")
+    parr = (ctypes.POINTER(mnb_plan) * max(n, 1))(*[ctypes.pointer(p) for p in plans])
+    yarr = (ctypes.c_void_p * max(n, 1))(*[_ptr(y) for y in Y_devs])
+    _check(lib().mnb_gemv_multi(ctypes.cast(parr, ctypes.c_void_p), n, _ptr(A_dev),
+                                ctypes.cast(yarr, ctypes.c_void_p), _ptr(ws_dev), ws_bytes,
+                                _stream(stream)), "mnb_gemv_multi")
 
 
 def mnb_gemm_workspace_size(plan: mnb_plan, M: int) -> int:

@@ -174,6 +174,36 @@ int32_t mnb_gemv(const mnb_plan* plan, const float* A_dev, float* Y_dev, void* w
   })
 }
 
+int32_t mnb_gemv_multi(const mnb_plan* const* plans, int32_t count, const float* A_dev,
+                       float* const* Y_dev, void* ws_dev, uint64_t ws_bytes, void* stream) {
+  MNB_GUARD({
+    if (!plans || !Y_dev || !A_dev || count < 1 || count > kMaxSegs) return MNB_ERR_INVALID_ARG;
+    Sizes s[kMaxSegs];
+    uint64_t need = 0;
+    for (int i = 0; i < count; ++i) {
+      int32_t rc = check_plan(plans[i], &s[i]);
+      if (rc != MNB_OK) return rc;
+      if (s[i].kind != kDenseInt4) return MNB_ERR_UNSUPPORTED;
+      if (!Y_dev[i] || s[i].K != s[0].K) return MNB_ERR_INVALID_ARG;
+      const uint64_t w = gemv_ws_bytes(s[i]);
+      need = w > need ? w : need;
+    }
+    int32_t rc = check_ws(ws_dev, ws_bytes, need);
+    if (rc != MNB_OK) return rc;
+    for (int i = 0; i < count; ++i)
+      if ((rc = check_device(plans[i])) != MNB_OK) return rc;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (gemv_multi_fusable(s, count)) {
+      if (launch_gemv_multi(s, plans, count, A_dev, Y_dev, st) != hipSuccess) return MNB_ERR_DEVICE;
+      return MNB_OK;
+    }
+    for (int i = 0; i < count; ++i)
+      if (launch_gemv(s[i], *plans[i], A_dev, Y_dev[i], ws_dev, st) != hipSuccess)
+        return MNB_ERR_DEVICE;
+    return MNB_OK;
+  })
+}
+
 int32_t mnb_gemm_workspace_size(const mnb_plan* plan, int64_t M, uint64_t* bytes) {
   MNB_GUARD({
     if (!bytes || M < 0) return MNB_ERR_INVALID_ARG;

@@ -419,16 +419,39 @@ constexpr int kNPT = 8 / kTeams;  // 16-byte pieces of A per thread
 // sub-block's 128 bytes, so the 16 lanes served per LDS cycle hit 64
 // distinct banks.  The A loads are issued before the weight loads; loads
 // complete in order, so waiting for A does not wait for the weights.
+// Up to kMaxSegs weight matrices with the same K, block size and zero-point
+// kind, multiplied by the same A in one launch: segment i owns workgroups
+// [first[i], first[i + 1]).
+struct GemvSegs {
+  const uint8_t* codes[kMaxSegs];
+  const float* scales[kMaxSegs];
+  const uint32_t* zeros[kMaxSegs];
+  float* Y[kMaxSegs];
+  int32_t N[kMaxSegs];
+  int32_t first[kMaxSegs + 1];
+  int32_t count;
+};
+
 template <int R, bool HAS_ZP>
 __global__ void __launch_bounds__(1024) gemv_int4_f32(
-    const float* __restrict__ A, const uint8_t* __restrict__ codes,
-    const float* __restrict__ scales, const uint32_t* __restrict__ zeros, float* __restrict__ Y,
-    int32_t K, int32_t N, int32_t row_bytes, int32_t nb, int32_t nsb, int32_t team,
-    int32_t bs_shift) {
+    const float* __restrict__ A, const GemvSegs sg, int32_t K, int32_t row_bytes, int32_t nb,
+    int32_t nsb, int32_t team, int32_t bs_shift) {
   // A: 64 * team sub-blocks of 128 bytes (the launcher sizes it), then the
   // team partials
   extern __shared__ __align__(16) u32x4 as[];
   float* tot = reinterpret_cast<float*>(as + 512 * team);
+
+  // this workgroup's segment (uniform)
+  int seg = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxSegs; ++i)
+    if (i < sg.count && (int)blockIdx.x >= sg.first[i]) seg = i;
+  const uint8_t* __restrict__ codes = sg.codes[seg];
+  const float* __restrict__ scales = sg.scales[seg];
+  const uint32_t* __restrict__ zeros = sg.zeros[seg];
+  float* __restrict__ Y = sg.Y[seg];
+  const int N = sg.N[seg];
+  const int blk = (int)blockIdx.x - sg.first[seg];
 
   const int tid = (int)threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -436,7 +459,7 @@ __global__ void __launch_bounds__(1024) gemv_int4_f32(
   // kTeams teams of `team` waves (one K chunk each), one row group per team
   const int tm = (wave >= team) + (wave >= 2 * team) + (wave >= 3 * team);
   const int wit = wave - tm * team;
-  const int n0 = ((int)blockIdx.x * kTeams + tm) * R;
+  const int n0 = (blk * kTeams + tm) * R;
 
   // A pieces of this thread: tid + nt * u (past K: zeros); the workgroup's
   // nt = 256 team threads hold all 8 * 64 * team pieces of its K chunks
@@ -608,19 +631,38 @@ hipError_t launch_fused(const Sizes& s, const mnb_plan& p, const float* A, float
   return hipGetLastError();
 }
 
+// s: the shape shared by the segments (K, block size, zero-point kind);
+// segment i multiplies plan p[i] (N = N[i]) into Y[i]
+template <int R, bool HAS_ZP>
+hipError_t launch_f32_segs(const Sizes& s, const mnb_plan* const* p, const int64_t* N, int count,
+                           const float* A, float* const* Y, int64_t nsb, int64_t nchunk,
+                           hipStream_t st) {
+  const int team = (int)nchunk;
+  GemvSegs sg{};
+  sg.count = count;
+  int64_t blocks = 0;
+  for (int i = 0; i < count; ++i) {
+    sg.codes[i] = static_cast<const uint8_t*>(p[i]->codes);
+    sg.scales[i] = static_cast<const float*>(p[i]->scales);
+    sg.zeros[i] = static_cast<const uint32_t*>(p[i]->zeros);
+    sg.Y[i] = Y[i];
+    sg.N[i] = (int32_t)N[i];
+    sg.first[i] = (int32_t)blocks;
+    blocks += ((N[i] + R - 1) / R + kTeams - 1) / kTeams;
+  }
+  sg.first[count] = (int32_t)blocks;
+  const size_t lds = (size_t)team * 8192 + (size_t)kTeams * team * R * 4;
+  hipLaunchKernelGGL((gemv_int4_f32<R, HAS_ZP>), dim3((unsigned)blocks), dim3(64 * kTeams * team),
+                     lds, st, A, sg, (int32_t)s.K, (int32_t)s.row_bytes, (int32_t)s.nb,
+                     (int32_t)nsb, team, bs_shift_of(s));
+  return hipGetLastError();
+}
+
 template <int R, bool HAS_ZP>
 hipError_t launch_f32(const Sizes& s, const mnb_plan& p, const float* A, float* Y, int64_t nsb,
                       int64_t nchunk, hipStream_t st) {
-  const int team = (int)nchunk;
-  const int64_t nrg = (s.N + R - 1) / R;
-  const int64_t blocks = (nrg + kTeams - 1) / kTeams;
-  const size_t lds = (size_t)team * 8192 + (size_t)kTeams * team * R * 4;
-  hipLaunchKernelGGL((gemv_int4_f32<R, HAS_ZP>), dim3((unsigned)blocks), dim3(64 * kTeams * team),
-                     lds, st, A, static_cast<const uint8_t*>(p.codes),
-                     static_cast<const float*>(p.scales), static_cast<const uint32_t*>(p.zeros), Y,
-                     (int32_t)s.K, (int32_t)s.N, (int32_t)s.row_bytes, (int32_t)s.nb, (int32_t)nsb,
-                     team, bs_shift_of(s));
-  return hipGetLastError();
+  const mnb_plan* pp = &p;
+  return launch_f32_segs<R, HAS_ZP>(s, &pp, &s.N, 1, A, &Y, nsb, nchunk, st);
 }
 
 template <int R, bool HAS_ZP>
@@ -649,6 +691,13 @@ hipError_t launch_ws(const Sizes& s, const mnb_plan& p, const float* A, float* Y
   return hipGetLastError();
 }
 
+// The plain fp32 path: N <= 32768, K <= 8192, and 32-bit offsets (rows of at
+// most 4 KiB of codes)
+bool f32_path(const Sizes& s) {
+  const int64_t nchunk = (n_subblocks(s) + 63) / 64;
+  return nchunk <= kMaxTeam && s.N <= kF32MaxRows && s.row_bytes * s.N < (int64_t(1) << 31);
+}
+
 template <bool HAS_ZP>
 hipError_t dispatch(const Sizes& s, const mnb_plan& p, const float* A, float* Y, void* ws,
                     hipStream_t st) {
@@ -656,10 +705,8 @@ hipError_t dispatch(const Sizes& s, const mnb_plan& p, const float* A, float* Y,
   const int64_t nchunk = (nsb + 63) / 64;
   if (nchunk > kMaxTeam) return launch_ws<8, HAS_ZP>(s, p, A, Y, ws, nsb, nchunk, st);
   // up to tens of thousands of rows: the plain fp32 path, two rows per wave
-  // (measured faster there; the digit planes pay off on long row streams);
-  // 32-bit offsets: rows of at most 4 KiB of codes, N <= 32768
-  if (s.N <= kF32MaxRows && s.row_bytes * s.N < (int64_t(1) << 31))
-    return launch_f32<2, HAS_ZP>(s, p, A, Y, nsb, nchunk, st);
+  // (measured faster there; the digit planes pay off on long row streams)
+  if (f32_path(s)) return launch_f32<2, HAS_ZP>(s, p, A, Y, nsb, nchunk, st);
   // rows per wave iteration: enough row groups to fill the chip for small N,
   // deeper load batches for large N
   const int64_t teams = kMaxTeam / nchunk;
@@ -670,6 +717,25 @@ hipError_t dispatch(const Sizes& s, const mnb_plan& p, const float* A, float* Y,
 }
 
 }  // namespace
+
+bool gemv_multi_fusable(const Sizes* s, int count) {
+  if (count < 1 || count > kMaxSegs) return false;
+  for (int i = 0; i < count; ++i)
+    if (!f32_path(s[i]) || s[i].K != s[0].K || s[i].bs != s[0].bs ||
+        (s[i].zeros != 0) != (s[0].zeros != 0))
+      return false;
+  return true;
+}
+
+hipError_t launch_gemv_multi(const Sizes* s, const mnb_plan* const* p, int count, const float* A,
+                             float* const* Y, hipStream_t st) {
+  const int64_t nsb = n_subblocks(s[0]);
+  const int64_t nchunk = (nsb + 63) / 64;
+  int64_t N[kMaxSegs];
+  for (int i = 0; i < count; ++i) N[i] = s[i].N;
+  return s[0].zeros ? launch_f32_segs<2, true>(s[0], p, N, count, A, Y, nsb, nchunk, st)
+                    : launch_f32_segs<2, false>(s[0], p, N, count, A, Y, nsb, nchunk, st);
+}
 
 uint64_t gemv_ws_bytes(const Sizes& s) {
   const int64_t nchunk = (n_subblocks(s) + 63) / 64;

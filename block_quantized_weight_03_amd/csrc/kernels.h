@@ -11,6 +11,12 @@ namespace mnb {
 
 // ---- M = 1 GEMV on dense INT4 plans (gemv.hip) ----------------------------
 uint64_t gemv_ws_bytes(const Sizes& s);
+// several dense plans with the same K, block size and zero-point kind times
+// one A in one launch (bit-identical to separate launches)
+constexpr int kMaxSegs = 4;
+bool gemv_multi_fusable(const Sizes* s, int count);
+hipError_t launch_gemv_multi(const Sizes* s, const mnb_plan* const* p, int count, const float* A,
+                             float* const* Y, hipStream_t st);
 hipError_t launch_gemv(const Sizes& s, const mnb_plan& p, const float* A, float* Y,
                        void* ws, hipStream_t st);
 

@@ -171,6 +171,21 @@ int32_t mnb_gemv_workspace_size(const mnb_plan* plan, uint64_t* bytes);
 int32_t mnb_gemv(const mnb_plan* plan, const float* A_dev, float* Y_dev,
                  void* ws_dev, uint64_t ws_bytes, void* stream);
 
+/* Several M = 1 GEMVs [PLAN K02] sharing one activation vector (e.g. the gate
+ * and up projections of a SwiGLU MLP, which read the same input):
+ *   for i < count:  Y_dev[i] = mnb_gemv(plans[i], A_dev),
+ * bit-identical to the separate calls.  All plans must be dense INT4 with the
+ * same K; when they also share the block size and zero-point kind and each
+ * takes the short-row fp32 path (N <= 32768, K <= 8192), one kernel launch
+ * does them all, otherwise they run one after another on the stream.
+ * plans: host array of count plan pointers; Y_dev: host array of count device
+ * pointers (fp32 [N_i], contiguous); count in [1, 4]; ws_dev as for mnb_gemv
+ * with the largest workspace any of the plans needs (shared, used by one GEMV
+ * at a time).  Errors: INVALID_ARG (count out of range, null pointers,
+ * different K), otherwise as for mnb_gemv. */
+int32_t mnb_gemv_multi(const mnb_plan* const* plans, int32_t count, const float* A_dev,
+                       float* const* Y_dev, void* ws_dev, uint64_t ws_bytes, void* stream);
+
 /* Workspace bytes mnb_gemm needs for this plan and M (may be 0). */
 int32_t mnb_gemm_workspace_size(const mnb_plan* plan, int64_t M, uint64_t* bytes);
 

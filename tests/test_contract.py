@@ -255,3 +255,17 @@ def test_qmoe_descriptor_and_shape_checks():
     pd, _, _k3 = host_prepare(mnb.dense_desc(64, 8), B, s, None)
     assert status_of(mnb.qmoe_workspace_size, pd, p2, q, 4) == UNSUP
     assert lib.mnb_gemv(ctypes.byref(p1), 1, 1, 256, 1 << 20, None) == UNSUP
+
+
+def test_gemv_multi_argument_checks_before_any_device_call():
+    """mnb_gemv_multi rejects a plan count outside [1, 4], a missing output and
+    plans of different K before it touches a device (host plans suffice)."""
+    p1, v1, d1 = host_prepare(mnb.dense_desc(64, 16), *dense_inputs(16, 64))
+    p2, v2, d2 = host_prepare(mnb.dense_desc(96, 16), *dense_inputs(16, 96, seed=5))
+    y = np.zeros(16, np.float32)
+    a = np.zeros(96, np.float32)
+    assert status_of(mnb.mnb_gemv_multi, [], a, [], None, 0, 0) == INVALID
+    assert status_of(mnb.mnb_gemv_multi, [p1] * 5, a, [y] * 5, None, 0, 0) == INVALID
+    assert status_of(mnb.mnb_gemv_multi, [p1, p1], a, [y, None], None, 0, 0) == INVALID
+    assert status_of(mnb.mnb_gemv_multi, [p1, p2], a, [y, y], None, 0, 0) == INVALID
+    assert status_of(mnb.mnb_gemv_multi, [p1, p2], None, [y, y], None, 0, 0) == INVALID

@@ -188,6 +188,51 @@ def test_gemv_non_finite_activation_poisons_output():
     assert np.isnan(run_gemv(w, a)).all()
 
 
+# mnb_gemv_multi: several plans times one A.  Fusable sets (same K, block
+# size and zero-point kind, short row streams) run in one launch; the others
+# one after another.  Either way every output equals its own mnb_gemv call
+# bit for bit, and each is within the GEMV bar of the oracle.
+@pytest.mark.parametrize("K,Ns,bs,zp", [
+    (2048, (6144, 6144), 32, False), (2050, (1024, 37, 300), 32, True),
+    (6144, (2048, 100), 64, False), (4096, (7, 513, 64, 2000), 128, True),
+    (256, (40000, 33), 32, False)])
+def test_gemv_multi_matches_separate_calls(orc, K, Ns, bs, zp):
+    say(f"gemv multi K={K} Ns={Ns} bs={bs} zp={zp}")
+    ws_, hosts = [], []
+    for i, N in enumerate(Ns):
+        w, B, s, Z = prepare(K, N, bs, zp, seed=K + 17 * i)
+        ws_.append(w)
+        hosts.append((B, s, Z))
+    a = synth.activations_f32(synth.seed_for(K, len(Ns)), 1, K)
+    A = torch.from_numpy(a.reshape(-1)).cuda()
+    guard = 64
+    Ygs = [torch.full((N + 2 * guard,), float("nan"), dtype=torch.float32, device="cuda") for N in Ns]
+    need = max(mnb.mnb_gemv_workspace_size(w.plan) for w in ws_) + 256
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    mnb.mnb_gemv_multi([w.plan for w in ws_], A, [Yg[guard:guard + N] for Yg, N in zip(Ygs, Ns)],
+                       ws, ws.numel())
+    torch.cuda.synchronize()
+    for w, Yg, N, (B, s, Z) in zip(ws_, Ygs, Ns, hosts):
+        g = Yg.cpu().numpy()
+        assert np.isnan(g[:guard]).all() and np.isnan(g[guard + N:]).all(), "guard band written"
+        y = g[guard:guard + N]
+        assert np.array_equal(y.view(np.uint32), run_gemv(w, a).view(np.uint32))
+        rows = None if N <= 4096 else np.unique(np.linspace(0, N - 1, 97).astype(int))
+        check(orc, y, a, B, s, Z, K, N, bs, rows)
+
+
+def test_gemv_multi_rejects_mixed_k():
+    say("gemv multi mixed K")
+    w1, *_ = prepare(64, 16, seed=3)
+    w2, *_ = prepare(96, 16, seed=4)
+    A = torch.zeros(96, device="cuda")
+    Y = [torch.empty(16, device="cuda") for _ in range(2)]
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(mnb.MnbError) as e:
+        mnb.mnb_gemv_multi([w1.plan, w2.plan], A, Y, ws, ws.numel())
+    assert e.value.status == -1
+
+
 def test_debug_unpack_and_dequant_bit_exact(orc):
     say("debug unpack / dequant")
     for K, N, bs, zp in ((2050, 37, 32, True), (256, 9, 128, False)):
