@@ -461,18 +461,20 @@ void split_k(Plan& p, const Sizes& s, int64_t M, int64_t step) {
   p.kc = steps_per * step;
 }
 
-// rows of A from which the LDS-streaming kernel is used, with 128 x 128
-// tiles, and from which with 256 x 256 tiles
-constexpr int64_t kLdsSmallMinM = 128;
-constexpr int64_t kLdsMinM = 1024;
+// rows of A from which the LDS-streaming kernel is used; it takes 128 x 128
+// tiles while they number at most kLds128MaxTiles (one and a half rounds of
+// two workgroups per CU: measured faster than 256 x 256 tiles up to there),
+// else 256 x 256 tiles
+constexpr int64_t kLdsMinM = 128;
+constexpr int64_t kLds128MaxTiles = 384;
 
 Plan choose(const Sizes& s, int64_t M, bool fast) {
   const int64_t N = s.N, K = s.K;
   (void)K;
-  if (fast && M >= kLdsSmallMinM && gemm_lds_supported(s, M)) {
+  if (fast && M >= kLdsMinM && gemm_lds_supported(s, M)) {
     Plan p;
     p.lds = true;
-    p.bm = M >= kLdsMinM ? 256 : 128;
+    p.bm = ((M + 127) / 128) * ((N + 127) / 128) <= kLds128MaxTiles ? 128 : 256;
     p.cfg = -1;
     p.tiles_n = (N + p.bm - 1) / p.bm;
     p.tiles = ((M + p.bm - 1) / p.bm) * p.tiles_n;

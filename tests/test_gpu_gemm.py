@@ -119,7 +119,7 @@ def test_gemm_deterministic():
 def test_gemm_rows_are_independent(M, lo, hi):
     """Row m of the output depends only on row m of A (no cross-row mixing in
     the tiling): a sub-batch that takes the same kernel (the register-staged
-    one below 128 rows, the 128 x 128 LDS-streaming one from 128 to 1023)
+    one below 128 rows, here the 128 x 128 LDS-streaming one above)
     gives the same bits.  Different kernels sum K in different orders."""
     say(f"gemm row independence M={M}")
     K, N = 512, 384
@@ -131,11 +131,14 @@ def test_gemm_rows_are_independent(M, lo, hi):
 
 
 # M >= 128 with K a multiple of 64 takes the LDS-streaming kernel (128 x 128
-# tiles below M = 1024, 256 x 256 from there): ragged M and N tails, one-stage
-# K, every block size, zero points, split K.
+# tiles while there are at most 384 of them, else 256 x 256): ragged M and N
+# tails, one-stage K, every block size, zero points, split K, on both tile
+# sizes (the last three cases have more than 384 tiles of 128 x 128).
 @pytest.mark.parametrize("M,K,N,bs,zp", [
     (1100, 320, 700, 64, True), (1025, 64, 33, 32, False), (1030, 384, 257, 128, True),
-    (1300, 192, 1000, 32, False), (1040, 4096, 300, 128, True), (600, 320, 700, 64, True)])
+    (1300, 192, 1000, 32, False), (1040, 4096, 300, 128, True), (600, 320, 700, 64, True),
+    (2048, 4096, 130, 128, False), (2100, 64, 3000, 32, True), (2600, 128, 2500, 64, False),
+    (4100, 320, 1600, 128, True)])
 def test_gemm_large_m_ragged_elementwise(orc, M, K, N, bs, zp):
     say(f"gemm large-M M={M} K={K} N={N} bs={bs} zp={zp}")
     w, B, s, Z = prepare(K, N, bs, zp, seed=M * 7 + K + N)
@@ -146,9 +149,9 @@ def test_gemm_large_m_ragged_elementwise(orc, M, K, N, bs, zp):
 
 def test_gemm_large_m_rows_are_independent():
     say("gemm large-M row independence")
-    M, K, N = 1500, 512, 2048
+    M, K, N = 4500, 512, 4096  # 256 x 256 tiles for the batch and the sub-batch
     w, *_ = prepare(K, N, seed=29)
     a = synth.activations_f32(30, M, K)
     y = run_gemm(w, a)
-    y_sub = run_gemm(w, a[100:1300])
-    assert np.array_equal(y[100:1300], y_sub)
+    y_sub = run_gemm(w, a[100:2300])
+    assert np.array_equal(y[100:2300], y_sub)
