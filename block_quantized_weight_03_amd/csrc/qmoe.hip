@@ -426,17 +426,26 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
     uint32_t rs;
     bool ok;
   };
+  // Tile-major offsets (N % 16 == 0, so every 16-row tile is full): group G =
+  // 4c + wg of row 16 rt + wn sits at rt (ng 192) + 768 c + 48 wn + 12 wg in a
+  // full chunk and at rt (ng 192) + 768 c + gl (12 wn) + 12 wg in a last chunk
+  // of gl < 4 groups; the wave's row tile is uniform, so only the lane term is
+  // per lane.  Groups past K use the chunk's last group (scale 0).
+  const int ng = Kc >> 5, nfull = ng >> 2, gl = ng - 4 * nfull;
+  const uint32_t lane_full = 48u * wn + 12u * wg;
+  const uint32_t lane_last = gl ? 12u * (uint32_t)(gl * wn + (wg < gl ? wg : gl - 1)) : lane_full;
   auto load_w = [&](WStage& st, int t, int c) {
     c = c < nch ? c : nch - 1;
     t = t < ntc ? t : ntc - 1;
-    const int row = (nt0 + t) * kQBN + wave * 16 + wn;
-    const bool rok = row < Nc;
-    const int kg = c * kQBK + 32 * wg;  // first code of this lane's group
-    st.ok = rok && kg < Kc;
-    const int rowc = rok ? row : 0;
-    const int G = kg < Kc ? (kg >> 5) : 0;
-    st.rw = *reinterpret_cast<const u32x3*>(wbase + int3_goff(Nc, Kc, rowc, G));
-    st.rs = sbase[(int64_t)rowc * g.nblk + ((uint32_t)(G * 32) >> bshift)];
+    const int rt = (nt0 + t) * (kQBN / 16) + wave;  // the wave's row tile
+    const bool rok = 16 * rt < Nc;                     // uniform
+    const int G = 4 * c + wg;
+    st.ok = rok && G < ng;
+    const uint32_t off = (uint32_t)(rok ? rt : 0) * (uint32_t)(ng * 192) + 768u * (uint32_t)c +
+                         (c < nfull ? lane_full : lane_last);
+    st.rw = *reinterpret_cast<const u32x3*>(wbase + off);
+    const int rowc = rok ? 16 * rt + wn : wn;
+    st.rs = sbase[rowc * (int)g.nblk + ((32 * (G < ng ? G : ng - 1)) >> bshift)];
   };
   // (a_src already includes this thread's column a_c)
   u32x4 ra[AP];
