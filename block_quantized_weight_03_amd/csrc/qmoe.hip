@@ -176,7 +176,7 @@ __global__ void __launch_bounds__(kGroupThreads) qmoe_group(const int32_t* __res
   int32_t* cnt = gsm;              // [E]
   int32_t* off = cnt + E;          // [E] exclusive offsets (scanned in place)
   int32_t* ioff = off + E;         // [E] exclusive item offsets
-  int32_t* tmp = ioff + E;         // [2 E] scan double buffer
+  int32_t* tmp = ioff + E;         // [2 E] exclusive offsets (first E)
   int32_t* hist = tmp + 2 * E;     // [kWaves][E]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t S = T * k;
@@ -193,24 +193,44 @@ __global__ void __launch_bounds__(kGroupThreads) qmoe_group(const int32_t* __res
   }
   __syncthreads();
 
-  // inclusive Hillis-Steele scans of counts and of items per expert
-  for (int e = tid; e < E; e += kGroupThreads) {
-    off[e] = cnt[e];
-    ioff[e] = (cnt[e] + bm - 1) / bm;
+  // inclusive scans of counts and of items per expert, by wave 0: lane l
+  // sums experts [P l, P l + P) in order, the lane totals are scanned with
+  // DPP row shifts and row broadcasts (no LDS round trips, one barrier)
+  if (wave == 0) {
+    const int P = (E + 63) >> 6;  // <= kMaxE / 64
+    int32_t sc = 0, si = 0;
+    for (int j = 0; j < P; ++j) {
+      const int e = P * lane + j;
+      if (e < E) {
+        sc += cnt[e];
+        si += (cnt[e] + bm - 1) / bm;
+      }
+    }
+    int32_t ic = sc, ii = si;  // inclusive over lanes
+    ic += __builtin_amdgcn_update_dpp(0, ic, 0x111, 0xF, 0xF, true);  // row_shr:1
+    ii += __builtin_amdgcn_update_dpp(0, ii, 0x111, 0xF, 0xF, true);
+    ic += __builtin_amdgcn_update_dpp(0, ic, 0x112, 0xF, 0xF, true);  // row_shr:2
+    ii += __builtin_amdgcn_update_dpp(0, ii, 0x112, 0xF, 0xF, true);
+    ic += __builtin_amdgcn_update_dpp(0, ic, 0x114, 0xF, 0xF, true);  // row_shr:4
+    ii += __builtin_amdgcn_update_dpp(0, ii, 0x114, 0xF, 0xF, true);
+    ic += __builtin_amdgcn_update_dpp(0, ic, 0x118, 0xF, 0xF, true);  // row_shr:8
+    ii += __builtin_amdgcn_update_dpp(0, ii, 0x118, 0xF, 0xF, true);
+    ic += __builtin_amdgcn_update_dpp(0, ic, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    ii += __builtin_amdgcn_update_dpp(0, ii, 0x142, 0xA, 0xF, false);
+    ic += __builtin_amdgcn_update_dpp(0, ic, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    ii += __builtin_amdgcn_update_dpp(0, ii, 0x143, 0xC, 0xF, false);
+    int32_t rc = ic - sc, ri = ii - si;  // exclusive: totals of the earlier lanes
+    for (int j = 0; j < P; ++j) {
+      const int e = P * lane + j;
+      if (e < E) {
+        rc += cnt[e];
+        ri += (cnt[e] + bm - 1) / bm;
+        off[e] = rc;
+        ioff[e] = ri;
+      }
+    }
   }
   __syncthreads();
-  for (int d = 1; d < E; d <<= 1) {
-    for (int e = tid; e < E; e += kGroupThreads) {
-      tmp[e] = off[e] + (e >= d ? off[e - d] : 0);
-      tmp[E + e] = ioff[e] + (e >= d ? ioff[e - d] : 0);
-    }
-    __syncthreads();
-    for (int e = tid; e < E; e += kGroupThreads) {
-      off[e] = tmp[e];
-      ioff[e] = tmp[E + e];
-    }
-    __syncthreads();
-  }
   // to exclusive, outputs, work items
   for (int e = tid; e < E; e += kGroupThreads) {
     const int32_t c = cnt[e];

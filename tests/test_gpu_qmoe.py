@@ -146,7 +146,8 @@ def test_tiny_predetermined_route_moe():
 
 @pytest.mark.parametrize("T,H,I,E,k,bs", [(5, 64, 64, 4, 2, 64), (3, 128, 64, 8, 3, 32),
                                           (17, 256, 128, 16, 4, 128), (33, 128, 96, 6, 6, 32),
-                                          (1, 64, 32, 3, 3, 32), (64, 192, 160, 12, 8, 32)])
+                                          (1, 64, 32, 3, 3, 32), (64, 192, 160, 12, 8, 32),
+                                          (40, 64, 32, 300, 8, 32)])
 def test_qmoe_small_shapes_all_outputs(orc, T, H, I, E, k, bs):
     say(f"qmoe small T={T} H={H} I={I} E={E} k={k} bs={bs}")
     x, logits, m = random_moe(T * 7 + E, T, H, I, E, k, bs)
