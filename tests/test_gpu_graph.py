@@ -76,9 +76,36 @@ def test_graph_gemv_and_gemm():
         torch.cuda.synchronize()
 
 
-def test_graph_qmoe():
-    say("graph qmoe")
-    T, H, I, E, k, bs = 48, 256, 128, 16, 4, 64
+def test_graph_gemv_multi():
+    say("graph gemv multi")
+    K = 2048
+    ws_ = [mnb.PreparedWeight(mnb.dense_desc(K, N), synth.int4_blocked_weights(10 + i, N, K, 32),
+                              synth.scales_f32(20 + i, (N, K // 32))) for i, N in enumerate((700, 1300))]
+    a = torch.from_numpy(synth.activations_f32(30, 1, K)[0]).cuda()
+    ys = [torch.empty(w.desc.N, device="cuda") for w in ws_]
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+
+    def run():
+        mnb.mnb_gemv_multi([w.plan for w in ws_], a, ys, ws, 256)
+
+    run()
+    torch.cuda.synchronize()
+    refs = [y.clone() for y in ys]
+    g = capture(run)
+    for _ in range(4):
+        for y in ys:
+            y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(y, r) for y, r in zip(ys, refs))
+        (a * 2).sum().item()
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T", [48, 2, 7])  # grouped path; decode with fused routing; decode
+def test_graph_qmoe(T):
+    say(f"graph qmoe T={T}")
+    H, I, E, k, bs = 256, 128, 16, 4, 64
     W1 = synth.int3_rows(1, E * 2 * I, H)
     s1 = synth.scales_f16(2, (E * 2 * I, H // bs))
     W2 = synth.int3_rows(3, E * H, I)
