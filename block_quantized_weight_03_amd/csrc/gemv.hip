@@ -409,16 +409,6 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 constexpr int kTeams = 4;  // row groups (teams of waves) per workgroup of the fp32 path
 constexpr int kNPT = 8 / kTeams;  // 16-byte pieces of A per thread
 
-// One-shot: every wave takes R consecutive rows of one K chunk, with 32-bit
-// index math throughout (the launcher checks that the codes of the matrix
-// span less than 2^31 bytes).  Inactive lanes and rows past N read through
-// an out-of-range buffer offset and so contribute exact zeros.  The
-// workgroup stages A once in LDS (each teams' waves read it from there, so
-// global A traffic is one copy per workgroup instead of one per wave):
-// 16-byte chunk j of sub-block i sits at chunk j ^ ((i >> 1) & 7) of the
-// sub-block's 128 bytes, so the 16 lanes served per LDS cycle hit 64
-// distinct banks.  The A loads are issued before the weight loads; loads
-// complete in order, so waiting for A does not wait for the weights.
 // Up to kMaxSegs weight matrices with the same K, block size and zero-point
 // kind, multiplied by the same A in one launch: segment i owns workgroups
 // [first[i], first[i + 1]).
@@ -432,6 +422,16 @@ struct GemvSegs {
   int32_t count;
 };
 
+// One-shot: every wave takes R consecutive rows of one K chunk, with 32-bit
+// index math throughout (the launcher checks that the codes of the matrix
+// span less than 2^31 bytes).  Inactive lanes and rows past N read through
+// an out-of-range buffer offset and so contribute exact zeros.  The
+// workgroup stages A once in LDS (every team's waves read it from there, so
+// global A traffic is one copy per workgroup instead of one per wave):
+// 16-byte chunk j of sub-block i sits at chunk j ^ ((i >> 1) & 7) of the
+// sub-block's 128 bytes, so the 16 lanes served per LDS cycle hit 64
+// distinct banks.  The A loads are issued before the weight loads; loads
+// complete in order, so waiting for A does not wait for the weights.
 template <int R, bool HAS_ZP>
 __global__ void __launch_bounds__(1024) gemv_int4_f32(
     const float* __restrict__ A, const GemvSegs sg, int32_t K, int32_t row_bytes, int32_t nb,
