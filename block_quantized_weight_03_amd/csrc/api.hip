@@ -263,6 +263,10 @@ static int32_t qmoe_common(const mnb_plan* fc1, const mnb_plan* fc2, const qmoe_
       th > (uint64_t)INT64_MAX / 64)
     return MNB_ERR_SIZE_OVERFLOW;
   if (!x || !logits || !out) return MNB_ERR_INVALID_ARG;
+  // the kernels move x rows in 16-byte and outputs in 8-byte pieces
+  if ((reinterpret_cast<uintptr_t>(x) & 15) || (reinterpret_cast<uintptr_t>(out) & 7) ||
+      (reinterpret_cast<uintptr_t>(logits) & 3))
+    return MNB_ERR_INVALID_ARG;
   if ((rc = check_ws(ws, ws_bytes, qmoe_ws_bytes(s1, s2, q->top_k, T))) != MNB_OK) return rc;
   if ((rc = check_device(fc1)) != MNB_OK) return rc;
   if ((rc = check_device(fc2)) != MNB_OK) return rc;

@@ -808,12 +808,18 @@ __global__ void __launch_bounds__(1024) qmoe_fc2_decode(MoeGemmArgs g, int64_t T
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) qmoe_combine(const float* __restrict__ slots, int64_t T,
                                                     int k, int64_t H, __half* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= T * H) return;
+  // four consecutive outputs per thread (H % 32 == 0): 16-byte slot loads
+  const int64_t i4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i4 >= T * H / 4) return;
+  const int64_t i = 4 * i4;
   const int64_t t = i / H, n = i % H;
-  float acc = 0.0f;
-  for (int j = 0; j < k; ++j) acc += slots[(t * k + j) * H + n];
-  out[i] = __float2half_rn(acc);
+  f32x4 acc = f32x4{0, 0, 0, 0};
+  for (int j = 0; j < k; ++j) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(slots + (t * k + j) * H + n);
+    acc = f32x4{acc.x + v.x, acc.y + v.y, acc.z + v.z, acc.w + v.w};
+  }
+  const half2t lo = half2t{(_Float16)acc.x, (_Float16)acc.y}, hi = half2t{(_Float16)acc.z, (_Float16)acc.w};
+  *reinterpret_cast<u32x2*>(out + i) = u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
 // debug: h rows back in slot order
@@ -962,7 +968,7 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
       hipLaunchKernelGGL((qmoe_gemm<false, 32>), dim3((unsigned)((items + 7) / 8 * 8 * ng2)), dim3(256), 0, st, a2, ng2, nt2);
     else
       hipLaunchKernelGGL((qmoe_gemm<false, kMaxBM>), dim3((unsigned)((items + 7) / 8 * 8 * ng2)), dim3(256), 0, st, a2, ng2, nt2);
-    hipLaunchKernelGGL(qmoe_combine, dim3((unsigned)((Tt * H + 255) / 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL(qmoe_combine, dim3((unsigned)((Tt * H / 4 + 255) / 256)), dim3(256), 0, st,
                        slots, Tt, k, H, reinterpret_cast<__half*>(out + t0 * H));
     if (dbg) {
       if (dbg->ids)

@@ -224,9 +224,9 @@ int32_t qmoe_workspace_size(const mnb_plan* fc1, const mnb_plan* fc2,
  *  fc1: QMoE plan with N = 2I, K = H (rows 2i = gate_i, 2i+1 = up_i);
  *  fc2: QMoE plan with N = H, K = I; both with the same num_experts E and
  *       block size.
- *  x_dev      fp16 [T, H] activations;
+ *  x_dev      fp16 [T, H] activations, 16-byte aligned;
  *  logits_dev fp32 [T, E] router logits;
- *  out_dev    fp16 [T, H].
+ *  out_dev    fp16 [T, H], 8-byte aligned (misaligned x or out: INVALID_ARG).
  * Computes, per token: top_k experts by logit (ties: lower index), weights
  * r_j = softmax over the selected logits (= fp32 softmax over all E then
  * renormalization); h = silu(x.W1g^T) * (x.W1u^T) rounded to fp16;

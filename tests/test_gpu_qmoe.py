@@ -243,3 +243,24 @@ def test_qmoe_routing_nan_logits_rank_last():
     res = m.run(x, logits, debug=True)
     assert not np.isin(res["ids"][0], [1, 5, 9]).any()
     assert ((res["ids"] >= 0) & (res["ids"] < E)).all()
+
+
+def test_qmoe_pointer_alignment():
+    """x must be 16-byte and out 8-byte aligned (the kernels move them in
+    16- and 8-byte pieces): misaligned pointers are rejected before any
+    launch; an output at an 8-byte (not 16-byte) offset works."""
+    say("qmoe pointer alignment")
+    T, H, I, E, k, bs = 40, 64, 32, 8, 2, 32
+    x, logits, m = random_moe(123, T, H, I, E, k, bs)
+    ref = m.run(x, logits)["out"]
+    assert np.array_equal(m.run(x, logits, guard=4)["out"].view(np.uint16), ref.view(np.uint16))
+    xb = torch.empty(T * H + 8, dtype=torch.float16, device="cuda")
+    xb[1:1 + T * H] = torch.from_numpy(x.reshape(-1)).cuda()
+    ld = torch.from_numpy(logits).cuda()
+    ob = torch.empty(T * H + 8, dtype=torch.float16, device="cuda")
+    ws = torch.empty(mnb.qmoe_workspace_size(m.p1.plan, m.p2.plan, m.q, T), dtype=torch.uint8,
+                     device="cuda")
+    for xs, os_ in ((xb[1:1 + T * H], ob[:T * H]), (xb[8:8 + T * H], ob[2:2 + T * H])):
+        with pytest.raises(mnb.MnbError) as e:
+            mnb.qmoe_forward(m.p1.plan, m.p2.plan, m.q, T, xs, ld, os_, ws, ws.numel())
+        assert e.value.status == -1
