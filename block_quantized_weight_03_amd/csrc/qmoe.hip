@@ -654,6 +654,41 @@ struct TileBatch {
   }
 };
 
+// Eight-row tiles, two K chunks per wave load: lane (n, g, h) = (lane & 7,
+// (lane >> 3) & 3, lane >> 5) takes group 4c + g of row n for the chunks
+// c = c0 + 2u + h (used where 16-row tiles would leave CUs idle).  Chunks or
+// groups past K are skipped per lane.
+struct HalfBatch {
+  static constexpr int kU = kDecBatch / 2;
+  u32x3 w[kU];
+  uint16_t s[kU];
+  int G[kU];
+  uint32_t ok;  // bit u: chunk and group inside K
+
+  __device__ __forceinline__ void load(const TileRef& t, int c0, int h) {
+    ok = 0;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int c = c0 + 2 * u + h;
+      const int Gr = 4 * c + t.g;
+      const bool v = c < t.nch && Gr < t.ng;
+      ok |= (v ? 1u : 0u) << u;
+      G[u] = v ? Gr : t.ng - 1;
+      w[u] = *reinterpret_cast<const u32x3*>(t.codes + int3_goff(t.N, t.K, t.row, G[u]));
+      s[u] = t.scales[t.row * t.nblk + ((32 * G[u]) >> t.bshift)];
+    }
+  }
+  __device__ __forceinline__ float dot(const _Float16* xs, uint32_t magic) const {
+    float acc = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if ((ok >> u) & 1u)
+        acc += group_dot_unscaled(w[u], (float)__builtin_bit_cast(_Float16, s[u]), magic,
+                                  reinterpret_cast<const u32x4*>(xs + 32 * G[u]));
+    return acc;
+  }
+};
+
 // Stages n 16-byte pieces of src into LDS dst with nt threads: the first two
 // pieces per thread are loaded by stage_first (before the caller issues its
 // weight loads: loads complete in order, so waiting for these does not wait
@@ -756,45 +791,47 @@ __global__ void __launch_bounds__(256) qmoe_fc1_decode(MoeGemmArgs g, int64_t T,
   }
 }
 
-// FC2 + combine: a workgroup per (token t, 16-row tile) with one wave per rank
+// FC2 + combine: a workgroup per (token t, 8-row half tile) with one wave per rank
 // j; the token's k rows of h are staged in LDS; wave j forms the partials of
 // expert ids[t, j]'s tile rows, then out[t, n] = fp16(sum_j r_j y_j[n]) with
 // y_j and the rank sum in fixed orders.
 __global__ void __launch_bounds__(1024) qmoe_fc2_decode(MoeGemmArgs g, int64_t T, __half* out,
                                                         float* slot_dbg) {
   extern __shared__ __align__(16) uint8_t sm[];
-  const int H = (int)g.N, I = (int)g.K, k = g.top_k, ntile = H >> 4;
+  const int H = (int)g.N, I = (int)g.K, k = g.top_k, ntile = H >> 3;  // 8-row tiles
   _Float16* hs = reinterpret_cast<_Float16*>(sm);
   float* red = reinterpret_cast<float*>(sm + 2 * k * I);  // I % 32 == 0: 16-byte aligned
   const int tid = threadIdx.x, lane = tid & 63;
   const int j = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t = (int)blockIdx.x / ntile, tile = (int)blockIdx.x % ntile;
   const int e = clamp_id(g.perm[t * k + j], g.E);  // perm holds the routed ids here
-  const TileRef tr = tile_ref(g, e, 16 * tile, lane);
+  TileRef tr = tile_ref(g, e, 8 * tile, lane & 7);
+  tr.g = (lane >> 3) & 3;
+  const int hsel = lane >> 5;
   const u32x4* hr = reinterpret_cast<const u32x4*>(static_cast<const _Float16*>(g.act) + (int64_t)t * k * I);
   Stage2 hst;
   hst.first(hr, k * I / 8, tid, 64 * k);
   __builtin_amdgcn_sched_barrier(0);
-  TileBatch b;
-  b.load(tr, 0, 1);
+  HalfBatch b;
+  b.load(tr, 0, hsel);
   __builtin_amdgcn_sched_barrier(0);
   hst.rest(hr, reinterpret_cast<u32x4*>(hs), k * I / 8, tid, 64 * k);
   __syncthreads();
   const uint32_t magic = opaque_magic();
   const _Float16* hj = hs + j * I;
   float acc = b.dot(hj, magic);
-  for (int c = kDecBatch; c < tr.nch; c += kDecBatch) {
-    b.load(tr, c, 1);
+  for (int c = 2 * HalfBatch::kU; c < tr.nch; c += 2 * HalfBatch::kU) {
+    b.load(tr, c, hsel);
     acc += b.dot(hj, magic);
   }
   red[j * 64 + lane] = acc;
   __syncthreads();
-  if (tid < 16) {
-    const int n = 16 * tile + tid;
+  if (tid < 8) {
+    const int n = 8 * tile + tid;
     float o = 0.0f;
     for (int r = 0; r < k; ++r) {
       float y = 0.0f;
-      for (int q = 0; q < 4; ++q) y += red[r * 64 + q * 16 + tid];
+      for (int q = 0; q < 8; ++q) y += red[r * 64 + q * 8 + tid];
       const float ry = g.wts[t * k + r] * y;
       if (slot_dbg) slot_dbg[((int64_t)t * k + r) * H + n] = ry;
       o += ry;
@@ -932,7 +969,7 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
     MoeGemmArgs a2{static_cast<const uint8_t*>(p2.codes), static_cast<const __half*>(p2.scales),
                    hbuf, s2.N, s2.K, s2.row_bytes, s2.nb, s2.bs, k, (int)E,
                    nullptr, nullptr, ids, nullptr, nullptr, wts, nullptr, nullptr};
-    hipLaunchKernelGGL(qmoe_fc2_decode, dim3((unsigned)(T * (H / 16))), dim3(64 * k),
+    hipLaunchKernelGGL(qmoe_fc2_decode, dim3((unsigned)(T * (H / 8))), dim3(64 * k),
                        (size_t)(2 * k * I + 4 * 64 * k), st, a2, T,
                        reinterpret_cast<__half*>(out), dbg ? dbg->slot : nullptr);
     if (dbg) {
