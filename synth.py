@@ -109,18 +109,22 @@ def int4_zero_points(seed: int, N: int, nb: int) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
-# INT3 QMoE inputs.
+# QMoE inputs (INT3 or INT4 row-local projections, fp16 scales).
 # ----------------------------------------------------------------------------
 
-def int3_rows(seed: int, rows: int, K: int) -> np.ndarray:
-    """uint8 [rows, ceil(3K/8)] of a uniform bit stream per row with the pad
-    bits beyond 3K cleared (canonical padding)."""
-    rb = (3 * K + 7) // 8
+def packed_rows(seed: int, rows: int, K: int, bits: int) -> np.ndarray:
+    """uint8 [rows, ceil(bits*K/8)] of a uniform bit stream per row with the
+    pad bits beyond bits*K cleared (canonical padding)."""
+    rb = (bits * K + 7) // 8
     W = random_bytes(seed, rows * rb).reshape(rows, rb)
-    used = (3 * K) % 8
+    used = (bits * K) % 8
     if used:
         W[:, rb - 1] &= np.uint8((1 << used) - 1)
     return W
+
+
+def int3_rows(seed: int, rows: int, K: int) -> np.ndarray:
+    return packed_rows(seed, rows, K, 3)
 
 
 def scales_f16(seed: int, shape, lo: float = 0.005, hi: float = 0.02) -> np.ndarray:

@@ -47,13 +47,18 @@ def dense_gemm(A, B, scales, zp, K: int, bs: int):
     return A64 @ W.T, np.abs(A64) @ np.abs(W).T
 
 
-def int3_weights(W: np.ndarray, s16: np.ndarray, K: int, bs: int) -> np.ndarray:
-    """W uint8 [..., rows, rb] (row-local 3-bit), s16 float16 [..., rows, K/bs]."""
+def moe_weights(W: np.ndarray, s16: np.ndarray, K: int, bs: int, bits: int = 3) -> np.ndarray:
+    """W uint8 [..., rows, rb] (row-local LSB-first codes of the given width),
+    s16 float16 [..., rows, K/bs]; implicit zero point 2**(bits-1)."""
     lead = W.shape[:-1]
     flat = W.reshape(-1, W.shape[-1])
-    q = np.stack([unpack_le(r, K, 3) for r in flat]).reshape(*lead, K)
+    q = np.stack([unpack_le(r, K, bits) for r in flat]).reshape(*lead, K)
     s = np.repeat(s16.astype(np.float64), bs, axis=-1)
-    return (q - 4).astype(np.float64) * s
+    return (q - (1 << (bits - 1))).astype(np.float64) * s
+
+
+def int3_weights(W: np.ndarray, s16: np.ndarray, K: int, bs: int) -> np.ndarray:
+    return moe_weights(W, s16, K, bs, 3)
 
 
 def softmax(v):
@@ -62,14 +67,14 @@ def softmax(v):
     return e / e.sum(axis=-1, keepdims=True)
 
 
-def qmoe_all_experts(x16, logits, W1, s1, W2, s2, k: int, bs: int):
+def qmoe_all_experts(x16, logits, W1, s1, W2, s2, k: int, bs: int, bits1: int = 3, bits2: int = 3):
     """Every expert evaluated for every token, then a k-hot mask of the
     renormalized top-k probabilities selects the mixture."""
     T, H = x16.shape
     E, twoI, _ = W1.shape
     I = twoI // 2
-    w1 = int3_weights(W1, s1, H, bs)          # [E, 2I, H]
-    w2 = int3_weights(W2, s2, I, bs)          # [E, H, I]
+    w1 = moe_weights(W1, s1, H, bs, bits1)    # [E, 2I, H]
+    w2 = moe_weights(W2, s2, I, bs, bits2)    # [E, H, I]
     x = x16.astype(np.float64)
     p = softmax(logits.astype(np.float64))    # [T, E]
     order = np.argsort(-logits, axis=1, kind="stable")[:, :k]

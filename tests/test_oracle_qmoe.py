@@ -146,3 +146,74 @@ def test_qmoe_tolerance_sum_covers_fp16_rounding_chain(orc):
     err = np.abs(out16 - o["out64"])
     assert (err <= 4e-3 * o["S"] + 0.5 * ulp + ulp).all()
     assert (o["S"] > 0).all()
+
+
+# ---------------------------------------------------------------------------
+# INT4 and mixed-width projections.  The P1 section of the INT3 QMoE page lets
+# each projection carry its own width, (FC1, FC2) in {(3,3), (3,4), (4,3)};
+# the same page's results table runs the all-INT4 (4,4) layer next to (3,3).
+# A 4-bit row-local LSB-first row puts even positions in the low nibble, and
+# the implicit zero point is 2^(bits - 1) = 8.
+# ---------------------------------------------------------------------------
+
+def _random_moe_bits(seed, T, H, I, E, bs, bits1, bits2):
+    x = synth.activations_f16(seed, T, H)
+    logits = synth.router_logits(seed + 1, T, E)
+    W1 = synth.packed_rows(seed + 2, E * 2 * I, H, bits1).reshape(E, 2 * I, -1)
+    s1 = synth.scales_f16(seed + 3, (E, 2 * I, H // bs))
+    W2 = synth.packed_rows(seed + 4, E * H, I, bits2).reshape(E, H, -1)
+    s2 = synth.scales_f16(seed + 5, (E, H, I // bs))
+    return x, logits, W1, s1, W2, s2
+
+
+@pytest.mark.parametrize("bits1,bits2,T,H,I,E,k,bs", [(4, 4, 5, 64, 64, 4, 2, 64),
+                                                      (4, 4, 3, 128, 64, 8, 3, 32),
+                                                      (3, 4, 4, 64, 128, 6, 2, 64),
+                                                      (4, 3, 2, 128, 128, 5, 1, 128)])
+def test_qmoe_mixed_width_brute_force(orc, bits1, bits2, T, H, I, E, k, bs):
+    x, logits, W1, s1, W2, s2 = _random_moe_bits(T * 31 + E, T, H, I, E, bs, bits1, bits2)
+    o = orc.qmoe(x, logits, W1, s1, W2, s2, k=k, bits1=bits1, bits2=bits2, bs=bs)
+    ref, order, rw = qmoe_all_experts(x, logits, W1, s1, W2, s2, k, bs, bits1, bits2)
+    assert np.array_equal(o["ids"], order)
+    scale = np.abs(ref).max() + 1e-300
+    np.testing.assert_allclose(o["out64"], ref, rtol=1e-10, atol=1e-12 * scale)
+    if bits2 == 4:
+        # reading the 4-bit FC2 rows as 3-bit streams changes the result
+        wrong = qmoe_all_experts(x, logits, W1, s1, W2, s2, k, bs, bits1, 3)[0]
+        assert np.abs(wrong - ref).max() > 1e-3 * scale
+
+
+def test_qmoe_int4_rows_are_low_nibble_first_dense_blocks(orc):
+    """A 4-bit row-local row with block-aligned K is byte for byte a dense
+    MatMulNBits row [nb, bs/2] (low nibble = even position, zero point 8), so
+    the stage values of one expert must equal products with the dense nibble
+    decode of the same bytes."""
+    from tests.np_brute import dense_weights
+    T, H, I, E, k, bs = 3, 128, 64, 1, 1, 32
+    x, logits, W1, s1, W2, s2 = _random_moe_bits(77, T, H, I, E, bs, 4, 4)
+    o = orc.qmoe(x, logits, W1, s1, W2, s2, k=k, bits1=4, bits2=4, bs=bs)
+    w1 = dense_weights(W1[0].reshape(2 * I, H // bs, bs // 2), s1[0].astype(np.float32), None, H, bs)
+    w2 = dense_weights(W2[0].reshape(H, I // bs, bs // 2), s2[0].astype(np.float32), None, I, bs)
+    xx = x.astype(np.float64)
+    G, U = xx @ w1[0::2].T, xx @ w1[1::2].T
+    np.testing.assert_allclose(o["g"][:, 0], G, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(o["u"][:, 0], U, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(o["r"], np.ones((T, 1)))
+    Y = (G / (1 + np.exp(-G)) * U) @ w2.T
+    np.testing.assert_allclose(o["out64"], Y, rtol=1e-11, atol=1e-12 * np.abs(Y).max())
+
+
+def test_qmoe_int4_codes_at_zero_point_give_zero(orc):
+    T, H, I, E, k, bs = 4, 64, 64, 4, 2, 64
+    x, logits, W1, s1, W2, s2 = _random_moe_bits(313, T, H, I, E, bs, 4, 4)
+    z1 = np.full_like(W1, 0x88)
+    z2 = np.full_like(W2, 0x88)
+    o = orc.qmoe(x, logits, z1, s1, z2, s2, k=k, bits1=4, bits2=4, bs=bs)
+    assert (o["out64"] == 0).all() and (o["S"] == 0).all() and (o["g"] == 0).all()
+    # codes 8 + 1 in FC1 and the x = 1 row: g = u = sum of the scales
+    o = orc.qmoe(np.ones((1, H), np.float16), logits[:1], np.full_like(W1, 0x99), s1,
+                 W2, s2, k=k, bits1=4, bits2=4, bs=bs)
+    for j in range(k):
+        e = o["ids"][0, j]
+        np.testing.assert_allclose(o["g"][0, j], s1[e, 0::2].astype(np.float64).sum(axis=1) * bs,
+                                   rtol=1e-14)
