@@ -313,20 +313,30 @@ def bench_extras(torch, mnb, dev):
                                        "frac_of_fp16_peak": round(tf / PEAK_FP16_TFLOPS, 4)}
         del w
     out["prefill_gemm"] = pre
-    # INT3 QMoE layer
+    # QMoE layer: all-INT3 projections, and the all-INT4 layer the INT3 QMoE
+    # page compares it with
+    out["qmoe_int3_layer"] = qmoe_extra(torch, dev, 3, 3)
+    out["qmoe_int4_layer"] = qmoe_extra(torch, dev, 4, 4)
+    return out
+
+
+def qmoe_extra(torch, dev, bits1, bits2):
+    """QMoE layer (hidden 2048, 128 experts, intermediate 768, top-8, block 64)
+    at T = 1, 128, 512 tokens, from graph replays over 4 weight copies."""
     H, I, E, k, bs = 2048, 768, 128, 8, 64
-    W1 = synth.int3_rows(synth.seed_for(5, 3), E * 2 * I, H)
+    W1 = synth.packed_rows(synth.seed_for(5, 3), E * 2 * I, H, bits1)
     s1 = synth.scales_f16(synth.seed_for(5, 4), (E * 2 * I, H // bs))
-    W2 = synth.int3_rows(synth.seed_for(5, 5), E * H, I)
+    W2 = synth.packed_rows(synth.seed_for(5, 5), E * H, I, bits2)
     s2 = synth.scales_f16(synth.seed_for(5, 6), (E * H, I // bs))
     copies = 4
     experts = []
     for c in range(copies):  # distinct device copies of the same expert bytes
-        experts.append((mnb.PreparedWeight(mnb.qmoe_proj_desc(H, 2 * I, E, bs), W1, s1),
-                        mnb.PreparedWeight(mnb.qmoe_proj_desc(I, H, E, bs), W2, s2)))
+        experts.append((mnb.PreparedWeight(mnb.qmoe_proj_desc(H, 2 * I, E, bs, bits1), W1, s1),
+                        mnb.PreparedWeight(mnb.qmoe_proj_desc(I, H, E, bs, bits2), W2, s2)))
     q = mnb.make_qmoe_desc(k)
-    per_expert = 2 * I * (3 * H // 8) + 2 * I * (H // bs) * 2 + H * (3 * I // 8) + H * (I // bs) * 2
-    moe = {}
+    per_expert = (2 * I * (bits1 * H // 8) + 2 * I * (H // bs) * 2 + H * (bits2 * I // 8)
+                  + H * (I // bs) * 2)
+    moe = {"bits": [bits1, bits2], "bytes_per_expert": per_expert}
     for T in (1, 128, 512):
         x = torch.from_numpy(synth.activations_f16(synth.seed_for(5, 1), T, H)).to(dev)
         lg = torch.from_numpy(synth.router_logits(synth.seed_for(5, 2), T, E)).to(dev)
@@ -342,8 +352,8 @@ def bench_extras(torch, mnb, dev):
                         "weight_GB/s": round(byts / us / 1e3, 1),
                         "frac_of_hbm_peak": round(byts / us / 1e3 / PEAK_HBM_GBS, 4),
                         "TFLOP/s": round(2.0 * T * k * (2 * I * H + H * I) / us / 1e6, 2)}
-    out["qmoe_int3_layer"] = moe
-    return out
+    del experts
+    return moe
 
 
 if __name__ == "__main__":

@@ -138,8 +138,9 @@ def dense_desc(K: int, N: int, block_size: int = 32, has_zero_points: bool = Fal
                     int(bool(has_zero_points)), MNB_ROWS_BLOCKED, 1)
 
 
-def qmoe_proj_desc(K: int, N: int, num_experts: int, block_size: int = 64) -> mnb_desc:
-    return mnb_desc(MNB_ABI_VERSION, 3, block_size, 0, K, N, MNB_DTYPE_F16, 0,
+def qmoe_proj_desc(K: int, N: int, num_experts: int, block_size: int = 64,
+                   bits: int = 3) -> mnb_desc:
+    return mnb_desc(MNB_ABI_VERSION, bits, block_size, 0, K, N, MNB_DTYPE_F16, 0,
                     MNB_ROWS_ROW_LOCAL, num_experts)
 
 

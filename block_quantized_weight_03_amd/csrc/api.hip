@@ -77,7 +77,7 @@ int32_t check_qmoe(const mnb_plan* fc1, const mnb_plan* fc2, const qmoe_desc* q,
   rc = check_plan(fc2, s2);
   if (rc != MNB_OK) return rc;
   if (q->abi_version != MNB_ABI_VERSION || q->reserved != 0) return MNB_ERR_INVALID_ARG;
-  if (s1->kind != kMoeInt3 || s2->kind != kMoeInt3) return MNB_ERR_UNSUPPORTED;
+  if (s1->kind != kMoe || s2->kind != kMoe) return MNB_ERR_UNSUPPORTED;
   if (q->normalize_routing_weights != 1 || q->activation != QMOE_ACT_SWIGLU ||
       q->gate_up != QMOE_GATE_UP_INTERLEAVED || q->weights_prepacked != 0 ||
       q->quant_type != QMOE_QUANT_INT)

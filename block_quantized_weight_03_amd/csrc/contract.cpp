@@ -54,17 +54,17 @@ int32_t check_desc(const mnb_desc* d, Sizes* s) {
   z.bits = d->bits;
   z.nb = d->K / d->block_size + (d->K % d->block_size ? 1 : 0);
 
-  if (d->bits == 4) {
+  if (d->bits == 4 && d->scale_dtype == MNB_DTYPE_F32) {
     // dense MatMulNBits profile
-    if (d->scale_dtype != MNB_DTYPE_F32 || d->row_layout != MNB_ROWS_BLOCKED || d->num_experts != 1)
-      return MNB_ERR_UNSUPPORTED;
+    if (d->row_layout != MNB_ROWS_BLOCKED || d->num_experts != 1) return MNB_ERR_UNSUPPORTED;
     z.kind = kDenseInt4;
-  } else if (d->bits == 3) {
-    // QMoE v1 INT3 profile
+  } else if (d->bits == 3 || d->bits == 4) {
+    // QMoE v1 projection profile: INT3, or INT4 for the mixed (3,4) / (4,3)
+    // width pairs and the all-INT4 layer
     if (d->scale_dtype != MNB_DTYPE_F16 || d->row_layout != MNB_ROWS_ROW_LOCAL || d->has_zero_points)
       return MNB_ERR_UNSUPPORTED;
     if (d->K % d->block_size) return MNB_ERR_UNSUPPORTED;  // block-aligned K
-    z.kind = kMoeInt3;
+    z.kind = kMoe;
   } else {
     return MNB_ERR_UNSUPPORTED;
   }
@@ -110,7 +110,7 @@ int32_t validate_content(const mnb_desc* d, const Sizes& s, const uint8_t* B,
                          const void* scales, const uint8_t* zp) {
   (void)d;
   (void)zp;
-  if (s.kind != kMoeInt3) return MNB_OK;
+  if (s.kind != kMoe) return MNB_OK;
   // finite, nonnegative FP16 scales: exponent 31 is Inf/NaN; a set sign bit
   // is only allowed on zero
   const uint64_t n = s.scales / 2;
@@ -154,26 +154,29 @@ void prepack(const Sizes& s, const uint8_t* B, const void* scales,
       }
     }
   } else {
-    // contract rows are LSB-first 3-bit streams; regroup every 32 codes into
+    // contract rows are LSB-first bit streams; regroup every 32 codes into
     // the pair-interleaved words, stored tile-major (same byte count)
+    const int64_t GB = 4 * s.bits;
     for (int64_t row = 0; row < s.rows; ++row) {
       const uint8_t* src = B + (uint64_t)row * (uint64_t)s.row_bytes;
       const int64_t e = row / s.N, n = row % s.N;
       for (int64_t G = 0; G < s.K / 32; ++G) {
-        uint32_t w[3] = {0, 0, 0};
+        uint32_t w[4] = {0, 0, 0, 0};
         for (int i = 0; i < 32; ++i) {
           uint32_t q = 0;
-          for (int t = 0; t < 3; ++t) {
-            const int64_t bit = 3 * (32 * G + i) + t;
+          for (int t = 0; t < s.bits; ++t) {
+            const int64_t bit = s.bits * (32 * G + i) + t;
             q |= (uint32_t)((src[bit >> 3] >> (bit & 7)) & 1u) << t;
           }
-          if (i < 30) {
+          if (s.bits == 4) {
+            w[int4_word(i)] |= q << int4_bit(i);
+          } else if (i < 30) {
             w[int3_word(i)] |= q << int3_bit(i);
           } else {
             for (int t = 0; t < 3; ++t) w[t] |= ((q >> t) & 1u) << (i == 30 ? 15 : 31);
           }
         }
-        std::memcpy(codes + int3_group_offset(s.N, s.K, e, n, G), w, 12);
+        std::memcpy(codes + moe_group_offset(s.N, s.K, GB, e, n, G), w, (size_t)GB);
       }
     }
   }
@@ -246,10 +249,14 @@ void unpack_host(const Sizes& s, const mnb_plan* p, int64_t expert,
           const uint8_t byte = src[b * (s.bs / 2) + j / 2];
           q = ((j & 1) ? (byte >> 4) : (byte & 15u)) ^ 8u;
         } else {
-          uint32_t w[3];
-          std::memcpy(w, base + int3_group_offset(s.N, s.K, row / s.N, row % s.N, k / 32), 12);
+          uint32_t w[4];
+          const int64_t GB = 4 * s.bits;
+          std::memcpy(w, base + moe_group_offset(s.N, s.K, GB, row / s.N, row % s.N, k / 32),
+                      (size_t)GB);
           const int i = (int)(k % 32);
-          if (i < 30) {
+          if (s.bits == 4) {
+            q = (w[int4_word(i)] >> int4_bit(i)) & 15u;
+          } else if (i < 30) {
             q = (w[int3_word(i)] >> int3_bit(i)) & 7u;
           } else {
             q = 0;

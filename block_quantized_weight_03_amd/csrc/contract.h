@@ -16,36 +16,48 @@ constexpr uint32_t kPlanMagic = 0x4D4E4250u;  // "MNBP"
 //              scales fp32 [N][nb]; zero points (if explicit) as uint32 words
 //              [ceil(N/8)][nb], nibble r of word (g, b) holding the zero point
 //              of row 8g + r, block b (one load gives a row group's points).
-//  INT3 QMoE:  codes: the same bytes per row as the contract, 3K/8, regrouped
-//              for the matrix-core dequantization.  Each group of 32 codes
-//              c0..c31 (k = 32G + i) of a row is three 32-bit words w0, w1,
-//              w2; word m holds the pairs (c[10m+2p], c[10m+2p+1]) for
-//              p = 0..4 at bits [3p, 3p+3) and [16+3p, 16+3p+3), so
-//              (w >> 3p) & 0x00070007 puts a pair in the two 16-bit halves;
-//              bit t of c30 is bit 15 of w_t and bit t of c31 is bit 31 of w_t.
+//  QMoE (INT3 or INT4 projections): codes: the same bytes per row as the
+//              contract, bits*K/8, regrouped for the matrix-core
+//              dequantization.  Each group of 32 codes c0..c31 (k = 32G + i)
+//              of a row is GB = 4*bits bytes:
+//              INT3: three 32-bit words w0, w1, w2; word m holds the pairs
+//              (c[10m+2p], c[10m+2p+1]) for p = 0..4 at bits [3p, 3p+3) and
+//              [16+3p, 16+3p+3), so (w >> 3p) & 0x00070007 puts a pair in the
+//              two 16-bit halves; bit t of c30 is bit 15 of w_t and bit t of
+//              c31 is bit 31 of w_t.
+//              INT4: four 32-bit words; word m holds the pairs (c[8m+2p],
+//              c[8m+2p+1]) for p = 0..3 at bits [4p, 4p+4) and [16+4p,
+//              16+4p+4), so (w >> 4p) & 0x000F000F puts a pair in the halves.
 //              The groups are stored tile-major: the rows of an expert in
 //              tiles of 16 (the last may hold fewer), each tile as a sequence
 //              of K chunks of 4 groups (128 codes; the last may hold fewer),
 //              each chunk as its rows' groups row by row; so one chunk of one
-//              tile is 16 x 48 contiguous bytes.  Scales fp16 [E*N][K/bs].
-constexpr uint32_t kLayoutVersion = 4;
+//              tile is 16 x 4 GB contiguous bytes.  Scales fp16 [E*N][K/bs].
+constexpr uint32_t kLayoutVersion = 5;
 constexpr uint64_t kSectionAlign = 256;
 
-enum Kind : int32_t { kDenseInt4 = 1, kMoeInt3 = 2 };
+enum Kind : int32_t { kDenseInt4 = 1, kMoe = 2 };
 
 // Word (within its group of three) and bit offset of INT3 code i (0..31) of a
 // group, for the codes stored in one 3-bit field (i < 30).
 constexpr int int3_word(int i) { return i / 10; }
 constexpr int int3_bit(int i) { return 3 * ((i % 10) / 2) + 16 * (i % 2); }
 
+// Word (within its group of four) and bit offset of INT4 code i (0..31) of a
+// group.
+constexpr int int4_word(int i) { return i / 8; }
+constexpr int int4_bit(int i) { return 4 * ((i % 8) / 2) + 16 * (i % 2); }
+
 // Byte offset, inside the code section, of 32-code group G of row n_local of
-// expert e (tile-major INT3 layout; K is a multiple of 32).
-inline uint64_t int3_group_offset(int64_t N, int64_t K, int64_t e, int64_t n_local, int64_t G) {
+// expert e (tile-major QMoE layout with GB-byte groups; K is a multiple of 32).
+inline uint64_t moe_group_offset(int64_t N, int64_t K, int64_t GB, int64_t e, int64_t n_local,
+                                 int64_t G) {
   const int64_t ng = K / 32, rt = n_local / 16, r = n_local % 16;
   const int64_t rcnt = (N - 16 * rt) < 16 ? (N - 16 * rt) : 16;
   const int64_t c = G / 4, g = G % 4;
   const int64_t gic = (ng - 4 * c) < 4 ? (ng - 4 * c) : 4;
-  return (uint64_t)(e * N + 16 * rt) * (uint64_t)(ng * 12) + (uint64_t)(rcnt * 48 * c + r * gic * 12 + g * 12);
+  return (uint64_t)(e * N + 16 * rt) * (uint64_t)(ng * GB) +
+         (uint64_t)(rcnt * 4 * GB * c + r * gic * GB + g * GB);
 }
 
 struct Sizes {
@@ -65,8 +77,9 @@ struct Sizes {
 // Checks a descriptor and fills every size with overflow-checked arithmetic.
 int32_t check_desc(const mnb_desc* d, Sizes* s);
 
-// Validates the host content of the weights (INT3: finite nonnegative fp16
-// scales and canonical row padding).  Dense INT4 content is not checked.
+// Validates the host content of the weights (QMoE projections: finite
+// nonnegative fp16 scales and canonical row padding).  Dense INT4 content is
+// not checked.
 int32_t validate_content(const mnb_desc* d, const Sizes& s, const uint8_t* B,
                          const void* scales, const uint8_t* zp);
 

@@ -19,17 +19,19 @@ struct Rows {
   const void* scales;
   const uint8_t* zeros;
   int64_t N, K, nb, bs, row_bytes, zrow, row_base;  // row_base = expert * N + row0
-  int kind;
+  int kind, bits;
 };
 
-// byte offset of 32-code group G of row n of expert e in the tile-major INT3
-// layout (rows in tiles of 16, each tile as chunks of 4 groups, row by row)
-__device__ __forceinline__ int64_t int3_goff(int64_t N, int64_t K, int64_t e, int64_t n, int64_t G) {
+// byte offset of 32-code group G of row n of expert e in the tile-major QMoE
+// layout with GB-byte groups (rows in tiles of 16, each tile as chunks of 4
+// groups, row by row)
+__device__ __forceinline__ int64_t moe_goff(int64_t N, int64_t K, int64_t GB, int64_t e, int64_t n,
+                                            int64_t G) {
   const int64_t ng = K / 32, rt = n / 16, r = n % 16;
   const int64_t rcnt = (N - 16 * rt) < 16 ? (N - 16 * rt) : 16;
   const int64_t c = G / 4, g = G % 4;
   const int64_t gic = (ng - 4 * c) < 4 ? (ng - 4 * c) : 4;
-  return (e * N + 16 * rt) * (ng * 12) + rcnt * 48 * c + r * gic * 12 + g * 12;
+  return (e * N + 16 * rt) * (ng * GB) + rcnt * 4 * GB * c + r * gic * GB + g * GB;
 }
 
 __device__ __forceinline__ unsigned code_of(const Rows& r, int64_t row, int64_t k) {
@@ -39,10 +41,11 @@ __device__ __forceinline__ unsigned code_of(const Rows& r, int64_t row, int64_t 
     const uint8_t byte = src[b * (r.bs / 2) + j / 2];
     return (((j & 1) ? (byte >> 4) : byte) & 15u) ^ 8u;
   }
-  // INT3: pair-interleaved groups of three words per 32 codes, tile-major
-  const uint32_t* w =
-      reinterpret_cast<const uint32_t*>(r.codes + int3_goff(r.N, r.K, row / r.N, row % r.N, k / 32));
+  // QMoE: pair-interleaved groups of bits words per 32 codes, tile-major
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(
+      r.codes + moe_goff(r.N, r.K, 4 * r.bits, row / r.N, row % r.N, k / 32));
   const int i = (int)(k % 32);
+  if (r.bits == 4) return (w[int4_word(i)] >> int4_bit(i)) & 15u;
   if (i < 30) return (w[int3_word(i)] >> int3_bit(i)) & 7u;
   const int b = i == 30 ? 15 : 31;
   return ((w[0] >> b) & 1u) | (((w[1] >> b) & 1u) << 1) | (((w[2] >> b) & 1u) << 2);
@@ -75,7 +78,7 @@ __global__ void debug_dequant_kernel(Rows r, int64_t nrows, __half* __restrict__
     v = fmaf((float)q, s, -((float)z * s));
   } else {
     const __half s = static_cast<const __half*>(r.scales)[grow * r.nb + b];
-    v = (float)((int)q - 4) * __half2float(s);  // exact in fp32
+    v = (float)((int)q - (1 << (r.bits - 1))) * __half2float(s);  // exact in fp32
   }
   out[i] = __float2half_rn(v);
 }
@@ -93,6 +96,7 @@ Rows make_rows(const Sizes& s, const mnb_plan& p, int64_t expert, int64_t row0) 
   r.zrow = (int64_t)s.zrow;
   r.row_base = expert * s.N + row0;
   r.kind = s.kind;
+  r.bits = (int)s.bits;
   return r;
 }
 

@@ -1,4 +1,4 @@
-// Top-k routed INT3 QMoE layer for gfx950.
+// Top-k routed QMoE layer with INT3 or INT4 expert projections for gfx950.
 //
 // Sources: onnxruntime PR "INT3 QMoE CUDA correctness baseline and Qwen
 // experimental results" (PR summary: routing, fused gate/up SwiGLU, an
@@ -19,8 +19,9 @@
 //              T*k slots into expert-grouped order that is stable in (token,
 //              rank) order, and the list of (expert, row-tile) work items.
 //  3. fc1:     per work item, G = X_e W1_e^T on the matrix cores (gathered
-//              token rows in LDS; INT3 weights dequantized in registers as
-//              fp16((q - 4) * s), once per item); epilogue
+//              token rows in LDS; INT3 / INT4 weights dequantized in
+//              registers as fp16((q - z) * s), z = 4 / 8, once per item);
+//              epilogue
 //              h_i = silu(g_i) * u_i from the interleaved gate/up columns,
 //              rounded to fp16.
 //  4. fc2:     per work item, Y_e = h_e W2_e^T; epilogue multiplies by the
@@ -29,6 +30,8 @@
 
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -282,15 +285,18 @@ __global__ void __launch_bounds__(kGroupThreads) qmoe_group(const int32_t* __res
 }
 
 // ---------------------------------------------------------------------------
-// 3./4. grouped INT3 GEMM (FC1 with SwiGLU epilogue, FC2 with route weights)
+// 3./4. grouped INT3 / INT4 GEMM (FC1 with SwiGLU epilogue, FC2 with route
+// weights); each projection takes its own width (pairs (3,3), (3,4), (4,3)
+// and (4,4))
 // ---------------------------------------------------------------------------
 //
 // A workgroup takes one work item (expert e, up to BM of its tokens) and 64
 // weight rows; wave w owns rows [16w, 16w + 16) and computes them for all of
 // the item's tokens with v_mfma_f32_16x16x32_f16 (C tiles of 16 tokens x 16
 // rows).  The weights never go through LDS: lane (n, g) = (lane & 15,
-// lane >> 4) loads the 12-byte group g (32 codes, k = 32g .. 32g + 31 of a
-// 128-wide K chunk) of its row straight into registers and dequantizes it once
+// lane >> 4) loads the 12-byte (INT3) or 16-byte (INT4) group g (32 codes,
+// k = 32g .. 32g + 31 of a 128-wide K chunk) of its row straight into
+// registers and dequantizes it once
 // for every token of the item.  K order inside an MFMA is free when both
 // operands share it: MFMA t of a chunk takes k = 32g + 8t + [0, 8) in lane
 // group g, on both sides.  The token rows of the chunk (gathered by route for
@@ -299,7 +305,7 @@ __global__ void __launch_bounds__(kGroupThreads) qmoe_group(const int32_t* __res
 //
 // Dequantization of a pair of codes from the private layout: one shift and one
 // and-or give the fp16 values 1024 + q in both halves, v_pk_add_f16 makes the
-// exact q - 4, v_pk_mul_f16 by the fp16 scale rounds once: fp16((q - 4) * s),
+// exact q - z, v_pk_mul_f16 by the fp16 scale rounds once: fp16((q - z) * s),
 // the same value as the exact fp32 product rounded to fp16.
 
 typedef _Float16 half2t __attribute__((ext_vector_type(2)));
@@ -307,29 +313,55 @@ typedef _Float16 half2t __attribute__((ext_vector_type(2)));
 // (a & m) | (b & ~m): one v_bfi_b32
 __device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); }
 
-// fp16 (q - 4) * s for the two codes in bits [0, 3) and [16, 19) of v;
-// magic holds 0x64006400 (1024.0 in both halves), in a register the compiler
-// cannot fold, so that the insert stays a single v_bfi_b32
-__device__ __forceinline__ uint32_t int3_pair(uint32_t v, uint32_t magic, half2t s2) {
-  half2t h = __builtin_bit_cast(half2t, bfi(0x00070007u, v, magic));  // 1024 + q
-  h = (h + half2t{(_Float16)-1028.0f, (_Float16)-1028.0f}) * s2;        // (q - 4) * s
-  return __builtin_bit_cast(uint32_t, h);
+// A group of 32 codes in the private layout: 4 * BITS bytes (three words
+// for INT3, four for INT4).
+template <int BITS> struct Group;
+template <> struct Group<3> { typedef u32x3 W; };
+template <> struct Group<4> { typedef u32x4 W; };
+
+// fp16 bias that turns 1024 + q into the exact q - z, z = 2^(BITS-1)
+template <int BITS>
+__device__ __forceinline__ half2t zero_bias() {
+  constexpr float b = -(1024.0f + (float)(1 << (BITS - 1)));
+  return half2t{(_Float16)b, (_Float16)b};
 }
 
-// the 32 codes of one group as four MFMA operands (8 consecutive k each)
-__device__ __forceinline__ void dequant_group(const u32x3 w, _Float16 s, uint32_t magic,
-                                              half8 (&out)[4]) {
-  const half2t s2 = half2t{s, s};
-  uint32_t p[16];
+// The 16 code pairs (c[2i], c[2i+1]) of a group as fp16 1024 + c in the two
+// halves of p[i]: the fp16 pattern of 1024 + c (c < 1024) is that of 1024
+// with c in its low mantissa bits, so each pair is one v_bfi_b32 into magic
+// (0x64006400, 1024.0 in both halves, kept in a register the compiler cannot
+// fold, so that the insert stays a single v_bfi_b32).  Words are copied into
+// scalars before use.
+__device__ __forceinline__ void raw_pairs(const u32x3 w, uint32_t magic, uint32_t (&p)[16]) {
 #pragma unroll
   for (int m = 0; m < 3; ++m) {
     const uint32_t x = m == 0 ? w.x : (m == 1 ? w.y : w.z);
 #pragma unroll
-    for (int q = 0; q < 5; ++q) p[5 * m + q] = int3_pair(x >> (3 * q), magic, s2);
+    for (int q = 0; q < 5; ++q) p[5 * m + q] = bfi(0x00070007u, x >> (3 * q), magic);
   }
-  const uint32_t c3031 = bfi(0x00010001u, w.x >> 15, bfi(0x00020002u, w.y >> 14, bfi(0x00040004u, w.z >> 13, magic)));
-  p[15] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2t, c3031) +
-                                        half2t{(_Float16)-1028.0f, (_Float16)-1028.0f}) * s2);
+  p[15] = bfi(0x00010001u, w.x >> 15, bfi(0x00020002u, w.y >> 14, bfi(0x00040004u, w.z >> 13, magic)));
+}
+__device__ __forceinline__ void raw_pairs(const u32x4 w, uint32_t magic, uint32_t (&p)[16]) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint32_t x = m == 0 ? w.x : (m == 1 ? w.y : (m == 2 ? w.z : w.w));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) p[4 * m + q] = bfi(0x000F000Fu, x >> (4 * q), magic);
+  }
+}
+
+// the 32 codes of one group as four MFMA operands (8 consecutive k each):
+// v_pk_add_f16 makes the exact q - z, v_pk_mul_f16 by the fp16 scale rounds
+// once, fp16((q - z) * s)
+template <int BITS>
+__device__ __forceinline__ void dequant_group(const typename Group<BITS>::W w, _Float16 s,
+                                              uint32_t magic, half8 (&out)[4]) {
+  const half2t s2 = half2t{s, s}, zb = zero_bias<BITS>();
+  uint32_t p[16];
+  raw_pairs(w, magic, p);
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    p[i] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2t, p[i]) + zb) * s2);
 #pragma unroll
   for (int t = 0; t < 4; ++t)
     out[t] = __builtin_bit_cast(half8, u32x4{p[4 * t], p[4 * t + 1], p[4 * t + 2], p[4 * t + 3]});
@@ -342,15 +374,18 @@ __device__ __forceinline__ uint32_t opaque_magic() {
 }
 
 // Byte offset, within one expert's codes, of 32-code group G of row n in the
-// tile-major INT3 layout: rows in tiles of 16 (the last may hold fewer), each
-// tile as K chunks of 4 groups (the last may hold fewer), each chunk row by
-// row; a full tile's chunk is 16 x 48 contiguous bytes.
-__device__ __forceinline__ uint32_t int3_goff(int N, int K, int n, int G) {
+// tile-major layout with GB = 4 BITS byte groups: rows in tiles of 16 (the
+// last may hold fewer), each tile as K chunks of 4 groups (the last may hold
+// fewer), each chunk row by row; a full tile's chunk is 16 x 4 GB contiguous
+// bytes.
+template <int BITS>
+__device__ __forceinline__ uint32_t moe_goff(int N, int K, int n, int G) {
+  constexpr int GB = 4 * BITS;
   const int ng = K >> 5, rt = n >> 4, r = n & 15;
   const int rcnt = min(16, N - 16 * rt);
   const int c = G >> 2, gg = G & 3;
   const int gic = min(4, ng - 4 * c);
-  return (uint32_t)(16 * rt * ng * 12 + rcnt * 48 * c + r * gic * 12 + gg * 12);
+  return (uint32_t)(16 * rt * ng * GB + rcnt * 4 * GB * c + r * gic * GB + gg * GB);
 }
 
 struct MoeGemmArgs {
@@ -377,8 +412,9 @@ constexpr int kQPitch = kQBK + 8;
 template <int BM>
 constexpr int ntg_of() { return BM == 32 ? 4 : 2; }
 
-template <bool FC1, int BM>
+template <bool FC1, int BM, int BITS>
 __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n, int64_t tiles_n) {
+  constexpr uint32_t GB = 4 * BITS;    // bytes per 32-code group
   constexpr int kNTG = ntg_of<BM>();
   constexpr int TM = BM / 16;          // 16-token MFMA tiles
   constexpr int AP = BM * 16 / 256;    // 16-byte activation chunks per thread and chunk
@@ -442,18 +478,18 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
   // (L2-resident) move one chunk ahead through registers into the other LDS
   // buffer.  Tiles past ntc repeat the last tile and are never stored.
   struct WStage {
-    u32x3 rw;
+    typename Group<BITS>::W rw;
     uint32_t rs;
     bool ok;
   };
   // Tile-major offsets (N % 16 == 0, so every 16-row tile is full): group G =
-  // 4c + wg of row 16 rt + wn sits at rt (ng 192) + 768 c + 48 wn + 12 wg in a
-  // full chunk and at rt (ng 192) + 768 c + gl (12 wn) + 12 wg in a last chunk
-  // of gl < 4 groups; the wave's row tile is uniform, so only the lane term is
-  // per lane.  Groups past K use the chunk's last group (scale 0).
+  // 4c + wg of row 16 rt + wn sits at rt (16 ng GB) + 64 GB c + 4 GB wn + GB wg
+  // in a full chunk and at rt (16 ng GB) + 64 GB c + gl (GB wn) + GB wg in a
+  // last chunk of gl < 4 groups; the wave's row tile is uniform, so only the
+  // lane term is per lane.  Groups past K use the chunk's last group (scale 0).
   const int ng = Kc >> 5, nfull = ng >> 2, gl = ng - 4 * nfull;
-  const uint32_t lane_full = 48u * wn + 12u * wg;
-  const uint32_t lane_last = gl ? 12u * (uint32_t)(gl * wn + (wg < gl ? wg : gl - 1)) : lane_full;
+  const uint32_t lane_full = 4 * GB * wn + GB * wg;
+  const uint32_t lane_last = gl ? GB * (uint32_t)(gl * wn + (wg < gl ? wg : gl - 1)) : lane_full;
   auto load_w = [&](WStage& st, int t, int c) {
     c = c < nch ? c : nch - 1;
     t = t < ntc ? t : ntc - 1;
@@ -461,9 +497,9 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
     const bool rok = 16 * rt < Nc;                     // uniform
     const int G = 4 * c + wg;
     st.ok = rok && G < ng;
-    const uint32_t off = (uint32_t)(rok ? rt : 0) * (uint32_t)(ng * 192) + 768u * (uint32_t)c +
+    const uint32_t off = (uint32_t)(rok ? rt : 0) * (uint32_t)(ng * 16 * GB) + 64 * GB * (uint32_t)c +
                          (c < nfull ? lane_full : lane_last);
-    st.rw = *reinterpret_cast<const u32x3*>(wbase + off);
+    st.rw = *reinterpret_cast<const typename Group<BITS>::W*>(wbase + off);
     const int rowc = rok ? 16 * rt + wn : wn;
     st.rs = sbase[rowc * (int)g.nblk + ((32 * (G < ng ? G : ng - 1)) >> bshift)];
   };
@@ -539,7 +575,7 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
 #pragma unroll
     for (int t = 0; t < kNTG; ++t) {
       half8 wf[4];
-      dequant_group(ws[t].rw, __builtin_bit_cast(_Float16, (uint16_t)(ws[t].ok ? ws[t].rs : 0u)), magic, wf);
+      dequant_group<BITS>(ws[t].rw, __builtin_bit_cast(_Float16, (uint16_t)(ws[t].ok ? ws[t].rs : 0u)), magic, wf);
       load_w(ws[t], t, c + 1);
       if (t < ntc) {
 #pragma unroll
@@ -577,22 +613,17 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
 // read of element .x, so elements are always copied into a scalar first.
 __device__ __forceinline__ half2t as_half2(uint32_t v) { return __builtin_bit_cast(half2t, v); }
 
-// s * sum_k (q_k - 4) a_k over one 32-code group, for the decode GEMVs: the
-// codes become exact fp16 (q - 4) (no per-code scale multiply), v_dot2 sums
+// s * sum_k (q_k - z) a_k over one 32-code group, for the decode GEMVs: the
+// codes become exact fp16 (q - z) (no per-code scale multiply), v_dot2 sums
 // the exact products in fp32 and the group's scale is applied once.
-__device__ __forceinline__ float group_dot_unscaled(const u32x3 w, float s, uint32_t magic,
-                                                    const u32x4* a16) {
-  const half2t m4 = half2t{(_Float16)-1028.0f, (_Float16)-1028.0f};
+template <int BITS>
+__device__ __forceinline__ float group_dot_unscaled(const typename Group<BITS>::W w, float s,
+                                                    uint32_t magic, const u32x4* a16) {
+  const half2t zb = zero_bias<BITS>();
   uint32_t p[16];
+  raw_pairs(w, magic, p);
 #pragma unroll
-  for (int m = 0; m < 3; ++m) {
-    const uint32_t x = m == 0 ? w.x : (m == 1 ? w.y : w.z);
-#pragma unroll
-    for (int q = 0; q < 5; ++q)
-      p[5 * m + q] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2t, bfi(0x00070007u, x >> (3 * q), magic)) + m4);
-  }
-  const uint32_t c3031 = bfi(0x00010001u, w.x >> 15, bfi(0x00020002u, w.y >> 14, bfi(0x00040004u, w.z >> 13, magic)));
-  p[15] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2t, c3031) + m4);
+  for (int i = 0; i < 16; ++i) p[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2t, p[i]) + zb);
   float acc = 0.0f;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -620,8 +651,9 @@ struct TileRef {
   int N, K, nblk, bshift, row, ng, nch, g;
 };
 
+template <int BITS>
 struct TileBatch {
-  u32x3 w[kDecBatch];
+  typename Group<BITS>::W w[kDecBatch];
   uint16_t s[kDecBatch];
   int G[kDecBatch];
   uint32_t ok;  // bit u: group G[u] lies inside K (the loaded scale is used as is)
@@ -637,7 +669,7 @@ struct TileBatch {
       const int Gr = 4 * (c0 + u * cstep) + t.g;
       ok |= (Gr < t.ng ? 1u : 0u) << u;
       G[u] = Gr < t.ng ? Gr : t.ng - 1;
-      w[u] = *reinterpret_cast<const u32x3*>(t.codes + int3_goff(t.N, t.K, t.row, G[u]));
+      w[u] = *reinterpret_cast<const typename Group<BITS>::W*>(t.codes + moe_goff<BITS>(t.N, t.K, t.row, G[u]));
       s[u] = t.scales[t.row * t.nblk + ((32 * G[u]) >> t.bshift)];
     }
   }
@@ -647,7 +679,7 @@ struct TileBatch {
     for (int u = 0; u < kDecBatch; ++u)
       if (u < cnt) {
         const uint16_t sc = (ok >> u) & 1u ? s[u] : (uint16_t)0;
-        acc += group_dot_unscaled(w[u], (float)__builtin_bit_cast(_Float16, sc), magic,
+        acc += group_dot_unscaled<BITS>(w[u], (float)__builtin_bit_cast(_Float16, sc), magic,
                                   reinterpret_cast<const u32x4*>(xs + 32 * G[u]));
       }
     return acc;
@@ -658,9 +690,10 @@ struct TileBatch {
 // (lane >> 3) & 3, lane >> 5) takes group 4c + g of row n for the chunks
 // c = c0 + 2u + h (used where 16-row tiles would leave CUs idle).  Chunks or
 // groups past K are skipped per lane.
+template <int BITS>
 struct HalfBatch {
   static constexpr int kU = kDecBatch / 2;
-  u32x3 w[kU];
+  typename Group<BITS>::W w[kU];
   uint16_t s[kU];
   int G[kU];
   uint32_t ok;  // bit u: chunk and group inside K
@@ -674,7 +707,7 @@ struct HalfBatch {
       const bool v = c < t.nch && Gr < t.ng;
       ok |= (v ? 1u : 0u) << u;
       G[u] = v ? Gr : t.ng - 1;
-      w[u] = *reinterpret_cast<const u32x3*>(t.codes + int3_goff(t.N, t.K, t.row, G[u]));
+      w[u] = *reinterpret_cast<const typename Group<BITS>::W*>(t.codes + moe_goff<BITS>(t.N, t.K, t.row, G[u]));
       s[u] = t.scales[t.row * t.nblk + ((32 * G[u]) >> t.bshift)];
     }
   }
@@ -683,7 +716,7 @@ struct HalfBatch {
 #pragma unroll
     for (int u = 0; u < kU; ++u)
       if ((ok >> u) & 1u)
-        acc += group_dot_unscaled(w[u], (float)__builtin_bit_cast(_Float16, s[u]), magic,
+        acc += group_dot_unscaled<BITS>(w[u], (float)__builtin_bit_cast(_Float16, s[u]), magic,
                                   reinterpret_cast<const u32x4*>(xs + 32 * G[u]));
     return acc;
   }
@@ -735,7 +768,7 @@ __device__ __forceinline__ TileRef tile_ref(const MoeGemmArgs& g, int e, int row
 // chunks w, w + 4, ... of expert ids[t, j]'s tile; partials are summed in a
 // fixed order and h[slot I + 8 tile + m] = fp16(silu(g_m) u_m) for gate row
 // 2m, up row 2m + 1.
-template <int kPer, bool ROUTE>
+template <int kPer, bool ROUTE, int BITS>
 __global__ void __launch_bounds__(256) qmoe_fc1_decode(MoeGemmArgs g, int64_t T,
                                                        const float* __restrict__ logits,
                                                        int32_t* __restrict__ ids,
@@ -767,7 +800,7 @@ __global__ void __launch_bounds__(256) qmoe_fc1_decode(MoeGemmArgs g, int64_t T,
     e = clamp_id(ids[slot], g.E);
   }
   const TileRef tr = tile_ref(g, e, 16 * tile, lane);
-  TileBatch b;
+  TileBatch<BITS> b;
   b.load(tr, wave, 4);
   __builtin_amdgcn_sched_barrier(0);
   xst.rest(xr, reinterpret_cast<u32x4*>(xs), K / 8, tid, 256);
@@ -795,6 +828,7 @@ __global__ void __launch_bounds__(256) qmoe_fc1_decode(MoeGemmArgs g, int64_t T,
 // j; the token's k rows of h are staged in LDS; wave j forms the partials of
 // expert ids[t, j]'s tile rows, then out[t, n] = fp16(sum_j r_j y_j[n]) with
 // y_j and the rank sum in fixed orders.
+template <int BITS>
 __global__ void __launch_bounds__(1024) qmoe_fc2_decode(MoeGemmArgs g, int64_t T, __half* out,
                                                         float* slot_dbg) {
   extern __shared__ __align__(16) uint8_t sm[];
@@ -812,7 +846,7 @@ __global__ void __launch_bounds__(1024) qmoe_fc2_decode(MoeGemmArgs g, int64_t T
   Stage2 hst;
   hst.first(hr, k * I / 8, tid, 64 * k);
   __builtin_amdgcn_sched_barrier(0);
-  HalfBatch b;
+  HalfBatch<BITS> b;
   b.load(tr, 0, hsel);
   __builtin_amdgcn_sched_barrier(0);
   hst.rest(hr, reinterpret_cast<u32x4*>(hs), k * I / 8, tid, 64 * k);
@@ -820,7 +854,7 @@ __global__ void __launch_bounds__(1024) qmoe_fc2_decode(MoeGemmArgs g, int64_t T
   const uint32_t magic = opaque_magic();
   const _Float16* hj = hs + j * I;
   float acc = b.dot(hj, magic);
-  for (int c = 2 * HalfBatch::kU; c < tr.nch; c += 2 * HalfBatch::kU) {
+  for (int c = 2 * HalfBatch<BITS>::kU; c < tr.nch; c += 2 * HalfBatch<BITS>::kU) {
     b.load(tr, c, hsel);
     acc += b.dot(hj, magic);
   }
@@ -907,6 +941,15 @@ Ws ws_layout(const Sizes& s1, const Sizes& s2, int k, int64_t T) {
   return w;
 }
 
+// Calls f with the code width (3 or 4) as a compile-time constant.
+template <typename F>
+void by_bits(int64_t bits, F&& f) {
+  if (bits == 4)
+    f(std::integral_constant<int, 4>());
+  else
+    f(std::integral_constant<int, 3>());
+}
+
 void launch_route(const float* logits, int64_t T, int E, int k, int32_t* ids, float* wts,
                   hipStream_t st) {
   const dim3 grid((unsigned)((T + 3) / 4)), block(256);
@@ -956,22 +999,27 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
                    nullptr, nullptr, ids, nullptr, nullptr, wts, hbuf, nullptr};
     const dim3 g1((unsigned)(S * (s1.N / 16))), b1(256);
     const size_t l1 = (size_t)(2 * H + 4 * 256 + 128);
-    if (S > kFusedRouteSlots) {
-      launch_route(logits, T, (int)E, k, ids, wts, st);
-      hipLaunchKernelGGL((qmoe_fc1_decode<2, false>), g1, b1, l1, st, a1, T, logits, ids, wts);
-    } else if (E <= 128) {
-      hipLaunchKernelGGL((qmoe_fc1_decode<2, true>), g1, b1, l1, st, a1, T, logits, ids, wts);
-    } else if (E <= 256) {
-      hipLaunchKernelGGL((qmoe_fc1_decode<4, true>), g1, b1, l1, st, a1, T, logits, ids, wts);
-    } else {
-      hipLaunchKernelGGL((qmoe_fc1_decode<kMaxE / 64, true>), g1, b1, l1, st, a1, T, logits, ids, wts);
-    }
+    if (S > kFusedRouteSlots) launch_route(logits, T, (int)E, k, ids, wts, st);
+    by_bits(s1.bits, [&](auto bits) {
+      constexpr int B = decltype(bits)::value;
+      if (S > kFusedRouteSlots)
+        hipLaunchKernelGGL((qmoe_fc1_decode<2, false, B>), g1, b1, l1, st, a1, T, logits, ids, wts);
+      else if (E <= 128)
+        hipLaunchKernelGGL((qmoe_fc1_decode<2, true, B>), g1, b1, l1, st, a1, T, logits, ids, wts);
+      else if (E <= 256)
+        hipLaunchKernelGGL((qmoe_fc1_decode<4, true, B>), g1, b1, l1, st, a1, T, logits, ids, wts);
+      else
+        hipLaunchKernelGGL((qmoe_fc1_decode<kMaxE / 64, true, B>), g1, b1, l1, st, a1, T, logits, ids, wts);
+    });
     MoeGemmArgs a2{static_cast<const uint8_t*>(p2.codes), static_cast<const __half*>(p2.scales),
                    hbuf, s2.N, s2.K, s2.row_bytes, s2.nb, s2.bs, k, (int)E,
                    nullptr, nullptr, ids, nullptr, nullptr, wts, nullptr, nullptr};
-    hipLaunchKernelGGL(qmoe_fc2_decode, dim3((unsigned)(T * (H / 8))), dim3(64 * k),
-                       (size_t)(2 * k * I + 4 * 64 * k), st, a2, T,
-                       reinterpret_cast<__half*>(out), dbg ? dbg->slot : nullptr);
+    by_bits(s2.bits, [&](auto bits) {
+      constexpr int B = decltype(bits)::value;
+      hipLaunchKernelGGL((qmoe_fc2_decode<B>), dim3((unsigned)(T * (H / 8))), dim3(64 * k),
+                         (size_t)(2 * k * I + 4 * 64 * k), st, a2, T,
+                         reinterpret_cast<__half*>(out), dbg ? dbg->slot : nullptr);
+    });
     if (dbg) {
       if (dbg->ids) (void)hipMemcpyAsync(dbg->ids, ids, S * 4, hipMemcpyDeviceToDevice, st);
       if (dbg->w) (void)hipMemcpyAsync(dbg->w, wts, S * 4, hipMemcpyDeviceToDevice, st);
@@ -993,18 +1041,26 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
                    go.counts, go.offsets, go.perm, go.items, go.nitems, wts, hbuf, nullptr};
     const int ntg = bm == 32 ? ntg_of<32>() : ntg_of<kMaxBM>();
     const int64_t nt1 = (s1.N + kQBN - 1) / kQBN, ng1 = (nt1 + ntg - 1) / ntg;
-    if (bm == 32)
-      hipLaunchKernelGGL((qmoe_gemm<true, 32>), dim3((unsigned)((items + 7) / 8 * 8 * ng1)), dim3(256), 0, st, a1, ng1, nt1);
-    else
-      hipLaunchKernelGGL((qmoe_gemm<true, kMaxBM>), dim3((unsigned)((items + 7) / 8 * 8 * ng1)), dim3(256), 0, st, a1, ng1, nt1);
+    const dim3 grid1((unsigned)((items + 7) / 8 * 8 * ng1));
+    by_bits(s1.bits, [&](auto bits) {
+      constexpr int B = decltype(bits)::value;
+      if (bm == 32)
+        hipLaunchKernelGGL((qmoe_gemm<true, 32, B>), grid1, dim3(256), 0, st, a1, ng1, nt1);
+      else
+        hipLaunchKernelGGL((qmoe_gemm<true, kMaxBM, B>), grid1, dim3(256), 0, st, a1, ng1, nt1);
+    });
     MoeGemmArgs a2{static_cast<const uint8_t*>(p2.codes), static_cast<const __half*>(p2.scales),
                    hbuf, s2.N, s2.K, s2.row_bytes, s2.nb, s2.bs, k, (int)E,
                    go.counts, go.offsets, go.perm, go.items, go.nitems, wts, nullptr, slots};
     const int64_t nt2 = (s2.N + kQBN - 1) / kQBN, ng2 = (nt2 + ntg - 1) / ntg;
-    if (bm == 32)
-      hipLaunchKernelGGL((qmoe_gemm<false, 32>), dim3((unsigned)((items + 7) / 8 * 8 * ng2)), dim3(256), 0, st, a2, ng2, nt2);
-    else
-      hipLaunchKernelGGL((qmoe_gemm<false, kMaxBM>), dim3((unsigned)((items + 7) / 8 * 8 * ng2)), dim3(256), 0, st, a2, ng2, nt2);
+    const dim3 grid2((unsigned)((items + 7) / 8 * 8 * ng2));
+    by_bits(s2.bits, [&](auto bits) {
+      constexpr int B = decltype(bits)::value;
+      if (bm == 32)
+        hipLaunchKernelGGL((qmoe_gemm<false, 32, B>), grid2, dim3(256), 0, st, a2, ng2, nt2);
+      else
+        hipLaunchKernelGGL((qmoe_gemm<false, kMaxBM, B>), grid2, dim3(256), 0, st, a2, ng2, nt2);
+    });
     hipLaunchKernelGGL(qmoe_combine, dim3((unsigned)((Tt * H / 4 + 255) / 256)), dim3(256), 0, st,
                        slots, Tt, k, H, reinterpret_cast<__half*>(out + t0 * H));
     if (dbg) {

@@ -1,7 +1,7 @@
 /*
  * mnb.h -- C ABI of the block-quantized weight-only matmul library for AMD
  * Instinct MI355X (gfx950): MatMulNBits GEMV / GEMM on packed INT4 weights and
- * a top-k routed INT3 QMoE layer.
+ * a top-k routed QMoE layer with INT3 or INT4 expert projections.
  *
  * Sources (page title, then section):
  *  [PLAN]  "Qwen3 Missing-Kernel Implementation Plan" (onnx-light CPU docs),
@@ -25,12 +25,15 @@
  *          fused interleaved gate/up, block sizes 32/64/128, block-aligned K,
  *          FP16 activations with FP16 scales, H from the activations, I from
  *          the fused FC1 rows; finite nonnegative scales; overflow-checked
- *          byte counts).  Sections "Latest Review Fixes" (N need not be
+ *          byte counts; independent projection widths, (FC1, FC2) in
+ *          {(3,3), (3,4), (4,3)}).  Sections "Latest Review Fixes" (N need not be
  *          aligned) and "Review Fixes and Padding Experiment Follow-up"
  *          (errors are status codes, no exceptions).
  *  [RUN]   same page, PR summary: CUDA QMoE execution with routing, fused
  *          gate/up SwiGLU, independent down projection, aggregation and
- *          bounded activation tiling, without materializing floating weights.
+ *          bounded activation tiling, without materializing floating weights,
+ *          for the width pairs (3,3), (3,4), (4,3); its results table runs
+ *          the all-INT4 (4,4) layer next to (3,3).
  *  [ROUTE] pegainfer PR "feat(qwen4): component kernels extracted from the
  *          brick PRs", section "Description": fp32 softmax, top-k,
  *          renormalized (norm_topk_prob) routing weights; branch combine.
@@ -84,14 +87,15 @@ enum { MNB_ROWS_BLOCKED = 0, MNB_ROWS_ROW_LOCAL = 1 };
  *  dense MatMulNBits [PLAN K01]: bits 4, block_size 32/64/128, scale_dtype
  *    F32, row_layout BLOCKED, num_experts 1, zero points optional, any
  *    K >= 1 and N >= 1;
- *  QMoE projection [P1]: bits 3, block_size 32/64/128, scale_dtype F16,
- *    row_layout ROW_LOCAL, num_experts >= 1, no explicit zero points,
- *    K a multiple of block_size, any N >= 1 (per-expert matrix [N, K]).
+ *  QMoE projection [P1]: bits 3 or 4, block_size 32/64/128, scale_dtype
+ *    F16, row_layout ROW_LOCAL, num_experts >= 1, no explicit zero points
+ *    (implicit 2^(bits-1): 4 or 8), K a multiple of block_size, any N >= 1
+ *    (per-expert matrix [N, K]).
  * accuracy_level must be 0..4; it is recorded, and the numerics are fixed by
  * the kernels (fp32 GEMV, fp16-input MFMA GEMM with fp32 accumulation). */
 typedef struct mnb_desc {
   int32_t abi_version;     /* MNB_ABI_VERSION                               */
-  int32_t bits;            /* 4 (dense) or 3 (QMoE)                          */
+  int32_t bits;            /* 4 (dense); 3 or 4 (QMoE)                       */
   int32_t block_size;      /* codes per scale along K: 32, 64 or 128         */
   int32_t accuracy_level;  /* 0..4                                            */
   int64_t K;               /* reduction length (columns of the logical W)    */
@@ -136,9 +140,10 @@ int32_t mnb_prepacked_size(const mnb_desc* desc, uint64_t* bytes);
 /* One-time preparation of constant weights [PLAN K01]:
  *  1. checks the descriptor and computes every byte count with overflow
  *     checks [P0];
- *  2. validates content: for bits 3, scales must be finite and >= 0 and the
- *     pad bits after K*3 in each row must be zero [P1]; dense INT4 content
- *     is not value-checked (non-finite scales propagate to the outputs);
+ *  2. validates content: for QMoE projections, scales must be finite and
+ *     >= 0 and the pad bits after K*bits in each row must be zero [P1];
+ *     dense INT4 content is not value-checked (non-finite scales propagate
+ *     to the outputs);
  *  3. repacks on the host into the private layout and uploads it to dst_dev
  *     with an asynchronous copy on `stream`, then waits for that stream.
  * Host inputs (read only; any alignment):
@@ -199,7 +204,7 @@ int32_t mnb_gemm(const mnb_plan* plan, int64_t M, const float* A_dev,
                  float* Y_dev, void* ws_dev, uint64_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
- * Top-k routed INT3 QMoE layer [P1][RUN][ROUTE].
+ * Top-k routed QMoE layer with INT3 or INT4 projections [P1][RUN][ROUTE].
  */
 enum { QMOE_ACT_SWIGLU = 1 };
 enum { QMOE_GATE_UP_INTERLEAVED = 1 };
@@ -223,13 +228,15 @@ int32_t qmoe_workspace_size(const mnb_plan* fc1, const mnb_plan* fc2,
 /* One QMoE layer on T tokens.
  *  fc1: QMoE plan with N = 2I, K = H (rows 2i = gate_i, 2i+1 = up_i);
  *  fc2: QMoE plan with N = H, K = I; both with the same num_experts E and
- *       block size.
+ *       block size; each projection has its own width (3 or 4 bits), so the
+ *       pairs (3,3), (3,4), (4,3) and (4,4) all run.
  *  x_dev      fp16 [T, H] activations, 16-byte aligned;
  *  logits_dev fp32 [T, E] router logits;
  *  out_dev    fp16 [T, H], 8-byte aligned (misaligned x or out: INVALID_ARG).
  * Computes, per token: top_k experts by logit (ties: lower index), weights
  * r_j = softmax over the selected logits (= fp32 softmax over all E then
- * renormalization); h = silu(x.W1g^T) * (x.W1u^T) rounded to fp16;
+ * renormalization); weights dequantize as (q - 2^(bits-1)) * s;
+ * h = silu(x.W1g^T) * (x.W1u^T) rounded to fp16;
  * out = fp16(sum_j r_j * h_j.W2^T) summed in rank order.
  * T = 0 is a no-op.  No host synchronisation (graph-capturable).
  * Errors: INVALID_ARG, UNSUPPORTED, STALE_PLAN, WORKSPACE_TOO_SMALL, DEVICE. */

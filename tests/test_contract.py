@@ -89,6 +89,14 @@ def test_descriptor_rejections():
     q = mnb.qmoe_proj_desc(128, 8, 2, 64)
     q.scale_dtype = mnb.MNB_DTYPE_F32
     assert size_status(q) == UNSUP
+    # INT4 QMoE projections (width pairs (3,4), (4,3), (4,4)): same profile
+    assert size_status(mnb.qmoe_proj_desc(2048, 1536, 128, 64, bits=4)) == OK
+    assert size_status(mnb.qmoe_proj_desc(96, 8, 2, 64, bits=4)) == UNSUP  # K not block aligned
+    for bits in (2, 5, 8):
+        assert size_status(mnb.qmoe_proj_desc(128, 8, 2, 64, bits=bits)) == UNSUP
+    q = mnb.qmoe_proj_desc(128, 8, 2, 64, bits=4)
+    q.row_layout = mnb.MNB_ROWS_BLOCKED
+    assert size_status(q) == UNSUP
 
 
 def test_size_overflow_is_detected():
@@ -152,13 +160,32 @@ def test_int3_host_prepack_round_trip_and_n127(orc):
         assert np.array_equal(sc.view(np.uint16), s[e * N:(e + 1) * N].view(np.uint16))
 
 
+@pytest.mark.parametrize("E,N,K,bs", [(3, 127, 256, 64), (2, 16, 128, 32), (1, 5, 384, 128),
+                                      (2, 40, 96, 32)])
+def test_int4_moe_host_prepack_round_trip(orc, E, N, K, bs):
+    """4-bit row-local rows regrouped into the private groups read back as the
+    oracle's codes (low nibble = even position), zero point 8, scales as given."""
+    W = synth.packed_rows(E * N + K, E * N, K, 4)
+    s = synth.scales_f16(5, (E * N, K // bs))
+    desc = mnb.qmoe_proj_desc(K, N, E, bs, bits=4)
+    assert mnb.mnb_prepacked_size(desc) <= W.nbytes + s.nbytes + 768
+    plan, _, _keep = host_prepare(desc, W, s, None)
+    for e in range(E):
+        codes, zeros, sc = mnb.mnb_debug_unpack_host(plan, e, 0, N)
+        ref = np.stack([orc.unpack_bits(W[e * N + r], K, 4) for r in range(N)])
+        assert np.array_equal(codes, ref)
+        assert (zeros == 8).all()
+        assert np.array_equal(sc.view(np.uint16), s[e * N:(e + 1) * N].view(np.uint16))
+
+
+@pytest.mark.parametrize("bits", [3, 4])
 @pytest.mark.parametrize("bad", [np.inf, -np.inf, np.nan, -0.5, -65504.0])
-def test_int3_scale_content_rejected(bad):
+def test_moe_scale_content_rejected(bad, bits):
     E, N, K, bs = 2, 4, 128, 64
-    W = synth.int3_rows(4, E * N, K)
+    W = synth.packed_rows(4, E * N, K, bits)
     s = synth.scales_f16(5, (E * N, K // bs))
     s[3, 1] = np.float16(bad)
-    desc = mnb.qmoe_proj_desc(K, N, E, bs)
+    desc = mnb.qmoe_proj_desc(K, N, E, bs, bits=bits)
     with pytest.raises(mnb.MnbError) as ei:
         host_prepare(desc, W, s, None)
     assert ei.value.status == CONTENT
@@ -250,6 +277,10 @@ def test_qmoe_descriptor_and_shape_checks():
     lib = mnb.lib()
     assert lib.qmoe_forward(ctypes.byref(p1), ctypes.byref(p2), ctypes.byref(q), 0, None, None,
                             None, None, 0, None) == OK  # T = 0: no-op
+    # mixed widths: an INT4 FC2 next to the INT3 FC1 is a valid layer
+    W2b = synth.packed_rows(5, E * H, I, 4)
+    p2b, _, _k4 = host_prepare(mnb.qmoe_proj_desc(I, H, E, bs, bits=4), W2b, s2, None)
+    assert mnb.qmoe_workspace_size(p1, p2b, q, 16) == mnb.qmoe_workspace_size(p1, p2, q, 16)
     # a dense plan is not a QMoE projection
     B, s, _ = dense_inputs(8, 64)
     pd, _, _k3 = host_prepare(mnb.dense_desc(64, 8), B, s, None)

@@ -1,4 +1,5 @@
-"""GPU parity of the INT3 QMoE layer against the fp64 oracle, through the C ABI.
+"""GPU parity of the QMoE layer (INT3, INT4 and mixed-width projections)
+against the fp64 oracle, through the C ABI.
 
 Sources: onnxruntime PR "INT3 QMoE CUDA correctness baseline and Qwen
 experimental results" (routing, fused interleaved gate/up SwiGLU, down
@@ -29,15 +30,16 @@ def say(*a):
 
 
 class Moe:
-    def __init__(self, x, logits, W1, s1, W2, s2, k, bs):
+    def __init__(self, x, logits, W1, s1, W2, s2, k, bs, bits1=3, bits2=3):
         self.E, twoI, _ = W1.shape
         self.I = twoI // 2
         self.H = x.shape[1]
         self.k, self.bs = k, bs
+        self.bits1, self.bits2 = bits1, bits2
         self.host = (W1, s1, W2, s2)
-        self.p1 = mnb.PreparedWeight(mnb.qmoe_proj_desc(self.H, twoI, self.E, bs),
+        self.p1 = mnb.PreparedWeight(mnb.qmoe_proj_desc(self.H, twoI, self.E, bs, bits1),
                                      W1.reshape(self.E * twoI, -1), s1.reshape(self.E * twoI, -1))
-        self.p2 = mnb.PreparedWeight(mnb.qmoe_proj_desc(self.I, self.H, self.E, bs),
+        self.p2 = mnb.PreparedWeight(mnb.qmoe_proj_desc(self.I, self.H, self.E, bs, bits2),
                                      W2.reshape(self.E * self.H, -1), s2.reshape(self.E * self.H, -1))
         self.q = mnb.make_qmoe_desc(k)
 
@@ -70,17 +72,18 @@ class Moe:
 
     def oracle(self, orc, x, logits):
         W1, s1, W2, s2 = self.host
-        return orc.qmoe(x, logits, W1, s1, W2, s2, k=self.k, bs=self.bs, nthreads=8)
+        return orc.qmoe(x, logits, W1, s1, W2, s2, k=self.k, bits1=self.bits1, bits2=self.bits2,
+                        bs=self.bs, nthreads=8)
 
 
-def random_moe(seed, T, H, I, E, k, bs):
+def random_moe(seed, T, H, I, E, k, bs, bits1=3, bits2=3):
     x = synth.activations_f16(synth.seed_for(seed, 1), T, H)
     logits = synth.router_logits(synth.seed_for(seed, 2), T, E)
-    W1 = synth.int3_rows(synth.seed_for(seed, 3), E * 2 * I, H).reshape(E, 2 * I, -1)
+    W1 = synth.packed_rows(synth.seed_for(seed, 3), E * 2 * I, H, bits1).reshape(E, 2 * I, -1)
     s1 = synth.scales_f16(synth.seed_for(seed, 4), (E, 2 * I, H // bs))
-    W2 = synth.int3_rows(synth.seed_for(seed, 5), E * H, I).reshape(E, H, -1)
+    W2 = synth.packed_rows(synth.seed_for(seed, 5), E * H, I, bits2).reshape(E, H, -1)
     s2 = synth.scales_f16(synth.seed_for(seed, 6), (E, H, I // bs))
-    return x, logits, Moe(x, logits, W1, s1, W2, s2, k, bs)
+    return x, logits, Moe(x, logits, W1, s1, W2, s2, k, bs, bits1, bits2)
 
 
 def half_ulp(a, b):
@@ -106,8 +109,8 @@ def check_stages(orc, m, res, o):
     assert (np.abs(res["h"].astype(np.float64) - o["h"]) <= hb).all()
     # FC2 fed the GPU's own h
     W1, s1, W2, s2 = m.host
-    y, yS = orc.qmoe_fc2(res["ids"], res["h"].astype(np.float64), W2, s2, m.H, m.I, m.E, bs=m.bs,
-                         nthreads=8)
+    y, yS = orc.qmoe_fc2(res["ids"], res["h"].astype(np.float64), W2, s2, m.H, m.I, m.E,
+                         bits2=m.bits2, bs=m.bs, nthreads=8)
     r = res["w"].astype(np.float64)[:, :, None]
     err = np.abs(res["slot"].astype(np.float64) - r * y)
     assert (err <= 4e-3 * r * yS + 1e-30).all()
@@ -155,6 +158,53 @@ def test_qmoe_small_shapes_all_outputs(orc, T, H, I, E, k, bs):
     o = m.oracle(orc, x, logits)
     check_end_to_end(res["out"], o)
     check_stages(orc, m, res, o)
+
+
+# Width pairs: each projection carries its own width, (FC1, FC2) in {(3,4),
+# (4,3)} next to (3,3), and the all-INT4 (4,4) layer that the INT3 QMoE page
+# compares against.  Shapes cover the per-slot decode path (T k <= 32) and the
+# grouped path, partial last K chunks (K = 96, 160) and all block sizes.
+@pytest.mark.parametrize("bits1,bits2", [(4, 4), (3, 4), (4, 3)])
+@pytest.mark.parametrize("T,H,I,E,k,bs", [(1, 64, 32, 3, 3, 32), (4, 128, 64, 8, 8, 64),
+                                          (5, 64, 64, 4, 2, 64), (17, 256, 128, 16, 4, 128),
+                                          (33, 128, 96, 6, 6, 32), (64, 192, 160, 12, 8, 32)])
+def test_qmoe_width_pairs_all_outputs(orc, bits1, bits2, T, H, I, E, k, bs):
+    say(f"qmoe widths ({bits1},{bits2}) T={T} H={H} I={I} E={E} k={k} bs={bs}")
+    x, logits, m = random_moe(T * 13 + E + bits1, T, H, I, E, k, bs, bits1, bits2)
+    res = m.run(x, logits, debug=True)
+    o = m.oracle(orc, x, logits)
+    check_end_to_end(res["out"], o)
+    check_stages(orc, m, res, o)
+
+
+@pytest.mark.parametrize("bits1,bits2,T", [(4, 4, 1), (4, 4, 128), (3, 4, 4), (4, 3, 40)])
+def test_qmoe_width_pairs_layer_config_sampled_tokens(orc, bits1, bits2, T):
+    """The layer shape (hidden 2048, 128 experts, intermediate 768, top-8,
+    block 64) with INT4 or mixed-width projections; sampled tokens."""
+    say(f"qmoe layer widths ({bits1},{bits2}) T={T}")
+    H, I, E, k, bs = 2048, 768, 128, 8, 64
+    x, logits, m = random_moe(11 + bits1 + 2 * bits2, T, H, I, E, k, bs, bits1, bits2)
+    res = m.run(x, logits, debug=True)
+    assert np.isfinite(res["out"]).all()
+    rng = np.random.default_rng(T + 1)
+    toks = np.unique(np.concatenate([[0, T - 1], rng.choice(T, min(T, 5), replace=False)]))
+    o = m.oracle(orc, x[toks], logits[toks])
+    check_end_to_end(res["out"][toks], o)
+    sub = {key: res[key][toks] for key in ("ids", "w", "h", "slot")}
+    check_stages(orc, m, sub, o)
+
+
+def test_qmoe_int4_codes_at_zero_point_give_zero():
+    say("qmoe int4 zero invariant")
+    for T in (2, 9):  # per-slot decode path and grouped path
+        H, I, E, k, bs = 128, 64, 4, 4, 64
+        x, logits, _ = random_moe(97, T, H, I, E, k, bs)
+        W1 = np.full((E, 2 * I, H // 2), 0x88, np.uint8)
+        W2 = np.full((E, H, I // 2), 0x88, np.uint8)
+        s1 = synth.scales_f16(94, (E, 2 * I, H // bs))
+        s2 = synth.scales_f16(95, (E, H, I // bs))
+        m = Moe(x, logits, W1, s1, W2, s2, k, bs, 4, 4)
+        assert (m.run(x, logits)["out"] == 0).all()
 
 
 def test_qmoe_more_tokens_than_one_tile(orc):
