@@ -295,6 +295,7 @@ def bench_extras(torch, mnb, dev):
                               "GB/s": round(vb / us / 1e3, 1),
                               "frac_of_hbm_peak": round(vb / us / 1e3 / PEAK_HBM_GBS, 4)}
     del vw
+    log("extras: vocabulary head done")
     # prefill GEMM at M = 16 .. 4096 on both shapes
     pre = {}
     for (K, N) in ((2048, 6144), (6144, 2048)):
@@ -313,10 +314,13 @@ def bench_extras(torch, mnb, dev):
                                        "frac_of_fp16_peak": round(tf / PEAK_FP16_TFLOPS, 4)}
         del w
     out["prefill_gemm"] = pre
+    log("extras: prefill GEMM done")
     # QMoE layer: all-INT3 projections, and the all-INT4 layer the INT3 QMoE
     # page compares it with
     out["qmoe_int3_layer"] = qmoe_extra(torch, dev, 3, 3)
+    log("extras: INT3 QMoE layer done")
     out["qmoe_int4_layer"] = qmoe_extra(torch, dev, 4, 4)
+    log("extras: INT4 QMoE layer done")
     return out
 
 
