@@ -317,14 +317,14 @@ def bench_extras(torch, mnb, dev):
     log("extras: prefill GEMM done")
     # QMoE layer: all-INT3 projections, and the all-INT4 layer the INT3 QMoE
     # page compares it with
-    out["qmoe_int3_layer"] = qmoe_extra(torch, dev, 3, 3)
+    out["qmoe_int3_layer"] = qmoe_extra(torch, mnb, dev, 3, 3)
     log("extras: INT3 QMoE layer done")
-    out["qmoe_int4_layer"] = qmoe_extra(torch, dev, 4, 4)
+    out["qmoe_int4_layer"] = qmoe_extra(torch, mnb, dev, 4, 4)
     log("extras: INT4 QMoE layer done")
     return out
 
 
-def qmoe_extra(torch, dev, bits1, bits2):
+def qmoe_extra(torch, mnb, dev, bits1, bits2):
     """QMoE layer (hidden 2048, 128 experts, intermediate 768, top-8, block 64)
     at T = 1, 128, 512 tokens, from graph replays over 4 weight copies."""
     H, I, E, k, bs = 2048, 768, 128, 8, 64
