@@ -176,3 +176,15 @@ def qmoe_fc2(ids, h, W2, s2, H, I, E, bits2=3, bs=64, nthreads=1):
                               _p(ids), _p(h), _p(W2), _p(s2), _p(y), _p(yS), INT(nthreads)),
            "qmoe_fc2")
     return y, yS
+
+
+def rtn_int3(W, bs):
+    """W: float32 [rows, K].  Returns (B uint8 [rows, ceil(3K/8)], scales
+    float16 [rows, K/bs], status uint8 [rows, K/bs])."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    rows, K = W.shape
+    B = np.zeros((rows, (3 * K + 7) // 8), np.uint8)
+    s = np.zeros((rows, K // bs), np.uint16)
+    st = np.zeros((rows, K // bs), np.uint8)
+    _check(lib().orc_rtn_int3(I64(rows), I64(K), INT(bs), _p(W), _p(B), _p(s), _p(st)), "rtn_int3")
+    return B, s.view(np.float16), st

@@ -376,3 +376,56 @@ int orc_qmoe_fc2(int64_t T, int64_t H, int64_t I, int E, int k, int bits2,
 }
 
 }  // extern "C"
+
+// INT3 RTN producer quantizer ([OLIVE]: scale max|w| / 3.5, zero point 4,
+// all-zero group scale 1 / 3.5 with code 4, non-finite weights and scales
+// that round to zero rejected; [P0]: stored-scale rounding).  The decisions
+// (the scale's fp16 rounding and each code's rounding) are taken in fp32, as
+// a producer working on fp32 weights does; see oracle.h.
+int orc_rtn_int3(int64_t rows, int64_t K, int bs, const float* W, uint8_t* B,
+                 uint16_t* scales, uint8_t* status) {
+  if (rows < 0 || K < 1 || bs < 1 || K % bs || (rows && (!W || !B || !scales || !status)))
+    return -1;
+  const int64_t nb = K / bs, rb = (3 * K + 7) / 8;
+  std::vector<uint8_t> codes(K);
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const float* g = W + r * K + b * bs;
+      bool finite = true;
+      float amax = 0.0f;
+      for (int j = 0; j < bs; ++j) {
+        if (!std::isfinite(g[j]))
+          finite = false;
+        else
+          amax = std::max(amax, std::fabs(g[j]));
+      }
+      uint8_t st = 0;
+      uint16_t s16 = 0;
+      if (!finite) {
+        st = 1;
+      } else if (amax == 0.0f) {
+        s16 = orc_f64_to_f16((double)(1.0f / 3.5f));
+      } else {
+        const float s = amax / 3.5f;
+        s16 = orc_f64_to_f16((double)s);  // fp32 -> fp64 is exact: one rounding
+        if ((s16 & 0x7FFF) == 0) st = 2;
+        else if ((s16 & 0x7FFF) == 0x7C00) st = 3;
+      }
+      if (st) s16 = 0;
+      const float sd = (float)orc_f16_to_f64(s16);
+      for (int j = 0; j < bs; ++j) {
+        int q = 4;
+        if (!st) {
+          const float t = g[j] / sd;
+          q = (int)std::nearbyint(t) + 4;
+          q = std::min(7, std::max(0, q));
+        }
+        codes[b * bs + j] = (uint8_t)q;
+      }
+      scales[r * nb + b] = s16;
+      status[r * nb + b] = st;
+    }
+    if (orc_pack_bits(codes.data(), K, 3, B + r * rb) != 0) return -2;
+  }
+  return 0;
+}

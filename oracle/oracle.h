@@ -16,12 +16,17 @@
  *          experimental results", embedded body of the stacked P0/P1 PR,
  *          section "P0: Portable Format and Numerical References" (row-local
  *          LSB-first UINT8 packing for widths 1..8, canonical padding, INT3
- *          offset-4 decoding, tiny predetermined-route SwiGLU MoE).
+ *          offset-4 decoding, deterministic RTN with stored-scale
+ *          rounding and subnormal-underflow reporting, tiny
+ *          predetermined-route SwiGLU MoE).
  *  [P1]    same body, section "P1: Compatible QMoE v1 Extension" (fused
  *          interleaved gate/up, activation_type swiglu, block sizes 32/64/128,
  *          I inferred from the fused FC1 rows).
  *  [OLIVE] same page, embedded Olive body ("Summary"): INT3 dequantization is
- *          (code - 4) * scale with implicit zero point 4.
+ *          (code - 4) * scale with implicit zero point 4; the symmetric RTN
+ *          scale policy max|w| / 3.5, all-zero groups with scale 1 / 3.5 and
+ *          code 4, and rejection of non-finite weights and of scales that
+ *          round to zero for a nonzero group.
  *  [ROUTE] pegainfer PR "feat(qwen4): component kernels extracted from the
  *          brick PRs", section "Description": MoE routing is an fp32 softmax,
  *          top-k, then renormalization of the selected probabilities
@@ -95,6 +100,21 @@ int orc_qmoe(int64_t T, int64_t H, int64_t I, int E, int k, int bits1,
 int orc_qmoe_fc2(int64_t T, int64_t H, int64_t I, int E, int k, int bits2,
                  int bs, const int32_t* ids, const double* h, const uint8_t* W2,
                  const uint16_t* s2, double* y, double* yS, int nthreads);
+
+/* ---- INT3 round-to-nearest producer quantizer [P0][OLIVE] -----------------
+ * W fp32 [rows, K], K a multiple of bs.  Per group of bs consecutive k of a
+ * row: amax = max |w|; the scale is fp16(amax / 3.5) with the division done
+ * in fp32 and the quotient rounded once to fp16 (the stored scale), or
+ * fp16(fp32(1 / 3.5)) for an all-zero group; each code is
+ * q = clamp(rint(w / s) + 4, 0, 7) with w / s an fp32 division by the STORED
+ * scale (stored-scale rounding) and rint rounding ties to even.
+ * Outputs: B uint8 [rows, ceil(3K/8)] row-local LSB-first; scales fp16
+ * [rows, K/bs]; status uint8 [rows, K/bs]: 0 ok, 1 a weight is NaN or
+ * infinite, 2 a nonzero group whose scale rounds to zero, 3 a scale beyond
+ * the fp16 range.  A group with a nonzero status gets scale 0 and codes 4.
+ * Returns 0 (also when a status is nonzero), negative on bad arguments.    */
+int orc_rtn_int3(int64_t rows, int64_t K, int bs, const float* W, uint8_t* B,
+                 uint16_t* scales, uint8_t* status);
 
 #ifdef __cplusplus
 }

@@ -36,3 +36,21 @@ def gemv_closed_forms():
 
 def tiny_moe():
     return {k: v for k, v in _lines("tiny_moe.txt")}
+
+
+def _values(text):
+    out = []
+    for part in text.split(","):
+        part = part.strip()
+        if "x" in part:
+            n, v = part.split("x")
+            out += [float(v)] * int(n)
+        else:
+            out.append(float(part))
+    return out
+
+
+def rtn_int3():
+    """[(name, weights, scale bits, status, bytes)] from rtn_int3.txt."""
+    return [(n, _values(w), int(s, 16), int(st), bytes.fromhex(b))
+            for n, w, s, st, b in _lines("rtn_int3.txt")]
