@@ -321,6 +321,8 @@ def bench_extras(torch, mnb, dev):
     log("extras: INT3 QMoE layer done")
     out["qmoe_int4_layer"] = qmoe_extra(torch, mnb, dev, 4, 4)
     log("extras: INT4 QMoE layer done")
+    out["int3_rtn_quantizer"] = rtn_extra(torch, mnb, dev)
+    log("extras: INT3 RTN quantizer done")
     return out
 
 
@@ -358,6 +360,26 @@ def qmoe_extra(torch, mnb, dev, bits1, bits2):
                         "TFLOP/s": round(2.0 * T * k * (2 * I * H + H * I) / us / 1e6, 2)}
     del experts
     return moe
+
+
+
+def rtn_extra(torch, mnb, dev):
+    """Producer-side INT3 RTN quantizer on the QMoE layer's FC1 stack (128
+    experts x 1536 rows, K = 2048, block 64) from fp32 weights in HBM; bytes =
+    fp32 weights read + codes, scales and status written."""
+    rows, K, bs = 128 * 1536, 2048, 64
+    gen = torch.Generator(device=dev).manual_seed(5)
+    W = torch.randn((rows, K), generator=gen, device=dev, dtype=torch.float32) * 0.02
+    B = torch.empty((rows, 3 * K // 8), dtype=torch.uint8, device=dev)
+    s = torch.empty((rows, K // bs), dtype=torch.float16, device=dev)
+    st = torch.empty((rows, K // bs), dtype=torch.uint8, device=dev)
+    call = lambda: mnb.mnb_quantize_int3_rtn(W, rows, K, bs, B, s, st)
+    us = 1e3 * graph_time(torch, [call], 3, min_calls=8)
+    byts = rows * K * 4 + rows * 3 * K // 8 + rows * (K // bs) * 3
+    res = {"rows": rows, "K": K, "block_size": bs, "us": round(us, 2),
+           "GB/s": round(byts / us / 1e3, 1), "frac_of_hbm_peak": round(byts / us / 1e3 / PEAK_HBM_GBS, 4)}
+    del W, B, s, st
+    return res
 
 
 if __name__ == "__main__":

@@ -296,6 +296,29 @@ int32_t qmoe_forward_debug(const mnb_plan* fc1, const mnb_plan* fc2, const qmoe_
   })
 }
 
+int32_t mnb_quantize_int3_rtn(const float* W_dev, int64_t rows, int64_t K, int32_t block_size,
+                              uint8_t* B_dev, uint16_t* scales_dev, uint8_t* status_dev,
+                              void* stream) {
+  MNB_GUARD({
+    if (rows < 0 || K < 1 || block_size < 1) return MNB_ERR_INVALID_ARG;
+    if (block_size != 32 && block_size != 64 && block_size != 128) return MNB_ERR_UNSUPPORTED;
+    if (K % block_size) return MNB_ERR_UNSUPPORTED;
+    uint64_t n;
+    if (__builtin_mul_overflow((uint64_t)rows, (uint64_t)K, &n) || n > (uint64_t)INT64_MAX / 4)
+      return MNB_ERR_SIZE_OVERFLOW;
+    if (rows == 0) return MNB_OK;
+    if (n / 8 / 256 >= (uint64_t)UINT32_MAX) return MNB_ERR_UNSUPPORTED;  // grid size
+    if (!W_dev || !B_dev || !scales_dev || !status_dev) return MNB_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(W_dev) % 16 || reinterpret_cast<uintptr_t>(B_dev) % 4 ||
+        reinterpret_cast<uintptr_t>(scales_dev) % 2)
+      return MNB_ERR_INVALID_ARG;
+    if (launch_rtn_int3(W_dev, rows, K, block_size, B_dev, scales_dev, status_dev,
+                        static_cast<hipStream_t>(stream)) != hipSuccess)
+      return MNB_ERR_DEVICE;
+    return MNB_OK;
+  })
+}
+
 int32_t mnb_debug_unpack_host(const mnb_plan* plan, int64_t expert, int64_t row0, int64_t nrows,
                               uint8_t* codes, uint8_t* zeros, void* scales) {
   MNB_GUARD({

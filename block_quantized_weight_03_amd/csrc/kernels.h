@@ -47,6 +47,12 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2,
                        const float* logits, uint16_t* out, void* ws, hipStream_t st,
                        const QmoeDebug* dbg);
 
+// ---- producer-side INT3 RTN quantizer (quant.hip) ---------------------------
+// W fp32 [rows, K] (16-byte aligned), K % bs == 0, bs in {32, 64, 128};
+// B [rows, 3K/8] (4-byte aligned), scales fp16 and status uint8 [rows, K/bs]
+hipError_t launch_rtn_int3(const float* W, int64_t rows, int64_t K, int bs, uint8_t* B,
+                           uint16_t* scales, uint8_t* status, hipStream_t st);
+
 // ---- test-only readers of the device layout (debug.hip) --------------------
 hipError_t launch_debug_unpack(const Sizes& s, const mnb_plan& p, int64_t expert,
                                int64_t row0, int64_t nrows, uint8_t* codes, hipStream_t st);

@@ -19,7 +19,7 @@
  *          experimental results", embedded body of the stacked P0/P1 PR,
  *          section "P0: Portable Format and Numerical References": row-local
  *          LSB-first UINT8 packing, checked size arithmetic, canonical
- *          padding, INT3 offset-4 decoding.
+ *          padding, INT3 offset-4 decoding, RTN with stored-scale rounding.
  *  [P1]    same body, section "P1: Compatible QMoE v1 Extension": INT3 QMoE
  *          profile (quant_type int, weights_prepacked 0, activation swiglu,
  *          fused interleaved gate/up, block sizes 32/64/128, block-aligned K,
@@ -34,6 +34,10 @@
  *          bounded activation tiling, without materializing floating weights,
  *          for the width pairs (3,3), (3,4), (4,3); its results table runs
  *          the all-INT4 (4,4) layer next to (3,3).
+ *  [OLIVE] same page, embedded Olive body ("Summary"): symmetric INT3 RTN
+ *          with scale max|w| / 3.5, zero point 4, all-zero groups at scale
+ *          1 / 3.5 and code 4; non-finite weights and unrepresentable scales
+ *          reported rather than clamped.
  *  [ROUTE] pegainfer PR "feat(qwen4): component kernels extracted from the
  *          brick PRs", section "Description": fp32 softmax, top-k,
  *          renormalized (norm_topk_prob) routing weights; branch combine.
@@ -244,6 +248,35 @@ int32_t qmoe_forward(const mnb_plan* fc1, const mnb_plan* fc2,
                      const qmoe_desc* q, int64_t T, const uint16_t* x_dev,
                      const float* logits_dev, uint16_t* out_dev, void* ws_dev,
                      uint64_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Producer-side INT3 round-to-nearest quantizer [P0][OLIVE]: fp32 weights to
+ * the QMoE projection contract (codes and scales ready for mnb_prepare with
+ * bits 3, ROW_LOCAL, F16 scales).  Per group of block_size consecutive k of a
+ * row: amax = max |w|; stored scale s = fp16(amax / 3.5) (fp32 quotient,
+ * rounded once to fp16), or fp16(1 / 3.5) for an all-zero group; codes
+ * q = clamp(rint(w / s) + 4, 0, 7) divided by the STORED scale in fp32,
+ * ties to even (stored-scale rounding).  Decoding is (q - 4) * s.
+ *  W_dev      fp32 [rows, K] row-major, 16-byte aligned (rows = E * N for a
+ *             stacked projection);
+ *  B_dev      uint8 [rows, 3K/8] out, row-local LSB-first 3-bit codes, 4-byte
+ *             aligned;
+ *  scales_dev fp16 [rows, K/block_size] out, 2-byte aligned;
+ *  status_dev uint8 [rows, K/block_size] out: 0 ok, 1 a weight is NaN or
+ *             infinite, 2 a nonzero group whose scale rounds to zero, 3 a
+ *             scale beyond the fp16 range.  A group with a nonzero status is
+ *             written with scale 0 and codes 4 and must be treated as a
+ *             rejected tensor [OLIVE: fail fast, never clamp a scale];
+ *             nonzero subnormal scales are status 0.
+ * block_size 32, 64 or 128; K a multiple of it.  Asynchronous on `stream`:
+ * the caller reads status_dev after the stream has finished.  rows = 0 is a
+ * no-op.  Deterministic.  Errors: INVALID_ARG (NULL or misaligned pointers,
+ * negative sizes), UNSUPPORTED (block size, K not block aligned),
+ * SIZE_OVERFLOW, DEVICE. */
+int32_t mnb_quantize_int3_rtn(const float* W_dev, int64_t rows, int64_t K,
+                              int32_t block_size, uint8_t* B_dev,
+                              uint16_t* scales_dev, uint8_t* status_dev,
+                              void* stream);
 
 #ifdef __cplusplus
 }

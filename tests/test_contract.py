@@ -300,3 +300,21 @@ def test_gemv_multi_argument_checks_before_any_device_call():
     assert status_of(mnb.mnb_gemv_multi, [p1, p1], a, [y, None], None, 0, 0) == INVALID
     assert status_of(mnb.mnb_gemv_multi, [p1, p2], a, [y, y], None, 0, 0) == INVALID
     assert status_of(mnb.mnb_gemv_multi, [p1, p2], None, [y, y], None, 0, 0) == INVALID
+
+
+def test_quantizer_argument_checks_before_any_device_call():
+    """Every check of mnb_quantize_int3_rtn runs on the host before a launch."""
+    lib = mnb.lib()
+    f = lib.mnb_quantize_int3_rtn
+    assert f(None, 0, 64, 32, None, None, None, None) == OK  # rows = 0: no-op
+    assert f(16, 4, 64, 48, 16, 16, 16, None) == UNSUP      # block size
+    assert f(16, 4, 96, 64, 16, 16, 16, None) == UNSUP      # K not block aligned
+    assert f(16, 4, 64, 0, 16, 16, 16, None) == INVALID
+    assert f(16, -1, 64, 32, 16, 16, 16, None) == INVALID
+    assert f(16, 4, 0, 32, 16, 16, 16, None) == INVALID
+    assert f(None, 4, 64, 32, 16, 16, 16, None) == INVALID  # null weights
+    assert f(16, 4, 64, 32, 16, None, 16, None) == INVALID  # null scales
+    assert f(8, 4, 64, 32, 16, 16, 16, None) == INVALID     # weights not 16-byte aligned
+    assert f(16, 4, 64, 32, 18, 16, 16, None) == INVALID    # codes not 4-byte aligned
+    assert f(16, 4, 64, 32, 16, 17, 16, None) == INVALID    # scales not 2-byte aligned
+    assert f(16, 2 ** 40, 2 ** 30, 32, 16, 16, 16, None) == OVERFLOW
