@@ -139,14 +139,20 @@ def route(logits, k):
     return ids, w
 
 
-def qmoe(x_f16, logits, W1, s1, W2, s2, k=8, bits1=3, bits2=3, bs=64, nthreads=1):
-    """x_f16: float16 [T,H]; s1, s2: float16.  Returns a dict of every output."""
+def _f16_or_none(b):
+    return None if b is None else np.ascontiguousarray(b, dtype=np.float16).view(np.uint16)
+
+
+def qmoe(x_f16, logits, W1, s1, W2, s2, k=8, bits1=3, bits2=3, bs=64, nthreads=1, b1=None, b2=None):
+    """x_f16: float16 [T,H]; s1, s2: float16; optional biases b1 float16 [E,2I]
+    and b2 float16 [E,H].  Returns a dict of every output."""
     x = np.ascontiguousarray(x_f16, dtype=np.float16).view(np.uint16)
     logits = np.ascontiguousarray(logits, dtype=np.float32)
     W1 = np.ascontiguousarray(W1, dtype=np.uint8)
     W2 = np.ascontiguousarray(W2, dtype=np.uint8)
     s1 = np.ascontiguousarray(s1, dtype=np.float16).view(np.uint16)
     s2 = np.ascontiguousarray(s2, dtype=np.float16).view(np.uint16)
+    b1, b2 = _f16_or_none(b1), _f16_or_none(b2)
     T, H = x.shape
     E = W1.shape[0]
     I = W1.shape[1] // 2
@@ -156,24 +162,26 @@ def qmoe(x_f16, logits, W1, s1, W2, s2, k=8, bits1=3, bits2=3, bs=64, nthreads=1
              gs=np.zeros((T, k, I)), us=np.zeros((T, k, I)))
     _check(lib().orc_qmoe(I64(T), I64(H), I64(I), INT(E), INT(k), INT(bits1), INT(bits2),
                           INT(bs), _p(x), _p(logits), _p(W1), _p(s1), _p(W2), _p(s2),
-                          _p(o["out16"]), _p(o["out64"]), _p(o["S"]), _p(o["ids"]), _p(o["r"]),
+                          _p(b1), _p(b2), _p(o["out16"]), _p(o["out64"]), _p(o["S"]), _p(o["ids"]), _p(o["r"]),
                           _p(o["g"]), _p(o["u"]), _p(o["h"]), _p(o["gs"]), _p(o["us"]),
                           INT(nthreads)), "qmoe")
     o["out"] = o["out16"].view(np.float16)
     return o
 
 
-def qmoe_fc2(ids, h, W2, s2, H, I, E, bits2=3, bs=64, nthreads=1):
+def qmoe_fc2(ids, h, W2, s2, H, I, E, bits2=3, bs=64, nthreads=1, b2=None):
     """h: fp64 [T,k,I].  Returns (y [T,k,H], yS [T,k,H])."""
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     h = np.ascontiguousarray(h, dtype=np.float64)
     W2 = np.ascontiguousarray(W2, dtype=np.uint8)
     s2 = np.ascontiguousarray(s2, dtype=np.float16).view(np.uint16)
+    b2 = _f16_or_none(b2)
     T, k = ids.shape
     y = np.zeros((T, k, H))
     yS = np.zeros((T, k, H))
     _check(lib().orc_qmoe_fc2(I64(T), I64(H), I64(I), INT(E), INT(k), INT(bits2), INT(bs),
-                              _p(ids), _p(h), _p(W2), _p(s2), _p(y), _p(yS), INT(nthreads)),
+                              _p(ids), _p(h), _p(W2), _p(s2), _p(b2), _p(y), _p(yS),
+                              INT(nthreads)),
            "qmoe_fc2")
     return y, yS
 

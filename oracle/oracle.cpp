@@ -262,7 +262,8 @@ int orc_route(int64_t T, int E, int k, const float* logits, int32_t* ids,
 int orc_qmoe(int64_t T, int64_t H, int64_t I, int E, int k, int bits1,
              int bits2, int bs, const uint16_t* x, const float* logits,
              const uint8_t* W1, const uint16_t* s1, const uint8_t* W2,
-             const uint16_t* s2, uint16_t* out16, double* out64, double* S,
+             const uint16_t* s2, const uint16_t* b1, const uint16_t* b2,
+             uint16_t* out16, double* out64, double* S,
              int32_t* ids, double* r, double* g, double* u, double* h,
              double* gs, double* us, int nthreads) {
   if (T < 0 || H < 1 || I < 1 || E < 1 || k < 1 || k > E || !bits_ok(bits1) ||
@@ -291,7 +292,14 @@ int orc_qmoe(int64_t T, int64_t H, int64_t I, int E, int k, int bits1,
           const int64_t rg = e * 2 * I + 2 * i, ru = rg + 1;
           moe_row(W1 + rg * rb1, s1 + rg * nb1, H, bits1, bs, wg.data());
           moe_row(W1 + ru * rb1, s1 + ru * nb1, H, bits1, bs, wu.data());
+          // an optional bias is one more product term, 1 * b ([P1] optional biases)
           double gg = 0, uu = 0, sg = 0, su = 0;
+          if (b1) {
+            gg = orc_f16_to_f64(b1[rg]);
+            uu = orc_f16_to_f64(b1[ru]);
+            sg = std::fabs(gg);
+            su = std::fabs(uu);
+          }
           for (int64_t c = 0; c < H; ++c) {
             gg += xd[(size_t)c] * wg[(size_t)c];
             uu += xd[(size_t)c] * wu[(size_t)c];
@@ -308,6 +316,10 @@ int orc_qmoe(int64_t T, int64_t H, int64_t I, int E, int k, int bits1,
           const int64_t row = e * H + n;
           moe_row(W2 + row * rb2, s2 + row * nb2, I, bits2, bs, w2.data());
           double y = 0, sy = 0;
+          if (b2) {
+            y = orc_f16_to_f64(b2[row]);
+            sy = std::fabs(y);
+          }
           for (int64_t i = 0; i < I; ++i) {
             const double gi = gv[(size_t)i], ui = uv[(size_t)i];
             const double sgm = sigmoid(gi);
@@ -346,7 +358,8 @@ int orc_qmoe(int64_t T, int64_t H, int64_t I, int E, int k, int bits1,
 
 int orc_qmoe_fc2(int64_t T, int64_t H, int64_t I, int E, int k, int bits2,
                  int bs, const int32_t* ids, const double* h, const uint8_t* W2,
-                 const uint16_t* s2, double* y, double* yS, int nthreads) {
+                 const uint16_t* s2, const uint16_t* b2, double* y, double* yS,
+                 int nthreads) {
   if (T < 0 || H < 1 || I < 1 || E < 1 || k < 1 || !bits_ok(bits2) || bs < 1 || I % bs)
     return -1;
   if (T == 0) return 0;
@@ -363,6 +376,10 @@ int orc_qmoe_fc2(int64_t T, int64_t H, int64_t I, int E, int k, int bits2,
         const int64_t row = e * H + n;
         moe_row(W2 + row * rb2, s2 + row * nb2, I, bits2, bs, w2.data());
         double acc = 0, sa = 0;
+        if (b2) {
+          acc = orc_f16_to_f64(b2[row]);
+          sa = std::fabs(acc);
+        }
         for (int64_t i = 0; i < I; ++i) {
           acc += hv[i] * w2[(size_t)i];
           sa += std::fabs(hv[i] * w2[(size_t)i]);

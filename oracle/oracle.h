@@ -83,7 +83,10 @@ int orc_route(int64_t T, int E, int k, const float* logits, int32_t* ids,
  * x fp16 [T,H]; logits fp32 [T,E];
  * W1 uint8 [E, 2I, ceil(bits1*H/8)], rows 2i = gate_i and 2i+1 = up_i;
  * s1 fp16 [E, 2I, H/bs]; W2 uint8 [E, H, ceil(bits2*I/8)]; s2 fp16 [E, H, I/bs];
- * implicit zero points 2^(bits-1).
+ * implicit zero points 2^(bits-1); optional biases ([P1] "optional biases";
+ * NULL = none): b1 fp16 [E, 2I] added to the gate/up rows before SwiGLU, b2
+ * fp16 [E, H] added to each expert's FC2 output before its routing weight;
+ * a bias counts as one more product term (1 * b) in the tolerance sums.
  * Outputs (any may be NULL): out16 fp16 [T,H]; out64 fp64 [T,H]; S fp64 [T,H]
  * (first-order tolerance sum, see orc_qmoe in oracle.cpp); ids int32 [T,k];
  * r fp64 [T,k]; g, u, h fp64 [T,k,I]; gs, us fp64 [T,k,I] (sum_k |x*w1| for
@@ -91,15 +94,18 @@ int orc_route(int64_t T, int E, int k, const float* logits, int32_t* ids,
 int orc_qmoe(int64_t T, int64_t H, int64_t I, int E, int k, int bits1,
              int bits2, int bs, const uint16_t* x, const float* logits,
              const uint8_t* W1, const uint16_t* s1, const uint8_t* W2,
-             const uint16_t* s2, uint16_t* out16, double* out64, double* S,
+             const uint16_t* s2, const uint16_t* b1, const uint16_t* b2,
+             uint16_t* out16, double* out64, double* S,
              int32_t* ids, double* r, double* g, double* u, double* h,
              double* gs, double* us, int nthreads);
 
 /* FC2 alone on caller-supplied fp64 activations h [T,k,I] for stage checks:
- * y fp64 [T,k,H] = h . w2[ids]^T and yS = sum_i |h_i * w2[n,i]|.           */
+ * y fp64 [T,k,H] = h . w2[ids]^T (+ b2[ids]) and yS = sum_i |h_i * w2[n,i]|
+ * (+ |b2|); b2 fp16 [E, H] or NULL.                                        */
 int orc_qmoe_fc2(int64_t T, int64_t H, int64_t I, int E, int k, int bits2,
                  int bs, const int32_t* ids, const double* h, const uint8_t* W2,
-                 const uint16_t* s2, double* y, double* yS, int nthreads);
+                 const uint16_t* s2, const uint16_t* b2, double* y, double* yS,
+                 int nthreads);
 
 /* ---- INT3 round-to-nearest producer quantizer [P0][OLIVE] -----------------
  * W fp32 [rows, K], K a multiple of bs.  Per group of bs consecutive k of a

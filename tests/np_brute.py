@@ -67,7 +67,8 @@ def softmax(v):
     return e / e.sum(axis=-1, keepdims=True)
 
 
-def qmoe_all_experts(x16, logits, W1, s1, W2, s2, k: int, bs: int, bits1: int = 3, bits2: int = 3):
+def qmoe_all_experts(x16, logits, W1, s1, W2, s2, k: int, bs: int, bits1: int = 3, bits2: int = 3,
+                     b1=None, b2=None):
     """Every expert evaluated for every token, then a k-hot mask of the
     renormalized top-k probabilities selects the mixture."""
     T, H = x16.shape
@@ -86,7 +87,12 @@ def qmoe_all_experts(x16, logits, W1, s1, W2, s2, k: int, bs: int, bits1: int = 
     for e in range(E):
         G = x @ w1[e, 0::2].T                 # [T, I]
         U = x @ w1[e, 1::2].T
+        if b1 is not None:
+            G = G + b1[e, 0::2].astype(np.float64)
+            U = U + b1[e, 1::2].astype(np.float64)
         Hh = G / (1.0 + np.exp(-G)) * U
         Y = Hh @ w2[e].T                      # [T, H]
+        if b2 is not None:
+            Y = Y + b2[e].astype(np.float64)
         out += rw[:, e:e + 1] * Y
     return out, order, np.take_along_axis(rw, order, axis=1)

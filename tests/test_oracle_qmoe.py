@@ -217,3 +217,53 @@ def test_qmoe_int4_codes_at_zero_point_give_zero(orc):
         e = o["ids"][0, j]
         np.testing.assert_allclose(o["g"][0, j], s1[e, 0::2].astype(np.float64).sum(axis=1) * bs,
                                    rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Optional biases (P1 section of the INT3 QMoE page: optional biases).  FC1's
+# bias is added to the gate and up rows before SwiGLU, FC2's to each expert's
+# output before its routing weight.
+# ---------------------------------------------------------------------------
+
+def _biases(seed, E, I, H):
+    b1 = synth.activations_f16(seed, E, 2 * I) * np.float16(0.5)
+    b2 = synth.activations_f16(seed + 1, E, H) * np.float16(0.25)
+    return b1, b2
+
+
+@pytest.mark.parametrize("bits1,bits2", [(3, 3), (4, 4), (3, 4)])
+def test_qmoe_biases_brute_force(orc, bits1, bits2):
+    T, H, I, E, k, bs = 5, 64, 64, 6, 2, 32
+    x, logits, W1, s1, W2, s2 = _random_moe_bits(71 + bits1, T, H, I, E, bs, bits1, bits2)
+    b1, b2 = _biases(5, E, I, H)
+    o = orc.qmoe(x, logits, W1, s1, W2, s2, k=k, bits1=bits1, bits2=bits2, bs=bs, b1=b1, b2=b2)
+    ref, _, _ = qmoe_all_experts(x, logits, W1, s1, W2, s2, k, bs, bits1, bits2, b1, b2)
+    np.testing.assert_allclose(o["out64"], ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max())
+    plain = orc.qmoe(x, logits, W1, s1, W2, s2, k=k, bits1=bits1, bits2=bits2, bs=bs)
+    assert np.abs(plain["out64"] - o["out64"]).max() > 1e-2  # the biases matter
+    # the tolerance sums grow by exactly the bias magnitudes (one more term each)
+    ids = o["ids"]
+    np.testing.assert_allclose(o["gs"] - plain["gs"],
+                               np.abs(b1[ids][:, :, 0::2].astype(np.float64)), rtol=1e-12, atol=1e-15)
+
+
+def test_qmoe_biases_closed_forms(orc):
+    """With every code at the zero point the weights vanish: g and u are the
+    FC1 biases, and the layer output is sum_j r_j b2[e_j]."""
+    T, H, I, E, k, bs = 3, 64, 32, 4, 2, 32
+    x, logits, W1, s1, W2, s2 = _random_moe_bits(91, T, H, I, E, bs, 4, 4)
+    b1, b2 = _biases(9, E, I, H)
+    z1, z2 = np.full_like(W1, 0x88), np.full_like(W2, 0x88)
+    o = orc.qmoe(x, logits, z1, s1, z2, s2, k=k, bits1=4, bits2=4, bs=bs, b1=b1, b2=b2)
+    ids = o["ids"]
+    np.testing.assert_array_equal(o["g"], b1[ids][:, :, 0::2].astype(np.float64))
+    np.testing.assert_array_equal(o["u"], b1[ids][:, :, 1::2].astype(np.float64))
+    want = (o["r"][:, :, None] * b2[ids].astype(np.float64)).sum(axis=1)
+    np.testing.assert_allclose(o["out64"], want, rtol=1e-15, atol=1e-18)
+    # FC1 weights at the zero point, FC2 real: h = silu(b_g) b_u enters FC2
+    o = orc.qmoe(x, logits, z1, s1, W2, s2, k=k, bits1=4, bits2=4, bs=bs, b1=b1, b2=b2)
+    g, u = o["g"], o["u"]
+    np.testing.assert_allclose(o["h"], g / (1 + np.exp(-g)) * u, rtol=1e-14)
+    y, _ = orc.qmoe_fc2(ids, o["h"], W2, s2, H, I, E, bits2=4, bs=bs, b2=b2)
+    np.testing.assert_allclose((o["r"][:, :, None] * y).sum(axis=1), o["out64"], rtol=1e-12,
+                               atol=1e-15)
