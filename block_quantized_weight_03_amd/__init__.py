@@ -82,7 +82,9 @@ SIGNATURES = {
     "mnb_debug_unpack_host": [_PPLAN, _I64, _I64, _I64, _P, _P, _P],
     "mnb_debug_unpack": [_PPLAN, _I64, _I64, _I64, _P, _P],
     "mnb_debug_dequant_f16": [_PPLAN, _I64, _I64, _I64, _P, _P],
-    "qmoe_forward_debug": [_PPLAN, _PPLAN, _PQ, _I64, _P, _P, _P, _P, _U64, _P, _P, _P, _P, _P],
+    "qmoe_forward_biased": [_PPLAN, _PPLAN, _PQ, _I64, _P, _P, _P, _P, _P, _P, _U64, _P],
+    "qmoe_forward_debug": [_PPLAN, _PPLAN, _PQ, _I64, _P, _P, _P, _P, _P, _P, _U64, _P, _P, _P, _P,
+                           _P],
     "mnb_quantize_int3_rtn": [_P, _I64, _I64, ctypes.c_int32, _P, _P, _P, _P],
 }
 
@@ -260,10 +262,20 @@ def quantize_int3_rtn(W, block_size: int = 64, stream=None):
     return B, s
 
 
+def qmoe_forward_biased(fc1: mnb_plan, fc2: mnb_plan, q: qmoe_desc, T: int, x_dev, logits_dev,
+                        fc1_bias_dev, fc2_bias_dev, out_dev, ws_dev, ws_bytes: int, stream=None):
+    _check(lib().qmoe_forward_biased(ctypes.byref(fc1), ctypes.byref(fc2), ctypes.byref(q), T,
+                                     _ptr(x_dev), _ptr(logits_dev), _ptr(fc1_bias_dev),
+                                     _ptr(fc2_bias_dev), _ptr(out_dev), _ptr(ws_dev), ws_bytes,
+                                     _stream(stream)), "qmoe_forward_biased")
+
+
 def qmoe_forward_debug(fc1, fc2, q, T, x_dev, logits_dev, out_dev, ws_dev, ws_bytes, stream=None,
-                       ids_dev=None, w_dev=None, h_dev=None, slot_dev=None):
+                       ids_dev=None, w_dev=None, h_dev=None, slot_dev=None, fc1_bias_dev=None,
+                       fc2_bias_dev=None):
     _check(lib().qmoe_forward_debug(ctypes.byref(fc1), ctypes.byref(fc2), ctypes.byref(q), T,
-                                    _ptr(x_dev), _ptr(logits_dev), _ptr(out_dev), _ptr(ws_dev),
+                                    _ptr(x_dev), _ptr(logits_dev), _ptr(fc1_bias_dev),
+                                    _ptr(fc2_bias_dev), _ptr(out_dev), _ptr(ws_dev),
                                     ws_bytes, _stream(stream), _ptr(ids_dev), _ptr(w_dev),
                                     _ptr(h_dev), _ptr(slot_dev)), "qmoe_forward_debug")
 

@@ -252,8 +252,9 @@ int32_t qmoe_workspace_size(const mnb_plan* fc1, const mnb_plan* fc2, const qmoe
 }
 
 static int32_t qmoe_common(const mnb_plan* fc1, const mnb_plan* fc2, const qmoe_desc* q,
-                           int64_t T, const uint16_t* x, const float* logits, uint16_t* out,
-                           void* ws, uint64_t ws_bytes, void* stream, const QmoeDebug* dbg) {
+                           int64_t T, const uint16_t* x, const float* logits, const uint16_t* b1,
+                           const uint16_t* b2, uint16_t* out, void* ws, uint64_t ws_bytes,
+                           void* stream, const QmoeDebug* dbg) {
   Sizes s1, s2;
   int32_t rc = check_qmoe(fc1, fc2, q, T, &s1, &s2);
   if (rc != MNB_OK) return rc;
@@ -265,12 +266,13 @@ static int32_t qmoe_common(const mnb_plan* fc1, const mnb_plan* fc2, const qmoe_
   if (!x || !logits || !out) return MNB_ERR_INVALID_ARG;
   // the kernels move x rows in 16-byte and outputs in 8-byte pieces
   if ((reinterpret_cast<uintptr_t>(x) & 15) || (reinterpret_cast<uintptr_t>(out) & 7) ||
-      (reinterpret_cast<uintptr_t>(logits) & 3))
+      (reinterpret_cast<uintptr_t>(logits) & 3) || (reinterpret_cast<uintptr_t>(b1) & 1) ||
+      (reinterpret_cast<uintptr_t>(b2) & 1))
     return MNB_ERR_INVALID_ARG;
   if ((rc = check_ws(ws, ws_bytes, qmoe_ws_bytes(s1, s2, q->top_k, T))) != MNB_OK) return rc;
   if ((rc = check_device(fc1)) != MNB_OK) return rc;
   if ((rc = check_device(fc2)) != MNB_OK) return rc;
-  if (launch_qmoe(s1, *fc1, s2, *fc2, q->top_k, T, x, logits, out, ws,
+  if (launch_qmoe(s1, *fc1, s2, *fc2, q->top_k, T, x, logits, b1, b2, out, ws,
                   static_cast<hipStream_t>(stream), dbg) != hipSuccess)
     return MNB_ERR_DEVICE;
   return MNB_OK;
@@ -280,19 +282,30 @@ int32_t qmoe_forward(const mnb_plan* fc1, const mnb_plan* fc2, const qmoe_desc* 
                      const uint16_t* x_dev, const float* logits_dev, uint16_t* out_dev,
                      void* ws_dev, uint64_t ws_bytes, void* stream) {
   MNB_GUARD({
-    return qmoe_common(fc1, fc2, q, T, x_dev, logits_dev, out_dev, ws_dev, ws_bytes, stream,
-                       nullptr);
+    return qmoe_common(fc1, fc2, q, T, x_dev, logits_dev, nullptr, nullptr, out_dev, ws_dev,
+                       ws_bytes, stream, nullptr);
+  })
+}
+
+int32_t qmoe_forward_biased(const mnb_plan* fc1, const mnb_plan* fc2, const qmoe_desc* q,
+                            int64_t T, const uint16_t* x_dev, const float* logits_dev,
+                            const uint16_t* fc1_bias_dev, const uint16_t* fc2_bias_dev,
+                            uint16_t* out_dev, void* ws_dev, uint64_t ws_bytes, void* stream) {
+  MNB_GUARD({
+    return qmoe_common(fc1, fc2, q, T, x_dev, logits_dev, fc1_bias_dev, fc2_bias_dev, out_dev,
+                       ws_dev, ws_bytes, stream, nullptr);
   })
 }
 
 int32_t qmoe_forward_debug(const mnb_plan* fc1, const mnb_plan* fc2, const qmoe_desc* q,
                            int64_t T, const uint16_t* x_dev, const float* logits_dev,
+                           const uint16_t* fc1_bias_dev, const uint16_t* fc2_bias_dev,
                            uint16_t* out_dev, void* ws_dev, uint64_t ws_bytes, void* stream,
                            int32_t* ids_dev, float* w_dev, uint16_t* h_dev, float* slot_dev) {
   MNB_GUARD({
     QmoeDebug dbg{ids_dev, w_dev, h_dev, slot_dev};
-    return qmoe_common(fc1, fc2, q, T, x_dev, logits_dev, out_dev, ws_dev, ws_bytes, stream,
-                       &dbg);
+    return qmoe_common(fc1, fc2, q, T, x_dev, logits_dev, fc1_bias_dev, fc2_bias_dev, out_dev,
+                       ws_dev, ws_bytes, stream, &dbg);
   })
 }
 

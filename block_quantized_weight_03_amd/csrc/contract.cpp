@@ -60,8 +60,9 @@ int32_t check_desc(const mnb_desc* d, Sizes* s) {
     z.kind = kDenseInt4;
   } else if (d->bits == 3 || d->bits == 4) {
     // QMoE v1 projection profile: INT3, or INT4 for the mixed (3,4) / (4,3)
-    // width pairs and the all-INT4 layer
-    if (d->scale_dtype != MNB_DTYPE_F16 || d->row_layout != MNB_ROWS_ROW_LOCAL || d->has_zero_points)
+    // width pairs and the all-INT4 layer; explicit zero points are accepted
+    // only as the implicit value (checked with the content)
+    if (d->scale_dtype != MNB_DTYPE_F16 || d->row_layout != MNB_ROWS_ROW_LOCAL)
       return MNB_ERR_UNSUPPORTED;
     if (d->K % d->block_size) return MNB_ERR_UNSUPPORTED;  // block-aligned K
     z.kind = kMoe;
@@ -88,7 +89,15 @@ int32_t check_desc(const mnb_desc* d, Sizes* s) {
   uint64_t nscale;
   if (!mul_ok(rows, (uint64_t)z.nb, &nscale)) return MNB_ERR_SIZE_OVERFLOW;
   if (!mul_ok(nscale, d->scale_dtype == MNB_DTYPE_F32 ? 4 : 2, &z.scales)) return MNB_ERR_SIZE_OVERFLOW;
-  if (d->has_zero_points) {
+  if (d->has_zero_points && z.kind == kMoe) {
+    // packed per-row block zero points, a row-local LSB-first stream of nb
+    // codes per row [E*N, ceil(nb*bits/8)]; validated, then implied (no
+    // prepacked section)
+    uint64_t zb, zt;
+    if (!mul_ok((uint64_t)z.nb, (uint64_t)z.bits, &zb) || !add_ok(zb, 7, &zb)) return MNB_ERR_SIZE_OVERFLOW;
+    z.zrow = zb / 8;
+    if (!mul_ok(rows, z.zrow, &zt)) return MNB_ERR_SIZE_OVERFLOW;
+  } else if (d->has_zero_points) {
     z.zrow = (uint64_t)(z.nb / 2 + (z.nb % 2));
     uint64_t zt;
     if (!mul_ok((uint64_t)z.N, z.zrow, &zt)) return MNB_ERR_SIZE_OVERFLOW;  // contract bytes
@@ -108,9 +117,26 @@ int32_t check_desc(const mnb_desc* d, Sizes* s) {
 
 int32_t validate_content(const mnb_desc* d, const Sizes& s, const uint8_t* B,
                          const void* scales, const uint8_t* zp) {
-  (void)d;
-  (void)zp;
   if (s.kind != kMoe) return MNB_OK;
+  // explicit zero points must all be the implicit 2^(bits-1) ([P1]: all-4
+  // explicit zero points for INT3), with canonical padding
+  if (d->has_zero_points) {
+    if (!zp) return MNB_ERR_INVALID_ARG;
+    const unsigned want = 1u << (s.bits - 1);
+    const int64_t zbits = s.nb * s.bits, zused = zbits % 8;
+    for (int64_t r = 0; r < s.rows; ++r) {
+      const uint8_t* zr = zp + (uint64_t)r * s.zrow;
+      for (int64_t b = 0; b < s.nb; ++b) {
+        unsigned z = 0;
+        for (int64_t t = 0; t < s.bits; ++t) {
+          const int64_t bit = b * s.bits + t;
+          z |= (unsigned)((zr[bit >> 3] >> (bit & 7)) & 1u) << t;
+        }
+        if (z != want) return MNB_ERR_CONTENT;
+      }
+      if (zused && (zr[s.zrow - 1] >> zused)) return MNB_ERR_CONTENT;
+    }
+  }
   // finite, nonnegative FP16 scales: exponent 31 is Inf/NaN; a set sign bit
   // is only allowed on zero
   const uint64_t n = s.scales / 2;

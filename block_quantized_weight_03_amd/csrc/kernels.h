@@ -42,10 +42,11 @@ struct QmoeDebug {
   float* slot;
 };
 uint64_t qmoe_ws_bytes(const Sizes& s1, const Sizes& s2, int top_k, int64_t T);
+// b1 fp16 [E][2I] and b2 fp16 [E][H]: optional projection biases (nullptr: none)
 hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2,
                        const mnb_plan& p2, int top_k, int64_t T, const uint16_t* x,
-                       const float* logits, uint16_t* out, void* ws, hipStream_t st,
-                       const QmoeDebug* dbg);
+                       const float* logits, const uint16_t* b1, const uint16_t* b2,
+                       uint16_t* out, void* ws, hipStream_t st, const QmoeDebug* dbg);
 
 // ---- producer-side INT3 RTN quantizer (quant.hip) ---------------------------
 // W fp32 [rows, K] (16-byte aligned), K % bs == 0, bs in {32, 64, 128};

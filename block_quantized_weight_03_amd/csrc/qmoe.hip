@@ -402,6 +402,7 @@ struct MoeGemmArgs {
   const float* wts;        // FC2: routing weights per slot
   __half* h_out;           // FC1 output [T*k][N/2] (grouped order)
   float* slot_out;         // FC2 output [T*k][N] (slot order)
+  const __half* bias;      // optional [E][N] projection bias (nullptr: none)
 };
 
 constexpr int kQBN = 64;         // weight rows per workgroup
@@ -544,7 +545,8 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = i * 16 + 4 * (lane >> 4) + r;
-        const float v = acc[t][i][r];
+        float v = acc[t][i][r];
+        if (g.bias && col < g.N) v += __half2float(g.bias[(int64_t)e * g.N + col]);
         if (FC1) {
           // interleaved gate/up: even row = gate_i, odd row = up_i
           const float partner = __shfl_xor(v, 1);
@@ -820,6 +822,11 @@ __global__ void __launch_bounds__(256) qmoe_fc1_decode(MoeGemmArgs g, int64_t T,
         gs += red[w * 64 + q * 16 + 2 * tid];
         us += red[w * 64 + q * 16 + 2 * tid + 1];
       }
+    if (g.bias) {
+      const __half* b = g.bias + (int64_t)e * N + 16 * tile + 2 * tid;
+      gs += __half2float(b[0]);
+      us += __half2float(b[1]);
+    }
     g.h_out[(int64_t)slot * I + 8 * tile + tid] = __float2half_rn(gs / (1.0f + expf(-gs)) * us);
   }
 }
@@ -866,6 +873,7 @@ __global__ void __launch_bounds__(1024) qmoe_fc2_decode(MoeGemmArgs g, int64_t T
     for (int r = 0; r < k; ++r) {
       float y = 0.0f;
       for (int q = 0; q < 8; ++q) y += red[r * 64 + q * 8 + tid];
+      if (g.bias) y += __half2float(g.bias[(int64_t)clamp_id(g.perm[t * k + r], g.E) * H + n]);
       const float ry = g.wts[t * k + r] * y;
       if (slot_dbg) slot_dbg[((int64_t)t * k + r) * H + n] = ry;
       o += ry;
@@ -970,8 +978,9 @@ uint64_t qmoe_ws_bytes(const Sizes& s1, const Sizes& s2, int top_k, int64_t T) {
 }
 
 hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, const mnb_plan& p2,
-                       int top_k, int64_t T, const uint16_t* x, const float* logits, uint16_t* out,
-                       void* ws, hipStream_t st, const QmoeDebug* dbg) {
+                       int top_k, int64_t T, const uint16_t* x, const float* logits,
+                       const uint16_t* b1, const uint16_t* b2, uint16_t* out, void* ws,
+                       hipStream_t st, const QmoeDebug* dbg) {
   const int64_t E = s1.E, H = s1.K, I = s2.K;
   const int k = top_k;
   // limits of these kernels (checked before any launch)
@@ -996,24 +1005,26 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
     const int64_t S = T * k;
     MoeGemmArgs a1{static_cast<const uint8_t*>(p1.codes), static_cast<const __half*>(p1.scales),
                    x, s1.N, s1.K, s1.row_bytes, s1.nb, s1.bs, k, (int)E,
-                   nullptr, nullptr, ids, nullptr, nullptr, wts, hbuf, nullptr};
-    const dim3 g1((unsigned)(S * (s1.N / 16))), b1(256);
+                   nullptr, nullptr, ids, nullptr, nullptr, wts, hbuf, nullptr,
+                   reinterpret_cast<const __half*>(b1)};
+    const dim3 g1((unsigned)(S * (s1.N / 16))), wg1(256);
     const size_t l1 = (size_t)(2 * H + 4 * 256 + 128);
     if (S > kFusedRouteSlots) launch_route(logits, T, (int)E, k, ids, wts, st);
     by_bits(s1.bits, [&](auto bits) {
       constexpr int B = decltype(bits)::value;
       if (S > kFusedRouteSlots)
-        hipLaunchKernelGGL((qmoe_fc1_decode<2, false, B>), g1, b1, l1, st, a1, T, logits, ids, wts);
+        hipLaunchKernelGGL((qmoe_fc1_decode<2, false, B>), g1, wg1, l1, st, a1, T, logits, ids, wts);
       else if (E <= 128)
-        hipLaunchKernelGGL((qmoe_fc1_decode<2, true, B>), g1, b1, l1, st, a1, T, logits, ids, wts);
+        hipLaunchKernelGGL((qmoe_fc1_decode<2, true, B>), g1, wg1, l1, st, a1, T, logits, ids, wts);
       else if (E <= 256)
-        hipLaunchKernelGGL((qmoe_fc1_decode<4, true, B>), g1, b1, l1, st, a1, T, logits, ids, wts);
+        hipLaunchKernelGGL((qmoe_fc1_decode<4, true, B>), g1, wg1, l1, st, a1, T, logits, ids, wts);
       else
-        hipLaunchKernelGGL((qmoe_fc1_decode<kMaxE / 64, true, B>), g1, b1, l1, st, a1, T, logits, ids, wts);
+        hipLaunchKernelGGL((qmoe_fc1_decode<kMaxE / 64, true, B>), g1, wg1, l1, st, a1, T, logits, ids, wts);
     });
     MoeGemmArgs a2{static_cast<const uint8_t*>(p2.codes), static_cast<const __half*>(p2.scales),
                    hbuf, s2.N, s2.K, s2.row_bytes, s2.nb, s2.bs, k, (int)E,
-                   nullptr, nullptr, ids, nullptr, nullptr, wts, nullptr, nullptr};
+                   nullptr, nullptr, ids, nullptr, nullptr, wts, nullptr, nullptr,
+                   reinterpret_cast<const __half*>(b2)};
     by_bits(s2.bits, [&](auto bits) {
       constexpr int B = decltype(bits)::value;
       hipLaunchKernelGGL((qmoe_fc2_decode<B>), dim3((unsigned)(T * (H / 8))), dim3(64 * k),
@@ -1038,7 +1049,8 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
                        items, bm, go);
     MoeGemmArgs a1{static_cast<const uint8_t*>(p1.codes), static_cast<const __half*>(p1.scales),
                    x + t0 * H, s1.N, s1.K, s1.row_bytes, s1.nb, s1.bs, k, (int)E,
-                   go.counts, go.offsets, go.perm, go.items, go.nitems, wts, hbuf, nullptr};
+                   go.counts, go.offsets, go.perm, go.items, go.nitems, wts, hbuf, nullptr,
+                   reinterpret_cast<const __half*>(b1)};
     const int ntg = bm == 32 ? ntg_of<32>() : ntg_of<kMaxBM>();
     const int64_t nt1 = (s1.N + kQBN - 1) / kQBN, ng1 = (nt1 + ntg - 1) / ntg;
     const dim3 grid1((unsigned)((items + 7) / 8 * 8 * ng1));
@@ -1051,7 +1063,8 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
     });
     MoeGemmArgs a2{static_cast<const uint8_t*>(p2.codes), static_cast<const __half*>(p2.scales),
                    hbuf, s2.N, s2.K, s2.row_bytes, s2.nb, s2.bs, k, (int)E,
-                   go.counts, go.offsets, go.perm, go.items, go.nitems, wts, nullptr, slots};
+                   go.counts, go.offsets, go.perm, go.items, go.nitems, wts, nullptr, slots,
+                   reinterpret_cast<const __half*>(b2)};
     const int64_t nt2 = (s2.N + kQBN - 1) / kQBN, ng2 = (nt2 + ntg - 1) / ntg;
     const dim3 grid2((unsigned)((items + 7) / 8 * 8 * ng2));
     by_bits(s2.bits, [&](auto bits) {

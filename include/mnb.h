@@ -92,9 +92,10 @@ enum { MNB_ROWS_BLOCKED = 0, MNB_ROWS_ROW_LOCAL = 1 };
  *    F32, row_layout BLOCKED, num_experts 1, zero points optional, any
  *    K >= 1 and N >= 1;
  *  QMoE projection [P1]: bits 3 or 4, block_size 32/64/128, scale_dtype
- *    F16, row_layout ROW_LOCAL, num_experts >= 1, no explicit zero points
- *    (implicit 2^(bits-1): 4 or 8), K a multiple of block_size, any N >= 1
- *    (per-expert matrix [N, K]).
+ *    F16, row_layout ROW_LOCAL, num_experts >= 1, zero points implicit
+ *    (2^(bits-1): 4 or 8) or explicit with every value equal to that
+ *    ("all-4 explicit zero points" for INT3), K a multiple of block_size,
+ *    any N >= 1 (per-expert matrix [N, K]).
  * accuracy_level must be 0..4; it is recorded, and the numerics are fixed by
  * the kernels (fp32 GEMV, fp16-input MFMA GEMM with fp32 accumulation). */
 typedef struct mnb_desc {
@@ -155,8 +156,11 @@ int32_t mnb_prepacked_size(const mnb_desc* desc, uint64_t* bytes);
  *                   [E*N, ceil(K*bits/8)] (ROW_LOCAL), E = num_experts;
  *  scales_host      fp32 or fp16 (per scale_dtype), [E*N, nb], index n*nb + b;
  *  zero_points_host NULL when has_zero_points == 0, else uint8
- *                   [N, ceil(nb/2)]: block b of row n in byte b/2, low
- *                   nibble for even b.
+ *                   dense: [N, ceil(nb/2)]: block b of row n in byte b/2,
+ *                   low nibble for even b;  QMoE: packed per-row block zero
+ *                   points [E*N, ceil(nb*bits/8)], row-local LSB-first like
+ *                   the codes, every one 2^(bits-1) with canonical padding
+ *                   (else CONTENT); they are validated and then implied.
  * dst_dev must hold mnb_prepacked_size(desc) bytes and be 256-byte aligned.
  * On success *plan describes the prepared weights; on failure *plan is
  * zeroed.  Errors: INVALID_ARG, UNSUPPORTED, SIZE_OVERFLOW, CONTENT,
@@ -248,6 +252,22 @@ int32_t qmoe_forward(const mnb_plan* fc1, const mnb_plan* fc2,
                      const qmoe_desc* q, int64_t T, const uint16_t* x_dev,
                      const float* logits_dev, uint16_t* out_dev, void* ws_dev,
                      uint64_t ws_bytes, void* stream);
+
+/* qmoe_forward with the optional projection biases [P1] ("optional
+ * biases"):
+ *  fc1_bias_dev fp16 [E, 2I] (row order of FC1: gate_i at 2i, up_i at
+ *               2i + 1), added to g and u before SwiGLU; NULL = none;
+ *  fc2_bias_dev fp16 [E, H], added to each expert's FC2 output before its
+ *               routing weight: out = fp16(sum_j r_j (h_j.W2^T + b2[e_j]));
+ *               NULL = none.
+ * Both 2-byte aligned (else INVALID_ARG); read only.  Everything else as for
+ * qmoe_forward, which is this call with two NULL biases. */
+int32_t qmoe_forward_biased(const mnb_plan* fc1, const mnb_plan* fc2,
+                            const qmoe_desc* q, int64_t T,
+                            const uint16_t* x_dev, const float* logits_dev,
+                            const uint16_t* fc1_bias_dev,
+                            const uint16_t* fc2_bias_dev, uint16_t* out_dev,
+                            void* ws_dev, uint64_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Producer-side INT3 round-to-nearest quantizer [P0][OLIVE]: fp32 weights to

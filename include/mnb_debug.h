@@ -50,17 +50,20 @@ int32_t mnb_debug_dequant_f16(const mnb_plan* plan, int64_t expert,
                               int64_t row0, int64_t nrows, uint16_t* out_dev,
                               void* stream);
 
-/* qmoe_forward that also copies out the routing and the intermediates:
+/* qmoe_forward_biased (biases may be NULL) that also copies out the routing
+ * and the intermediates:
  *  ids_dev   int32 [T, top_k] selected experts, rank order;
  *  w_dev     fp32  [T, top_k] renormalized routing weights;
  *  h_dev     fp16  [T, top_k, I] SwiGLU activations fed to FC2;
- *  slot_dev  fp32  [T, top_k, H] r_j * (h_j . W2^T) before the combine.
+ *  slot_dev  fp32  [T, top_k, H] r_j * (h_j . W2^T + b2) before the combine.
  * Any of the four may be NULL. */
 int32_t qmoe_forward_debug(const mnb_plan* fc1, const mnb_plan* fc2,
                            const qmoe_desc* q, int64_t T,
                            const uint16_t* x_dev, const float* logits_dev,
-                           uint16_t* out_dev, void* ws_dev, uint64_t ws_bytes,
-                           void* stream, int32_t* ids_dev, float* w_dev,
+                           const uint16_t* fc1_bias_dev,
+                           const uint16_t* fc2_bias_dev, uint16_t* out_dev,
+                           void* ws_dev, uint64_t ws_bytes, void* stream,
+                           int32_t* ids_dev, float* w_dev,
                            uint16_t* h_dev, float* slot_dev);
 
 #ifdef __cplusplus

@@ -83,8 +83,9 @@ def test_descriptor_rejections():
     # INT3 QMoE profile
     q = mnb.qmoe_proj_desc(2048, 1536, 128, 64)
     assert size_status(q) == OK
-    q.has_zero_points = 1
-    assert size_status(q) == UNSUP
+    size = mnb.mnb_prepacked_size(q)
+    q.has_zero_points = 1  # explicit zero points: validated, then implied
+    assert size_status(q) == OK and mnb.mnb_prepacked_size(q) == size
     assert size_status(mnb.qmoe_proj_desc(100, 8, 2, 64)) == UNSUP  # K not block aligned
     q = mnb.qmoe_proj_desc(128, 8, 2, 64)
     q.scale_dtype = mnb.MNB_DTYPE_F32
@@ -318,3 +319,34 @@ def test_quantizer_argument_checks_before_any_device_call():
     assert f(16, 4, 64, 32, 18, 16, 16, None) == INVALID    # codes not 4-byte aligned
     assert f(16, 4, 64, 32, 16, 17, 16, None) == INVALID    # scales not 2-byte aligned
     assert f(16, 2 ** 40, 2 ** 30, 32, 16, 16, 16, None) == OVERFLOW
+
+
+@pytest.mark.parametrize("bits,K,bs", [(3, 128, 64), (4, 128, 32), (3, 320, 32), (4, 384, 128)])
+def test_moe_explicit_zero_points_must_equal_the_implicit_value(orc, bits, K, bs):
+    """Packed per-row block zero points of a QMoE projection are accepted only
+    when every one is 2^(bits-1) with canonical padding; the prepared bytes
+    are then those of the implicit-zero-point plan."""
+    E, N = 2, 24
+    nb = K // bs
+    W = synth.packed_rows(bits + K, E * N, K, bits)
+    s = synth.scales_f16(6, (E * N, nb))
+    zrow = orc.pack_bits(np.full(nb, 1 << (bits - 1), np.uint8), bits)
+    Z = np.tile(zrow, (E * N, 1))
+    d0 = mnb.qmoe_proj_desc(K, N, E, bs, bits=bits)
+    dz = mnb.qmoe_proj_desc(K, N, E, bs, bits=bits)
+    dz.has_zero_points = 1
+    _, v0, _k0 = host_prepare(d0, W, s, None)
+    _, vz, _kz = host_prepare(dz, W, s, Z)
+    assert np.array_equal(v0, vz)
+    bad = Z.copy()
+    bad[E * N - 1] = orc.pack_bits(np.array([1 << (bits - 1)] * (nb - 1) + [(1 << (bits - 1)) - 1],
+                                            np.uint8), bits)
+    with pytest.raises(mnb.MnbError) as e:
+        host_prepare(dz, W, s, bad)
+    assert e.value.status == CONTENT
+    if (nb * bits) % 8:
+        pad = Z.copy()
+        pad[3, -1] |= np.uint8(0x80)  # a set pad bit after nb * bits
+        with pytest.raises(mnb.MnbError) as e:
+            host_prepare(dz, W, s, pad)
+        assert e.value.status == CONTENT

@@ -30,13 +30,16 @@ def say(*a):
 
 
 class Moe:
-    def __init__(self, x, logits, W1, s1, W2, s2, k, bs, bits1=3, bits2=3):
+    def __init__(self, x, logits, W1, s1, W2, s2, k, bs, bits1=3, bits2=3, b1=None, b2=None):
         self.E, twoI, _ = W1.shape
         self.I = twoI // 2
         self.H = x.shape[1]
         self.k, self.bs = k, bs
         self.bits1, self.bits2 = bits1, bits2
         self.host = (W1, s1, W2, s2)
+        self.b1, self.b2 = b1, b2  # optional fp16 biases [E, 2I], [E, H]
+        self.b1d = None if b1 is None else torch.from_numpy(np.ascontiguousarray(b1)).cuda()
+        self.b2d = None if b2 is None else torch.from_numpy(np.ascontiguousarray(b2)).cuda()
         self.p1 = mnb.PreparedWeight(mnb.qmoe_proj_desc(self.H, twoI, self.E, bs, bits1),
                                      W1.reshape(self.E * twoI, -1), s1.reshape(self.E * twoI, -1))
         self.p2 = mnb.PreparedWeight(mnb.qmoe_proj_desc(self.I, self.H, self.E, bs, bits2),
@@ -59,7 +62,10 @@ class Moe:
                        h_dev=torch.empty((T, k, I), dtype=torch.float16, device="cuda"),
                        slot_dev=torch.empty((T, k, H), dtype=torch.float32, device="cuda"))
             mnb.qmoe_forward_debug(self.p1.plan, self.p2.plan, self.q, T, xd, ld, out, ws, ws.numel(),
-                                   **dbg)
+                                   fc1_bias_dev=self.b1d, fc2_bias_dev=self.b2d, **dbg)
+        elif self.b1 is not None or self.b2 is not None:
+            mnb.qmoe_forward_biased(self.p1.plan, self.p2.plan, self.q, T, xd, ld, self.b1d, self.b2d,
+                                    out, ws, ws.numel())
         else:
             mnb.qmoe_forward(self.p1.plan, self.p2.plan, self.q, T, xd, ld, out, ws, ws.numel())
         torch.cuda.synchronize()
@@ -73,17 +79,21 @@ class Moe:
     def oracle(self, orc, x, logits):
         W1, s1, W2, s2 = self.host
         return orc.qmoe(x, logits, W1, s1, W2, s2, k=self.k, bits1=self.bits1, bits2=self.bits2,
-                        bs=self.bs, nthreads=8)
+                        bs=self.bs, nthreads=8, b1=self.b1, b2=self.b2)
 
 
-def random_moe(seed, T, H, I, E, k, bs, bits1=3, bits2=3):
+def random_moe(seed, T, H, I, E, k, bs, bits1=3, bits2=3, bias=False):
     x = synth.activations_f16(synth.seed_for(seed, 1), T, H)
     logits = synth.router_logits(synth.seed_for(seed, 2), T, E)
     W1 = synth.packed_rows(synth.seed_for(seed, 3), E * 2 * I, H, bits1).reshape(E, 2 * I, -1)
     s1 = synth.scales_f16(synth.seed_for(seed, 4), (E, 2 * I, H // bs))
     W2 = synth.packed_rows(synth.seed_for(seed, 5), E * H, I, bits2).reshape(E, H, -1)
     s2 = synth.scales_f16(synth.seed_for(seed, 6), (E, H, I // bs))
-    return x, logits, Moe(x, logits, W1, s1, W2, s2, k, bs, bits1, bits2)
+    b1 = b2 = None
+    if bias:
+        b1 = synth.activations_f16(synth.seed_for(seed, 7), E, 2 * I) * np.float16(0.5)
+        b2 = synth.activations_f16(synth.seed_for(seed, 8), E, H) * np.float16(0.25)
+    return x, logits, Moe(x, logits, W1, s1, W2, s2, k, bs, bits1, bits2, b1, b2)
 
 
 def half_ulp(a, b):
@@ -110,7 +120,7 @@ def check_stages(orc, m, res, o):
     # FC2 fed the GPU's own h
     W1, s1, W2, s2 = m.host
     y, yS = orc.qmoe_fc2(res["ids"], res["h"].astype(np.float64), W2, s2, m.H, m.I, m.E,
-                         bits2=m.bits2, bs=m.bs, nthreads=8)
+                         bits2=m.bits2, bs=m.bs, nthreads=8, b2=m.b2)
     r = res["w"].astype(np.float64)[:, :, None]
     err = np.abs(res["slot"].astype(np.float64) - r * y)
     assert (err <= 4e-3 * r * yS + 1e-30).all()
@@ -205,6 +215,51 @@ def test_qmoe_int4_codes_at_zero_point_give_zero():
         s2 = synth.scales_f16(95, (E, H, I // bs))
         m = Moe(x, logits, W1, s1, W2, s2, k, bs, 4, 4)
         assert (m.run(x, logits)["out"] == 0).all()
+
+
+# Optional biases (P1 section of the INT3 QMoE page): FC1's added to gate and
+# up before SwiGLU, FC2's to each expert's output before its routing weight.
+# Shapes cover the decode path with fused routing (T k <= 8), with a routing
+# launch (8 < T k <= 32), both token tiles of the grouped path and an FC2 with
+# a half-empty last 64-row tile (H = 96).
+@pytest.mark.parametrize("bits1,bits2", [(3, 3), (4, 4), (3, 4)])
+@pytest.mark.parametrize("T,H,I,E,k,bs", [(1, 64, 32, 3, 3, 32), (4, 128, 64, 8, 8, 64),
+                                          (17, 96, 64, 16, 4, 32), (64, 192, 160, 12, 8, 32)])
+def test_qmoe_biases_all_outputs(orc, bits1, bits2, T, H, I, E, k, bs):
+    say(f"qmoe biases ({bits1},{bits2}) T={T} H={H} I={I} E={E} k={k} bs={bs}")
+    x, logits, m = random_moe(T * 5 + E + 3 * bits2, T, H, I, E, k, bs, bits1, bits2, bias=True)
+    res = m.run(x, logits, debug=True)
+    o = m.oracle(orc, x, logits)
+    check_end_to_end(res["out"], o)
+    check_stages(orc, m, res, o)
+    # the biased entry point (no debug copies) gives the same bits
+    assert np.array_equal(m.run(x, logits)["out"].view(np.uint16), res["out"].view(np.uint16))
+
+
+def test_qmoe_biased_entry_with_null_biases_is_qmoe_forward():
+    say("qmoe biased entry, null biases")
+    for T in (3, 40):
+        x, logits, m = random_moe(55 + T, T, 128, 64, 8, 4, 64)
+        ref = m.run(x, logits)["out"]
+        xd, ld = torch.from_numpy(x).cuda(), torch.from_numpy(logits).cuda()
+        out = torch.empty((T, 128), dtype=torch.float16, device="cuda")
+        ws = torch.empty(mnb.qmoe_workspace_size(m.p1.plan, m.p2.plan, m.q, T), dtype=torch.uint8,
+                         device="cuda")
+        mnb.qmoe_forward_biased(m.p1.plan, m.p2.plan, m.q, T, xd, ld, None, None, out, ws,
+                                ws.numel())
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint16), ref.view(np.uint16))
+
+
+def test_qmoe_biases_layer_config_sampled_tokens(orc):
+    say("qmoe layer with biases T=128")
+    T, H, I, E, k, bs = 128, 2048, 768, 128, 8, 64
+    x, logits, m = random_moe(17, T, H, I, E, k, bs, bias=True)
+    res = m.run(x, logits, debug=True)
+    toks = np.array([0, 5, 77, T - 1])
+    o = m.oracle(orc, x[toks], logits[toks])
+    check_end_to_end(res["out"][toks], o)
+    check_stages(orc, m, {key: res[key][toks] for key in ("ids", "w", "h", "slot")}, o)
 
 
 def test_qmoe_more_tokens_than_one_tile(orc):
