@@ -139,20 +139,44 @@ def route(logits, k):
     return ids, w
 
 
-def _f16_or_none(b):
-    return None if b is None else np.ascontiguousarray(b, dtype=np.float16).view(np.uint16)
+def _bits16(a, dtype):
+    """16-bit patterns of fp16 values (dtype "f16": a float16 array) or of
+    bfloat16 values (dtype "bf16": a uint16 array of bfloat16 patterns)."""
+    if a is None:
+        return None
+    if dtype == "bf16":
+        a = np.ascontiguousarray(a)
+        assert a.dtype == np.uint16, "bf16 values are passed as uint16 patterns"
+        return a
+    return np.ascontiguousarray(a, dtype=np.float16).view(np.uint16)
 
 
-def qmoe(x_f16, logits, W1, s1, W2, s2, k=8, bits1=3, bits2=3, bs=64, nthreads=1, b1=None, b2=None):
-    """x_f16: float16 [T,H]; s1, s2: float16; optional biases b1 float16 [E,2I]
-    and b2 float16 [E,H].  Returns a dict of every output."""
-    x = np.ascontiguousarray(x_f16, dtype=np.float16).view(np.uint16)
+def bf16_to_f64(h: np.ndarray) -> np.ndarray:
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.zeros(h.shape, np.float64)
+    _check(lib().orc_bf16_to_f64_array(_p(h), I64(h.size), _p(out)), "bf16_to_f64")
+    return out
+
+
+def f64_to_bf16(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.zeros(x.shape, np.uint16)
+    _check(lib().orc_f64_to_bf16_array(_p(x), I64(x.size), _p(out)), "f64_to_bf16")
+    return out
+
+
+def qmoe(x_f16, logits, W1, s1, W2, s2, k=8, bits1=3, bits2=3, bs=64, nthreads=1, b1=None, b2=None,
+         dtype="f16"):
+    """x: [T,H]; s1, s2; optional biases b1 [E,2I] and b2 [E,H]; all float16
+    (dtype "f16") or uint16 bfloat16 patterns (dtype "bf16").  Returns a dict
+    of every output; "out16" holds the 16-bit patterns of out."""
+    dt = 1 if dtype == "bf16" else 0
+    x = _bits16(x_f16, dtype)
     logits = np.ascontiguousarray(logits, dtype=np.float32)
     W1 = np.ascontiguousarray(W1, dtype=np.uint8)
     W2 = np.ascontiguousarray(W2, dtype=np.uint8)
-    s1 = np.ascontiguousarray(s1, dtype=np.float16).view(np.uint16)
-    s2 = np.ascontiguousarray(s2, dtype=np.float16).view(np.uint16)
-    b1, b2 = _f16_or_none(b1), _f16_or_none(b2)
+    s1, s2 = _bits16(s1, dtype), _bits16(s2, dtype)
+    b1, b2 = _bits16(b1, dtype), _bits16(b2, dtype)
     T, H = x.shape
     E = W1.shape[0]
     I = W1.shape[1] // 2
@@ -161,26 +185,25 @@ def qmoe(x_f16, logits, W1, s1, W2, s2, k=8, bits1=3, bits2=3, bs=64, nthreads=1
              g=np.zeros((T, k, I)), u=np.zeros((T, k, I)), h=np.zeros((T, k, I)),
              gs=np.zeros((T, k, I)), us=np.zeros((T, k, I)))
     _check(lib().orc_qmoe(I64(T), I64(H), I64(I), INT(E), INT(k), INT(bits1), INT(bits2),
-                          INT(bs), _p(x), _p(logits), _p(W1), _p(s1), _p(W2), _p(s2),
+                          INT(bs), INT(dt), _p(x), _p(logits), _p(W1), _p(s1), _p(W2), _p(s2),
                           _p(b1), _p(b2), _p(o["out16"]), _p(o["out64"]), _p(o["S"]), _p(o["ids"]), _p(o["r"]),
                           _p(o["g"]), _p(o["u"]), _p(o["h"]), _p(o["gs"]), _p(o["us"]),
                           INT(nthreads)), "qmoe")
-    o["out"] = o["out16"].view(np.float16)
+    o["out"] = o["out16"].view(np.float16) if dt == 0 else bf16_to_f64(o["out16"])
     return o
 
 
-def qmoe_fc2(ids, h, W2, s2, H, I, E, bits2=3, bs=64, nthreads=1, b2=None):
+def qmoe_fc2(ids, h, W2, s2, H, I, E, bits2=3, bs=64, nthreads=1, b2=None, dtype="f16"):
     """h: fp64 [T,k,I].  Returns (y [T,k,H], yS [T,k,H])."""
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     h = np.ascontiguousarray(h, dtype=np.float64)
     W2 = np.ascontiguousarray(W2, dtype=np.uint8)
-    s2 = np.ascontiguousarray(s2, dtype=np.float16).view(np.uint16)
-    b2 = _f16_or_none(b2)
+    s2, b2 = _bits16(s2, dtype), _bits16(b2, dtype)
     T, k = ids.shape
     y = np.zeros((T, k, H))
     yS = np.zeros((T, k, H))
     _check(lib().orc_qmoe_fc2(I64(T), I64(H), I64(I), INT(E), INT(k), INT(bits2), INT(bs),
-                              _p(ids), _p(h), _p(W2), _p(s2), _p(b2), _p(y), _p(yS),
+                              INT(1 if dtype == "bf16" else 0), _p(ids), _p(h), _p(W2), _p(s2), _p(b2), _p(y), _p(yS),
                               INT(nthreads)),
            "qmoe_fc2")
     return y, yS

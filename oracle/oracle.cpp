@@ -90,12 +90,16 @@ bool dense_args_ok(int64_t K, int64_t N, int bits, int bs) {
 // INT3 QMoE row dequantization ([P0], [OLIVE]): a row of K codes is one
 // row-local LSB-first bit stream of ceil(bits*K/8) bytes; block b of the row
 // uses scale s[b]; w = (q - 2^(bits-1)) * s.
-void moe_row(const uint8_t* row, const uint16_t* s, int64_t K, int bits, int bs,
+// A 16-bit activation / scale / bias value: IEEE binary16 (dtype 0) or
+// bfloat16 (dtype 1), widened exactly.
+double h16(uint16_t v, int dtype) { return dtype ? orc_bf16_to_f64(v) : orc_f16_to_f64(v); }
+
+void moe_row(const uint8_t* row, const uint16_t* s, int64_t K, int bits, int bs, int dtype,
              double* w) {
   const double z = (double)(1u << (bits - 1));
   for (int64_t k = 0; k < K; ++k) {
     const double q = (double)code_at(row, k, bits);
-    w[k] = (q - z) * orc_f16_to_f64(s[k / bs]);
+    w[k] = (q - z) * h16(s[k / bs], dtype);
   }
 }
 
@@ -169,6 +173,56 @@ uint16_t orc_f64_to_f16(double x) {
   }
   if (exp > 15) return (uint16_t)(sign | 0x7C00);
   return (uint16_t)(sign | (uint16_t)((exp + 15) << 10) | (uint16_t)m);
+}
+
+// bfloat16: the top 16 bits of an IEEE binary32 (1 sign bit, 8 exponent bits,
+// 7 fraction bits).
+double orc_bf16_to_f64(uint16_t b) {
+  const int sign = b >> 15;
+  const int e = (b >> 7) & 255;
+  const int m = b & 127;
+  double v;
+  if (e == 0)
+    v = std::ldexp((double)m, -133);  // subnormal: m * 2^(1 - 127 - 7)
+  else if (e == 255)
+    v = m ? std::nan("") : INFINITY;
+  else
+    v = std::ldexp((double)(128 + m), e - 134);
+  return sign ? -v : v;
+}
+
+// Round to nearest, ties to even, with overflow to infinity.
+uint16_t orc_f64_to_bf16(double x) {
+  const uint16_t sign = std::signbit(x) ? 0x8000 : 0;
+  if (std::isnan(x)) return (uint16_t)(sign | 0x7FC0);
+  const double a = std::fabs(x);
+  // the largest finite bf16 is (2 - 2^-7) 2^127; halfway to 2^128 rounds up
+  if (a >= std::ldexp(2.0 - std::ldexp(1.0, -8), 127)) return (uint16_t)(sign | 0x7F80);
+  if (a < std::ldexp(1.0, -126)) {
+    // subnormal: multiples of 2^-133; rounding up to 128 yields the smallest normal
+    const double q = std::nearbyint(std::ldexp(a, 133));
+    return (uint16_t)(sign | (uint16_t)q);
+  }
+  int E;
+  std::frexp(a, &E);
+  int exp = E - 1;
+  double m = std::nearbyint((std::ldexp(a, -exp) - 1.0) * 128.0);
+  if (m >= 128.0) {
+    m = 0.0;
+    exp += 1;
+  }
+  if (exp > 127) return (uint16_t)(sign | 0x7F80);
+  return (uint16_t)(sign | (uint16_t)((exp + 127) << 7) | (uint16_t)m);
+}
+
+int orc_bf16_to_f64_array(const uint16_t* h, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_to_f64(h[i]);
+  return 0;
+}
+
+int orc_f64_to_bf16_array(const double* x, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_f64_to_bf16(x[i]);
+  return 0;
 }
 
 int orc_f16_to_f64_array(const uint16_t* h, int64_t n, double* out) {
@@ -260,14 +314,14 @@ int orc_route(int64_t T, int E, int k, const float* logits, int32_t* ids,
 //   S[t][n] = sum_j r_j sum_i |w2[n][i]| (|h_i| + |dh/dg| gs_i + |dh/du| us_i)
 // with gs_i = sum_k |x_k w1[2i][k]| and us_i = sum_k |x_k w1[2i+1][k]|.
 int orc_qmoe(int64_t T, int64_t H, int64_t I, int E, int k, int bits1,
-             int bits2, int bs, const uint16_t* x, const float* logits,
+             int bits2, int bs, int dtype, const uint16_t* x, const float* logits,
              const uint8_t* W1, const uint16_t* s1, const uint8_t* W2,
              const uint16_t* s2, const uint16_t* b1, const uint16_t* b2,
              uint16_t* out16, double* out64, double* S,
              int32_t* ids, double* r, double* g, double* u, double* h,
              double* gs, double* us, int nthreads) {
   if (T < 0 || H < 1 || I < 1 || E < 1 || k < 1 || k > E || !bits_ok(bits1) ||
-      !bits_ok(bits2) || bs < 1 || H % bs || I % bs)
+      !bits_ok(bits2) || bs < 1 || H % bs || I % bs || (dtype != 0 && dtype != 1))
     return -1;
   if (T == 0) return 0;
   if (!x || !logits || !W1 || !s1 || !W2 || !s2) return -1;
@@ -282,7 +336,7 @@ int orc_qmoe(int64_t T, int64_t H, int64_t I, int E, int k, int bits1,
     std::vector<double> gv((size_t)I), uv((size_t)I), hv((size_t)I), gsv((size_t)I), usv((size_t)I);
     std::vector<double> acc((size_t)H), sacc((size_t)H);
     for (int64_t t = lo; t < hi; ++t) {
-      for (int64_t c = 0; c < H; ++c) xd[(size_t)c] = orc_f16_to_f64(x[t * H + c]);
+      for (int64_t c = 0; c < H; ++c) xd[(size_t)c] = h16(x[t * H + c], dtype);
       std::fill(acc.begin(), acc.end(), 0.0);
       std::fill(sacc.begin(), sacc.end(), 0.0);
       for (int j = 0; j < k; ++j) {
@@ -290,13 +344,13 @@ int orc_qmoe(int64_t T, int64_t H, int64_t I, int E, int k, int bits1,
         const double rj = rw[(size_t)(t * k + j)];
         for (int64_t i = 0; i < I; ++i) {
           const int64_t rg = e * 2 * I + 2 * i, ru = rg + 1;
-          moe_row(W1 + rg * rb1, s1 + rg * nb1, H, bits1, bs, wg.data());
-          moe_row(W1 + ru * rb1, s1 + ru * nb1, H, bits1, bs, wu.data());
+          moe_row(W1 + rg * rb1, s1 + rg * nb1, H, bits1, bs, dtype, wg.data());
+          moe_row(W1 + ru * rb1, s1 + ru * nb1, H, bits1, bs, dtype, wu.data());
           // an optional bias is one more product term, 1 * b ([P1] optional biases)
           double gg = 0, uu = 0, sg = 0, su = 0;
           if (b1) {
-            gg = orc_f16_to_f64(b1[rg]);
-            uu = orc_f16_to_f64(b1[ru]);
+            gg = h16(b1[rg], dtype);
+            uu = h16(b1[ru], dtype);
             sg = std::fabs(gg);
             su = std::fabs(uu);
           }
@@ -314,10 +368,10 @@ int orc_qmoe(int64_t T, int64_t H, int64_t I, int E, int k, int bits1,
         }
         for (int64_t n = 0; n < H; ++n) {
           const int64_t row = e * H + n;
-          moe_row(W2 + row * rb2, s2 + row * nb2, I, bits2, bs, w2.data());
+          moe_row(W2 + row * rb2, s2 + row * nb2, I, bits2, bs, dtype, w2.data());
           double y = 0, sy = 0;
           if (b2) {
-            y = orc_f16_to_f64(b2[row]);
+            y = h16(b2[row], dtype);
             sy = std::fabs(y);
           }
           for (int64_t i = 0; i < I; ++i) {
@@ -344,7 +398,8 @@ int orc_qmoe(int64_t T, int64_t H, int64_t I, int E, int k, int bits1,
       }
       for (int64_t n = 0; n < H; ++n) {
         if (out64) out64[t * H + n] = acc[(size_t)n];
-        if (out16) out16[t * H + n] = orc_f64_to_f16(acc[(size_t)n]);
+        if (out16)
+          out16[t * H + n] = dtype ? orc_f64_to_bf16(acc[(size_t)n]) : orc_f64_to_f16(acc[(size_t)n]);
         if (S) S[t * H + n] = sacc[(size_t)n];
       }
     }
@@ -357,10 +412,11 @@ int orc_qmoe(int64_t T, int64_t H, int64_t I, int E, int k, int bits1,
 }
 
 int orc_qmoe_fc2(int64_t T, int64_t H, int64_t I, int E, int k, int bits2,
-                 int bs, const int32_t* ids, const double* h, const uint8_t* W2,
+                 int bs, int dtype, const int32_t* ids, const double* h, const uint8_t* W2,
                  const uint16_t* s2, const uint16_t* b2, double* y, double* yS,
                  int nthreads) {
-  if (T < 0 || H < 1 || I < 1 || E < 1 || k < 1 || !bits_ok(bits2) || bs < 1 || I % bs)
+  if (T < 0 || H < 1 || I < 1 || E < 1 || k < 1 || !bits_ok(bits2) || bs < 1 || I % bs ||
+      (dtype != 0 && dtype != 1))
     return -1;
   if (T == 0) return 0;
   if (!ids || !h || !W2 || !s2 || !y) return -1;
@@ -374,10 +430,10 @@ int orc_qmoe_fc2(int64_t T, int64_t H, int64_t I, int E, int k, int bits2,
       const double* hv = h + tj * I;
       for (int64_t n = 0; n < H; ++n) {
         const int64_t row = e * H + n;
-        moe_row(W2 + row * rb2, s2 + row * nb2, I, bits2, bs, w2.data());
+        moe_row(W2 + row * rb2, s2 + row * nb2, I, bits2, bs, dtype, w2.data());
         double acc = 0, sa = 0;
         if (b2) {
-          acc = orc_f16_to_f64(b2[row]);
+          acc = h16(b2[row], dtype);
           sa = std::fabs(acc);
         }
         for (int64_t i = 0; i < I; ++i) {

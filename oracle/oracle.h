@@ -54,6 +54,12 @@ uint16_t orc_f64_to_f16(double x);
 int orc_f16_to_f64_array(const uint16_t* h, int64_t n, double* out);
 int orc_f64_to_f16_array(const double* x, int64_t n, uint16_t* out);
 
+/* ---- bfloat16 conversions (RN-even; bf16 = top half of binary32) --------- */
+double orc_bf16_to_f64(uint16_t b);
+uint16_t orc_f64_to_bf16(double x);
+int orc_bf16_to_f64_array(const uint16_t* h, int64_t n, double* out);
+int orc_f64_to_bf16_array(const double* x, int64_t n, uint16_t* out);
+
 /* ---- MatMulNBits [PLAN K01-K03] -------------------------------------------
  * A fp32 [M,K]; B uint8 [N, nb, bs*bits/8] with nb = ceil(K/bs); scales fp32
  * [N, nb]; zp NULL (implicit 2^(bits-1)) or uint8 [N, ceil(nb*bits/8)] of
@@ -80,7 +86,9 @@ int orc_route(int64_t T, int E, int k, const float* logits, int32_t* ids,
               double* weights);
 
 /* ---- INT3 QMoE layer [P0][P1][OLIVE] --------------------------------------
- * x fp16 [T,H]; logits fp32 [T,E];
+ * dtype 0: x, scales, biases and out are IEEE fp16; dtype 1: all bfloat16
+ * ([P1]: matching FP16/BF16 activation and scale types).
+ * x [T,H]; logits fp32 [T,E];
  * W1 uint8 [E, 2I, ceil(bits1*H/8)], rows 2i = gate_i and 2i+1 = up_i;
  * s1 fp16 [E, 2I, H/bs]; W2 uint8 [E, H, ceil(bits2*I/8)]; s2 fp16 [E, H, I/bs];
  * implicit zero points 2^(bits-1); optional biases ([P1] "optional biases";
@@ -92,7 +100,7 @@ int orc_route(int64_t T, int E, int k, const float* logits, int32_t* ids,
  * r fp64 [T,k]; g, u, h fp64 [T,k,I]; gs, us fp64 [T,k,I] (sum_k |x*w1| for
  * the gate and up rows).                                                    */
 int orc_qmoe(int64_t T, int64_t H, int64_t I, int E, int k, int bits1,
-             int bits2, int bs, const uint16_t* x, const float* logits,
+             int bits2, int bs, int dtype, const uint16_t* x, const float* logits,
              const uint8_t* W1, const uint16_t* s1, const uint8_t* W2,
              const uint16_t* s2, const uint16_t* b1, const uint16_t* b2,
              uint16_t* out16, double* out64, double* S,
@@ -103,7 +111,7 @@ int orc_qmoe(int64_t T, int64_t H, int64_t I, int E, int k, int bits1,
  * y fp64 [T,k,H] = h . w2[ids]^T (+ b2[ids]) and yS = sum_i |h_i * w2[n,i]|
  * (+ |b2|); b2 fp16 [E, H] or NULL.                                        */
 int orc_qmoe_fc2(int64_t T, int64_t H, int64_t I, int E, int k, int bits2,
-                 int bs, const int32_t* ids, const double* h, const uint8_t* W2,
+                 int bs, int dtype, const int32_t* ids, const double* h, const uint8_t* W2,
                  const uint16_t* s2, const uint16_t* b2, double* y, double* yS,
                  int nthreads);
 

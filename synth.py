@@ -132,6 +132,25 @@ def scales_f16(seed: int, shape, lo: float = 0.005, hi: float = 0.02) -> np.ndar
     return (lo + (hi - lo) * uniform01(seed, n)).astype(np.float16).reshape(shape)
 
 
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """uint16 bfloat16 patterns of float32 values, rounded to nearest even
+    (the storage rounding of a bfloat16 tensor; inputs here are finite)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def scales_bf16(seed: int, shape, lo: float = 0.005, hi: float = 0.02) -> np.ndarray:
+    """uint16 bfloat16 patterns of uniform scales."""
+    n = int(np.prod(shape))
+    return to_bf16_bits((lo + (hi - lo) * uniform01(seed, n)).astype(np.float32)).reshape(shape)
+
+
+def activations_bf16(seed: int, T: int, H: int) -> np.ndarray:
+    """uint16 bfloat16 patterns of N(0,1) activations."""
+    return to_bf16_bits(normal(seed, T * H).astype(np.float32)).reshape(T, H)
+
+
 def activations_f16(seed: int, T: int, H: int) -> np.ndarray:
     return normal(seed, T * H).astype(np.float16).reshape(T, H)
 

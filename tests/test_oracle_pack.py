@@ -87,3 +87,41 @@ def test_f16_encode_matches_numpy(orc):
             ref = vals.astype(np.float16).view(np.uint16)
         assert np.array_equal(got, ref)
     assert orc.f64_to_f16(np.array([np.nan]))[0] & 0x7C00 == 0x7C00
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 conversions, against torch's CPU bfloat16 (an independent
+# implementation): every pattern widens exactly; narrowing of binary32
+# values rounds to nearest even, including exact halfway points, overflow
+# and subnormals.
+# ---------------------------------------------------------------------------
+
+def test_bf16_widening_all_patterns(orc):
+    torch = pytest.importorskip("torch")
+    pats = np.arange(65536, dtype=np.uint16)
+    ref = torch.from_numpy(pats.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = orc.bf16_to_f64(pats)
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_bf16_narrowing_round_to_nearest_even(orc):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(0)
+    finite = np.arange(65536, dtype=np.uint16)
+    finite = finite[(finite & 0x7F80) != 0x7F80]
+    base = torch.from_numpy(finite.view(np.int16)).view(torch.bfloat16).to(torch.float32).numpy()
+    # halfway between neighbours (exact in binary32), quarter points, randoms
+    nxt = torch.from_numpy((finite + 1).astype(np.uint16).view(np.int16)).view(torch.bfloat16)
+    nxt = nxt.to(torch.float32).numpy()
+    ok = np.isfinite(nxt) & (np.sign(nxt) == np.sign(base))
+    half = (base[ok].astype(np.float64) + nxt[ok].astype(np.float64)) / 2
+    quarter = base[ok].astype(np.float64) * 0.75 + nxt[ok].astype(np.float64) * 0.25
+    rand = (rng.standard_normal(20000) * np.exp(rng.uniform(-90, 90, 20000))).astype(np.float32)
+    x = np.concatenate([base, half.astype(np.float32), quarter.astype(np.float32), rand,
+                        np.float32([3.4e38, -3.4e38, 1e-40, -1e-45, 0.0, -0.0])])
+    assert np.array_equal(x.astype(np.float64).astype(np.float32), x)  # all exact in binary32
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = orc.f64_to_bf16(x.astype(np.float64))
+    assert np.array_equal(got, ref)

@@ -267,3 +267,46 @@ def test_qmoe_biases_closed_forms(orc):
     y, _ = orc.qmoe_fc2(ids, o["h"], W2, s2, H, I, E, bits2=4, bs=bs, b2=b2)
     np.testing.assert_allclose((o["r"][:, :, None] * y).sum(axis=1), o["out64"], rtol=1e-12,
                                atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 layers (P1 section of the INT3 QMoE page: FP16 or BF16, with the
+# activation and scale types matching).  Inputs are bfloat16 patterns; the
+# brute force widens them with torch's bfloat16 (independent of the oracle).
+# ---------------------------------------------------------------------------
+
+def _bf16_f64(bits):
+    torch = pytest.importorskip("torch")
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(
+        torch.float64).numpy()
+
+
+@pytest.mark.parametrize("bits1,bits2,bs", [(3, 3, 64), (4, 4, 32), (4, 3, 128)])
+def test_qmoe_bf16_brute_force(orc, bits1, bits2, bs):
+    T, H, I, E, k = 4, 128, 128, 5, 2
+    x = synth.activations_bf16(31, T, H)
+    logits = synth.router_logits(32, T, E)
+    W1 = synth.packed_rows(33, E * 2 * I, H, bits1).reshape(E, 2 * I, -1)
+    s1 = synth.scales_bf16(34, (E, 2 * I, H // bs))
+    W2 = synth.packed_rows(35, E * H, I, bits2).reshape(E, H, -1)
+    s2 = synth.scales_bf16(36, (E, H, I // bs))
+    b1 = synth.activations_bf16(37, E, 2 * I)
+    b2 = synth.activations_bf16(38, E, H)
+    o = orc.qmoe(x, logits, W1, s1, W2, s2, k=k, bits1=bits1, bits2=bits2, bs=bs, b1=b1, b2=b2,
+                 dtype="bf16")
+    ref, order, _ = qmoe_all_experts(_bf16_f64(x), logits, W1, _bf16_f64(s1), W2, _bf16_f64(s2),
+                                     k, bs, bits1, bits2, _bf16_f64(b1), _bf16_f64(b2))
+    assert np.array_equal(o["ids"], order)
+    np.testing.assert_allclose(o["out64"], ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max())
+    # out is the bfloat16 rounding of out64: within half a bf16 step, and the
+    # widened pattern matches torch's reading of it
+    np.testing.assert_array_equal(o["out"], _bf16_f64(o["out16"]))
+    assert (np.abs(o["out"] - o["out64"]) <= np.abs(o["out64"]) * 2.0 ** -8 + 1e-38).all()
+    # the same bytes read as fp16 give a different layer (the dtype is honoured)
+    o16 = orc.qmoe(x.view(np.float16), logits, W1, s1.view(np.float16), W2, s2.view(np.float16),
+                   k=k, bits1=bits1, bits2=bits2, bs=bs)
+    assert not np.allclose(o16["out64"], o["out64"])
+    # FC2 alone with the bf16 dtype reproduces the combine
+    y, _ = orc.qmoe_fc2(o["ids"], o["h"], W2, s2, H, I, E, bits2=bits2, bs=bs, b2=b2, dtype="bf16")
+    np.testing.assert_allclose((o["r"][:, :, None] * y).sum(axis=1), o["out64"], rtol=1e-12,
+                               atol=1e-14 * np.abs(ref).max())
