@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmnb.so")
 
 MNB_ABI_VERSION = 1
-MNB_DTYPE_F32, MNB_DTYPE_F16 = 0, 1
+MNB_DTYPE_F32, MNB_DTYPE_F16, MNB_DTYPE_BF16 = 0, 1, 2
 MNB_ROWS_BLOCKED, MNB_ROWS_ROW_LOCAL = 0, 1
 QMOE_ACT_SWIGLU = 1
 QMOE_GATE_UP_INTERLEAVED = 1
@@ -142,8 +142,8 @@ def dense_desc(K: int, N: int, block_size: int = 32, has_zero_points: bool = Fal
 
 
 def qmoe_proj_desc(K: int, N: int, num_experts: int, block_size: int = 64,
-                   bits: int = 3) -> mnb_desc:
-    return mnb_desc(MNB_ABI_VERSION, bits, block_size, 0, K, N, MNB_DTYPE_F16, 0,
+                   bits: int = 3, scale_dtype: int = MNB_DTYPE_F16) -> mnb_desc:
+    return mnb_desc(MNB_ABI_VERSION, bits, block_size, 0, K, N, scale_dtype, 0,
                     MNB_ROWS_ROW_LOCAL, num_experts)
 
 

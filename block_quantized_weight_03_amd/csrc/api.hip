@@ -86,6 +86,8 @@ int32_t check_qmoe(const mnb_plan* fc1, const mnb_plan* fc2, const qmoe_desc* q,
   if (s1->E != s2->E || s1->N % 2 || s2->K != s1->N / 2 || s2->N != s1->K)
     return MNB_ERR_INVALID_ARG;
   if (s1->bs != s2->bs) return MNB_ERR_UNSUPPORTED;
+  // one 16-bit type for activations and scales across the layer [P1]
+  if (fc1->desc.scale_dtype != fc2->desc.scale_dtype) return MNB_ERR_UNSUPPORTED;
   if (q->top_k < 1 || q->top_k > s1->E) return MNB_ERR_INVALID_ARG;
   return MNB_OK;
 }

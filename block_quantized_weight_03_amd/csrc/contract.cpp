@@ -40,7 +40,9 @@ int32_t check_desc(const mnb_desc* d, Sizes* s) {
   if (d->K < 1 || d->N < 1 || d->num_experts < 1) return MNB_ERR_INVALID_ARG;
   if (d->accuracy_level < 0 || d->accuracy_level > 4) return MNB_ERR_INVALID_ARG;
   if (d->has_zero_points != 0 && d->has_zero_points != 1) return MNB_ERR_INVALID_ARG;
-  if (d->scale_dtype != MNB_DTYPE_F32 && d->scale_dtype != MNB_DTYPE_F16) return MNB_ERR_INVALID_ARG;
+  if (d->scale_dtype != MNB_DTYPE_F32 && d->scale_dtype != MNB_DTYPE_F16 &&
+      d->scale_dtype != MNB_DTYPE_BF16)
+    return MNB_ERR_INVALID_ARG;
   if (d->row_layout != MNB_ROWS_BLOCKED && d->row_layout != MNB_ROWS_ROW_LOCAL) return MNB_ERR_INVALID_ARG;
   if (d->bits < 1 || d->bits > 8) return MNB_ERR_INVALID_ARG;
   if (d->block_size < 1) return MNB_ERR_INVALID_ARG;
@@ -62,7 +64,8 @@ int32_t check_desc(const mnb_desc* d, Sizes* s) {
     // QMoE v1 projection profile: INT3, or INT4 for the mixed (3,4) / (4,3)
     // width pairs and the all-INT4 layer; explicit zero points are accepted
     // only as the implicit value (checked with the content)
-    if (d->scale_dtype != MNB_DTYPE_F16 || d->row_layout != MNB_ROWS_ROW_LOCAL)
+    if ((d->scale_dtype != MNB_DTYPE_F16 && d->scale_dtype != MNB_DTYPE_BF16) ||
+        d->row_layout != MNB_ROWS_ROW_LOCAL)
       return MNB_ERR_UNSUPPORTED;
     if (d->K % d->block_size) return MNB_ERR_UNSUPPORTED;  // block-aligned K
     z.kind = kMoe;
@@ -137,12 +140,13 @@ int32_t validate_content(const mnb_desc* d, const Sizes& s, const uint8_t* B,
       if (zused && (zr[s.zrow - 1] >> zused)) return MNB_ERR_CONTENT;
     }
   }
-  // finite, nonnegative FP16 scales: exponent 31 is Inf/NaN; a set sign bit
-  // is only allowed on zero
+  // finite, nonnegative FP16 / BF16 scales: an all-ones exponent is Inf/NaN
+  // (fp16 0x7C00, bf16 0x7F80); a set sign bit is only allowed on zero
+  const uint16_t expo = d->scale_dtype == MNB_DTYPE_BF16 ? 0x7F80u : 0x7C00u;
   const uint64_t n = s.scales / 2;
   for (uint64_t i = 0; i < n; ++i) {
     const uint16_t h = load_u16(scales, i);
-    if ((h & 0x7C00u) == 0x7C00u) return MNB_ERR_CONTENT;
+    if ((h & expo) == expo) return MNB_ERR_CONTENT;
     if ((h & 0x8000u) && (h & 0x7FFFu)) return MNB_ERR_CONTENT;
   }
   // canonical padding: bits after K*bits in the last byte of a row are zero

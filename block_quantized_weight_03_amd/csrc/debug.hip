@@ -20,6 +20,7 @@ struct Rows {
   const uint8_t* zeros;
   int64_t N, K, nb, bs, row_bytes, zrow, row_base;  // row_base = expert * N + row0
   int kind, bits;
+  bool bf16;  // QMoE plan with bfloat16 scales (outputs bfloat16 patterns)
 };
 
 // byte offset of 32-code group G of row n of expert e in the tile-major QMoE
@@ -58,7 +59,7 @@ __global__ void debug_unpack_kernel(Rows r, int64_t nrows, uint8_t* __restrict__
   out[i] = (uint8_t)code_of(r, r.row_base + row, k);
 }
 
-__global__ void debug_dequant_kernel(Rows r, int64_t nrows, __half* __restrict__ out) {
+__global__ void debug_dequant_kernel(Rows r, int64_t nrows, uint16_t* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= nrows * r.K) return;
   const int64_t row = i / r.K, k = i % r.K;
@@ -77,10 +78,15 @@ __global__ void debug_dequant_kernel(Rows r, int64_t nrows, __half* __restrict__
     // (for z = 8, -(z*s) is exact and this is fp32((q - 8) * s))
     v = fmaf((float)q, s, -((float)z * s));
   } else {
-    const __half s = static_cast<const __half*>(r.scales)[grow * r.nb + b];
-    v = (float)((int)q - (1 << (r.bits - 1))) * __half2float(s);  // exact in fp32
+    const uint16_t sb = static_cast<const uint16_t*>(r.scales)[grow * r.nb + b];
+    const float s = r.bf16 ? __uint_as_float((uint32_t)sb << 16) : __half2float(__ushort_as_half(sb));
+    v = (float)((int)q - (1 << (r.bits - 1))) * s;  // exact in fp32
+    if (r.bf16) {
+      out[i] = __builtin_bit_cast(uint16_t, (__bf16)v);
+      return;
+    }
   }
-  out[i] = __float2half_rn(v);
+  out[i] = __half_as_ushort(__float2half_rn(v));
 }
 
 Rows make_rows(const Sizes& s, const mnb_plan& p, int64_t expert, int64_t row0) {
@@ -97,6 +103,7 @@ Rows make_rows(const Sizes& s, const mnb_plan& p, int64_t expert, int64_t row0) 
   r.row_base = expert * s.N + row0;
   r.kind = s.kind;
   r.bits = (int)s.bits;
+  r.bf16 = p.desc.scale_dtype == MNB_DTYPE_BF16;
   return r;
 }
 
@@ -116,7 +123,7 @@ hipError_t launch_debug_dequant_f16(const Sizes& s, const mnb_plan& p, int64_t e
   const int64_t n = nrows * s.K;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(debug_dequant_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                     make_rows(s, p, expert, row0), nrows, reinterpret_cast<__half*>(out));
+                     make_rows(s, p, expert, row0), nrows, out);
   return hipGetLastError();
 }
 

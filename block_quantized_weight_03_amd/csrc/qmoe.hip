@@ -39,6 +39,8 @@ namespace mnb {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -319,18 +321,54 @@ template <int BITS> struct Group;
 template <> struct Group<3> { typedef u32x3 W; };
 template <> struct Group<4> { typedef u32x4 W; };
 
+// 16-bit activation / scale / output type of a layer: IEEE fp16 (BF = false)
+// or bfloat16 (BF = true); the INT3 QMoE profile takes either, with the
+// activation and scale types matching.  kMagic is the base B (1024 or 128)
+// in both 16-bit halves: B + c is exact for every code c in either format.
+template <bool BF> struct Dt;
+template <> struct Dt<false> {
+  static constexpr uint32_t kMagic = 0x64006400u;
+  static constexpr float kBase = 1024.0f;
+  __device__ static float to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+  __device__ static uint16_t from_f32(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+};
+template <> struct Dt<true> {
+  static constexpr uint32_t kMagic = 0x43004300u;
+  static constexpr float kBase = 128.0f;
+  __device__ static float to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+  __device__ static uint16_t from_f32(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+};
+
 // fp16 bias that turns 1024 + q into the exact q - z, z = 2^(BITS-1)
 template <int BITS>
 __device__ __forceinline__ half2t zero_bias() {
-  constexpr float b = -(1024.0f + (float)(1 << (BITS - 1)));
+  constexpr float b = -(Dt<false>::kBase + (float)(1 << (BITS - 1)));
   return half2t{(_Float16)b, (_Float16)b};
 }
 
-// The 16 code pairs (c[2i], c[2i+1]) of a group as fp16 1024 + c in the two
-// halves of p[i]: the fp16 pattern of 1024 + c (c < 1024) is that of 1024
-// with c in its low mantissa bits, so each pair is one v_bfi_b32 into magic
-// (0x64006400, 1024.0 in both halves, kept in a register the compiler cannot
-// fold, so that the insert stays a single v_bfi_b32).  Words are copied into
+// the two 16-bit halves of a bfloat16 pair word as fp32 (exact)
+__device__ __forceinline__ float bf_lo(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t p) { return __uint_as_float(p & 0xFFFF0000u); }
+__device__ __forceinline__ uint32_t bf_pack(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)lo, (__bf16)hi});  // v_cvt_pk_bf16_f32, RNE
+}
+
+// v_mfma_f32_16x16x32 on fp16 or bfloat16 operands held as raw words
+template <bool BF>
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (BF)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),
+                                                  __builtin_bit_cast(half8, b), c, 0, 0, 0);
+}
+
+// The 16 code pairs (c[2i], c[2i+1]) of a group as B + c in the two 16-bit
+// halves of p[i] (B = 1024 in fp16, 128 in bfloat16): the pattern of B + c is
+// that of B with c in its low mantissa bits, so each pair is one v_bfi_b32
+// into magic (B in both halves, kept in a register the compiler cannot fold,
+// so that the insert stays a single v_bfi_b32).  Words are copied into
 // scalars before use.
 __device__ __forceinline__ void raw_pairs(const u32x3 w, uint32_t magic, uint32_t (&p)[16]) {
 #pragma unroll
@@ -350,25 +388,35 @@ __device__ __forceinline__ void raw_pairs(const u32x4 w, uint32_t magic, uint32_
   }
 }
 
-// the 32 codes of one group as four MFMA operands (8 consecutive k each):
-// v_pk_add_f16 makes the exact q - z, v_pk_mul_f16 by the fp16 scale rounds
-// once, fp16((q - z) * s)
-template <int BITS>
-__device__ __forceinline__ void dequant_group(const typename Group<BITS>::W w, _Float16 s,
-                                              uint32_t magic, half8 (&out)[4]) {
-  const half2t s2 = half2t{s, s}, zb = zero_bias<BITS>();
+// the 32 codes of one group as four MFMA operands (8 consecutive k each),
+// each weight rounded once, fp16((q - z) * s) or bf16((q - z) * s):
+// fp16: v_pk_add_f16 makes the exact q - z, v_pk_mul_f16 by the scale rounds;
+// bf16: (B + q) s - (B + z) s in one fp32 fma is exact, v_cvt_pk_bf16_f32
+// rounds.
+template <int BITS, bool BF>
+__device__ __forceinline__ void dequant_group(const typename Group<BITS>::W w, uint16_t sbits,
+                                              uint32_t magic, u32x4 (&out)[4]) {
   uint32_t p[16];
   raw_pairs(w, magic, p);
+  if constexpr (BF) {
+    const float s = Dt<true>::to_f32(sbits);
+    const float nb = -(Dt<true>::kBase + (float)(1 << (BITS - 1))) * s;  // exact
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    p[i] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2t, p[i]) + zb) * s2);
+    for (int i = 0; i < 16; ++i) p[i] = bf_pack(fmaf(bf_lo(p[i]), s, nb), fmaf(bf_hi(p[i]), s, nb));
+  } else {
+    const _Float16 s = __builtin_bit_cast(_Float16, sbits);
+    const half2t s2 = half2t{s, s}, zb = zero_bias<BITS>();
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
-    out[t] = __builtin_bit_cast(half8, u32x4{p[4 * t], p[4 * t + 1], p[4 * t + 2], p[4 * t + 3]});
+    for (int i = 0; i < 16; ++i)
+      p[i] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(half2t, p[i]) + zb) * s2);
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) out[t] = u32x4{p[4 * t], p[4 * t + 1], p[4 * t + 2], p[4 * t + 3]};
 }
 
+template <bool BF>
 __device__ __forceinline__ uint32_t opaque_magic() {
-  uint32_t m = 0x64006400u;
+  uint32_t m = Dt<BF>::kMagic;
   asm volatile("" : "+v"(m));
   return m;
 }
@@ -390,8 +438,8 @@ __device__ __forceinline__ uint32_t moe_goff(int N, int K, int n, int G) {
 
 struct MoeGemmArgs {
   const uint8_t* codes;    // [E][N][row_bytes], pair-interleaved groups
-  const __half* scales;    // [E][N][K/bs]
-  const void* act;         // FC1: x fp16 [T][K]; FC2: h fp16 [T*k][K] (grouped order)
+  const uint16_t* scales;  // [E][N][K/bs], fp16 or bf16
+  const void* act;         // FC1: x [T][K]; FC2: h [T*k][K] (grouped order); fp16 or bf16
   int64_t N, K, row_bytes, nblk, bs;
   int top_k, E;
   const int32_t* counts;
@@ -400,9 +448,9 @@ struct MoeGemmArgs {
   const int32_t* items;
   const int32_t* nitems;
   const float* wts;        // FC2: routing weights per slot
-  __half* h_out;           // FC1 output [T*k][N/2] (grouped order)
+  uint16_t* h_out;         // FC1 output [T*k][N/2] (grouped order), fp16 or bf16
   float* slot_out;         // FC2 output [T*k][N] (slot order)
-  const __half* bias;      // optional [E][N] projection bias (nullptr: none)
+  const uint16_t* bias;    // optional [E][N] projection bias (nullptr: none)
 };
 
 constexpr int kQBN = 64;         // weight rows per workgroup
@@ -413,7 +461,7 @@ constexpr int kQPitch = kQBK + 8;
 template <int BM>
 constexpr int ntg_of() { return BM == 32 ? 4 : 2; }
 
-template <bool FC1, int BM, int BITS>
+template <bool FC1, int BM, int BITS, bool BF>
 __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n, int64_t tiles_n) {
   constexpr uint32_t GB = 4 * BITS;    // bytes per 32-code group
   constexpr int kNTG = ntg_of<BM>();
@@ -465,7 +513,7 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
   const int Kc = (int)g.K;
   const int nch = (Kc + kQBK - 1) / kQBK;
   const int bshift = g.bs == 32 ? 5 : (g.bs == 64 ? 6 : 7);
-  const uint32_t magic = opaque_magic();
+  const uint32_t magic = opaque_magic<BF>();
   const uint8_t* wbase = g.codes + (int64_t)e * g.N * g.row_bytes;  // this expert's codes
   const int Nc = (int)g.N;
   const uint16_t* sbase = reinterpret_cast<const uint16_t*>(g.scales) + (int64_t)e * g.N * g.nblk;
@@ -546,14 +594,14 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
       for (int r = 0; r < 4; ++r) {
         const int row = i * 16 + 4 * (lane >> 4) + r;
         float v = acc[t][i][r];
-        if (g.bias && col < g.N) v += __half2float(g.bias[(int64_t)e * g.N + col]);
+        if (g.bias && col < g.N) v += Dt<BF>::to_f32(g.bias[(int64_t)e * g.N + col]);
         if (FC1) {
           // interleaved gate/up: even row = gate_i, odd row = up_i
           const float partner = __shfl_xor(v, 1);
           if ((lane & 1) == 0 && row < rows && col < g.N) {
             const float gt = v, up = partner;
             const float hv = gt / (1.0f + expf(-gt)) * up;
-            g.h_out[(seg0 + row) * (g.N / 2) + col / 2] = __float2half_rn(hv);
+            g.h_out[(seg0 + row) * (g.N / 2) + col / 2] = Dt<BF>::from_f32(hv);
           }
         } else {
           if (row < rows && col < g.N) {
@@ -576,8 +624,8 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
     const int b = c & 1;
 #pragma unroll
     for (int t = 0; t < kNTG; ++t) {
-      half8 wf[4];
-      dequant_group<BITS>(ws[t].rw, __builtin_bit_cast(_Float16, (uint16_t)(ws[t].ok ? ws[t].rs : 0u)), magic, wf);
+      u32x4 wf[4];
+      dequant_group<BITS, BF>(ws[t].rw, (uint16_t)(ws[t].ok ? ws[t].rs : 0u), magic, wf);
       load_w(ws[t], t, c + 1);
       if (t < ntc) {
 #pragma unroll
@@ -586,8 +634,8 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
 #pragma unroll
           for (int i = 0; i < TM; ++i) {
             if (i < vt) {
-              const half8 a = *reinterpret_cast<const half8*>(&As[b][(i * 16 + fr) * kQPitch + kk]);
-              acc[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, wf[q], acc[t][i], 0, 0, 0);
+              const u32x4 a = *reinterpret_cast<const u32x4*>(&As[b][(i * 16 + fr) * kQPitch + kk]);
+              acc[t][i] = mfma16x16x32<BF>(a, wf[q], acc[t][i]);
             }
           }
         }
@@ -616,24 +664,39 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
 __device__ __forceinline__ half2t as_half2(uint32_t v) { return __builtin_bit_cast(half2t, v); }
 
 // s * sum_k (q_k - z) a_k over one 32-code group, for the decode GEMVs: the
-// codes become exact fp16 (q - z) (no per-code scale multiply), v_dot2 sums
-// the exact products in fp32 and the group's scale is applied once.
-template <int BITS>
+// codes become exact fp16 / bf16 (q - z) (no per-code scale multiply), v_dot2
+// sums the exact products in fp32 and the group's scale is applied once.
+template <int BITS, bool BF>
 __device__ __forceinline__ float group_dot_unscaled(const typename Group<BITS>::W w, float s,
                                                     uint32_t magic, const u32x4* a16) {
-  const half2t zb = zero_bias<BITS>();
   uint32_t p[16];
   raw_pairs(w, magic, p);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) p[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2t, p[i]) + zb);
   float acc = 0.0f;
+  if constexpr (BF) {
+    const float zb = -(Dt<true>::kBase + (float)(1 << (BITS - 1)));
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const u32x4 av = a16[t];
-    acc = __builtin_amdgcn_fdot2(as_half2(p[4 * t]), as_half2(av.x), acc, false);
-    acc = __builtin_amdgcn_fdot2(as_half2(p[4 * t + 1]), as_half2(av.y), acc, false);
-    acc = __builtin_amdgcn_fdot2(as_half2(p[4 * t + 2]), as_half2(av.z), acc, false);
-    acc = __builtin_amdgcn_fdot2(as_half2(p[4 * t + 3]), as_half2(av.w), acc, false);
+    for (int i = 0; i < 16; ++i) p[i] = bf_pack(bf_lo(p[i]) + zb, bf_hi(p[i]) + zb);  // exact
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const u32x4 av = a16[t];
+      const uint32_t a0 = av.x, a1 = av.y, a2 = av.z, a3 = av.w;
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p[4 * t]), __builtin_bit_cast(bf16x2, a0), acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p[4 * t + 1]), __builtin_bit_cast(bf16x2, a1), acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p[4 * t + 2]), __builtin_bit_cast(bf16x2, a2), acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p[4 * t + 3]), __builtin_bit_cast(bf16x2, a3), acc, false);
+    }
+  } else {
+    const half2t zb = zero_bias<BITS>();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2t, p[i]) + zb);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const u32x4 av = a16[t];
+      acc = __builtin_amdgcn_fdot2(as_half2(p[4 * t]), as_half2(av.x), acc, false);
+      acc = __builtin_amdgcn_fdot2(as_half2(p[4 * t + 1]), as_half2(av.y), acc, false);
+      acc = __builtin_amdgcn_fdot2(as_half2(p[4 * t + 2]), as_half2(av.z), acc, false);
+      acc = __builtin_amdgcn_fdot2(as_half2(p[4 * t + 3]), as_half2(av.w), acc, false);
+    }
   }
   return acc * s;
 }
@@ -653,7 +716,7 @@ struct TileRef {
   int N, K, nblk, bshift, row, ng, nch, g;
 };
 
-template <int BITS>
+template <int BITS, bool BF>
 struct TileBatch {
   typename Group<BITS>::W w[kDecBatch];
   uint16_t s[kDecBatch];
@@ -681,7 +744,7 @@ struct TileBatch {
     for (int u = 0; u < kDecBatch; ++u)
       if (u < cnt) {
         const uint16_t sc = (ok >> u) & 1u ? s[u] : (uint16_t)0;
-        acc += group_dot_unscaled<BITS>(w[u], (float)__builtin_bit_cast(_Float16, sc), magic,
+        acc += group_dot_unscaled<BITS, BF>(w[u], Dt<BF>::to_f32(sc), magic,
                                   reinterpret_cast<const u32x4*>(xs + 32 * G[u]));
       }
     return acc;
@@ -692,7 +755,7 @@ struct TileBatch {
 // (lane >> 3) & 3, lane >> 5) takes group 4c + g of row n for the chunks
 // c = c0 + 2u + h (used where 16-row tiles would leave CUs idle).  Chunks or
 // groups past K are skipped per lane.
-template <int BITS>
+template <int BITS, bool BF>
 struct HalfBatch {
   static constexpr int kU = kDecBatch / 2;
   typename Group<BITS>::W w[kU];
@@ -718,7 +781,7 @@ struct HalfBatch {
 #pragma unroll
     for (int u = 0; u < kU; ++u)
       if ((ok >> u) & 1u)
-        acc += group_dot_unscaled<BITS>(w[u], (float)__builtin_bit_cast(_Float16, s[u]), magic,
+        acc += group_dot_unscaled<BITS, BF>(w[u], Dt<BF>::to_f32(s[u]), magic,
                                   reinterpret_cast<const u32x4*>(xs + 32 * G[u]));
     return acc;
   }
@@ -751,7 +814,7 @@ __device__ __forceinline__ TileRef tile_ref(const MoeGemmArgs& g, int e, int row
   t.N = (int)g.N;
   t.K = (int)g.K;
   t.codes = g.codes + (int64_t)e * t.N * g.row_bytes;
-  t.scales = reinterpret_cast<const uint16_t*>(g.scales) + (int64_t)e * t.N * g.nblk;
+  t.scales = g.scales + (int64_t)e * t.N * g.nblk;
   t.nblk = (int)g.nblk;
   t.bshift = g.bs == 32 ? 5 : (g.bs == 64 ? 6 : 7);
   t.row = row0 + (lane & 15);
@@ -770,7 +833,7 @@ __device__ __forceinline__ TileRef tile_ref(const MoeGemmArgs& g, int e, int row
 // chunks w, w + 4, ... of expert ids[t, j]'s tile; partials are summed in a
 // fixed order and h[slot I + 8 tile + m] = fp16(silu(g_m) u_m) for gate row
 // 2m, up row 2m + 1.
-template <int kPer, bool ROUTE, int BITS>
+template <int kPer, bool ROUTE, int BITS, bool BF>
 __global__ void __launch_bounds__(256) qmoe_fc1_decode(MoeGemmArgs g, int64_t T,
                                                        const float* __restrict__ logits,
                                                        int32_t* __restrict__ ids,
@@ -802,12 +865,12 @@ __global__ void __launch_bounds__(256) qmoe_fc1_decode(MoeGemmArgs g, int64_t T,
     e = clamp_id(ids[slot], g.E);
   }
   const TileRef tr = tile_ref(g, e, 16 * tile, lane);
-  TileBatch<BITS> b;
+  TileBatch<BITS, BF> b;
   b.load(tr, wave, 4);
   __builtin_amdgcn_sched_barrier(0);
   xst.rest(xr, reinterpret_cast<u32x4*>(xs), K / 8, tid, 256);
   __syncthreads();
-  const uint32_t magic = opaque_magic();
+  const uint32_t magic = opaque_magic<BF>();
   float acc = b.dot(xs, magic);
   for (int c = wave + 4 * kDecBatch; c < tr.nch; c += 4 * kDecBatch) {
     b.load(tr, c, 4);
@@ -823,11 +886,11 @@ __global__ void __launch_bounds__(256) qmoe_fc1_decode(MoeGemmArgs g, int64_t T,
         us += red[w * 64 + q * 16 + 2 * tid + 1];
       }
     if (g.bias) {
-      const __half* b = g.bias + (int64_t)e * N + 16 * tile + 2 * tid;
-      gs += __half2float(b[0]);
-      us += __half2float(b[1]);
+      const uint16_t* b = g.bias + (int64_t)e * N + 16 * tile + 2 * tid;
+      gs += Dt<BF>::to_f32(b[0]);
+      us += Dt<BF>::to_f32(b[1]);
     }
-    g.h_out[(int64_t)slot * I + 8 * tile + tid] = __float2half_rn(gs / (1.0f + expf(-gs)) * us);
+    g.h_out[(int64_t)slot * I + 8 * tile + tid] = Dt<BF>::from_f32(gs / (1.0f + expf(-gs)) * us);
   }
 }
 
@@ -835,8 +898,8 @@ __global__ void __launch_bounds__(256) qmoe_fc1_decode(MoeGemmArgs g, int64_t T,
 // j; the token's k rows of h are staged in LDS; wave j forms the partials of
 // expert ids[t, j]'s tile rows, then out[t, n] = fp16(sum_j r_j y_j[n]) with
 // y_j and the rank sum in fixed orders.
-template <int BITS>
-__global__ void __launch_bounds__(1024) qmoe_fc2_decode(MoeGemmArgs g, int64_t T, __half* out,
+template <int BITS, bool BF>
+__global__ void __launch_bounds__(1024) qmoe_fc2_decode(MoeGemmArgs g, int64_t T, uint16_t* out,
                                                         float* slot_dbg) {
   extern __shared__ __align__(16) uint8_t sm[];
   const int H = (int)g.N, I = (int)g.K, k = g.top_k, ntile = H >> 3;  // 8-row tiles
@@ -853,15 +916,15 @@ __global__ void __launch_bounds__(1024) qmoe_fc2_decode(MoeGemmArgs g, int64_t T
   Stage2 hst;
   hst.first(hr, k * I / 8, tid, 64 * k);
   __builtin_amdgcn_sched_barrier(0);
-  HalfBatch<BITS> b;
+  HalfBatch<BITS, BF> b;
   b.load(tr, 0, hsel);
   __builtin_amdgcn_sched_barrier(0);
   hst.rest(hr, reinterpret_cast<u32x4*>(hs), k * I / 8, tid, 64 * k);
   __syncthreads();
-  const uint32_t magic = opaque_magic();
+  const uint32_t magic = opaque_magic<BF>();
   const _Float16* hj = hs + j * I;
   float acc = b.dot(hj, magic);
-  for (int c = 2 * HalfBatch<BITS>::kU; c < tr.nch; c += 2 * HalfBatch<BITS>::kU) {
+  for (int c = 2 * HalfBatch<BITS, BF>::kU; c < tr.nch; c += 2 * HalfBatch<BITS, BF>::kU) {
     b.load(tr, c, hsel);
     acc += b.dot(hj, magic);
   }
@@ -873,20 +936,21 @@ __global__ void __launch_bounds__(1024) qmoe_fc2_decode(MoeGemmArgs g, int64_t T
     for (int r = 0; r < k; ++r) {
       float y = 0.0f;
       for (int q = 0; q < 8; ++q) y += red[r * 64 + q * 8 + tid];
-      if (g.bias) y += __half2float(g.bias[(int64_t)clamp_id(g.perm[t * k + r], g.E) * H + n]);
+      if (g.bias) y += Dt<BF>::to_f32(g.bias[(int64_t)clamp_id(g.perm[t * k + r], g.E) * H + n]);
       const float ry = g.wts[t * k + r] * y;
       if (slot_dbg) slot_dbg[((int64_t)t * k + r) * H + n] = ry;
       o += ry;
     }
-    out[(int64_t)t * H + n] = __float2half_rn(o);
+    out[(int64_t)t * H + n] = Dt<BF>::from_f32(o);
   }
 }
 
 // ---------------------------------------------------------------------------
 // 5. combine
 // ---------------------------------------------------------------------------
+template <bool BF>
 __global__ void __launch_bounds__(256) qmoe_combine(const float* __restrict__ slots, int64_t T,
-                                                    int k, int64_t H, __half* __restrict__ out) {
+                                                    int k, int64_t H, uint16_t* __restrict__ out) {
   // four consecutive outputs per thread (H % 32 == 0): 16-byte slot loads
   const int64_t i4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i4 >= T * H / 4) return;
@@ -897,13 +961,14 @@ __global__ void __launch_bounds__(256) qmoe_combine(const float* __restrict__ sl
     const f32x4 v = *reinterpret_cast<const f32x4*>(slots + (t * k + j) * H + n);
     acc = f32x4{acc.x + v.x, acc.y + v.y, acc.z + v.z, acc.w + v.w};
   }
-  const half2t lo = half2t{(_Float16)acc.x, (_Float16)acc.y}, hi = half2t{(_Float16)acc.z, (_Float16)acc.w};
-  *reinterpret_cast<u32x2*>(out + i) = u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+  const uint32_t lo = (uint32_t)Dt<BF>::from_f32(acc.x) | ((uint32_t)Dt<BF>::from_f32(acc.y) << 16);
+  const uint32_t hi = (uint32_t)Dt<BF>::from_f32(acc.z) | ((uint32_t)Dt<BF>::from_f32(acc.w) << 16);
+  *reinterpret_cast<u32x2*>(out + i) = u32x2{lo, hi};
 }
 
 // debug: h rows back in slot order
-__global__ void qmoe_gather_h(const __half* __restrict__ h, const int32_t* __restrict__ inv,
-                              int64_t S, int64_t I, __half* __restrict__ dst) {
+__global__ void qmoe_gather_h(const uint16_t* __restrict__ h, const int32_t* __restrict__ inv,
+                              int64_t S, int64_t I, uint16_t* __restrict__ dst) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= S * I) return;
   const int64_t slot = i / I, c = i % I;
@@ -949,13 +1014,21 @@ Ws ws_layout(const Sizes& s1, const Sizes& s2, int k, int64_t T) {
   return w;
 }
 
-// Calls f with the code width (3 or 4) as a compile-time constant.
+// Calls f with the code width (3 or 4) and the bfloat16 flag as compile-time
+// constants.
 template <typename F>
-void by_bits(int64_t bits, F&& f) {
-  if (bits == 4)
-    f(std::integral_constant<int, 4>());
-  else
-    f(std::integral_constant<int, 3>());
+void by_kind(int64_t bits, bool bf, F&& f) {
+  if (bits == 4) {
+    if (bf)
+      f(std::integral_constant<int, 4>(), std::true_type());
+    else
+      f(std::integral_constant<int, 4>(), std::false_type());
+  } else {
+    if (bf)
+      f(std::integral_constant<int, 3>(), std::true_type());
+    else
+      f(std::integral_constant<int, 3>(), std::false_type());
+  }
 }
 
 void launch_route(const float* logits, int64_t T, int E, int k, int32_t* ids, float* wts,
@@ -995,41 +1068,45 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
   GroupOut go{reinterpret_cast<int32_t*>(w + L.counts), reinterpret_cast<int32_t*>(w + L.offsets),
               reinterpret_cast<int32_t*>(w + L.perm), reinterpret_cast<int32_t*>(w + L.inv),
               reinterpret_cast<int32_t*>(w + L.items), reinterpret_cast<int32_t*>(w + L.nitems)};
-  __half* hbuf = reinterpret_cast<__half*>(w + L.h);
+  uint16_t* hbuf = reinterpret_cast<uint16_t*>(w + L.h);
   float* slots = reinterpret_cast<float*>(w + L.slots);
+  // activations, scales, biases, h and out share the plans' 16-bit type
+  const bool bf = p1.desc.scale_dtype == MNB_DTYPE_BF16;
   const size_t group_lds = (size_t)(5 + kGroupThreads / 64) * E * 4;
 
   // few tokens: per-slot GEMVs, no grouping (every slot reads its expert once);
   // the activation rows they stage in LDS bound H and k * I
   if (T * k <= kDecodeSlots && H <= 16384 && k * I <= 16384) {
     const int64_t S = T * k;
-    MoeGemmArgs a1{static_cast<const uint8_t*>(p1.codes), static_cast<const __half*>(p1.scales),
+    MoeGemmArgs a1{static_cast<const uint8_t*>(p1.codes), static_cast<const uint16_t*>(p1.scales),
                    x, s1.N, s1.K, s1.row_bytes, s1.nb, s1.bs, k, (int)E,
                    nullptr, nullptr, ids, nullptr, nullptr, wts, hbuf, nullptr,
-                   reinterpret_cast<const __half*>(b1)};
+                   b1};
     const dim3 g1((unsigned)(S * (s1.N / 16))), wg1(256);
     const size_t l1 = (size_t)(2 * H + 4 * 256 + 128);
     if (S > kFusedRouteSlots) launch_route(logits, T, (int)E, k, ids, wts, st);
-    by_bits(s1.bits, [&](auto bits) {
+    by_kind(s1.bits, bf, [&](auto bits, auto bfc) {
       constexpr int B = decltype(bits)::value;
+      constexpr bool BF = decltype(bfc)::value;
       if (S > kFusedRouteSlots)
-        hipLaunchKernelGGL((qmoe_fc1_decode<2, false, B>), g1, wg1, l1, st, a1, T, logits, ids, wts);
+        hipLaunchKernelGGL((qmoe_fc1_decode<2, false, B, BF>), g1, wg1, l1, st, a1, T, logits, ids, wts);
       else if (E <= 128)
-        hipLaunchKernelGGL((qmoe_fc1_decode<2, true, B>), g1, wg1, l1, st, a1, T, logits, ids, wts);
+        hipLaunchKernelGGL((qmoe_fc1_decode<2, true, B, BF>), g1, wg1, l1, st, a1, T, logits, ids, wts);
       else if (E <= 256)
-        hipLaunchKernelGGL((qmoe_fc1_decode<4, true, B>), g1, wg1, l1, st, a1, T, logits, ids, wts);
+        hipLaunchKernelGGL((qmoe_fc1_decode<4, true, B, BF>), g1, wg1, l1, st, a1, T, logits, ids, wts);
       else
-        hipLaunchKernelGGL((qmoe_fc1_decode<kMaxE / 64, true, B>), g1, wg1, l1, st, a1, T, logits, ids, wts);
+        hipLaunchKernelGGL((qmoe_fc1_decode<kMaxE / 64, true, B, BF>), g1, wg1, l1, st, a1, T, logits, ids, wts);
     });
-    MoeGemmArgs a2{static_cast<const uint8_t*>(p2.codes), static_cast<const __half*>(p2.scales),
+    MoeGemmArgs a2{static_cast<const uint8_t*>(p2.codes), static_cast<const uint16_t*>(p2.scales),
                    hbuf, s2.N, s2.K, s2.row_bytes, s2.nb, s2.bs, k, (int)E,
                    nullptr, nullptr, ids, nullptr, nullptr, wts, nullptr, nullptr,
-                   reinterpret_cast<const __half*>(b2)};
-    by_bits(s2.bits, [&](auto bits) {
+                   b2};
+    by_kind(s2.bits, bf, [&](auto bits, auto bfc) {
       constexpr int B = decltype(bits)::value;
-      hipLaunchKernelGGL((qmoe_fc2_decode<B>), dim3((unsigned)(T * (H / 8))), dim3(64 * k),
-                         (size_t)(2 * k * I + 4 * 64 * k), st, a2, T,
-                         reinterpret_cast<__half*>(out), dbg ? dbg->slot : nullptr);
+      constexpr bool BF = decltype(bfc)::value;
+      hipLaunchKernelGGL((qmoe_fc2_decode<B, BF>), dim3((unsigned)(T * (H / 8))), dim3(64 * k),
+                         (size_t)(2 * k * I + 4 * 64 * k), st, a2, T, out,
+                         dbg ? dbg->slot : nullptr);
     });
     if (dbg) {
       if (dbg->ids) (void)hipMemcpyAsync(dbg->ids, ids, S * 4, hipMemcpyDeviceToDevice, st);
@@ -1047,35 +1124,40 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
     launch_route(logits + t0 * E, Tt, (int)E, k, ids, wts, st);
     hipLaunchKernelGGL(qmoe_group, dim3(1), dim3(kGroupThreads), group_lds, st, ids, Tt, k, (int)E,
                        items, bm, go);
-    MoeGemmArgs a1{static_cast<const uint8_t*>(p1.codes), static_cast<const __half*>(p1.scales),
+    MoeGemmArgs a1{static_cast<const uint8_t*>(p1.codes), static_cast<const uint16_t*>(p1.scales),
                    x + t0 * H, s1.N, s1.K, s1.row_bytes, s1.nb, s1.bs, k, (int)E,
                    go.counts, go.offsets, go.perm, go.items, go.nitems, wts, hbuf, nullptr,
-                   reinterpret_cast<const __half*>(b1)};
+                   b1};
     const int ntg = bm == 32 ? ntg_of<32>() : ntg_of<kMaxBM>();
     const int64_t nt1 = (s1.N + kQBN - 1) / kQBN, ng1 = (nt1 + ntg - 1) / ntg;
     const dim3 grid1((unsigned)((items + 7) / 8 * 8 * ng1));
-    by_bits(s1.bits, [&](auto bits) {
+    by_kind(s1.bits, bf, [&](auto bits, auto bfc) {
       constexpr int B = decltype(bits)::value;
+      constexpr bool BF = decltype(bfc)::value;
       if (bm == 32)
-        hipLaunchKernelGGL((qmoe_gemm<true, 32, B>), grid1, dim3(256), 0, st, a1, ng1, nt1);
+        hipLaunchKernelGGL((qmoe_gemm<true, 32, B, BF>), grid1, dim3(256), 0, st, a1, ng1, nt1);
       else
-        hipLaunchKernelGGL((qmoe_gemm<true, kMaxBM, B>), grid1, dim3(256), 0, st, a1, ng1, nt1);
+        hipLaunchKernelGGL((qmoe_gemm<true, kMaxBM, B, BF>), grid1, dim3(256), 0, st, a1, ng1, nt1);
     });
-    MoeGemmArgs a2{static_cast<const uint8_t*>(p2.codes), static_cast<const __half*>(p2.scales),
+    MoeGemmArgs a2{static_cast<const uint8_t*>(p2.codes), static_cast<const uint16_t*>(p2.scales),
                    hbuf, s2.N, s2.K, s2.row_bytes, s2.nb, s2.bs, k, (int)E,
                    go.counts, go.offsets, go.perm, go.items, go.nitems, wts, nullptr, slots,
-                   reinterpret_cast<const __half*>(b2)};
+                   b2};
     const int64_t nt2 = (s2.N + kQBN - 1) / kQBN, ng2 = (nt2 + ntg - 1) / ntg;
     const dim3 grid2((unsigned)((items + 7) / 8 * 8 * ng2));
-    by_bits(s2.bits, [&](auto bits) {
+    by_kind(s2.bits, bf, [&](auto bits, auto bfc) {
       constexpr int B = decltype(bits)::value;
+      constexpr bool BF = decltype(bfc)::value;
       if (bm == 32)
-        hipLaunchKernelGGL((qmoe_gemm<false, 32, B>), grid2, dim3(256), 0, st, a2, ng2, nt2);
+        hipLaunchKernelGGL((qmoe_gemm<false, 32, B, BF>), grid2, dim3(256), 0, st, a2, ng2, nt2);
       else
-        hipLaunchKernelGGL((qmoe_gemm<false, kMaxBM, B>), grid2, dim3(256), 0, st, a2, ng2, nt2);
+        hipLaunchKernelGGL((qmoe_gemm<false, kMaxBM, B, BF>), grid2, dim3(256), 0, st, a2, ng2, nt2);
     });
-    hipLaunchKernelGGL(qmoe_combine, dim3((unsigned)((Tt * H / 4 + 255) / 256)), dim3(256), 0, st,
-                       slots, Tt, k, H, reinterpret_cast<__half*>(out + t0 * H));
+    const dim3 gridc((unsigned)((Tt * H / 4 + 255) / 256));
+    if (bf)
+      hipLaunchKernelGGL(qmoe_combine<true>, gridc, dim3(256), 0, st, slots, Tt, k, H, out + t0 * H);
+    else
+      hipLaunchKernelGGL(qmoe_combine<false>, gridc, dim3(256), 0, st, slots, Tt, k, H, out + t0 * H);
     if (dbg) {
       if (dbg->ids)
         (void)hipMemcpyAsync(dbg->ids + t0 * k, ids, S * 4, hipMemcpyDeviceToDevice, st);
@@ -1084,7 +1166,7 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
         (void)hipMemcpyAsync(dbg->slot + t0 * k * H, slots, S * H * 4, hipMemcpyDeviceToDevice, st);
       if (dbg->h)
         hipLaunchKernelGGL(qmoe_gather_h, dim3((unsigned)((S * I + 255) / 256)), dim3(256), 0, st,
-                           hbuf, go.inv, S, I, reinterpret_cast<__half*>(dbg->h + t0 * k * I));
+                           hbuf, go.inv, S, I, dbg->h + t0 * k * I);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -79,7 +79,7 @@ typedef enum mnb_status {
   MNB_ERR_HOST_MEMORY = -8          /* host staging allocation failed          */
 } mnb_status;
 
-enum { MNB_DTYPE_F32 = 0, MNB_DTYPE_F16 = 1 };
+enum { MNB_DTYPE_F32 = 0, MNB_DTYPE_F16 = 1, MNB_DTYPE_BF16 = 2 };
 
 /* Row layouts of B.  BLOCKED: each row is ceil(K/bs) blocks of bs*bits/8
  * bytes, the K tail padded to a whole block [PLAN K01].  ROW_LOCAL: each row
@@ -92,7 +92,7 @@ enum { MNB_ROWS_BLOCKED = 0, MNB_ROWS_ROW_LOCAL = 1 };
  *    F32, row_layout BLOCKED, num_experts 1, zero points optional, any
  *    K >= 1 and N >= 1;
  *  QMoE projection [P1]: bits 3 or 4, block_size 32/64/128, scale_dtype
- *    F16, row_layout ROW_LOCAL, num_experts >= 1, zero points implicit
+ *    F16 or BF16, row_layout ROW_LOCAL, num_experts >= 1, zero points implicit
  *    (2^(bits-1): 4 or 8) or explicit with every value equal to that
  *    ("all-4 explicit zero points" for INT3), K a multiple of block_size,
  *    any N >= 1 (per-expert matrix [N, K]).
@@ -105,7 +105,7 @@ typedef struct mnb_desc {
   int32_t accuracy_level;  /* 0..4                                            */
   int64_t K;               /* reduction length (columns of the logical W)    */
   int64_t N;               /* output features (rows of W, per expert)        */
-  int32_t scale_dtype;     /* MNB_DTYPE_F32 (dense) / MNB_DTYPE_F16 (QMoE)   */
+  int32_t scale_dtype;     /* MNB_DTYPE_F32 (dense); F16 or BF16 (QMoE)      */
   int32_t has_zero_points; /* 0 = implicit 2^(bits-1), 1 = explicit          */
   int32_t row_layout;      /* MNB_ROWS_BLOCKED / MNB_ROWS_ROW_LOCAL          */
   int32_t num_experts;     /* 1 for dense; E for a stacked QMoE projection   */
@@ -154,7 +154,8 @@ int32_t mnb_prepacked_size(const mnb_desc* desc, uint64_t* bytes);
  * Host inputs (read only; any alignment):
  *  B_host           uint8, [E*N, nb, bs*bits/8] (BLOCKED) or
  *                   [E*N, ceil(K*bits/8)] (ROW_LOCAL), E = num_experts;
- *  scales_host      fp32 or fp16 (per scale_dtype), [E*N, nb], index n*nb + b;
+ *  scales_host      fp32, fp16 or bf16 (per scale_dtype), [E*N, nb], index
+ *                   n*nb + b;
  *  zero_points_host NULL when has_zero_points == 0, else uint8
  *                   dense: [N, ceil(nb/2)]: block b of row n in byte b/2,
  *                   low nibble for even b;  QMoE: packed per-row block zero
@@ -238,13 +239,18 @@ int32_t qmoe_workspace_size(const mnb_plan* fc1, const mnb_plan* fc2,
  *  fc2: QMoE plan with N = H, K = I; both with the same num_experts E and
  *       block size; each projection has its own width (3 or 4 bits), so the
  *       pairs (3,3), (3,4), (4,3) and (4,4) all run.
- *  x_dev      fp16 [T, H] activations, 16-byte aligned;
+ *  x_dev      [T, H] activations, 16-byte aligned, in the plans' 16-bit type:
+ *             fp16 for F16 plans, bf16 for BF16 plans ([P1]: matching
+ *             FP16/BF16 activation and scale types; both plans must share
+ *             scale_dtype, else UNSUPPORTED);
  *  logits_dev fp32 [T, E] router logits;
- *  out_dev    fp16 [T, H], 8-byte aligned (misaligned x or out: INVALID_ARG).
+ *  out_dev    [T, H] in the same 16-bit type, 8-byte aligned (misaligned x or
+ *             out: INVALID_ARG).
  * Computes, per token: top_k experts by logit (ties: lower index), weights
  * r_j = softmax over the selected logits (= fp32 softmax over all E then
  * renormalization); weights dequantize as (q - 2^(bits-1)) * s;
- * h = silu(x.W1g^T) * (x.W1u^T) rounded to fp16;
+ * weights enter the matrix cores rounded once to the layer's type,
+ * h = silu(x.W1g^T) * (x.W1u^T) rounded to that type;
  * out = fp16(sum_j r_j * h_j.W2^T) summed in rank order.
  * T = 0 is a no-op.  No host synchronisation (graph-capturable).
  * Errors: INVALID_ARG, UNSUPPORTED, STALE_PLAN, WORKSPACE_TOO_SMALL, DEVICE. */
@@ -255,10 +261,11 @@ int32_t qmoe_forward(const mnb_plan* fc1, const mnb_plan* fc2,
 
 /* qmoe_forward with the optional projection biases [P1] ("optional
  * biases"):
- *  fc1_bias_dev fp16 [E, 2I] (row order of FC1: gate_i at 2i, up_i at
+ *  fc1_bias_dev [E, 2I] in the layer's 16-bit type (row order of FC1: gate_i at 2i, up_i at
  *               2i + 1), added to g and u before SwiGLU; NULL = none;
- *  fc2_bias_dev fp16 [E, H], added to each expert's FC2 output before its
- *               routing weight: out = fp16(sum_j r_j (h_j.W2^T + b2[e_j]));
+ *  fc2_bias_dev [E, H] in that type, added to each expert's FC2 output
+ *               before its routing weight:
+ *               out = round(sum_j r_j (h_j.W2^T + b2[e_j]));
  *               NULL = none.
  * Both 2-byte aligned (else INVALID_ARG); read only.  Everything else as for
  * qmoe_forward, which is this call with two NULL biases. */

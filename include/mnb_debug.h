@@ -44,8 +44,9 @@ int32_t mnb_debug_unpack(const mnb_plan* plan, int64_t expert, int64_t row0,
 /* Device dequantization of rows [row0, row0 + nrows) of expert `expert` into
  * out_dev [nrows, K] using the exact rounding chain of the matrix-core path:
  * dense INT4: fp16(fma(q, s, -(z * s))) with the fma and z * s in fp32 (for the
- * implicit z = 8 this equals fp16(fp32((q - 8) * s))); INT3: fp16((q - 4) * s16)
- * with one rounding.  out_dev holds binary16 values. */
+ * implicit z = 8 this equals fp16(fp32((q - 8) * s))); QMoE: (q - 2^(bits-1)) * s
+ * rounded once to the plan's 16-bit scale type.  out_dev holds binary16
+ * patterns (bfloat16 patterns for BF16 QMoE plans). */
 int32_t mnb_debug_dequant_f16(const mnb_plan* plan, int64_t expert,
                               int64_t row0, int64_t nrows, uint16_t* out_dev,
                               void* stream);

@@ -350,3 +350,40 @@ def test_moe_explicit_zero_points_must_equal_the_implicit_value(orc, bits, K, bs
         with pytest.raises(mnb.MnbError) as e:
             host_prepare(dz, W, s, pad)
         assert e.value.status == CONTENT
+
+
+@pytest.mark.parametrize("bad", [0x7F80, 0xFF80, 0x7FC0, 0xBF00, 0x8001])
+def test_bf16_moe_scale_content_rejected(bad):
+    """bfloat16 QMoE scales: finite and nonnegative (exponent 0xFF is Inf/NaN;
+    a sign bit only on zero)."""
+    E, N, K, bs = 2, 4, 128, 64
+    W = synth.packed_rows(4, E * N, K, 3)
+    s = synth.scales_bf16(5, (E * N, K // bs))
+    desc = mnb.qmoe_proj_desc(K, N, E, bs, 3, mnb.MNB_DTYPE_BF16)
+    ok = s.copy()
+    ok[0, 0] = 0x8000  # -0 is accepted
+    host_prepare(desc, W, ok, None)
+    s[3, 1] = bad
+    with pytest.raises(mnb.MnbError) as ei:
+        host_prepare(desc, W, s, None)
+    assert ei.value.status == CONTENT
+
+
+def test_qmoe_layer_dtypes_must_match():
+    E, H, I, bs = 4, 128, 64, 64
+    p = {}
+    keep = []
+    for dt in (mnb.MNB_DTYPE_F16, mnb.MNB_DTYPE_BF16):
+        W1 = synth.packed_rows(1, E * 2 * I, H, 3)
+        W2 = synth.packed_rows(3, E * H, I, 3)
+        s1 = synth.scales_bf16(2, (E * 2 * I, H // bs))  # any bits: valid in both formats
+        s2 = synth.scales_bf16(4, (E * H, I // bs))
+        p1, _, k1 = host_prepare(mnb.qmoe_proj_desc(H, 2 * I, E, bs, 3, dt), W1, s1, None)
+        p2, _, k2 = host_prepare(mnb.qmoe_proj_desc(I, H, E, bs, 3, dt), W2, s2, None)
+        p[dt] = (p1, p2)
+        keep += [k1, k2]
+    q = mnb.make_qmoe_desc(2)
+    assert mnb.qmoe_workspace_size(*p[mnb.MNB_DTYPE_BF16], q, 8) == \
+        mnb.qmoe_workspace_size(*p[mnb.MNB_DTYPE_F16], q, 8)
+    assert status_of(mnb.qmoe_workspace_size, p[mnb.MNB_DTYPE_F16][0], p[mnb.MNB_DTYPE_BF16][1],
+                     q, 8) == UNSUP

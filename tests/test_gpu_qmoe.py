@@ -29,8 +29,24 @@ def say(*a):
     sys.stdout.flush()
 
 
+def bf16_f64(bits):
+    """float64 values of uint16 bfloat16 patterns (torch's reading)."""
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def dev16(a):
+    """A float16 array, or uint16 bfloat16 patterns, as a device tensor of the
+    same bits."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
 class Moe:
-    def __init__(self, x, logits, W1, s1, W2, s2, k, bs, bits1=3, bits2=3, b1=None, b2=None):
+    def __init__(self, x, logits, W1, s1, W2, s2, k, bs, bits1=3, bits2=3, b1=None, b2=None,
+                 dtype="f16"):
         self.E, twoI, _ = W1.shape
         self.I = twoI // 2
         self.H = x.shape[1]
@@ -38,20 +54,26 @@ class Moe:
         self.bits1, self.bits2 = bits1, bits2
         self.host = (W1, s1, W2, s2)
         self.b1, self.b2 = b1, b2  # optional fp16 biases [E, 2I], [E, H]
-        self.b1d = None if b1 is None else torch.from_numpy(np.ascontiguousarray(b1)).cuda()
-        self.b2d = None if b2 is None else torch.from_numpy(np.ascontiguousarray(b2)).cuda()
-        self.p1 = mnb.PreparedWeight(mnb.qmoe_proj_desc(self.H, twoI, self.E, bs, bits1),
+        self.b1d = None if b1 is None else dev16(b1)
+        self.b2d = None if b2 is None else dev16(b2)
+        self.dtype = dtype  # "f16": float16 arrays; "bf16": uint16 bfloat16 patterns
+        sd = mnb.MNB_DTYPE_BF16 if dtype == "bf16" else mnb.MNB_DTYPE_F16
+        self.p1 = mnb.PreparedWeight(mnb.qmoe_proj_desc(self.H, twoI, self.E, bs, bits1, sd),
                                      W1.reshape(self.E * twoI, -1), s1.reshape(self.E * twoI, -1))
-        self.p2 = mnb.PreparedWeight(mnb.qmoe_proj_desc(self.I, self.H, self.E, bs, bits2),
+        self.p2 = mnb.PreparedWeight(mnb.qmoe_proj_desc(self.I, self.H, self.E, bs, bits2, sd),
                                      W2.reshape(self.E * self.H, -1), s2.reshape(self.E * self.H, -1))
         self.q = mnb.make_qmoe_desc(k)
 
     def run(self, x, logits, debug=False, guard=128):
         T = x.shape[0]
         H, I, k = self.H, self.I, self.k
-        xd = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+        bf = self.dtype == "bf16"
+        xd = dev16(x)
         ld = torch.from_numpy(np.ascontiguousarray(logits)).cuda()
-        og = torch.full((T * H + 2 * guard,), float("nan"), dtype=torch.float16, device="cuda")
+        if bf:  # bfloat16 NaN patterns as the guard
+            og = torch.full((T * H + 2 * guard,), 0x7FC0, dtype=torch.int16, device="cuda")
+        else:
+            og = torch.full((T * H + 2 * guard,), float("nan"), dtype=torch.float16, device="cuda")
         out = og[guard:guard + T * H]
         need = mnb.qmoe_workspace_size(self.p1.plan, self.p2.plan, self.q, T)
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
@@ -59,7 +81,8 @@ class Moe:
         if debug:
             dbg = dict(ids_dev=torch.empty((T, k), dtype=torch.int32, device="cuda"),
                        w_dev=torch.empty((T, k), dtype=torch.float32, device="cuda"),
-                       h_dev=torch.empty((T, k, I), dtype=torch.float16, device="cuda"),
+                       h_dev=torch.empty((T, k, I), dtype=torch.int16 if bf else torch.float16,
+                                         device="cuda"),
                        slot_dev=torch.empty((T, k, H), dtype=torch.float32, device="cuda"))
             mnb.qmoe_forward_debug(self.p1.plan, self.p2.plan, self.q, T, xd, ld, out, ws, ws.numel(),
                                    fc1_bias_dev=self.b1d, fc2_bias_dev=self.b2d, **dbg)
@@ -70,19 +93,27 @@ class Moe:
             mnb.qmoe_forward(self.p1.plan, self.p2.plan, self.q, T, xd, ld, out, ws, ws.numel())
         torch.cuda.synchronize()
         g = og.cpu().numpy()
+        if bf:
+            g = bf16_f64(g.view(np.uint16))
         assert np.isnan(g[:guard]).all() and np.isnan(g[guard + T * H:]).all(), "guard band written"
         res = {"out": g[guard:guard + T * H].reshape(T, H).copy()}
+        if bf:
+            res["out_bits"] = og.cpu().numpy().view(np.uint16)[guard:guard + T * H].reshape(T, H)
         for key, v in dbg.items():
             res[key[:-4]] = v.cpu().numpy()
+        if bf and "h" in res:
+            res["h"] = bf16_f64(res["h"].view(np.uint16))
         return res
 
     def oracle(self, orc, x, logits):
         W1, s1, W2, s2 = self.host
         return orc.qmoe(x, logits, W1, s1, W2, s2, k=self.k, bits1=self.bits1, bits2=self.bits2,
-                        bs=self.bs, nthreads=8, b1=self.b1, b2=self.b2)
+                        bs=self.bs, nthreads=8, b1=self.b1, b2=self.b2, dtype=self.dtype)
 
 
-def random_moe(seed, T, H, I, E, k, bs, bits1=3, bits2=3, bias=False):
+def random_moe(seed, T, H, I, E, k, bs, bits1=3, bits2=3, bias=False, dtype="f16"):
+    if dtype == "bf16":
+        return random_moe_bf16(seed, T, H, I, E, k, bs, bits1, bits2, bias)
     x = synth.activations_f16(synth.seed_for(seed, 1), T, H)
     logits = synth.router_logits(synth.seed_for(seed, 2), T, E)
     W1 = synth.packed_rows(synth.seed_for(seed, 3), E * 2 * I, H, bits1).reshape(E, 2 * I, -1)
@@ -96,14 +127,33 @@ def random_moe(seed, T, H, I, E, k, bs, bits1=3, bits2=3, bias=False):
     return x, logits, Moe(x, logits, W1, s1, W2, s2, k, bs, bits1, bits2, b1, b2)
 
 
-def half_ulp(a, b):
+def random_moe_bf16(seed, T, H, I, E, k, bs, bits1, bits2, bias):
+    """bfloat16 activations, scales and biases (uint16 patterns)."""
+    x = synth.activations_bf16(synth.seed_for(seed, 1), T, H)
+    logits = synth.router_logits(synth.seed_for(seed, 2), T, E)
+    W1 = synth.packed_rows(synth.seed_for(seed, 3), E * 2 * I, H, bits1).reshape(E, 2 * I, -1)
+    s1 = synth.scales_bf16(synth.seed_for(seed, 4), (E, 2 * I, H // bs))
+    W2 = synth.packed_rows(synth.seed_for(seed, 5), E * H, I, bits2).reshape(E, H, -1)
+    s2 = synth.scales_bf16(synth.seed_for(seed, 6), (E, H, I // bs))
+    b1 = b2 = None
+    if bias:
+        b1 = synth.to_bf16_bits(synth.normal(synth.seed_for(seed, 7), E * 2 * I).astype(np.float32)
+                                * 0.5).reshape(E, 2 * I)
+        b2 = synth.to_bf16_bits(synth.normal(synth.seed_for(seed, 8), E * H).astype(np.float32)
+                                * 0.25).reshape(E, H)
+    return x, logits, Moe(x, logits, W1, s1, W2, s2, k, bs, bits1, bits2, b1, b2, dtype="bf16")
+
+
+def half_ulp(a, b, dtype="f16"):
     m = np.maximum(np.abs(a.astype(np.float64)), np.abs(b.astype(np.float64)))
+    if dtype == "bf16":  # 8 significant bits; normal range only
+        return 0.5 * np.exp2(np.floor(np.log2(np.maximum(m, 2.0 ** -126))) - 7)
     return 0.5 * np.spacing(m.astype(np.float16)).astype(np.float64)
 
 
-def check_end_to_end(got, o):
+def check_end_to_end(got, o, dtype="f16"):
     err = np.abs(got.astype(np.float64) - o["out64"])
-    bound = 4e-3 * o["S"] + half_ulp(got, o["out"])
+    bound = 4e-3 * o["S"] + half_ulp(got, o["out"], dtype)
     assert (err <= bound).all(), f"{(err > bound).sum()} elements out of bound"
 
 
@@ -115,12 +165,14 @@ def check_stages(orc, m, res, o):
     sg = 1.0 / (1.0 + np.exp(-g))
     dg = np.abs(u * sg * (1.0 + g * (1.0 - sg)))
     du = np.abs(g * sg)
-    hb = 4e-3 * (dg * o["gs"] + du * o["us"]) + half_ulp(res["h"], o["h"].astype(np.float16)) * 2
+    dt = m.dtype
+    hq = o["h"].astype(np.float16) if dt == "f16" else o["h"]
+    hb = 4e-3 * (dg * o["gs"] + du * o["us"]) + half_ulp(res["h"], hq, dt) * 2
     assert (np.abs(res["h"].astype(np.float64) - o["h"]) <= hb).all()
     # FC2 fed the GPU's own h
     W1, s1, W2, s2 = m.host
     y, yS = orc.qmoe_fc2(res["ids"], res["h"].astype(np.float64), W2, s2, m.H, m.I, m.E,
-                         bits2=m.bits2, bs=m.bs, nthreads=8, b2=m.b2)
+                         bits2=m.bits2, bs=m.bs, nthreads=8, b2=m.b2, dtype=dt)
     r = res["w"].astype(np.float64)[:, :, None]
     err = np.abs(res["slot"].astype(np.float64) - r * y)
     assert (err <= 4e-3 * r * yS + 1e-30).all()
@@ -260,6 +312,50 @@ def test_qmoe_biases_layer_config_sampled_tokens(orc):
     o = m.oracle(orc, x[toks], logits[toks])
     check_end_to_end(res["out"][toks], o)
     check_stages(orc, m, {key: res[key][toks] for key in ("ids", "w", "h", "slot")}, o)
+
+
+# bfloat16 layers (P1: FP16/BF16 with matching activation and scale types):
+# weights enter the matrix cores as bf16((q - z) s) (one rounding, 2^-9
+# relative), x and h are bf16, out is rounded to bf16 once; with x exact
+# each product carries one rounding, inside the 4e-3 S bar, and the output
+# bound takes half a bf16 step.
+@pytest.mark.parametrize("bits1,bits2", [(3, 3), (4, 4), (3, 4)])
+@pytest.mark.parametrize("T,H,I,E,k,bs,bias", [(1, 64, 32, 3, 3, 32, True),
+                                               (4, 128, 64, 8, 8, 64, False),
+                                               (17, 96, 64, 16, 4, 32, True),
+                                               (64, 256, 128, 12, 8, 128, False),
+                                               (40, 192, 160, 10, 8, 32, False)])
+def test_qmoe_bf16_all_outputs(orc, bits1, bits2, T, H, I, E, k, bs, bias):
+    say(f"qmoe bf16 ({bits1},{bits2}) T={T} H={H} I={I} E={E} k={k} bs={bs} bias={bias}")
+    x, logits, m = random_moe(T * 3 + E + bits1, T, H, I, E, k, bs, bits1, bits2, bias, "bf16")
+    res = m.run(x, logits, debug=True)
+    o = m.oracle(orc, x, logits)
+    check_end_to_end(res["out"], o, "bf16")
+    check_stages(orc, m, res, o)
+    again = m.run(x, logits)
+    assert np.array_equal(again["out_bits"], res["out_bits"])
+
+
+@pytest.mark.parametrize("T", [1, 128])
+def test_qmoe_bf16_layer_config_sampled_tokens(orc, T):
+    say(f"qmoe bf16 layer T={T}")
+    H, I, E, k, bs = 2048, 768, 128, 8, 64
+    x, logits, m = random_moe(29, T, H, I, E, k, bs, 3, 3, False, "bf16")
+    res = m.run(x, logits, debug=True)
+    assert np.isfinite(res["out"]).all()
+    toks = np.unique(np.array([0, T // 2, T - 1]))
+    o = m.oracle(orc, x[toks], logits[toks])
+    check_end_to_end(res["out"][toks], o, "bf16")
+    check_stages(orc, m, {key: res[key][toks] for key in ("ids", "w", "h", "slot")}, o)
+
+
+def test_qmoe_mixed_dtypes_rejected():
+    say("qmoe fp16 / bf16 plans mixed")
+    _, _, m16 = random_moe(3, 2, 64, 32, 4, 2, 32)
+    _, _, mbf = random_moe(3, 2, 64, 32, 4, 2, 32, dtype="bf16")
+    with pytest.raises(mnb.MnbError) as e:
+        mnb.qmoe_workspace_size(m16.p1.plan, mbf.p2.plan, m16.q, 2)
+    assert e.value.status == -2
 
 
 def test_qmoe_more_tokens_than_one_tile(orc):
