@@ -321,32 +321,42 @@ def bench_extras(torch, mnb, dev):
     log("extras: INT3 QMoE layer done")
     out["qmoe_int4_layer"] = qmoe_extra(torch, mnb, dev, 4, 4)
     log("extras: INT4 QMoE layer done")
+    out["qmoe_int3_layer_bf16"] = qmoe_extra(torch, mnb, dev, 3, 3, bf16=True)
+    log("extras: bf16 INT3 QMoE layer done")
     out["int3_rtn_quantizer"] = rtn_extra(torch, mnb, dev)
     log("extras: INT3 RTN quantizer done")
     return out
 
 
-def qmoe_extra(torch, mnb, dev, bits1, bits2):
+def qmoe_extra(torch, mnb, dev, bits1, bits2, bf16=False):
     """QMoE layer (hidden 2048, 128 experts, intermediate 768, top-8, block 64)
-    at T = 1, 128, 512 tokens, from graph replays over 4 weight copies."""
+    at T = 1, 128, 512 tokens, from graph replays over 4 weight copies; fp16
+    or bfloat16 activations and scales."""
     H, I, E, k, bs = 2048, 768, 128, 8, 64
+    scales = synth.scales_bf16 if bf16 else synth.scales_f16
     W1 = synth.packed_rows(synth.seed_for(5, 3), E * 2 * I, H, bits1)
-    s1 = synth.scales_f16(synth.seed_for(5, 4), (E * 2 * I, H // bs))
+    s1 = scales(synth.seed_for(5, 4), (E * 2 * I, H // bs))
     W2 = synth.packed_rows(synth.seed_for(5, 5), E * H, I, bits2)
-    s2 = synth.scales_f16(synth.seed_for(5, 6), (E * H, I // bs))
+    s2 = scales(synth.seed_for(5, 6), (E * H, I // bs))
+    sd = mnb.MNB_DTYPE_BF16 if bf16 else mnb.MNB_DTYPE_F16
     copies = 4
     experts = []
     for c in range(copies):  # distinct device copies of the same expert bytes
-        experts.append((mnb.PreparedWeight(mnb.qmoe_proj_desc(H, 2 * I, E, bs, bits1), W1, s1),
-                        mnb.PreparedWeight(mnb.qmoe_proj_desc(I, H, E, bs, bits2), W2, s2)))
+        experts.append((mnb.PreparedWeight(mnb.qmoe_proj_desc(H, 2 * I, E, bs, bits1, sd), W1, s1),
+                        mnb.PreparedWeight(mnb.qmoe_proj_desc(I, H, E, bs, bits2, sd), W2, s2)))
     q = mnb.make_qmoe_desc(k)
     per_expert = (2 * I * (bits1 * H // 8) + 2 * I * (H // bs) * 2 + H * (bits2 * I // 8)
                   + H * (I // bs) * 2)
-    moe = {"bits": [bits1, bits2], "bytes_per_expert": per_expert}
+    moe = {"bits": [bits1, bits2], "dtype": "bf16" if bf16 else "f16",
+           "bytes_per_expert": per_expert}
     for T in (1, 128, 512):
-        x = torch.from_numpy(synth.activations_f16(synth.seed_for(5, 1), T, H)).to(dev)
+        if bf16:  # bfloat16 patterns, carried as int16
+            xa = synth.activations_bf16(synth.seed_for(5, 1), T, H).view(np.int16)
+        else:
+            xa = synth.activations_f16(synth.seed_for(5, 1), T, H)
+        x = torch.from_numpy(xa).to(dev)
         lg = torch.from_numpy(synth.router_logits(synth.seed_for(5, 2), T, E)).to(dev)
-        o = torch.empty((T, H), dtype=torch.float16, device=dev)
+        o = torch.empty((T, H), dtype=torch.int16 if bf16 else torch.float16, device=dev)
         need = mnb.qmoe_workspace_size(experts[0][0].plan, experts[0][1].plan, q, T)
         qws = torch.empty(need, dtype=torch.uint8, device=dev)
         calls = [lambda p=p, x=x, lg=lg, o=o, qws=qws, T=T: mnb.qmoe_forward(
