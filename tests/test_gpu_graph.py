@@ -126,3 +126,75 @@ def test_graph_qmoe(T):
     ref = out.clone()
     g = capture(run)
     replay_and_check(g, out, ref, lambda: (x.float() * 3).sum().item())
+
+
+@pytest.mark.parametrize("T,bits1,bits2,bf16", [(48, 4, 3, False), (2, 3, 4, True), (40, 4, 4, True),
+                                                (7, 3, 3, False)])
+def test_graph_qmoe_biased_widths_dtypes(T, bits1, bits2, bf16):
+    """qmoe_forward_biased with mixed widths and fp16 or bf16 layers."""
+    say(f"graph qmoe biased T={T} widths ({bits1},{bits2}) bf16={bf16}")
+    H, I, E, k, bs = 256, 128, 16, 4, 64
+    sd = mnb.MNB_DTYPE_BF16 if bf16 else mnb.MNB_DTYPE_F16
+    scales = synth.scales_bf16 if bf16 else synth.scales_f16
+    W1 = synth.packed_rows(1, E * 2 * I, H, bits1)
+    W2 = synth.packed_rows(3, E * H, I, bits2)
+    p1 = mnb.PreparedWeight(mnb.qmoe_proj_desc(H, 2 * I, E, bs, bits1, sd), W1,
+                            scales(2, (E * 2 * I, H // bs)))
+    p2 = mnb.PreparedWeight(mnb.qmoe_proj_desc(I, H, E, bs, bits2, sd), W2, scales(4, (E * H, I // bs)))
+    q = mnb.make_qmoe_desc(k)
+
+    def dev16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+    if bf16:
+        x = dev16(synth.activations_bf16(5, T, H))
+        b1 = dev16(synth.activations_bf16(7, E, 2 * I))
+        b2 = dev16(synth.activations_bf16(8, E, H))
+    else:
+        x = dev16(synth.activations_f16(5, T, H))
+        b1 = dev16(synth.activations_f16(7, E, 2 * I))
+        b2 = dev16(synth.activations_f16(8, E, H))
+    lg = torch.from_numpy(synth.router_logits(6, T, E)).cuda()
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    ws = torch.empty(mnb.qmoe_workspace_size(p1.plan, p2.plan, q, T), dtype=torch.uint8, device="cuda")
+
+    def run():
+        mnb.qmoe_forward_biased(p1.plan, p2.plan, q, T, x, lg, b1, b2, out, ws, ws.numel())
+
+    run()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    g = capture(run)
+    for _ in range(4):
+        out.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        (lg * 3).sum().item()
+        torch.cuda.synchronize()
+
+
+def test_graph_rtn_quantizer():
+    say("graph rtn quantizer")
+    rows, K, bs = 300, 256, 32
+    W = torch.from_numpy((synth.normal(9, rows * K) * 0.1).astype(np.float32).reshape(rows, K)).cuda()
+    B = torch.empty((rows, 3 * K // 8), dtype=torch.uint8, device="cuda")
+    s = torch.empty((rows, K // bs), dtype=torch.float16, device="cuda")
+    st = torch.empty((rows, K // bs), dtype=torch.uint8, device="cuda")
+
+    def run():
+        mnb.mnb_quantize_int3_rtn(W, rows, K, bs, B, s, st)
+
+    run()
+    torch.cuda.synchronize()
+    refs = (B.clone(), s.clone(), st.clone())
+    g = capture(run)
+    for _ in range(4):
+        B.fill_(0x5A)
+        s.fill_(7.0)
+        st.fill_(9)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(B, refs[0]) and torch.equal(s, refs[1]) and torch.equal(st, refs[2])
+        (W * 2).sum().item()
+        torch.cuda.synchronize()
