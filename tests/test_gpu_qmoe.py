@@ -465,3 +465,32 @@ def test_qmoe_pointer_alignment():
         with pytest.raises(mnb.MnbError) as e:
             mnb.qmoe_forward(m.p1.plan, m.p2.plan, m.q, T, xs, ld, os_, ws, ws.numel())
         assert e.value.status == -1
+
+
+# Path boundaries for the width / dtype variants: one expert and top-1; the
+# fused-routing decode limit (T k = 8 / 9), the decode / grouped limit
+# (T k = 32 / 33), more than 256 experts (16 experts per routing lane) and
+# top-16.
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("bits1,bits2", [(4, 4), (4, 3)])
+@pytest.mark.parametrize("T,E,k", [(3, 1, 1), (40, 1, 1), (1, 8, 8), (9, 9, 1), (4, 16, 8),
+                                   (33, 16, 1), (1, 300, 8), (3, 300, 16)])
+def test_qmoe_variant_path_boundaries(orc, dtype, bits1, bits2, T, E, k):
+    say(f"qmoe boundary {dtype} ({bits1},{bits2}) T={T} E={E} k={k}")
+    H, I, bs = 64, 32, 32
+    x, logits, m = random_moe(T * 11 + E * 3 + k + bits2, T, H, I, E, k, bs, bits1, bits2,
+                              bias=(T % 2 == 1), dtype=dtype)
+    res = m.run(x, logits, debug=True)
+    o = m.oracle(orc, x, logits)
+    check_end_to_end(res["out"], o, dtype)
+    check_stages(orc, m, res, o)
+
+
+def test_qmoe_bf16_no_tokens_is_a_no_op():
+    say("qmoe bf16 T=0")
+    _, _, m = random_moe(5, 1, 64, 32, 4, 2, 32, dtype="bf16")
+    lib = mnb.lib()
+    import ctypes
+    assert lib.qmoe_forward_biased(ctypes.byref(m.p1.plan), ctypes.byref(m.p2.plan),
+                                   ctypes.byref(m.q), 0, None, None, None, None, None, None, 0,
+                                   None) == 0
