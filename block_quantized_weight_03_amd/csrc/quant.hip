@@ -13,10 +13,10 @@
 // packing).
 //
 // The work is a stream over the weights (4 bytes in, 3/8 byte + 2/bs out per
-// weight), so the kernel is shaped for HBM: each lane takes 8 consecutive
-// weights as two 16-byte loads, the bs/8 lanes of a group combine their
-// maxima with lane shuffles, and every 4 lanes merge their 24 code bits into
-// three coalesced 32-bit stores (8 codes of 3 bits are exactly 3 bytes, and
+// weight), so the kernel is shaped for HBM: each lane takes pieces of 8
+// consecutive weights as two 16-byte loads each, the bs/8 lanes of a group
+// combine their maxima with lane shuffles, and every 4 lanes merge their 24
+// code bits into three coalesced 32-bit stores (8 codes of 3 bits are exactly 3 bytes, and
 // 4 lanes' 12 bytes start on a 4-byte boundary of the row).
 
 #include <hip/hip_fp16.h>
@@ -32,23 +32,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // Status of a group (also the meaning of the status output):
 //  0 ok, 1 a weight is NaN or infinite, 2 a nonzero group whose scale rounds
 //  to zero in fp16, 3 a scale beyond the fp16 range.
+//
+// One 8-weight piece i: a, b are its two 16-byte halves (zeros when invalid).
 template <int BS>
-__global__ void __launch_bounds__(256) rtn_int3_kernel(const float* __restrict__ W, int64_t pieces,
-                                                       uint32_t* __restrict__ B,
-                                                       uint16_t* __restrict__ scales,
-                                                       uint8_t* __restrict__ status) {
+__device__ __forceinline__ void rtn_piece(f32x4 a, f32x4 b, int64_t i, bool valid,
+                                          uint32_t* __restrict__ B, uint16_t* __restrict__ scales,
+                                          uint8_t* __restrict__ status) {
   constexpr int L = BS / 8;  // lanes per group (4, 8 or 16)
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // 8-weight piece
-  // Groups are whole runs of L pieces (K is a multiple of BS), so a group is
-  // either entirely inside the grid's valid range or entirely outside; every
-  // lane still takes part in the shuffles.
-  const bool valid = i < pieces;
-  f32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-  if (valid) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(W) + 2 * i;
-    a = __builtin_nontemporal_load(src);
-    b = __builtin_nontemporal_load(src + 1);
-  }
   float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   float amax = 0.0f;
   int finite = 1;
@@ -101,13 +91,47 @@ __global__ void __launch_bounds__(256) rtn_int3_kernel(const float* __restrict__
   }
 }
 
+// Each thread takes kPieces pieces a grid apart (all loads issued before any
+// is used, so several 16-byte loads per lane are in flight).  Groups are
+// whole runs of L consecutive pieces (K is a multiple of BS) and the grid
+// stride is a multiple of 256, so a group is either entirely inside the
+// valid range or entirely outside; every lane still takes part in the
+// shuffles.
+constexpr int kPieces = 2;
+
+template <int BS>
+__global__ void __launch_bounds__(256) rtn_int3_kernel(const float* __restrict__ W, int64_t pieces,
+                                                       uint32_t* __restrict__ B,
+                                                       uint16_t* __restrict__ scales,
+                                                       uint8_t* __restrict__ status) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  f32x4 a[kPieces], b[kPieces];
+#pragma unroll
+  for (int u = 0; u < kPieces; ++u) {
+    const int64_t i = i0 + u * stride;
+    a[u] = f32x4{0, 0, 0, 0};
+    b[u] = f32x4{0, 0, 0, 0};
+    if (i < pieces) {
+      const f32x4* src = reinterpret_cast<const f32x4*>(W) + 2 * i;
+      a[u] = __builtin_nontemporal_load(src);
+      b[u] = __builtin_nontemporal_load(src + 1);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kPieces; ++u) {
+    const int64_t i = i0 + u * stride;
+    rtn_piece<BS>(a[u], b[u], i, i < pieces, B, scales, status);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_rtn_int3(const float* W, int64_t rows, int64_t K, int bs, uint8_t* B,
                            uint16_t* scales, uint8_t* status, hipStream_t st) {
   const int64_t pieces = rows * (K / 8);
   if (pieces == 0) return hipSuccess;
-  const dim3 grid((unsigned)((pieces + 255) / 256)), block(256);
+  const dim3 grid((unsigned)((pieces + 256 * kPieces - 1) / (256 * kPieces))), block(256);
   uint32_t* B32 = reinterpret_cast<uint32_t*>(B);
   if (bs == 32)
     hipLaunchKernelGGL(rtn_int3_kernel<32>, grid, block, 0, st, W, pieces, B32, scales, status);
