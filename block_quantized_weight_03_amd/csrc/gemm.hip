@@ -564,6 +564,7 @@ uint64_t gemm_ws_bytes(const Sizes& s, int64_t M) {
 
 hipError_t launch_gemm(const Sizes& s, const mnb_plan& p, int64_t M, const float* A, float* Y,
                        void* ws, hipStream_t st) {
+  if (gemm_small_supported(s, M, A)) return launch_gemm_small(s, p, M, A, Y, st);
   const Plan pl = choose(s, M, fast_ok(s, M, A));
   hipError_t e;
   if (pl.lds) {

@@ -1,0 +1,200 @@
+// Small-M GEMM (M <= 16) on dense INT4 weights for gfx950: one launch, no
+// workspace (used for M <= 4, or M <= 16 with N >= 4096; see
+// gemm_small_supported).
+//
+// Operation ("Qwen3 Missing-Kernel Implementation Plan", section "PR
+// sequence", step K03, small-M/prefill on the same compressed weights):
+//   Y[m,n] = sum_{k<K} A[m,k] * (q[n,k] - z[n,b]) * s[n,b],  b = k / bs,
+// with the rounding chain of the other matrix-core paths: A rounded to fp16,
+// each weight rounded once as fp16(fma(q, s, -(z*s))) from fp32, products
+// accumulated in fp32.
+//
+// At M <= 16 the product is a stream over the weights that must keep enough
+// bytes in flight to cover HBM latency.  A workgroup owns one 16-row weight
+// tile; its W waves split the 128-code K chunks into contiguous ranges, and
+// each wave issues the 16-byte loads of all its chunks before it uses the
+// first, so the whole weight matrix is in flight at once.  Lane (r, g) =
+// (lane & 15, lane >> 4) takes 32-code block 4c + g of row r in chunk c, and
+// the activations of token r at the same 32 k straight from L2 into its MFMA
+// operand (fp32 -> fp16 in registers, one chunk ahead): each A chunk is used
+// by one wave of the workgroup, so staging it in LDS would buy no reuse.  The
+// W partial 16 x 16 tiles are summed in LDS in a fixed order, so there is no
+// A pre-pass, no split partial in HBM and no reduction launch.
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace mnb {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, half2v{(_Float16)a, (_Float16)b});  // v_cvt_pk_f16_f32, RNE
+}
+
+// 8 activations (two float4) as one fp16 MFMA operand
+__device__ __forceinline__ half8 a_operand(const f32x4 x, const f32x4 y) {
+  return __builtin_bit_cast(half8, u32x4{pk_f16(x.x, x.y), pk_f16(x.z, x.w), pk_f16(y.x, y.y),
+                                         pk_f16(y.z, y.w)});
+}
+
+// 8 codes of one 32-bit word of the prepared layout (nibble j = (q - 8) in
+// two's complement, even k in the low nibble) as fp16(fma(q, s, -(z s))),
+// in k order
+__device__ __forceinline__ half8 w_operand(uint32_t word, float s, float nzs) {
+  const uint32_t x = word ^ 0x88888888u;  // back to q
+  const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+  uint32_t p[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    p[j] = pk_f16(fmaf((float)((lo >> (8 * j)) & 0xFFu), s, nzs),
+                  fmaf((float)((hi >> (8 * j)) & 0xFFu), s, nzs));
+  return __builtin_bit_cast(half8, u32x4{p[0], p[1], p[2], p[3]});
+}
+
+// CPW: chunks per wave (at least ceil(nch / W); extra slots reload the last
+// chunk of the range and are not used).  M <= 16, K % 128 == 0.
+template <int CPW, int W, bool HAS_ZP>
+__global__ void __launch_bounds__(64 * W) gemm_int4_small(
+    const float* __restrict__ A, const uint8_t* __restrict__ codes,
+    const float* __restrict__ scales, const uint32_t* __restrict__ zeros, float* __restrict__ Y,
+    int32_t M, int32_t N, int32_t K, int64_t row_bytes, int64_t nb, int32_t bs_shift) {
+  __shared__ f32x4 red[W][64];
+  const int lane = (int)(threadIdx.x & 63);
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int n0 = (int)blockIdx.x * 16;
+  const int nch = K >> 7;
+  const int c_beg = nch * wave / W, c_end = nch * (wave + 1) / W;
+  const int cnt = c_end - c_beg;  // wave-uniform, <= CPW
+  const int r = lane & 15, g = lane >> 4;
+  const int row = min(n0 + r, N - 1);  // rows past N compute a copy of the last row (not stored)
+  const int tok = min(r, M - 1);       // tokens past M likewise
+  const uint8_t* wrow = codes + (int64_t)row * row_bytes;
+  const float* srow = scales + (int64_t)row * nb;
+  const uint32_t* zrow = HAS_ZP ? zeros + (int64_t)(row >> 3) * nb : nullptr;
+  const int zsh = 4 * (row & 7);
+
+  // every chunk of the range in flight before the first is used (clamped:
+  // a wave with no chunk reloads chunk 0 and adds nothing)
+  u32x4 wq[CPW];
+  float sc[CPW], nz[CPW];
+#pragma unroll
+  for (int u = 0; u < CPW; ++u) {
+    int c = c_beg + u;
+    c = c < c_end ? c : c_end - 1;
+    c = c < 0 ? 0 : c;
+    const int G = 4 * c + g;  // 32-code block index along the row
+    wq[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow + (int64_t)G * 16));
+    const int b = G >> bs_shift;
+    sc[u] = __builtin_nontemporal_load(srow + b);
+    nz[u] = HAS_ZP ? (float)((__builtin_nontemporal_load(zrow + b) >> zsh) & 15u) : 8.0f;
+  }
+  const float* arow = A + (int64_t)tok * K + 32 * g;
+  f32x4 a0[8], a1[8];
+  auto load_a = [&](f32x4 (&a)[8], int u) {
+    int c = c_beg + u;
+    c = c < c_end ? c : c_end - 1;
+    c = c < 0 ? 0 : c;
+    const f32x4* src = reinterpret_cast<const f32x4*>(arow + 128 * c);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = src[i];
+  };
+  f32x4 acc = f32x4{0, 0, 0, 0};
+  auto chunk = [&](const f32x4 (&a)[8], int u) {
+    const float s = sc[u], nzs = -(nz[u] * s);
+    const u32x4 w = wq[u];
+    const uint32_t w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
+    // MFMA t takes k = 32 g + 8 t + [0, 8) in lane group g on both sides
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_operand(a[0], a[1]), w_operand(w0, s, nzs), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_operand(a[2], a[3]), w_operand(w1, s, nzs), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_operand(a[4], a[5]), w_operand(w2, s, nzs), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_operand(a[6], a[7]), w_operand(w3, s, nzs), acc, 0, 0, 0);
+  };
+  load_a(a0, 0);
+#pragma unroll
+  for (int u = 0; u < CPW; u += 2) {
+    if (u < cnt) {
+      if (u + 1 < cnt) load_a(a1, u + 1);
+      chunk(a0, u);
+    }
+    if (u + 1 < CPW && u + 1 < cnt) {
+      if (u + 2 < cnt) load_a(a0, u + 2);
+      chunk(a1, u + 1);
+    }
+  }
+  // lane l holds tokens 4 (l >> 4) + i of weight row n0 + (l & 15)
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    f32x4 o = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < W; ++w) {
+      const f32x4 v = red[w][lane];
+      o = f32x4{o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w};
+    }
+    const int n = n0 + r;
+    if (n < N) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * g + i;
+        if (m < M) Y[(int64_t)m * N + n] = o[i];
+      }
+    }
+  }
+}
+
+template <int CPW, int W>
+hipError_t launch_cw(const Sizes& s, const mnb_plan& p, int64_t M, const float* A, float* Y,
+                     int bs_shift, hipStream_t st) {
+  const dim3 grid((unsigned)((s.N + 15) / 16)), block(64 * W);
+  if (s.zeros)
+    hipLaunchKernelGGL((gemm_int4_small<CPW, W, true>), grid, block, 0, st, A,
+                       static_cast<const uint8_t*>(p.codes), static_cast<const float*>(p.scales),
+                       static_cast<const uint32_t*>(p.zeros), Y, (int32_t)M, (int32_t)s.N,
+                       (int32_t)s.K, s.row_bytes, s.nb, bs_shift);
+  else
+    hipLaunchKernelGGL((gemm_int4_small<CPW, W, false>), grid, block, 0, st, A,
+                       static_cast<const uint8_t*>(p.codes), static_cast<const float*>(p.scales),
+                       nullptr, Y, (int32_t)M, (int32_t)s.N, (int32_t)s.K, s.row_bytes, s.nb,
+                       bs_shift);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Used where it is the faster kernel: a workgroup per 16-row tile covers the
+// chip only with at least one tile per CU (N >= 4096), and every workgroup
+// reads all of A from L2, which dominates past a few rows of A.  Measured
+// (graph replays): K = 2048, N = 6144, M = 1/4/8/16: 6.4/7.5/8.6/11.0 us
+// against 10.9/11.6/11.8/12.4 us for the split-K kernel; K = 6144, N = 2048
+// (128 tiles): M = 1/4 9.2/10.6 against 11.4/11.5 us, but M = 8/16
+// 12.6/16.4 against 11.5/12.0 us.
+bool gemm_small_supported(const Sizes& s, int64_t M, const void* A) {
+  const bool shape = M >= 1 && M <= 16 && s.K % 128 == 0 && s.K <= 8192 &&
+                     s.N <= (int64_t(1) << 30) && (reinterpret_cast<uintptr_t>(A) & 15) == 0;
+  return shape && (M <= 4 || (s.N + 15) / 16 >= 256);
+}
+
+hipError_t launch_gemm_small(const Sizes& s, const mnb_plan& p, int64_t M, const float* A,
+                             float* Y, hipStream_t st) {
+  const int nch = (int)(s.K / 128);
+  const int bs_shift = s.bs == 32 ? 0 : (s.bs == 64 ? 1 : 2);
+  // 4 waves per tile up to 16 chunks (K <= 2048), 8 beyond; chunks per wave
+  // rounded up to an instantiated count
+  if (nch <= 16) {
+    const int cpw = (nch + 3) / 4;
+    if (cpw <= 2) return launch_cw<2, 4>(s, p, M, A, Y, bs_shift, st);
+    return launch_cw<4, 4>(s, p, M, A, Y, bs_shift, st);
+  }
+  const int cpw = (nch + 7) / 8;
+  if (cpw <= 4) return launch_cw<4, 8>(s, p, M, A, Y, bs_shift, st);
+  if (cpw <= 6) return launch_cw<6, 8>(s, p, M, A, Y, bs_shift, st);
+  return launch_cw<8, 8>(s, p, M, A, Y, bs_shift, st);
+}
+
+}  // namespace mnb

@@ -25,6 +25,12 @@ uint64_t gemm_ws_bytes(const Sizes& s, int64_t M);
 hipError_t launch_gemm(const Sizes& s, const mnb_plan& p, int64_t M, const float* A,
                        float* Y, void* ws, hipStream_t st);
 
+// single-launch small-M kernel (gemm_small.hip): M <= 4, or M <= 16 with
+// N >= 4096; K % 128 == 0, K <= 8192, A 16-byte aligned; needs no workspace
+bool gemm_small_supported(const Sizes& s, int64_t M, const void* A);
+hipError_t launch_gemm_small(const Sizes& s, const mnb_plan& p, int64_t M, const float* A,
+                             float* Y, hipStream_t st);
+
 // large-M kernel streaming fp16 A and the codes through LDS (gemm_lds.hip);
 // its workspace starts with an fp16 copy of A, then the split partials
 bool gemm_lds_supported(const Sizes& s, int64_t M);

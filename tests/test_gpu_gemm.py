@@ -158,3 +158,37 @@ def test_gemm_large_m_rows_are_independent():
     y = run_gemm(w, a)
     y_sub = run_gemm(w, a[100:2300])
     assert np.array_equal(y[100:2300], y_sub)
+
+
+# The single-launch small-M kernel (M <= 4, or M <= 16 with N >= 4096; K a
+# multiple of 128 up to 8192): one 16-row weight tile per workgroup, K chunks
+# split over 4 or 8 waves (with waves that get no chunk when K is short),
+# rows of N past the last whole tile, every block size, zero points; then
+# the limits beside it (K = 8320, M = 17, M = 8 with N = 2048) that take the
+# other kernels.
+@pytest.mark.parametrize("M,K,N,bs,zp", [
+    (1, 128, 17, 32, True), (16, 8192, 4112, 128, True), (7, 384, 4100, 64, False),
+    (16, 2176, 4096, 32, True), (12, 6272, 4128, 64, False), (2, 256, 5, 128, True),
+    (16, 2048, 6144, 32, False), (4, 6144, 2048, 64, True), (3, 8192, 33, 32, False),
+    (16, 8320, 40, 32, False), (17, 2048, 70, 32, True), (8, 2048, 2048, 32, False)])
+def test_gemm_single_launch_small_m(orc, M, K, N, bs, zp):
+    say(f"gemm single-launch small M={M} K={K} N={N} bs={bs} zp={zp}")
+    w, B, s, Z = prepare(K, N, bs, zp, seed=M * 7 + K + N)
+    a = synth.activations_f32(synth.seed_for(M + K, 3), M, K)
+    y = run_gemm(w, a)
+    check(orc, y, a, B, s, Z, K, N, bs)
+    assert np.array_equal(run_gemm(w, a).view(np.uint32), y.view(np.uint32))  # deterministic
+
+
+def test_gemm_small_m_exact_integer_and_zero_cases(orc):
+    say("gemm small-M exact cases")
+    M, K, N = 9, 1024, 4096
+    _, B, _, _ = prepare(K, N, seed=31)
+    s = np.full((N, K // 32), 0.25, np.float32)
+    w = mnb.PreparedWeight(mnb.dense_desc(K, N), B, s, None)
+    a = synth.small_int_activations(32, M, K)
+    _, y64, _ = orc.mnb_gemm(a, B, s, None, K, N)
+    assert np.array_equal(run_gemm(w, a).astype(np.float64), y64)
+    Bz = np.full((N, K // 32, 16), 0x88, np.uint8)
+    wz = mnb.PreparedWeight(mnb.dense_desc(K, N), Bz, synth.scales_f32(33, (N, K // 32)), None)
+    assert (run_gemm(wz, synth.activations_f32(34, M, K)) == 0).all()
