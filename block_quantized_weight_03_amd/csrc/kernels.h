@@ -40,7 +40,7 @@ hipError_t launch_gemm_lds(const Sizes& s, const mnb_plan& p, int64_t M, const f
                            void* ws, float* Y, float* part, int32_t splits, int64_t kc, int bm,
                            hipStream_t st);
 
-// ---- INT3 QMoE (qmoe.hip) -------------------------------------------------
+// ---- QMoE with INT3 / INT4 projections, fp16 or bf16 (qmoe.hip) ----------
 struct QmoeDebug {
   int32_t* ids;
   float* w;

@@ -1,4 +1,4 @@
-// TEST INFRASTRUCTURE ONLY -- fp64 CPU reference for MatMulNBits and INT3 QMoE.
+// TEST INFRASTRUCTURE ONLY -- fp64 CPU reference for MatMulNBits, the QMoE layer and the INT3 RTN quantizer.
 //
 // Plain, slow and meant to be read against the pages (see oracle.h for the
 // source list).  Every quantity is computed in double precision and rounded

@@ -1,6 +1,7 @@
 /*
  * TEST INFRASTRUCTURE ONLY.  fp64 CPU reference ("oracle") for block-quantized
- * weight-only matmul (MatMulNBits) and the INT3 top-k QMoE layer.
+ * weight-only matmul (MatMulNBits), the top-k QMoE layer (INT3 / INT4 projections,
+ * fp16 or bf16) and the INT3 round-to-nearest producer quantizer.
  *
  * Only the tests, smoke() and the benchmark's CPU-baseline leg may load this
  * library.  It shares no code, header or table with the HIP library: the two
