@@ -198,3 +198,26 @@ def test_graph_rtn_quantizer():
         assert torch.equal(B, refs[0]) and torch.equal(s, refs[1]) and torch.equal(st, refs[2])
         (W * 2).sum().item()
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M,N", [(4, 300), (16, 4096)])
+def test_graph_single_launch_small_m_gemm(M, N):
+    """The single-launch small-M GEMM (no workspace) replayed from a graph."""
+    say(f"graph small-M gemm M={M} N={N}")
+    K = 1024
+    nb = K // 32
+    w = mnb.PreparedWeight(mnb.dense_desc(K, N, 32, True), synth.int4_blocked_weights(7, N, K, 32),
+                           synth.scales_f32(8, (N, nb)), synth.int4_zero_points(9, N, nb))
+    a = torch.from_numpy(synth.activations_f32(10, M, K)).cuda()
+    y = torch.empty((M, N), device="cuda")
+    ws = torch.empty(max(mnb.mnb_gemm_workspace_size(w.plan, M), 256), dtype=torch.uint8,
+                     device="cuda")
+
+    def run():
+        mnb.mnb_gemm(w.plan, M, a, y, ws, ws.numel())
+
+    run()
+    torch.cuda.synchronize()
+    ref = y.clone()
+    g = capture(run)
+    replay_and_check(g, y, ref, lambda: (a * 3).sum().item())
