@@ -247,10 +247,40 @@ def main():
     gu = gemv_bytes(LAYER[gate][1], LAYER[gate][2]) + gemv_bytes(LAYER[up][1], LAYER[up][2])
     per_proj["gate+up (one launch)"] = {"us": round(us, 3), "GB/s": round(gu / us / 1e3, 1)}
 
+    # ---- separately labelled extras: step-time spread over single replays,
+    # one eager call with its launch, and a hot-cache figure (never the HBM one)
+    reps = []
+    for _ in range(30):
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        r0.record()
+        full.replay()
+        r1.record()
+        torch.cuda.synchronize()
+        reps.append(r0.elapsed_time(r1) * 1e3 / copies)
+    q = np.percentile(reps, [10, 50, 90])
+    spread = {"us_per_step_p10": round(float(q[0]), 3), "median": round(float(q[1]), 3),
+              "p90": round(float(q[2]), 3), "replays": len(reps), "steps_per_replay": copies}
+    o = [n for n, _, _ in LAYER].index("o_proj")
+    one = []
+    for _ in range(50):
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        mnb.mnb_gemv(layers[0][o].plan, acts[o][1], outs[o], gemv_ws, gemv_ws.numel())
+        torch.cuda.synchronize()
+        one.append((time.perf_counter() - h0) * 1e6)
+    single = {"projection": "o_proj", "us_median": round(float(np.median(one)), 2),
+              "timing": "host wall clock around one eager call and a synchronize"}
+    hot_us = 1e3 * graph_time(torch, [lambda: mnb.mnb_gemv(layers[0][o].plan, acts[o][1], outs[o],
+                                                           gemv_ws, gemv_ws.numel())], 10)
+    hot = {"projection": "o_proj", "us": round(hot_us, 3),
+           "GB/s": round(gemv_bytes(LAYER[o][1], LAYER[o][2]) / hot_us / 1e3, 1),
+           "note": "one weight copy replayed, cache-resident: not an HBM figure"}
+
     del full, part
     torch.cuda.synchronize()
 
-    extra = {"per_projection": per_proj}
+    extra = {"per_projection": per_proj, "step_spread": spread, "single_call_latency": single,
+             "hot_cache_gemv": hot}
     if not args.no_extras:
         extra.update(bench_extras(torch, mnb, dev))
 
@@ -271,9 +301,10 @@ def main():
 
 
 def bench_extras(torch, mnb, dev):
-    """Vocabulary head GEMV, prefill GEMM and INT3 QMoE, each timed from graph
-    replays of its own launches (weights rotated where the working set would
-    fit in the Infinity Cache)."""
+    """Vocabulary head GEMV, prefill GEMM, the QMoE layer (INT3, INT4, bf16)
+    and the INT3 RTN quantizer, each timed from graph replays of its own
+    launches (weights rotated where the working set would fit in the
+    Infinity Cache)."""
     out = {}
     # vocabulary head: K=2048, N=151936, explicit zero points
     K, N = 2048, 151936
@@ -370,7 +401,6 @@ def qmoe_extra(torch, mnb, dev, bits1, bits2, bf16=False):
                         "TFLOP/s": round(2.0 * T * k * (2 * I * H + H * I) / us / 1e6, 2)}
     del experts
     return moe
-
 
 
 def rtn_extra(torch, mnb, dev):
