@@ -58,41 +58,47 @@ __device__ __forceinline__ half8 w_operand(uint32_t word, float s, float nzs) {
 }
 
 // CPW: chunks per wave (at least ceil(nch / W); extra slots reload the last
-// chunk of the range and are not used).  M <= 16, K % 128 == 0.
-template <int CPW, int W, bool HAS_ZP>
+// chunk of the range and are not used); RT: 16-row weight tiles per
+// workgroup, each wave computing all of them so that one A load feeds RT
+// MFMAs.  M <= 16, K % 128 == 0.
+template <int CPW, int W, int RT, bool HAS_ZP>
 __global__ void __launch_bounds__(64 * W) gemm_int4_small(
     const float* __restrict__ A, const uint8_t* __restrict__ codes,
     const float* __restrict__ scales, const uint32_t* __restrict__ zeros, float* __restrict__ Y,
     int32_t M, int32_t N, int32_t K, int64_t row_bytes, int64_t nb, int32_t bs_shift) {
-  __shared__ f32x4 red[W][64];
+  __shared__ f32x4 red[W][RT][64];
   const int lane = (int)(threadIdx.x & 63);
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int n0 = (int)blockIdx.x * 16;
+  const int n0 = (int)blockIdx.x * 16 * RT;
   const int nch = K >> 7;
   const int c_beg = nch * wave / W, c_end = nch * (wave + 1) / W;
   const int cnt = c_end - c_beg;  // wave-uniform, <= CPW
   const int r = lane & 15, g = lane >> 4;
-  const int row = min(n0 + r, N - 1);  // rows past N compute a copy of the last row (not stored)
-  const int tok = min(r, M - 1);       // tokens past M likewise
-  const uint8_t* wrow = codes + (int64_t)row * row_bytes;
-  const float* srow = scales + (int64_t)row * nb;
-  const uint32_t* zrow = HAS_ZP ? zeros + (int64_t)(row >> 3) * nb : nullptr;
-  const int zsh = 4 * (row & 7);
+  const int tok = min(r, M - 1);  // tokens past M compute a copy of the last one (not stored)
 
   // every chunk of the range in flight before the first is used (clamped:
-  // a wave with no chunk reloads chunk 0 and adds nothing)
-  u32x4 wq[CPW];
-  float sc[CPW], nz[CPW];
+  // a wave with no chunk reloads chunk 0 and adds nothing); rows past N
+  // compute a copy of the last row (not stored)
+  u32x4 wq[RT][CPW];
+  float sc[RT][CPW], nz[RT][CPW];
 #pragma unroll
-  for (int u = 0; u < CPW; ++u) {
-    int c = c_beg + u;
-    c = c < c_end ? c : c_end - 1;
-    c = c < 0 ? 0 : c;
-    const int G = 4 * c + g;  // 32-code block index along the row
-    wq[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow + (int64_t)G * 16));
-    const int b = G >> bs_shift;
-    sc[u] = __builtin_nontemporal_load(srow + b);
-    nz[u] = HAS_ZP ? (float)((__builtin_nontemporal_load(zrow + b) >> zsh) & 15u) : 8.0f;
+  for (int t = 0; t < RT; ++t) {
+    const int row = min(n0 + 16 * t + r, N - 1);
+    const uint8_t* wrow = codes + (int64_t)row * row_bytes;
+    const float* srow = scales + (int64_t)row * nb;
+    const uint32_t* zrow = HAS_ZP ? zeros + (int64_t)(row >> 3) * nb : nullptr;
+    const int zsh = 4 * (row & 7);
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      int c = c_beg + u;
+      c = c < c_end ? c : c_end - 1;
+      c = c < 0 ? 0 : c;
+      const int G = 4 * c + g;  // 32-code block index along the row
+      wq[t][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow + (int64_t)G * 16));
+      const int b = G >> bs_shift;
+      sc[t][u] = __builtin_nontemporal_load(srow + b);
+      nz[t][u] = HAS_ZP ? (float)((__builtin_nontemporal_load(zrow + b) >> zsh) & 15u) : 8.0f;
+    }
   }
   const float* arow = A + (int64_t)tok * K + 32 * g;
   f32x4 a0[8], a1[8];
@@ -104,16 +110,23 @@ __global__ void __launch_bounds__(64 * W) gemm_int4_small(
 #pragma unroll
     for (int i = 0; i < 8; ++i) a[i] = src[i];
   };
-  f32x4 acc = f32x4{0, 0, 0, 0};
+  f32x4 acc[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) acc[t] = f32x4{0, 0, 0, 0};
   auto chunk = [&](const f32x4 (&a)[8], int u) {
-    const float s = sc[u], nzs = -(nz[u] * s);
-    const u32x4 w = wq[u];
-    const uint32_t w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
-    // MFMA t takes k = 32 g + 8 t + [0, 8) in lane group g on both sides
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_operand(a[0], a[1]), w_operand(w0, s, nzs), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_operand(a[2], a[3]), w_operand(w1, s, nzs), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_operand(a[4], a[5]), w_operand(w2, s, nzs), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_operand(a[6], a[7]), w_operand(w3, s, nzs), acc, 0, 0, 0);
+    const half8 a0 = a_operand(a[0], a[1]), a1 = a_operand(a[2], a[3]);
+    const half8 a2 = a_operand(a[4], a[5]), a3 = a_operand(a[6], a[7]);
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const float s = sc[t][u], nzs = -(nz[t][u] * s);
+      const u32x4 w = wq[t][u];
+      const uint32_t w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
+      // MFMA i takes k = 32 g + 8 i + [0, 8) in lane group g on both sides
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, w_operand(w0, s, nzs), acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, w_operand(w1, s, nzs), acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2, w_operand(w2, s, nzs), acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a3, w_operand(w3, s, nzs), acc[t], 0, 0, 0);
+    }
   };
   load_a(a0, 0);
 #pragma unroll
@@ -127,17 +140,19 @@ __global__ void __launch_bounds__(64 * W) gemm_int4_small(
       chunk(a1, u + 1);
     }
   }
-  // lane l holds tokens 4 (l >> 4) + i of weight row n0 + (l & 15)
-  red[wave][lane] = acc;
+  // lane l holds tokens 4 (l >> 4) + i of weight row n0 + 16 t + (l & 15)
+#pragma unroll
+  for (int t = 0; t < RT; ++t) red[wave][t][lane] = acc[t];
   __syncthreads();
-  if (wave == 0) {
-    f32x4 o = red[0][lane];
+  if (wave < RT) {  // wave t sums tile t over the waves, in wave order
+    const int t = wave;
+    f32x4 o = red[0][t][lane];
 #pragma unroll
     for (int w = 1; w < W; ++w) {
-      const f32x4 v = red[w][lane];
+      const f32x4 v = red[w][t][lane];
       o = f32x4{o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w};
     }
-    const int n = n0 + r;
+    const int n = n0 + 16 * t + r;
     if (n < N) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -148,32 +163,44 @@ __global__ void __launch_bounds__(64 * W) gemm_int4_small(
   }
 }
 
-template <int CPW, int W>
+template <int CPW, int W, int RT = 1>
 hipError_t launch_cw(const Sizes& s, const mnb_plan& p, int64_t M, const float* A, float* Y,
                      int bs_shift, hipStream_t st) {
-  const dim3 grid((unsigned)((s.N + 15) / 16)), block(64 * W);
+  const dim3 grid((unsigned)((s.N + 16 * RT - 1) / (16 * RT))), block(64 * W);
   if (s.zeros)
-    hipLaunchKernelGGL((gemm_int4_small<CPW, W, true>), grid, block, 0, st, A,
+    hipLaunchKernelGGL((gemm_int4_small<CPW, W, RT, true>), grid, block, 0, st, A,
                        static_cast<const uint8_t*>(p.codes), static_cast<const float*>(p.scales),
                        static_cast<const uint32_t*>(p.zeros), Y, (int32_t)M, (int32_t)s.N,
                        (int32_t)s.K, s.row_bytes, s.nb, bs_shift);
   else
-    hipLaunchKernelGGL((gemm_int4_small<CPW, W, false>), grid, block, 0, st, A,
+    hipLaunchKernelGGL((gemm_int4_small<CPW, W, RT, false>), grid, block, 0, st, A,
                        static_cast<const uint8_t*>(p.codes), static_cast<const float*>(p.scales),
                        nullptr, Y, (int32_t)M, (int32_t)s.N, (int32_t)s.K, s.row_bytes, s.nb,
                        bs_shift);
   return hipGetLastError();
 }
 
+int cus() {
+  static int n = 0;
+  if (!n) {
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
+      n = prop.multiProcessorCount;
+    if (n <= 0) n = 256;
+  }
+  return n;
+}
+
 }  // namespace
 
-// Used where it is the faster kernel: a workgroup per 16-row tile covers the
+// Used where it is the faster kernel: a workgroup per weight tile covers the
 // chip only with at least one tile per CU (N >= 4096), and every workgroup
 // reads all of A from L2, which dominates past a few rows of A.  Measured
-// (graph replays): K = 2048, N = 6144, M = 1/4/8/16: 6.4/7.5/8.6/11.0 us
-// against 10.9/11.6/11.8/12.4 us for the split-K kernel; K = 6144, N = 2048
-// (128 tiles): M = 1/4 9.2/10.6 against 11.4/11.5 us, but M = 8/16
-// 12.6/16.4 against 11.5/12.0 us.
+// (graph replays): K = 2048, N = 6144, M = 1/4/8/16: 5.6-6.0/6.7/7.3/8.2 us
+// (32-row tiles) against 10.9/11.6/11.8/12.4 us for the split-K kernel;
+// K = 6144, N = 2048 (128 tiles): M = 1/4 9.2/10.6 against 11.4/11.5 us, but
+// M = 8/16 12.6/16.4 against 11.5/12.0 us.
 bool gemm_small_supported(const Sizes& s, int64_t M, const void* A) {
   const bool shape = M >= 1 && M <= 16 && s.K % 128 == 0 && s.K <= 8192 &&
                      s.N <= (int64_t(1) << 30) && (reinterpret_cast<uintptr_t>(A) & 15) == 0;
@@ -184,9 +211,14 @@ hipError_t launch_gemm_small(const Sizes& s, const mnb_plan& p, int64_t M, const
                              float* Y, hipStream_t st) {
   const int nch = (int)(s.K / 128);
   const int bs_shift = s.bs == 32 ? 0 : (s.bs == 64 ? 1 : 2);
-  // 4 waves per tile up to 16 chunks (K <= 2048), 8 beyond; chunks per wave
-  // rounded up to an instantiated count
+  // up to 16 chunks (K <= 2048): 4 waves per 16-row tile while the tiles fit
+  // one round of one workgroup per CU, else 32-row tiles (two per wave, each
+  // A load feeding both) over 8 waves, which keeps one round (K = 2048, M =
+  // 16: N = 6144 8.2 against 11.0 us, N = 4096 6.8 against 8.1 us for the
+  // other choice); 8 waves per 16-row tile beyond 16 chunks.  Chunks per wave
+  // are rounded up to an instantiated count.
   if (nch <= 16) {
+    if ((s.N + 15) / 16 > cus()) return launch_cw<2, 8, 2>(s, p, M, A, Y, bs_shift, st);
     const int cpw = (nch + 3) / 4;
     if (cpw <= 2) return launch_cw<2, 4>(s, p, M, A, Y, bs_shift, st);
     return launch_cw<4, 4>(s, p, M, A, Y, bs_shift, st);

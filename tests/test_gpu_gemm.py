@@ -168,6 +168,7 @@ def test_gemm_large_m_rows_are_independent():
 # other kernels.
 @pytest.mark.parametrize("M,K,N,bs,zp", [
     (1, 128, 17, 32, True), (16, 8192, 4112, 128, True), (7, 384, 4100, 64, False),
+    (16, 1024, 4144, 64, True), (5, 2048, 6160, 32, False), (9, 128, 8200, 128, True),
     (16, 2176, 4096, 32, True), (12, 6272, 4128, 64, False), (2, 256, 5, 128, True),
     (16, 2048, 6144, 32, False), (4, 6144, 2048, 64, True), (3, 8192, 33, 32, False),
     (16, 8320, 40, 32, False), (17, 2048, 70, 32, True), (8, 2048, 2048, 32, False)])
