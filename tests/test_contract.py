@@ -387,3 +387,27 @@ def test_qmoe_layer_dtypes_must_match():
         mnb.qmoe_workspace_size(*p[mnb.MNB_DTYPE_F16], q, 8)
     assert status_of(mnb.qmoe_workspace_size, p[mnb.MNB_DTYPE_F16][0], p[mnb.MNB_DTYPE_BF16][1],
                      q, 8) == UNSUP
+
+
+def test_biased_qmoe_pointer_checks_before_any_device_call():
+    """qmoe_forward_biased rejects misaligned activations, outputs and biases
+    before it touches a device (host plans suffice to reach those checks)."""
+    E, H, I, bs = 4, 128, 64, 64
+    W1 = synth.packed_rows(1, E * 2 * I, H, 4)
+    W2 = synth.packed_rows(3, E * H, I, 3)
+    s1 = synth.scales_f16(2, (E * 2 * I, H // bs))
+    s2 = synth.scales_f16(4, (E * H, I // bs))
+    p1, _, _k1 = host_prepare(mnb.qmoe_proj_desc(H, 2 * I, E, bs, 4), W1, s1, None)
+    p2, _, _k2 = host_prepare(mnb.qmoe_proj_desc(I, H, E, bs, 3), W2, s2, None)
+    q = mnb.make_qmoe_desc(2)
+    lib = mnb.lib()
+    f = lib.qmoe_forward_biased
+    args = lambda x, b1, b2, out: (ctypes.byref(p1), ctypes.byref(p2), ctypes.byref(q), 8, x, 4096,
+                                   b1, b2, out, 1 << 20, 1 << 30, None)
+    assert f(*args(4096 + 8, None, None, 8192)) == INVALID   # x not 16-byte aligned
+    assert f(*args(4096, None, None, 8192 + 4)) == INVALID   # out not 8-byte aligned
+    assert f(*args(4096, 1001, None, 8192)) == INVALID       # FC1 bias not 2-byte aligned
+    assert f(*args(4096, None, 3, 8192)) == INVALID          # FC2 bias not 2-byte aligned
+    assert f(*args(None, None, None, 8192)) == INVALID       # no activations
+    assert f(ctypes.byref(p1), ctypes.byref(p2), ctypes.byref(q), 0, None, None, None, None, None,
+             None, 0, None) == OK                            # T = 0: no-op
