@@ -5,7 +5,8 @@
 // independent down projection and aggregation, with bounded activation tiling
 // and no floating expert weights; embedded P0/P1 body, section "P0" for the
 // row-local LSB-first 3-bit format and "P1" for the fused interleaved gate/up
-// and swiglu profile; embedded Olive body for the (code - 4) * scale decode)
+// and swiglu profile, the (3,4) / (4,3) width pairs, FP16/BF16 types and the
+// optional biases; embedded Olive body for the (code - 4) * scale decode)
 // and pegainfer PR "feat(qwen4): component kernels extracted from the brick
 // PRs" (fp32 softmax routing, top-k, renormalized weights, branch combine).
 //
@@ -702,9 +703,10 @@ __device__ __forceinline__ float group_dot_unscaled(const typename Group<BITS>::
 }
 
 // Partial dot products of the 16-row weight tile at row0 of one expert with
-// an fp16 activation row held in LDS: lane (n, g) = (lane & 15, lane >> 4)
-// takes group 4c + g of row row0 + n for the chunks c = c0, c0 + cstep, ...
-// (one 768-byte load per wave and chunk in the tile-major layout).  Loads
+// an fp16 / bf16 activation row held in LDS: lane (n, g) = (lane & 15,
+// lane >> 4) takes group 4c + g of row row0 + n for the chunks c = c0,
+// c0 + cstep, ... (one 768-byte (INT3) or 1024-byte (INT4) load per wave and
+// chunk in the tile-major layout).  Loads
 // are issued in batches of kDecBatch chunks before any is used, the first
 // batch before the activations are staged; groups past K read a valid group
 // with scale 0.
