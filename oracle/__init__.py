@@ -209,13 +209,15 @@ def qmoe_fc2(ids, h, W2, s2, H, I, E, bits2=3, bs=64, nthreads=1, b2=None, dtype
     return y, yS
 
 
-def rtn_int3(W, bs):
+def rtn_int3(W, bs, dtype="f16"):
     """W: float32 [rows, K].  Returns (B uint8 [rows, ceil(3K/8)], scales
-    float16 [rows, K/bs], status uint8 [rows, K/bs])."""
+    [rows, K/bs] (float16, or uint16 bfloat16 patterns for dtype "bf16"),
+    status uint8 [rows, K/bs])."""
     W = np.ascontiguousarray(W, dtype=np.float32)
     rows, K = W.shape
     B = np.zeros((rows, (3 * K + 7) // 8), np.uint8)
     s = np.zeros((rows, K // bs), np.uint16)
     st = np.zeros((rows, K // bs), np.uint8)
-    _check(lib().orc_rtn_int3(I64(rows), I64(K), INT(bs), _p(W), _p(B), _p(s), _p(st)), "rtn_int3")
-    return B, s.view(np.float16), st
+    _check(lib().orc_rtn_int3(I64(rows), I64(K), INT(bs), INT(1 if dtype == "bf16" else 0), _p(W),
+                              _p(B), _p(s), _p(st)), "rtn_int3")
+    return B, (s if dtype == "bf16" else s.view(np.float16)), st

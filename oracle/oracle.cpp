@@ -455,10 +455,14 @@ int orc_qmoe_fc2(int64_t T, int64_t H, int64_t I, int E, int k, int bits2,
 // that round to zero rejected; [P0]: stored-scale rounding).  The decisions
 // (the scale's fp16 rounding and each code's rounding) are taken in fp32, as
 // a producer working on fp32 weights does; see oracle.h.
-int orc_rtn_int3(int64_t rows, int64_t K, int bs, const float* W, uint8_t* B,
+int orc_rtn_int3(int64_t rows, int64_t K, int bs, int dtype, const float* W, uint8_t* B,
                  uint16_t* scales, uint8_t* status) {
-  if (rows < 0 || K < 1 || bs < 1 || K % bs || (rows && (!W || !B || !scales || !status)))
+  if (rows < 0 || K < 1 || bs < 1 || K % bs || (dtype != 0 && dtype != 1) ||
+      (rows && (!W || !B || !scales || !status)))
     return -1;
+  // the stored scale type: fp16 (exponent field 0x7C00) or bf16 (0x7F80)
+  auto store = [dtype](float v) { return dtype ? orc_f64_to_bf16((double)v) : orc_f64_to_f16((double)v); };
+  const uint16_t inf_bits = dtype ? 0x7F80 : 0x7C00;
   const int64_t nb = K / bs, rb = (3 * K + 7) / 8;
   std::vector<uint8_t> codes(K);
   for (int64_t r = 0; r < rows; ++r) {
@@ -477,15 +481,15 @@ int orc_rtn_int3(int64_t rows, int64_t K, int bs, const float* W, uint8_t* B,
       if (!finite) {
         st = 1;
       } else if (amax == 0.0f) {
-        s16 = orc_f64_to_f16((double)(1.0f / 3.5f));
+        s16 = store(1.0f / 3.5f);
       } else {
         const float s = amax / 3.5f;
-        s16 = orc_f64_to_f16((double)s);  // fp32 -> fp64 is exact: one rounding
+        s16 = store(s);  // fp32 -> fp64 is exact: one rounding
         if ((s16 & 0x7FFF) == 0) st = 2;
-        else if ((s16 & 0x7FFF) == 0x7C00) st = 3;
+        else if ((s16 & 0x7FFF) == inf_bits) st = 3;
       }
       if (st) s16 = 0;
-      const float sd = (float)orc_f16_to_f64(s16);
+      const float sd = (float)(dtype ? orc_bf16_to_f64(s16) : orc_f16_to_f64(s16));
       for (int j = 0; j < bs; ++j) {
         int q = 4;
         if (!st) {

@@ -118,17 +118,18 @@ int orc_qmoe_fc2(int64_t T, int64_t H, int64_t I, int E, int k, int bits2,
 
 /* ---- INT3 round-to-nearest producer quantizer [P0][OLIVE] -----------------
  * W fp32 [rows, K], K a multiple of bs.  Per group of bs consecutive k of a
- * row: amax = max |w|; the scale is fp16(amax / 3.5) with the division done
- * in fp32 and the quotient rounded once to fp16 (the stored scale), or
- * fp16(fp32(1 / 3.5)) for an all-zero group; each code is
+ * row: amax = max |w|; the scale is amax / 3.5 with the division done in
+ * fp32 and the quotient rounded once to the stored type (dtype 0: fp16,
+ * 1: bf16 [P1]: FP16/BF16 scales), or the stored fp32(1 / 3.5) for an
+ * all-zero group; each code is
  * q = clamp(rint(w / s) + 4, 0, 7) with w / s an fp32 division by the STORED
  * scale (stored-scale rounding) and rint rounding ties to even.
- * Outputs: B uint8 [rows, ceil(3K/8)] row-local LSB-first; scales fp16
- * [rows, K/bs]; status uint8 [rows, K/bs]: 0 ok, 1 a weight is NaN or
- * infinite, 2 a nonzero group whose scale rounds to zero, 3 a scale beyond
- * the fp16 range.  A group with a nonzero status gets scale 0 and codes 4.
+ * Outputs: B uint8 [rows, ceil(3K/8)] row-local LSB-first; scales 16-bit
+ * patterns [rows, K/bs]; status uint8 [rows, K/bs]: 0 ok, 1 a weight is NaN
+ * or infinite, 2 a nonzero group whose scale rounds to zero, 3 a scale
+ * beyond the stored type's range.  A group with a nonzero status gets scale 0 and codes 4.
  * Returns 0 (also when a status is nonzero), negative on bad arguments.    */
-int orc_rtn_int3(int64_t rows, int64_t K, int bs, const float* W, uint8_t* B,
+int orc_rtn_int3(int64_t rows, int64_t K, int bs, int dtype, const float* W, uint8_t* B,
                  uint16_t* scales, uint8_t* status);
 
 #ifdef __cplusplus

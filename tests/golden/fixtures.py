@@ -50,7 +50,8 @@ def _values(text):
     return out
 
 
-def rtn_int3():
-    """[(name, weights, scale bits, status, bytes)] from rtn_int3.txt."""
+def rtn_int3(name="rtn_int3.txt"):
+    """[(name, weights, scale bits, status, bytes)] from rtn_int3.txt (fp16
+    scales) or rtn_int3_bf16.txt (bfloat16 scales)."""
     return [(n, _values(w), int(s, 16), int(st), bytes.fromhex(b))
-            for n, w, s, st, b in _lines("rtn_int3.txt")]
+            for n, w, s, st, b in _lines(name)]

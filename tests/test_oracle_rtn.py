@@ -99,3 +99,36 @@ def test_status_groups_do_not_affect_their_neighbours(orc):
 def test_argument_errors(orc):
     with pytest.raises(ValueError):
         orc.rtn_int3(np.zeros((2, 48), np.float32), 32)  # K not a multiple of bs
+
+
+# bfloat16 stored scales (P1 section of the INT3 QMoE page: FP16 or BF16
+# scales; the Olive body's dtype-specific subnormal-scale regressions)
+@pytest.mark.parametrize("case", fixtures.rtn_int3("rtn_int3_bf16.txt"), ids=lambda c: c[0])
+def test_hand_derived_groups_bf16(orc, case):
+    name, w, scale_bits, status, want = case
+    B, s, st = orc.rtn_int3(np.array([w], np.float32), 32, "bf16")
+    assert B[0].tobytes() == want, name
+    assert int(s[0, 0]) == scale_bits, name
+    assert int(st[0, 0]) == status, name
+
+
+def test_bf16_scales_are_the_nearest_bfloat16(orc):
+    """The stored bf16 scale is the bfloat16 value nearest amax / 3.5 (torch's
+    bfloat16 rounding of the fp32 quotient, an independent implementation),
+    and every code is the nearest of the eight levels of that scale."""
+    torch = pytest.importorskip("torch")
+    rows, K, bs = 40, 256, 64
+    mag = np.exp(synth.normal(11, rows * K // bs) * 4).reshape(rows, K // bs)
+    W = (synth.normal(12, rows * K).reshape(rows, K // bs, bs) * mag[:, :, None]).astype(np.float32)
+    B, s, st = orc.rtn_int3(W.reshape(rows, K), bs, "bf16")
+    assert (st == 0).all()
+    amax = np.abs(W).max(axis=2)
+    want = torch.from_numpy(amax / np.float32(3.5)).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(s.view(np.int16), want)
+    sd = torch.from_numpy(s.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    q = np.stack([unpack_le(B[r], K, 3) for r in range(rows)]).reshape(rows, K // bs, bs)
+    w = W.astype(np.float64)
+    levels = (np.arange(8) - 4.0)[None, None, None, :] * sd[:, :, None, None]
+    dist = np.abs(w[..., None] - levels)
+    mine = np.take_along_axis(dist, q[..., None], axis=3)[..., 0]
+    assert (mine <= dist.min(axis=3) + 1e-6 * sd[:, :, None]).all()
