@@ -413,7 +413,7 @@ def rtn_extra(torch, mnb, dev):
     B = torch.empty((rows, 3 * K // 8), dtype=torch.uint8, device=dev)
     s = torch.empty((rows, K // bs), dtype=torch.float16, device=dev)
     st = torch.empty((rows, K // bs), dtype=torch.uint8, device=dev)
-    call = lambda: mnb.mnb_quantize_int3_rtn(W, rows, K, bs, B, s, st)
+    call = lambda: mnb.mnb_quantize_int3_rtn(W, rows, K, bs, B, s, st, None, mnb.MNB_DTYPE_F16)
     us = 1e3 * graph_time(torch, [call], 3, min_calls=8)
     byts = rows * K * 4 + rows * 3 * K // 8 + rows * (K // bs) * 3
     res = {"rows": rows, "K": K, "block_size": bs, "us": round(us, 2),

@@ -85,7 +85,7 @@ SIGNATURES = {
     "qmoe_forward_biased": [_PPLAN, _PPLAN, _PQ, _I64, _P, _P, _P, _P, _P, _P, _U64, _P],
     "qmoe_forward_debug": [_PPLAN, _PPLAN, _PQ, _I64, _P, _P, _P, _P, _P, _P, _U64, _P, _P, _P, _P,
                            _P],
-    "mnb_quantize_int3_rtn": [_P, _I64, _I64, ctypes.c_int32, _P, _P, _P, _P],
+    "mnb_quantize_int3_rtn": [_P, _I64, _I64, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P],
 }
 
 _lib = None
@@ -240,23 +240,26 @@ def qmoe_forward(fc1: mnb_plan, fc2: mnb_plan, q: qmoe_desc, T: int, x_dev, logi
 
 
 def mnb_quantize_int3_rtn(W_dev, rows: int, K: int, block_size: int, B_dev, scales_dev,
-                          status_dev, stream=None):
+                          status_dev, stream=None, scale_dtype: int = MNB_DTYPE_F16):
     """Enqueues the INT3 RTN quantizer; read status_dev after the stream ends."""
-    _check(lib().mnb_quantize_int3_rtn(_ptr(W_dev), rows, K, block_size, _ptr(B_dev),
+    _check(lib().mnb_quantize_int3_rtn(_ptr(W_dev), rows, K, block_size, scale_dtype, _ptr(B_dev),
                                        _ptr(scales_dev), _ptr(status_dev), _stream(stream)),
            "mnb_quantize_int3_rtn")
 
 
-def quantize_int3_rtn(W, block_size: int = 64, stream=None):
-    """fp32 device weights [rows, K] -> (B uint8 [rows, 3K/8], scales fp16
-    [rows, K/bs]) as device tensors; raises MnbError(CONTENT) when a group is
-    rejected (non-finite weight or a scale fp16 cannot store)."""
+def quantize_int3_rtn(W, block_size: int = 64, stream=None, scale_dtype: int = MNB_DTYPE_F16):
+    """fp32 device weights [rows, K] -> (B uint8 [rows, 3K/8], scales [rows,
+    K/bs]: float16, or bfloat16 patterns in int16 for MNB_DTYPE_BF16) as device
+    tensors; raises MnbError(CONTENT) when a group is rejected (non-finite
+    weight or a scale the type cannot store)."""
     import torch
     rows, K = W.shape
     B = torch.empty((rows, 3 * K // 8), dtype=torch.uint8, device=W.device)
-    s = torch.empty((rows, K // block_size), dtype=torch.float16, device=W.device)
+    s = torch.empty((rows, K // block_size),
+                    dtype=torch.int16 if scale_dtype == MNB_DTYPE_BF16 else torch.float16,
+                    device=W.device)
     st = torch.empty((rows, K // block_size), dtype=torch.uint8, device=W.device)
-    mnb_quantize_int3_rtn(W, rows, K, block_size, B, s, st, stream)
+    mnb_quantize_int3_rtn(W, rows, K, block_size, B, s, st, stream, scale_dtype)
     if rows and int(st.max().item()) != 0:
         raise MnbError(-4, "quantize_int3_rtn")  # MNB_ERR_CONTENT
     return B, s

@@ -312,10 +312,13 @@ int32_t qmoe_forward_debug(const mnb_plan* fc1, const mnb_plan* fc2, const qmoe_
 }
 
 int32_t mnb_quantize_int3_rtn(const float* W_dev, int64_t rows, int64_t K, int32_t block_size,
-                              uint8_t* B_dev, uint16_t* scales_dev, uint8_t* status_dev,
-                              void* stream) {
+                              int32_t scale_dtype, uint8_t* B_dev, uint16_t* scales_dev,
+                              uint8_t* status_dev, void* stream) {
   MNB_GUARD({
     if (rows < 0 || K < 1 || block_size < 1) return MNB_ERR_INVALID_ARG;
+    if (scale_dtype != MNB_DTYPE_F16 && scale_dtype != MNB_DTYPE_BF16) {
+      return scale_dtype == MNB_DTYPE_F32 ? MNB_ERR_UNSUPPORTED : MNB_ERR_INVALID_ARG;
+    }
     if (block_size != 32 && block_size != 64 && block_size != 128) return MNB_ERR_UNSUPPORTED;
     if (K % block_size) return MNB_ERR_UNSUPPORTED;
     uint64_t n;
@@ -327,8 +330,8 @@ int32_t mnb_quantize_int3_rtn(const float* W_dev, int64_t rows, int64_t K, int32
     if (reinterpret_cast<uintptr_t>(W_dev) % 16 || reinterpret_cast<uintptr_t>(B_dev) % 4 ||
         reinterpret_cast<uintptr_t>(scales_dev) % 2)
       return MNB_ERR_INVALID_ARG;
-    if (launch_rtn_int3(W_dev, rows, K, block_size, B_dev, scales_dev, status_dev,
-                        static_cast<hipStream_t>(stream)) != hipSuccess)
+    if (launch_rtn_int3(W_dev, rows, K, block_size, scale_dtype == MNB_DTYPE_BF16, B_dev,
+                        scales_dev, status_dev, static_cast<hipStream_t>(stream)) != hipSuccess)
       return MNB_ERR_DEVICE;
     return MNB_OK;
   })

@@ -56,8 +56,9 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2,
 
 // ---- producer-side INT3 RTN quantizer (quant.hip) ---------------------------
 // W fp32 [rows, K] (16-byte aligned), K % bs == 0, bs in {32, 64, 128};
-// B [rows, 3K/8] (4-byte aligned), scales fp16 and status uint8 [rows, K/bs]
-hipError_t launch_rtn_int3(const float* W, int64_t rows, int64_t K, int bs, uint8_t* B,
+// B [rows, 3K/8] (4-byte aligned), scales fp16 or bf16 (bf16) and status
+// uint8 [rows, K/bs]
+hipError_t launch_rtn_int3(const float* W, int64_t rows, int64_t K, int bs, bool bf16, uint8_t* B,
                            uint16_t* scales, uint8_t* status, hipStream_t st);
 
 // ---- test-only readers of the device layout (debug.hip) --------------------

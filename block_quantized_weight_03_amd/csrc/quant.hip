@@ -1,6 +1,6 @@
 // Producer-side INT3 round-to-nearest quantizer for gfx950: fp32 weights
-// [rows, K] -> row-local LSB-first 3-bit codes, fp16 scales and a status per
-// group, in the QMoE projection contract (ready for mnb_prepare).
+// [rows, K] -> row-local LSB-first 3-bit codes, fp16 or bf16 scales and a
+// status per group, in the QMoE projection contract (ready for mnb_prepare).
 //
 // Sources: onnxruntime PR "INT3 QMoE CUDA correctness baseline and Qwen
 // experimental results": embedded Olive body, "Summary" (symmetric scale
@@ -10,7 +10,7 @@
 // subnormal stored scales stay allowed) and embedded P0/P1 body, section
 // "P0: Portable Format and Numerical References" (RTN with stored-scale
 // rounding: codes are taken against the scale as stored; row-local LSB-first
-// packing).
+// packing; FP16 or BF16 scales, P1 section).
 //
 // The work is a stream over the weights (4 bytes in, 3/8 byte + 2/bs out per
 // weight), so the kernel is shaped for HBM: each lane takes pieces of 8
@@ -29,12 +29,26 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// The stored scale type: fp16, or bf16 (the top half of an fp32).
+template <bool BF> __device__ __forceinline__ uint16_t store16(float v) {
+  if constexpr (BF)
+    return __builtin_bit_cast(uint16_t, (__bf16)v);  // round to nearest even
+  else
+    return __half_as_ushort(__float2half_rn(v));
+}
+template <bool BF> __device__ __forceinline__ float load16(uint16_t b) {
+  if constexpr (BF)
+    return __uint_as_float((uint32_t)b << 16);
+  else
+    return __half2float(__ushort_as_half(b));
+}
+
 // Status of a group (also the meaning of the status output):
 //  0 ok, 1 a weight is NaN or infinite, 2 a nonzero group whose scale rounds
-//  to zero in fp16, 3 a scale beyond the fp16 range.
+//  to zero in the stored type, 3 a scale beyond its range.
 //
 // One 8-weight piece i: a, b are its two 16-byte halves (zeros when invalid).
-template <int BS>
+template <int BS, bool BF>
 __device__ __forceinline__ void rtn_piece(f32x4 a, f32x4 b, int64_t i, bool valid,
                                           uint32_t* __restrict__ B, uint16_t* __restrict__ scales,
                                           uint8_t* __restrict__ status) {
@@ -53,22 +67,23 @@ __device__ __forceinline__ void rtn_piece(f32x4 a, f32x4 b, int64_t i, bool vali
     amax = fmaxf(amax, __shfl_xor(amax, m));
     finite &= __shfl_xor(finite, m);
   }
-  // the stored scale: the fp32 quotient rounded once to fp16
+  // the stored scale: the fp32 quotient rounded once to the stored type
+  constexpr uint16_t kInf = BF ? 0x7F80u : 0x7C00u;
   int st = 0;
   uint16_t s16 = 0;
   if (!finite) {
     st = 1;
   } else if (amax == 0.0f) {
-    s16 = __half_as_ushort(__float2half_rn(1.0f / 3.5f));
+    s16 = store16<BF>(1.0f / 3.5f);
   } else {
-    s16 = __half_as_ushort(__float2half_rn(amax / 3.5f));
+    s16 = store16<BF>(amax / 3.5f);
     if ((s16 & 0x7FFFu) == 0)
       st = 2;
-    else if ((s16 & 0x7FFFu) == 0x7C00u)
+    else if ((s16 & 0x7FFFu) == kInf)
       st = 3;
   }
   if (st) s16 = 0;
-  const float sd = __half2float(__ushort_as_half(s16));
+  const float sd = load16<BF>(s16);
   // codes against the stored scale; ties to even; groups with a status keep 4
   uint32_t c24 = 0;
 #pragma unroll
@@ -99,7 +114,7 @@ __device__ __forceinline__ void rtn_piece(f32x4 a, f32x4 b, int64_t i, bool vali
 // shuffles.
 constexpr int kPieces = 2;
 
-template <int BS>
+template <int BS, bool BF>
 __global__ void __launch_bounds__(256) rtn_int3_kernel(const float* __restrict__ W, int64_t pieces,
                                                        uint32_t* __restrict__ B,
                                                        uint16_t* __restrict__ scales,
@@ -121,24 +136,35 @@ __global__ void __launch_bounds__(256) rtn_int3_kernel(const float* __restrict__
 #pragma unroll
   for (int u = 0; u < kPieces; ++u) {
     const int64_t i = i0 + u * stride;
-    rtn_piece<BS>(a[u], b[u], i, i < pieces, B, scales, status);
+    rtn_piece<BS, BF>(a[u], b[u], i, i < pieces, B, scales, status);
   }
 }
 
 }  // namespace
 
-hipError_t launch_rtn_int3(const float* W, int64_t rows, int64_t K, int bs, uint8_t* B,
+namespace {
+template <bool BF>
+void launch_rtn_t(const float* W, int64_t pieces, int bs, uint32_t* B32, uint16_t* scales,
+                  uint8_t* status, hipStream_t st) {
+  const dim3 grid((unsigned)((pieces + 256 * kPieces - 1) / (256 * kPieces))), block(256);
+  if (bs == 32)
+    hipLaunchKernelGGL((rtn_int3_kernel<32, BF>), grid, block, 0, st, W, pieces, B32, scales, status);
+  else if (bs == 64)
+    hipLaunchKernelGGL((rtn_int3_kernel<64, BF>), grid, block, 0, st, W, pieces, B32, scales, status);
+  else
+    hipLaunchKernelGGL((rtn_int3_kernel<128, BF>), grid, block, 0, st, W, pieces, B32, scales, status);
+}
+}  // namespace
+
+hipError_t launch_rtn_int3(const float* W, int64_t rows, int64_t K, int bs, bool bf16, uint8_t* B,
                            uint16_t* scales, uint8_t* status, hipStream_t st) {
   const int64_t pieces = rows * (K / 8);
   if (pieces == 0) return hipSuccess;
-  const dim3 grid((unsigned)((pieces + 256 * kPieces - 1) / (256 * kPieces))), block(256);
   uint32_t* B32 = reinterpret_cast<uint32_t*>(B);
-  if (bs == 32)
-    hipLaunchKernelGGL(rtn_int3_kernel<32>, grid, block, 0, st, W, pieces, B32, scales, status);
-  else if (bs == 64)
-    hipLaunchKernelGGL(rtn_int3_kernel<64>, grid, block, 0, st, W, pieces, B32, scales, status);
+  if (bf16)
+    launch_rtn_t<true>(W, pieces, bs, B32, scales, status, st);
   else
-    hipLaunchKernelGGL(rtn_int3_kernel<128>, grid, block, 0, st, W, pieces, B32, scales, status);
+    launch_rtn_t<false>(W, pieces, bs, B32, scales, status, st);
   return hipGetLastError();
 }
 

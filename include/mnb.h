@@ -279,31 +279,34 @@ int32_t qmoe_forward_biased(const mnb_plan* fc1, const mnb_plan* fc2,
 /* ---------------------------------------------------------------------------
  * Producer-side INT3 round-to-nearest quantizer [P0][OLIVE]: fp32 weights to
  * the QMoE projection contract (codes and scales ready for mnb_prepare with
- * bits 3, ROW_LOCAL, F16 scales).  Per group of block_size consecutive k of a
- * row: amax = max |w|; stored scale s = fp16(amax / 3.5) (fp32 quotient,
- * rounded once to fp16), or fp16(1 / 3.5) for an all-zero group; codes
+ * bits 3, ROW_LOCAL and F16 or BF16 scales [P1]).  Per group of block_size
+ * consecutive k of a row: amax = max |w|; stored scale s = amax / 3.5 (fp32
+ * quotient, rounded once to the scale type), or the stored fp32(1 / 3.5) for
+ * an all-zero group; codes
  * q = clamp(rint(w / s) + 4, 0, 7) divided by the STORED scale in fp32,
  * ties to even (stored-scale rounding).  Decoding is (q - 4) * s.
  *  W_dev      fp32 [rows, K] row-major, 16-byte aligned (rows = E * N for a
  *             stacked projection);
  *  B_dev      uint8 [rows, 3K/8] out, row-local LSB-first 3-bit codes, 4-byte
  *             aligned;
- *  scales_dev fp16 [rows, K/block_size] out, 2-byte aligned;
+ *  scale_dtype MNB_DTYPE_F16 or MNB_DTYPE_BF16 (F32: UNSUPPORTED);
+ *  scales_dev [rows, K/block_size] out in that type, 2-byte aligned;
  *  status_dev uint8 [rows, K/block_size] out: 0 ok, 1 a weight is NaN or
  *             infinite, 2 a nonzero group whose scale rounds to zero, 3 a
- *             scale beyond the fp16 range.  A group with a nonzero status is
+ *             scale beyond the type's range.  A group with a nonzero status is
  *             written with scale 0 and codes 4 and must be treated as a
  *             rejected tensor [OLIVE: fail fast, never clamp a scale];
  *             nonzero subnormal scales are status 0.
  * block_size 32, 64 or 128; K a multiple of it.  Asynchronous on `stream`:
  * the caller reads status_dev after the stream has finished.  rows = 0 is a
  * no-op.  Deterministic.  Errors: INVALID_ARG (NULL or misaligned pointers,
- * negative sizes), UNSUPPORTED (block size, K not block aligned),
+ * negative sizes, unknown scale type), UNSUPPORTED (block size, K not block
+ * aligned, F32 scales),
  * SIZE_OVERFLOW, DEVICE. */
 int32_t mnb_quantize_int3_rtn(const float* W_dev, int64_t rows, int64_t K,
-                              int32_t block_size, uint8_t* B_dev,
-                              uint16_t* scales_dev, uint8_t* status_dev,
-                              void* stream);
+                              int32_t block_size, int32_t scale_dtype,
+                              uint8_t* B_dev, uint16_t* scales_dev,
+                              uint8_t* status_dev, void* stream);
 
 #ifdef __cplusplus
 }

@@ -307,18 +307,23 @@ def test_quantizer_argument_checks_before_any_device_call():
     """Every check of mnb_quantize_int3_rtn runs on the host before a launch."""
     lib = mnb.lib()
     f = lib.mnb_quantize_int3_rtn
-    assert f(None, 0, 64, 32, None, None, None, None) == OK  # rows = 0: no-op
-    assert f(16, 4, 64, 48, 16, 16, 16, None) == UNSUP      # block size
-    assert f(16, 4, 96, 64, 16, 16, 16, None) == UNSUP      # K not block aligned
-    assert f(16, 4, 64, 0, 16, 16, 16, None) == INVALID
-    assert f(16, -1, 64, 32, 16, 16, 16, None) == INVALID
-    assert f(16, 4, 0, 32, 16, 16, 16, None) == INVALID
-    assert f(None, 4, 64, 32, 16, 16, 16, None) == INVALID  # null weights
-    assert f(16, 4, 64, 32, 16, None, 16, None) == INVALID  # null scales
-    assert f(8, 4, 64, 32, 16, 16, 16, None) == INVALID     # weights not 16-byte aligned
-    assert f(16, 4, 64, 32, 18, 16, 16, None) == INVALID    # codes not 4-byte aligned
-    assert f(16, 4, 64, 32, 16, 17, 16, None) == INVALID    # scales not 2-byte aligned
-    assert f(16, 2 ** 40, 2 ** 30, 32, 16, 16, 16, None) == OVERFLOW
+    F16, BF16 = mnb.MNB_DTYPE_F16, mnb.MNB_DTYPE_BF16
+    assert f(None, 0, 64, 32, F16, None, None, None, None) == OK  # rows = 0: no-op
+    assert f(None, 0, 64, 32, BF16, None, None, None, None) == OK
+    assert f(16, 4, 64, 48, F16, 16, 16, 16, None) == UNSUP      # block size
+    assert f(16, 4, 96, 64, BF16, 16, 16, 16, None) == UNSUP     # K not block aligned
+    assert f(16, 4, 64, 32, mnb.MNB_DTYPE_F32, 16, 16, 16, None) == UNSUP  # fp32 scales
+    assert f(16, 4, 64, 32, 3, 16, 16, 16, None) == INVALID      # unknown scale type
+    assert f(16, 4, 64, 32, -1, 16, 16, 16, None) == INVALID
+    assert f(16, 4, 64, 0, F16, 16, 16, 16, None) == INVALID
+    assert f(16, -1, 64, 32, F16, 16, 16, 16, None) == INVALID
+    assert f(16, 4, 0, 32, F16, 16, 16, 16, None) == INVALID
+    assert f(None, 4, 64, 32, F16, 16, 16, 16, None) == INVALID  # null weights
+    assert f(16, 4, 64, 32, F16, 16, None, 16, None) == INVALID  # null scales
+    assert f(8, 4, 64, 32, F16, 16, 16, 16, None) == INVALID     # weights not 16-byte aligned
+    assert f(16, 4, 64, 32, F16, 18, 16, 16, None) == INVALID    # codes not 4-byte aligned
+    assert f(16, 4, 64, 32, BF16, 16, 17, 16, None) == INVALID   # scales not 2-byte aligned
+    assert f(16, 2 ** 40, 2 ** 30, 32, F16, 16, 16, 16, None) == OVERFLOW
 
 
 @pytest.mark.parametrize("bits,K,bs", [(3, 128, 64), (4, 128, 32), (3, 320, 32), (4, 384, 128)])

@@ -174,16 +174,18 @@ def test_graph_qmoe_biased_widths_dtypes(T, bits1, bits2, bf16):
         torch.cuda.synchronize()
 
 
-def test_graph_rtn_quantizer():
-    say("graph rtn quantizer")
+@pytest.mark.parametrize("bf16", [False, True])
+def test_graph_rtn_quantizer(bf16):
+    say(f"graph rtn quantizer bf16={bf16}")
     rows, K, bs = 300, 256, 32
     W = torch.from_numpy((synth.normal(9, rows * K) * 0.1).astype(np.float32).reshape(rows, K)).cuda()
     B = torch.empty((rows, 3 * K // 8), dtype=torch.uint8, device="cuda")
     s = torch.empty((rows, K // bs), dtype=torch.float16, device="cuda")
     st = torch.empty((rows, K // bs), dtype=torch.uint8, device="cuda")
+    sd = mnb.MNB_DTYPE_BF16 if bf16 else mnb.MNB_DTYPE_F16
 
     def run():
-        mnb.mnb_quantize_int3_rtn(W, rows, K, bs, B, s, st)
+        mnb.mnb_quantize_int3_rtn(W, rows, K, bs, B, s, st, None, sd)
 
     run()
     torch.cuda.synchronize()

@@ -6,8 +6,8 @@ experimental results", embedded Olive body ("Summary": scale max|w| / 3.5,
 zero point 4, all-zero group scale 1 / 3.5 with code 4, rejection of
 non-finite weights and unrepresentable scales) and embedded P0/P1 body,
 section "P0" (stored-scale rounding, row-local LSB-first packing, golden
-bytes).  The codes are integers decided in fp32 on both sides, so the bar is
-bit equality.
+bytes) and section "P1" (FP16 or BF16 scales).  The codes are integers decided
+in fp32 on both sides, so the bar is bit equality, for both stored types.
 """
 import sys
 
@@ -28,7 +28,10 @@ def say(*a):
     sys.stdout.flush()
 
 
-def gpu_rtn(W, bs):
+DTYPES = {"f16": mnb.MNB_DTYPE_F16, "bf16": mnb.MNB_DTYPE_BF16}
+
+
+def gpu_rtn(W, bs, dtype="f16"):
     rows, K = W.shape
     Wd = torch.from_numpy(np.ascontiguousarray(W, dtype=np.float32)).cuda()
     # guard bands around every output catch writes past the end
@@ -37,7 +40,7 @@ def gpu_rtn(W, bs):
     sg = torch.full((rows * (K // bs) + 2 * g,), 0x5A5A, dtype=torch.int16, device="cuda")
     tg = torch.full((rows * (K // bs) + 2 * g,), 0xEE, dtype=torch.uint8, device="cuda")
     B, s, st = Bg[g:-g], sg[g:-g], tg[g:-g]
-    mnb.mnb_quantize_int3_rtn(Wd, rows, K, bs, B, s, st)
+    mnb.mnb_quantize_int3_rtn(Wd, rows, K, bs, B, s, st, None, DTYPES[dtype])
     torch.cuda.synchronize()
     for buf, fill in ((Bg, 0xA5), (tg, 0xEE)):
         h = buf.cpu().numpy()
@@ -48,30 +51,33 @@ def gpu_rtn(W, bs):
             st.cpu().numpy().reshape(rows, -1))
 
 
-def check_against_oracle(orc, W, bs):
-    B, s, st = gpu_rtn(W, bs)
-    oB, os_, ost = orc.rtn_int3(W, bs)
+def check_against_oracle(orc, W, bs, dtype="f16"):
+    B, s, st = gpu_rtn(W, bs, dtype)
+    oB, os_, ost = orc.rtn_int3(W, bs, dtype)
     assert np.array_equal(st, ost)
     assert np.array_equal(s, os_.view(np.uint16))
     assert np.array_equal(B, oB)
     return st
 
 
-def test_hand_derived_groups():
-    say("rtn golden groups")
-    cases = fixtures.rtn_int3()
+@pytest.mark.parametrize("name,dtype", [("rtn_int3.txt", "f16"), ("rtn_int3_bf16.txt", "bf16")])
+def test_hand_derived_groups(name, dtype):
+    say(f"rtn golden groups {dtype}")
+    cases = fixtures.rtn_int3(name)
     W = np.array([c[1] for c in cases], np.float32)
-    B, s, st = gpu_rtn(W, 32)
+    B, s, st = gpu_rtn(W, 32, dtype)
     for r, (name, _, scale_bits, status, want) in enumerate(cases):
         assert B[r].tobytes() == want, name
         assert int(s[r, 0]) == scale_bits, name
         assert int(st[r, 0]) == status, name
 
 
-def spread_weights(seed, rows, K, bs):
+def spread_weights(seed, rows, K, bs, dtype="f16"):
     """N(0,1) weights with group magnitudes spread over ~10 decades, so that
     normal and subnormal fp16 scales both occur, plus all-zero groups and
-    groups that must be rejected."""
+    groups that must be rejected.  For bf16 the underflow row sits in the
+    fp32 subnormal range (no finite fp32 scale overflows bf16), and one row
+    takes a nonzero subnormal bf16 scale."""
     nb = K // bs
     mag = np.exp(synth.normal(seed, rows * nb) * 3.0).reshape(rows, nb) * 1e-2
     W = (synth.normal(seed + 1, rows * K).reshape(rows, nb, bs) * mag[:, :, None]).astype(np.float32)
@@ -79,89 +85,119 @@ def spread_weights(seed, rows, K, bs):
     if rows > 3 and nb > 1:
         W[1, 1, 3] = np.nan
         W[2, 0, bs - 1] = -np.inf
-        W[3, nb - 1] *= np.float32(1e-12) / np.abs(W[3, nb - 1]).max()  # scale underflows
-        W[rows - 1, 0, 0] = np.float32(3e5)  # scale overflows fp16
+        if dtype == "f16":
+            W[3, nb - 1] *= np.float32(1e-12) / np.abs(W[3, nb - 1]).max()  # scale underflows
+            W[rows - 1, 0, 0] = np.float32(3e5)  # scale overflows fp16
+        else:
+            g = W[3, nb - 1].astype(np.float64)
+            W[3, nb - 1] = (g * (1e-44 / np.abs(g).max())).astype(np.float32)  # underflows bf16
+            g = W[rows - 1, 0].astype(np.float64)
+            W[rows - 1, 0] = (g * (1e-39 / np.abs(g).max())).astype(np.float32)  # subnormal scale
     return W.reshape(rows, K)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("bs", [32, 64, 128])
 @pytest.mark.parametrize("rows,nb", [(1, 1), (5, 3), (67, 4), (130, 7)])
-def test_random_weights_match_oracle_bit_for_bit(orc, rows, nb, bs):
-    say(f"rtn rows={rows} K={nb * bs} bs={bs}")
-    W = spread_weights(rows * 17 + nb + bs, rows, nb * bs, bs)
-    st = check_against_oracle(orc, W, bs)
+def test_random_weights_match_oracle_bit_for_bit(orc, rows, nb, bs, dtype):
+    say(f"rtn {dtype} rows={rows} K={nb * bs} bs={bs}")
+    W = spread_weights(rows * 17 + nb + bs, rows, nb * bs, bs, dtype)
+    st = check_against_oracle(orc, W, bs, dtype)
     if rows > 3 and nb > 1:
-        assert set(np.unique(st).tolist()) == {0, 1, 2, 3}
+        assert set(np.unique(st).tolist()) == ({0, 1, 2, 3} if dtype == "f16" else {0, 1, 2})
 
 
-def test_ties_and_scale_rounding_edges(orc):
+def stored_value(v, dtype):
+    """v rounded to the stored type, as float32 (normal range)."""
+    if dtype == "f16":
+        return np.float16(v).astype(np.float32)
+    b = synth.to_bf16_bits(np.array([v], np.float32))
+    return (b.astype(np.uint32) << 16).view(np.float32)[0]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_ties_and_scale_rounding_edges(orc, dtype):
     """Weights on exact half steps of the stored scale (ties to even) and
-    groups whose amax / 3.5 sits next to fp16 rounding boundaries."""
-    say("rtn ties")
+    groups whose amax / 3.5 sits next to, or exactly on, a rounding midpoint
+    of the stored type (3.5 times a midpoint is exact in fp32, so the quotient
+    is the midpoint itself and the tie goes to even)."""
+    say(f"rtn ties {dtype}")
     bs = 32
     rows = 64
+    sig = 11 if dtype == "f16" else 8  # significant bits of the stored type
     rng = np.random.default_rng(3)
     W = np.zeros((rows, 4 * bs), np.float32)
     for r in range(rows):
         for g in range(4):
-            s16 = np.float16(rng.uniform(0.01, 2.0)).astype(np.float32)
+            s = stored_value(rng.uniform(0.01, 2.0), dtype)
             halves = rng.integers(-7, 8, bs).astype(np.float32) * 0.5   # k/2 steps, |w| <= 3.5 s
-            grp = halves * s16
-            grp[0] = np.float32(3.5) * s16 * np.float32(1 + (r % 3 - 1) * 2 ** -12)
+            grp = halves * s
+            if r % 4 == 3:  # amax / 3.5 is the midpoint above s
+                mid = np.float32(s * (1 + 2.0 ** -sig))
+                grp[0] = np.float32(3.5) * mid
+            else:
+                grp[0] = np.float32(3.5) * s * np.float32(1 + (r % 4 - 1) * 2.0 ** -(sig + 1))
             W[r, g * bs:(g + 1) * bs] = grp
-    check_against_oracle(orc, W, bs)
+    check_against_oracle(orc, W, bs, dtype)
 
 
-def test_layer_sized_projection_sampled_rows(orc):
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_layer_sized_projection_sampled_rows(orc, dtype):
     """One expert-stack's worth of FC1 rows (16 experts x 1536 rows, K = 2048,
     block 64): the oracle recomputes a sample of rows (rows are independent)."""
-    say("rtn layer-sized")
+    say(f"rtn layer-sized {dtype}")
     rows, K, bs = 16 * 1536, 2048, 64
     gen = torch.Generator(device="cuda").manual_seed(11)
     Wd = torch.randn((rows, K), generator=gen, device="cuda", dtype=torch.float32) * 0.02
     B = torch.empty((rows, 3 * K // 8), dtype=torch.uint8, device="cuda")
-    s = torch.empty((rows, K // bs), dtype=torch.float16, device="cuda")
+    s = torch.empty((rows, K // bs), dtype=torch.int16, device="cuda")
     st = torch.empty((rows, K // bs), dtype=torch.uint8, device="cuda")
-    mnb.mnb_quantize_int3_rtn(Wd, rows, K, bs, B, s, st)
+    mnb.mnb_quantize_int3_rtn(Wd, rows, K, bs, B, s, st, None, DTYPES[dtype])
     torch.cuda.synchronize()
     assert int(st.max().item()) == 0
     pick = np.unique(np.concatenate([[0, rows - 1], np.random.default_rng(1).choice(rows, 40)]))
     Wh = Wd[torch.from_numpy(pick).cuda()].cpu().numpy()
-    oB, os_, ost = orc.rtn_int3(Wh, bs)
+    oB, os_, ost = orc.rtn_int3(Wh, bs, dtype)
     assert np.array_equal(B[torch.from_numpy(pick).cuda()].cpu().numpy(), oB)
     assert np.array_equal(s[torch.from_numpy(pick).cuda()].cpu().numpy().view(np.uint16),
                           os_.view(np.uint16))
     # deterministic
     B2 = torch.empty_like(B)
-    mnb.mnb_quantize_int3_rtn(Wd, rows, K, bs, B2, s, st)
+    mnb.mnb_quantize_int3_rtn(Wd, rows, K, bs, B2, s, st, None, DTYPES[dtype])
     torch.cuda.synchronize()
     assert torch.equal(B, B2)
 
 
-def test_quantized_weights_feed_the_qmoe_layer(orc):
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_quantized_weights_feed_the_qmoe_layer(orc, dtype):
     """The quantizer's output is the QMoE projection contract: prepared as is,
-    the layer matches the oracle run on the same codes and scales."""
-    say("rtn -> qmoe")
+    the layer (with activations of the scales' type) matches the oracle run on
+    the same codes and scales."""
+    say(f"rtn -> qmoe {dtype}")
     from tests.test_gpu_qmoe import Moe, check_end_to_end
     T, H, I, E, k, bs = 6, 128, 64, 4, 2, 64
     W1 = (synth.normal(21, E * 2 * I * H) * 0.05).astype(np.float32).reshape(E * 2 * I, H)
     W2 = (synth.normal(22, E * H * I) * 0.05).astype(np.float32).reshape(E * H, I)
-    B1, s1 = mnb.quantize_int3_rtn(torch.from_numpy(W1).cuda(), bs)
-    B2, s2 = mnb.quantize_int3_rtn(torch.from_numpy(W2).cuda(), bs)
+    B1, s1 = mnb.quantize_int3_rtn(torch.from_numpy(W1).cuda(), bs, scale_dtype=DTYPES[dtype])
+    B2, s2 = mnb.quantize_int3_rtn(torch.from_numpy(W2).cuda(), bs, scale_dtype=DTYPES[dtype])
     B1, s1 = B1.cpu().numpy().reshape(E, 2 * I, -1), s1.cpu().numpy().reshape(E, 2 * I, -1)
     B2, s2 = B2.cpu().numpy().reshape(E, H, -1), s2.cpu().numpy().reshape(E, H, -1)
-    oB1, os1, _ = orc.rtn_int3(W1, bs)
+    if dtype == "bf16":
+        s1, s2 = s1.view(np.uint16), s2.view(np.uint16)
+    oB1, os1, _ = orc.rtn_int3(W1, bs, dtype)
     assert np.array_equal(B1.reshape(E * 2 * I, -1), oB1)
-    x = synth.activations_f16(23, T, H)
+    assert np.array_equal(s1.reshape(E * 2 * I, -1).view(np.uint16), os1.view(np.uint16))
+    x = synth.activations_f16(23, T, H) if dtype == "f16" else synth.activations_bf16(23, T, H)
     logits = synth.router_logits(24, T, E)
-    m = Moe(x, logits, B1, s1, B2, s2, k, bs)
-    check_end_to_end(m.run(x, logits)["out"], m.oracle(orc, x, logits))
+    m = Moe(x, logits, B1, s1, B2, s2, k, bs, dtype=dtype)
+    check_end_to_end(m.run(x, logits)["out"], m.oracle(orc, x, logits), dtype)
 
 
-def test_rejected_tensor_raises():
-    say("rtn rejection")
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_rejected_tensor_raises(dtype):
+    say(f"rtn rejection {dtype}")
     W = torch.ones((2, 64), dtype=torch.float32, device="cuda")
     W[1, 40] = float("nan")
     with pytest.raises(mnb.MnbError) as e:
-        mnb.quantize_int3_rtn(W, 32)
+        mnb.quantize_int3_rtn(W, 32, scale_dtype=DTYPES[dtype])
     assert e.value.status == -4
