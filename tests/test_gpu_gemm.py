@@ -150,6 +150,32 @@ def test_gemm_large_m_ragged_elementwise(orc, M, K, N, bs, zp):
     check(orc, y, a, B, s, Z, K, N, bs)
 
 
+@pytest.mark.parametrize("M,K,N,zp", [(128, 6144, 2048, False), (512, 6144, 2048, True),
+                                       (4096, 6144, 2048, False)])
+def test_gemm_split_k_reuses_a_dirty_workspace(orc, M, K, N, zp):
+    """Split K on the LDS-streaming kernel (12, 4 and 2 splits here): one
+    workspace, filled with 0xFF before the first call, serves three calls;
+    every call gives the same bits (nothing depends on what the workspace
+    held), and sampled rows match the oracle."""
+    say(f"gemm split-K dirty workspace M={M} K={K} N={N} zp={zp}")
+    w, B, s, Z = prepare(K, N, 32, zp, seed=M + K + 3)
+    a = synth.activations_f32(synth.seed_for(31, M), M, K)
+    A = torch.from_numpy(a).cuda()
+    need = mnb.mnb_gemm_workspace_size(w.plan, M)
+    ws = torch.full((max(need, 256),), 0xFF, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(3):
+        Y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        mnb.mnb_gemm(w.plan, M, A, Y, ws, ws.numel())
+        torch.cuda.synchronize()
+        outs.append(Y.cpu().numpy())
+    assert np.isfinite(outs[0]).all()
+    for y in outs[1:]:
+        assert np.array_equal(y.view(np.uint32), outs[0].view(np.uint32))
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(M).choice(M, 6)]))
+    check(orc, outs[0][rows], a[rows], B, s, Z, K, N, 32)
+
+
 def test_gemm_large_m_rows_are_independent():
     say("gemm large-M row independence")
     M, K, N = 4500, 512, 4096  # 256 x 256 tiles for the batch and the sub-batch
