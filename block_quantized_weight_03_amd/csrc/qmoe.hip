@@ -635,8 +635,18 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
   store_a(0, 0);
   load_a(1);
   __syncthreads();
+  // Chunk c first moves the activations of chunk c + 1 from registers to LDS
+  // buffer b ^ 1 (last read in chunk c - 1, before the barrier that ended
+  // it) and loads those of chunk c + 2, then refills the weight stages.
+  // Vector loads complete in order, so activation loads issued after a
+  // weight load of a later chunk would make the LDS store wait for that
+  // weight load too; issued first, they leave kWS chunks of weights in flight.
   auto chunk = [&](WStage (&ws)[kNTG], int c) {
     const int b = c & 1;
+    if (c + 1 < nch) {
+      store_a(b ^ 1, c + 1);
+      load_a(c + 2);
+    }
 #pragma unroll
     for (int t = 0; t < kNTG; ++t) {
       u32x4 wf[4];
@@ -656,11 +666,7 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
         }
       }
     }
-    if (c + 1 < nch) {
-      store_a(b ^ 1, c + 1);
-      load_a(c + 2);
-      __syncthreads();
-    }
+    if (c + 1 < nch) __syncthreads();
   };
   if constexpr (kWS == 2) {
     for (int c = 0; c < nch; c += 2) {
