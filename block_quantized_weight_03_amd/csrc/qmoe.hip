@@ -549,7 +549,9 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
     st.ok = rok && G < ng;
     const uint32_t off = (uint32_t)(rok ? rt : 0) * (uint32_t)(ng * 16 * GB) + 64 * GB * (uint32_t)c +
                          (c < nfull ? lane_full : lane_last);
-    st.rw = *reinterpret_cast<const typename Group<BITS>::W*>(wbase + off);
+    // streamed once: nontemporal, so that the weight stream does not push the
+    // item's activation rows out of L2 (measured: 4% faster INT4 FC1 at 128 tokens)
+    st.rw = __builtin_nontemporal_load(reinterpret_cast<const typename Group<BITS>::W*>(wbase + off));
     const int rowc = rok ? 16 * rt + wn : wn;
     st.rs = sbase[rowc * (int)g.nblk + ((32 * (G < ng ? G : ng - 1)) >> bshift)];
   };
