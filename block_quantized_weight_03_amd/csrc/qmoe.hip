@@ -620,8 +620,9 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
   // c % kWS, which then takes chunk c + kWS.  With 64-token items (many
   // workgroups per CU, each weight feeding more MFMAs) two stages keep two
   // chunks of the HBM stream in flight per wave (measured 3-4% faster at 512
-  // tokens); with 32-token items one stage is faster (the grid leaves
-  // registers to spare, and the doubled loop body costs instruction fetch).
+  // tokens); with 32-token items one stage is faster (measured 3-12% at 128
+  // tokens: the grid there puts only about three waves on a SIMD, and the
+  // doubled loop body costs instruction fetch).
   // For two stages the chunk loop is unrolled by two so that each stage keeps
   // its registers (moving a register whose load is in flight would wait for
   // it).
