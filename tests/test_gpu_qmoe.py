@@ -209,10 +209,14 @@ def test_tiny_predetermined_route_moe():
     assert (res["out"][1] == 0).all()
 
 
+# (the last two cases take 64-token items with an odd number of K chunks
+# above one, H = 384 and 320: the two-stage weight loop, unrolled by two,
+# then ends on its first half)
 @pytest.mark.parametrize("T,H,I,E,k,bs", [(5, 64, 64, 4, 2, 64), (3, 128, 64, 8, 3, 32),
                                           (17, 256, 128, 16, 4, 128), (33, 128, 96, 6, 6, 32),
                                           (1, 64, 32, 3, 3, 32), (64, 192, 160, 12, 8, 32),
-                                          (40, 64, 32, 300, 8, 32)])
+                                          (40, 64, 32, 300, 8, 32), (64, 384, 160, 8, 8, 32),
+                                          (70, 320, 96, 8, 8, 32)])
 def test_qmoe_small_shapes_all_outputs(orc, T, H, I, E, k, bs):
     say(f"qmoe small T={T} H={H} I={I} E={E} k={k} bs={bs}")
     x, logits, m = random_moe(T * 7 + E, T, H, I, E, k, bs)
@@ -229,7 +233,8 @@ def test_qmoe_small_shapes_all_outputs(orc, T, H, I, E, k, bs):
 @pytest.mark.parametrize("bits1,bits2", [(4, 4), (3, 4), (4, 3)])
 @pytest.mark.parametrize("T,H,I,E,k,bs", [(1, 64, 32, 3, 3, 32), (4, 128, 64, 8, 8, 64),
                                           (5, 64, 64, 4, 2, 64), (17, 256, 128, 16, 4, 128),
-                                          (33, 128, 96, 6, 6, 32), (64, 192, 160, 12, 8, 32)])
+                                          (33, 128, 96, 6, 6, 32), (64, 192, 160, 12, 8, 32),
+                                          (64, 384, 160, 8, 8, 32)])
 def test_qmoe_width_pairs_all_outputs(orc, bits1, bits2, T, H, I, E, k, bs):
     say(f"qmoe widths ({bits1},{bits2}) T={T} H={H} I={I} E={E} k={k} bs={bs}")
     x, logits, m = random_moe(T * 13 + E + bits1, T, H, I, E, k, bs, bits1, bits2)
