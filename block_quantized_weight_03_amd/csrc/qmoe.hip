@@ -457,15 +457,21 @@ struct MoeGemmArgs {
 constexpr int kQBN = 64;         // weight rows per workgroup
 constexpr int kQBK = 128;        // K per chunk
 constexpr int kQPitch = kQBK + 8;
-// 64-row weight tiles per workgroup: 4 with 32-token tiles, 2 with 64 (their
-// accumulators would otherwise cost occupancy)
-template <int BM>
-constexpr int ntg_of() { return BM == 32 ? 4 : 2; }
+// 64-row weight tiles per workgroup: with 64-token tiles 2 (their
+// accumulators would otherwise cost occupancy); with 32-token tiles 2 for
+// INT3 and 4 for INT4 (measured at 128 tokens: INT3 95.6 -> 92.9 us and bf16
+// 113.7 -> 107.9 with 2, INT4 98.3 -> 103.4)
+template <int BM, int BITS>
+constexpr int ntg_of() { return BM == 32 ? (BITS == 3 ? 2 : 4) : 2; }
+int ntg_for(int bm, int bits) {
+  if (bm == 32) return bits == 3 ? ntg_of<32, 3>() : ntg_of<32, 4>();
+  return bits == 3 ? ntg_of<64, 3>() : ntg_of<64, 4>();
+}
 
 template <bool FC1, int BM, int BITS, bool BF>
 __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n, int64_t tiles_n) {
   constexpr uint32_t GB = 4 * BITS;    // bytes per 32-code group
-  constexpr int kNTG = ntg_of<BM>();
+  constexpr int kNTG = ntg_of<BM, BITS>();
   constexpr int TM = BM / 16;          // 16-token MFMA tiles
   constexpr int AP = BM * 16 / 256;    // 16-byte activation chunks per thread and chunk
   __shared__ __align__(16) _Float16 As[2][BM * kQPitch];
@@ -1161,8 +1167,8 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
                    x + t0 * H, s1.N, s1.K, s1.row_bytes, s1.nb, s1.bs, k, (int)E,
                    go.counts, go.offsets, go.perm, go.items, go.nitems, wts, hbuf, nullptr,
                    b1};
-    const int ntg = bm == 32 ? ntg_of<32>() : ntg_of<kMaxBM>();
-    const int64_t nt1 = (s1.N + kQBN - 1) / kQBN, ng1 = (nt1 + ntg - 1) / ntg;
+    const int ntg1 = ntg_for(bm, (int)s1.bits), ntg2 = ntg_for(bm, (int)s2.bits);
+    const int64_t nt1 = (s1.N + kQBN - 1) / kQBN, ng1 = (nt1 + ntg1 - 1) / ntg1;
     const dim3 grid1((unsigned)((items + 7) / 8 * 8 * ng1));
     by_kind(s1.bits, bf, [&](auto bits, auto bfc) {
       constexpr int B = decltype(bits)::value;
@@ -1176,7 +1182,7 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
                    hbuf, s2.N, s2.K, s2.row_bytes, s2.nb, s2.bs, k, (int)E,
                    go.counts, go.offsets, go.perm, go.items, go.nitems, wts, nullptr, slots,
                    b2};
-    const int64_t nt2 = (s2.N + kQBN - 1) / kQBN, ng2 = (nt2 + ntg - 1) / ntg;
+    const int64_t nt2 = (s2.N + kQBN - 1) / kQBN, ng2 = (nt2 + ntg2 - 1) / ntg2;
     const dim3 grid2((unsigned)((items + 7) / 8 * 8 * ng2));
     by_kind(s2.bits, bf, [&](auto bits, auto bfc) {
       constexpr int B = decltype(bits)::value;
