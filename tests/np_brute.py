@@ -96,3 +96,71 @@ def qmoe_all_experts(x16, logits, W1, s1, W2, s2, k: int, bs: int, bits1: int = 
             Y = Y + b2[e].astype(np.float64)
         out += rw[:, e:e + 1] * Y
     return out, order, np.take_along_axis(rw, order, axis=1)
+
+
+def silu_derivative(g):
+    """d/dg [g * sigmoid(g)] by complex-step differentiation, Im f(g + i*h) / h
+    with h = 1e-30: accurate to rounding and obtained without writing the
+    closed-form derivative, so a wrong closed form elsewhere cannot hide."""
+    step = 1e-30
+    z = np.asarray(g, dtype=np.float64) + 1j * step
+    return (z / (1.0 + np.exp(-z))).imag / step
+
+
+def qmoe_tolerance_sums(x16, logits, W1, s1, W2, s2, k: int, bs: int, bits1: int = 3,
+                        bits2: int = 3, b1=None, b2=None):
+    """The QMoE tolerance sums for every expert, as whole-tensor products.
+
+    gs[t, e, i] = sum_c |x[t, c] w1[e, 2i, c]| (+ |b1[e, 2i]|), us likewise on
+    row 2i + 1, and the end-to-end sum
+    S[t, n] = sum_e rw[t, e] sum_i |w2[e, n, i]| (|h| + |dh/dg| gs + |dh/du| us),
+    with rw the renormalized top-k weights masked to the selected experts (zero
+    elsewhere), dh/dg = u silu'(g) and dh/du = silu(g).  Returns (gs, us, S)
+    with gs and us shaped [T, E, I]."""
+    T, H = x16.shape
+    E, twoI, _ = W1.shape
+    I = twoI // 2
+    w1 = moe_weights(W1, s1, H, bs, bits1)
+    w2 = moe_weights(W2, s2, I, bs, bits2)
+    x = x16.astype(np.float64)
+    p = softmax(logits.astype(np.float64))
+    order = np.argsort(-logits, axis=1, kind="stable")[:, :k]
+    mask = np.zeros((T, E))
+    np.put_along_axis(mask, order, 1.0, axis=1)
+    rw = p * mask
+    rw = rw / rw.sum(axis=1, keepdims=True)
+    gs = np.zeros((T, E, I))
+    us = np.zeros((T, E, I))
+    S = np.zeros((T, H))
+    for e in range(E):
+        G = x @ w1[e, 0::2].T
+        U = x @ w1[e, 1::2].T
+        gs[:, e] = np.abs(x) @ np.abs(w1[e, 0::2]).T
+        us[:, e] = np.abs(x) @ np.abs(w1[e, 1::2]).T
+        if b1 is not None:
+            bg = b1[e, 0::2].astype(np.float64)
+            bu = b1[e, 1::2].astype(np.float64)
+            G, U = G + bg, U + bu
+            gs[:, e] += np.abs(bg)
+            us[:, e] += np.abs(bu)
+        silu = G / (1.0 + np.exp(-G))
+        V = np.abs(silu * U) + np.abs(U * silu_derivative(G)) * gs[:, e] + np.abs(silu) * us[:, e]
+        Ye = V @ np.abs(w2[e]).T
+        if b2 is not None:
+            Ye = Ye + np.abs(b2[e].astype(np.float64))
+        S += rw[:, e:e + 1] * Ye
+    return gs, us, S
+
+
+def fc2_tolerance_sum(ids, h, W2, s2, I: int, bs: int, bits2: int = 3, b2=None):
+    """yS[t, j, n] = sum_i |h[t, j, i] w2[ids[t, j], n, i]| (+ |b2[ids[t, j], n]|)."""
+    w2 = moe_weights(W2, s2, I, bs, bits2)
+    T, k = ids.shape
+    yS = np.zeros((T, k, w2.shape[1]))
+    for t in range(T):
+        for j in range(k):
+            e = ids[t, j]
+            yS[t, j] = np.abs(w2[e]) @ np.abs(h[t, j])
+            if b2 is not None:
+                yS[t, j] += np.abs(b2[e].astype(np.float64))
+    return yS

@@ -310,3 +310,68 @@ def test_qmoe_bf16_brute_force(orc, bits1, bits2, bs):
     y, _ = orc.qmoe_fc2(o["ids"], o["h"], W2, s2, H, I, E, bits2=bits2, bs=bs, b2=b2, dtype="bf16")
     np.testing.assert_allclose((o["r"][:, :, None] * y).sum(axis=1), o["out64"], rtol=1e-12,
                                atol=1e-14 * np.abs(ref).max())
+
+
+# ---------------------------------------------------------------------------
+# The tolerance sums.  Every QMoE bound on the GPU is 4e-3 times a sum the
+# oracle returns (gs, us for FC1; yS for FC2 fed the GPU's h; S for the layer),
+# so each sum is pinned here to an independent whole-tensor numpy form: every
+# expert evaluated, a masked routing-weight matrix, |x| @ |w|^T products and
+# the SwiGLU derivative by complex-step differentiation (INT3 QMoE page, P0
+# section: independent scalar references; the first-order propagation of a
+# per-product bound through h = silu(g) * u).
+# ---------------------------------------------------------------------------
+
+def _bf16_moe(seed, T, H, I, E, bs, bits1, bits2):
+    x = synth.activations_bf16(seed, T, H)
+    logits = synth.router_logits(seed + 1, T, E)
+    W1 = synth.packed_rows(seed + 2, E * 2 * I, H, bits1).reshape(E, 2 * I, -1)
+    s1 = synth.scales_bf16(seed + 3, (E, 2 * I, H // bs))
+    W2 = synth.packed_rows(seed + 4, E * H, I, bits2).reshape(E, H, -1)
+    s2 = synth.scales_bf16(seed + 5, (E, H, I // bs))
+    return x, logits, W1, s1, W2, s2
+
+
+@pytest.mark.parametrize("bits1,bits2", [(3, 3), (4, 4), (3, 4), (4, 3)])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("biased", [False, True])
+def test_qmoe_tolerance_sums_independent(orc, bits1, bits2, dtype, biased):
+    from tests.np_brute import fc2_tolerance_sum, qmoe_tolerance_sums
+    T, H, I, E, k, bs = 5, 128, 64, 6, 3, 32
+    seed = 400 + 10 * bits1 + bits2
+    if dtype == "bf16":
+        x, logits, W1, s1, W2, s2 = _bf16_moe(seed, T, H, I, E, bs, bits1, bits2)
+        b1 = synth.activations_bf16(seed + 7, E, 2 * I) if biased else None
+        b2 = synth.activations_bf16(seed + 8, E, H) if biased else None
+        wid = _bf16_f64
+    else:
+        x, logits, W1, s1, W2, s2 = _random_moe_bits(seed, T, H, I, E, bs, bits1, bits2)
+        b1, b2 = _biases(seed + 7, E, I, H) if biased else (None, None)
+        wid = lambda a: a.astype(np.float64)  # noqa: E731
+    o = orc.qmoe(x, logits, W1, s1, W2, s2, k=k, bits1=bits1, bits2=bits2, bs=bs, b1=b1, b2=b2,
+                 dtype=dtype)
+    nb = lambda a: None if a is None else wid(a)  # noqa: E731
+    gs, us, S = qmoe_tolerance_sums(wid(x), logits, W1, wid(s1), W2, wid(s2), k, bs, bits1, bits2,
+                                    nb(b1), nb(b2))
+    ids = o["ids"].astype(np.int64)
+    np.testing.assert_allclose(o["gs"], np.take_along_axis(gs, ids[:, :, None], axis=1), rtol=1e-12)
+    np.testing.assert_allclose(o["us"], np.take_along_axis(us, ids[:, :, None], axis=1), rtol=1e-12)
+    np.testing.assert_allclose(o["S"], S, rtol=1e-12)
+    # FC2 fed an arbitrary h (here the oracle's, with signs flipped on half of
+    # it: the sum takes magnitudes) and the expert ids of the routing
+    h = o["h"] * np.where(np.arange(I) % 2, -1.0, 1.0)
+    _, yS = orc.qmoe_fc2(o["ids"], h, W2, s2, H, I, E, bits2=bits2, bs=bs, b2=b2, dtype=dtype)
+    np.testing.assert_allclose(yS, fc2_tolerance_sum(o["ids"], h, W2, wid(s2), I, bs, bits2, nb(b2)),
+                               rtol=1e-12)
+
+
+def test_silu_derivative_complex_step_matches_finite_differences():
+    """The complex-step derivative used above, against a central difference
+    (error O(step^2)) at points spanning both signs and the minimum of silu."""
+    from tests.np_brute import silu_derivative
+    g = np.array([-8.0, -3.0, -1.2784645, -0.5, 0.0, 0.25, 1.0, 4.0, 12.0])
+    d = 1e-5
+    silu = lambda v: v / (1.0 + np.exp(-v))  # noqa: E731
+    fd = (silu(g + d) - silu(g - d)) / (2 * d)
+    np.testing.assert_allclose(silu_derivative(g), fd, rtol=0, atol=1e-9)
+    assert abs(silu_derivative(np.array([0.0]))[0] - 0.5) < 1e-15
