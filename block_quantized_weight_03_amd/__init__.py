@@ -77,15 +77,15 @@ SIGNATURES = {
     "mnb_gemm": [_PPLAN, _I64, _P, _P, _P, _U64, _P],
     "qmoe_workspace_size": [_PPLAN, _PPLAN, _PQ, _I64, _PU64],
     "qmoe_forward": [_PPLAN, _PPLAN, _PQ, _I64, _P, _P, _P, _P, _U64, _P],
+    "qmoe_forward_biased": [_PPLAN, _PPLAN, _PQ, _I64, _P, _P, _P, _P, _P, _P, _U64, _P],
+    "mnb_quantize_int3_rtn": [_P, _I64, _I64, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P],
     # include/mnb_debug.h
     "mnb_prepare_host": [_PD, _P, _P, _P, _P, _U64, _PPLAN],
     "mnb_debug_unpack_host": [_PPLAN, _I64, _I64, _I64, _P, _P, _P],
     "mnb_debug_unpack": [_PPLAN, _I64, _I64, _I64, _P, _P],
     "mnb_debug_dequant_f16": [_PPLAN, _I64, _I64, _I64, _P, _P],
-    "qmoe_forward_biased": [_PPLAN, _PPLAN, _PQ, _I64, _P, _P, _P, _P, _P, _P, _U64, _P],
     "qmoe_forward_debug": [_PPLAN, _PPLAN, _PQ, _I64, _P, _P, _P, _P, _P, _P, _U64, _P, _P, _P, _P,
                            _P],
-    "mnb_quantize_int3_rtn": [_P, _I64, _I64, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P],
 }
 
 _lib = None

@@ -89,6 +89,7 @@ int32_t check_qmoe(const mnb_plan* fc1, const mnb_plan* fc2, const qmoe_desc* q,
   // one 16-bit type for activations and scales across the layer [P1]
   if (fc1->desc.scale_dtype != fc2->desc.scale_dtype) return MNB_ERR_UNSUPPORTED;
   if (q->top_k < 1 || q->top_k > s1->E) return MNB_ERR_INVALID_ARG;
+  if (!qmoe_supported(*s1, *s2, q->top_k)) return MNB_ERR_UNSUPPORTED;
   return MNB_OK;
 }
 

@@ -12,6 +12,8 @@
 #include "contract.h"
 
 #include <cstring>
+#include <thread>
+#include <vector>
 
 namespace mnb {
 namespace {
@@ -160,6 +162,96 @@ int32_t validate_content(const mnb_desc* d, const Sizes& s, const uint8_t* B,
   return MNB_OK;
 }
 
+namespace {
+
+// Runs f(lo, hi) over [0, items) on up to 16 host threads when the work is
+// large enough to pay for them (bytes: the data the items cover).
+template <typename F>
+void parallel_items(int64_t items, uint64_t bytes, F&& f) {
+  unsigned nt = std::thread::hardware_concurrency();
+  nt = nt < 1 ? 1 : (nt > 16 ? 16 : nt);
+  if (bytes < (uint64_t(8) << 20) || items < 2 * (int64_t)nt) nt = 1;
+  if (nt == 1) {
+    f(int64_t(0), items);
+    return;
+  }
+  std::vector<std::thread> pool;
+  pool.reserve(nt);
+  for (unsigned t = 0; t < nt; ++t) {
+    const int64_t lo = items * t / nt, hi = items * (t + 1) / nt;
+    try {
+      pool.emplace_back([&f, lo, hi] { f(lo, hi); });
+    } catch (...) {
+      f(lo, hi);  // no thread available: this range runs here
+    }
+  }
+  for (auto& th : pool) th.join();
+}
+
+// The 32 three-bit codes of contract bytes src[0..12) (row-local, LSB-first:
+// code i at bits [3i, 3i + 3)) as the three pair-interleaved words of the
+// private layout: word m takes codes 10m .. 10m + 9, the even ones in its low
+// half and the odd ones in its high half (3 bits each); bit t of codes 30 and
+// 31 goes to bits 15 and 31 of word t.
+inline void int3_group_words(const uint8_t* src, uint32_t w[3]) {
+  uint64_t lo = 0;
+  uint32_t hi = 0;
+  std::memcpy(&lo, src, 8);
+  std::memcpy(&hi, src + 8, 4);
+  const unsigned __int128 v = (unsigned __int128)lo | ((unsigned __int128)hi << 64);
+  for (int m = 0; m < 3; ++m) {
+    const uint32_t x = (uint32_t)(v >> (30 * m)) & 0x3FFFFFFFu;
+    uint32_t ev = 0, od = 0;
+    for (int p = 0; p < 5; ++p) {
+      ev |= ((x >> (6 * p)) & 7u) << (3 * p);
+      od |= ((x >> (6 * p + 3)) & 7u) << (3 * p);
+    }
+    w[m] = ev | (od << 16);
+  }
+  const uint32_t c30 = (uint32_t)(v >> 90) & 7u, c31 = (uint32_t)(v >> 93) & 7u;
+  for (int t = 0; t < 3; ++t) w[t] |= (((c30 >> t) & 1u) << 15) | (((c31 >> t) & 1u) << 31);
+}
+
+// The 32 four-bit codes of contract bytes src[0..16) (code i in byte i / 2,
+// low nibble for even i) as four words: word m takes codes 8m .. 8m + 7, the
+// even ones in its low half and the odd ones in its high half.
+inline void int4_group_words(const uint8_t* src, uint32_t w[4]) {
+  for (int m = 0; m < 4; ++m) {
+    uint32_t x;
+    std::memcpy(&x, src + 4 * m, 4);
+    const uint32_t ev = (x & 0xFu) | ((x >> 4) & 0xF0u) | ((x >> 8) & 0xF00u) | ((x >> 12) & 0xF000u);
+    const uint32_t od = ((x >> 4) & 0xFu) | ((x >> 8) & 0xF0u) | ((x >> 12) & 0xF00u) |
+                        ((x >> 16) & 0xF000u);
+    w[m] = ev | (od << 16);
+  }
+}
+
+// Writes the tile-major groups of rows [16 rt, 16 rt + rcnt) of expert e: the
+// tile's chunks of 4 groups in K order, each chunk row by row, which is the
+// order of moe_group_offset, so the tile's bytes are written front to back.
+void pack_moe_tile(const Sizes& s, const uint8_t* B, uint8_t* codes, int64_t e, int64_t rt) {
+  const int64_t GB = 4 * s.bits, ng = s.K / 32;
+  const int64_t rcnt = (s.N - 16 * rt) < 16 ? (s.N - 16 * rt) : 16;
+  const int64_t row0 = e * s.N + 16 * rt;
+  uint8_t* out = codes + moe_group_offset(s.N, s.K, GB, e, 16 * rt, 0);
+  for (int64_t c = 0; c < ng; c += 4) {
+    const int64_t gic = (ng - c) < 4 ? (ng - c) : 4;
+    for (int64_t r = 0; r < rcnt; ++r) {
+      const uint8_t* src = B + (uint64_t)(row0 + r) * (uint64_t)s.row_bytes + (uint64_t)(c * GB);
+      for (int64_t g = 0; g < gic; ++g, out += GB, src += GB) {
+        uint32_t w[4];
+        if (s.bits == 4)
+          int4_group_words(src, w);
+        else
+          int3_group_words(src, w);
+        std::memcpy(out, w, (size_t)GB);
+      }
+    }
+  }
+}
+
+}  // namespace
+
 void prepack(const Sizes& s, const uint8_t* B, const void* scales,
              const uint8_t* zp, uint8_t* dst) {
   std::memset(dst, 0, s.total);
@@ -185,30 +277,13 @@ void prepack(const Sizes& s, const uint8_t* B, const void* scales,
     }
   } else {
     // contract rows are LSB-first bit streams; regroup every 32 codes into
-    // the pair-interleaved words, stored tile-major (same byte count)
-    const int64_t GB = 4 * s.bits;
-    for (int64_t row = 0; row < s.rows; ++row) {
-      const uint8_t* src = B + (uint64_t)row * (uint64_t)s.row_bytes;
-      const int64_t e = row / s.N, n = row % s.N;
-      for (int64_t G = 0; G < s.K / 32; ++G) {
-        uint32_t w[4] = {0, 0, 0, 0};
-        for (int i = 0; i < 32; ++i) {
-          uint32_t q = 0;
-          for (int t = 0; t < s.bits; ++t) {
-            const int64_t bit = s.bits * (32 * G + i) + t;
-            q |= (uint32_t)((src[bit >> 3] >> (bit & 7)) & 1u) << t;
-          }
-          if (s.bits == 4) {
-            w[int4_word(i)] |= q << int4_bit(i);
-          } else if (i < 30) {
-            w[int3_word(i)] |= q << int3_bit(i);
-          } else {
-            for (int t = 0; t < 3; ++t) w[t] |= ((q >> t) & 1u) << (i == 30 ? 15 : 31);
-          }
-        }
-        std::memcpy(codes + moe_group_offset(s.N, s.K, GB, e, n, G), w, (size_t)GB);
-      }
-    }
+    // the pair-interleaved words, stored tile-major (same byte count).  Each
+    // (expert, 16-row tile) writes one contiguous piece of the code section,
+    // so the tiles are spread over host threads.
+    const int64_t tiles = (s.N + 15) / 16, items = s.E * tiles;
+    parallel_items(items, (uint64_t)s.codes, [&](int64_t lo, int64_t hi) {
+      for (int64_t it = lo; it < hi; ++it) pack_moe_tile(s, B, codes, it / tiles, it % tiles);
+    });
   }
   std::memcpy(dst + s.off_scales, scales, s.scales);
   if (s.zeros) {

@@ -47,6 +47,9 @@ struct QmoeDebug {
   uint16_t* h;
   float* slot;
 };
+// what the kernels support beyond the contract checks: at most 1024 experts,
+// top_k <= 16, each expert's codes addressable with 32-bit offsets
+bool qmoe_supported(const Sizes& s1, const Sizes& s2, int top_k);
 uint64_t qmoe_ws_bytes(const Sizes& s1, const Sizes& s2, int top_k, int64_t T);
 // b1 fp16 [E][2I] and b2 fp16 [E][H]: optional projection biases (nullptr: none)
 hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2,

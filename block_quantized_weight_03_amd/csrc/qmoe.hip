@@ -52,6 +52,7 @@ constexpr int kTokTile = 512;   // tokens per pass (bounds the workspace)
 constexpr int kDecodeSlots = 32; // T * k up to which the per-slot decode path runs
 constexpr int kFusedRouteSlots = 8;  // T * k up to which FC1 also routes (one launch less)
 constexpr int kMaxE = 1024;     // experts supported by the grouping kernel
+constexpr int kMaxTopK = 16;    // experts per token supported by the routing kernels
 constexpr int kGroupThreads = 1024;
 
 // ---------------------------------------------------------------------------
@@ -459,8 +460,9 @@ constexpr int kQBK = 128;        // K per chunk
 constexpr int kQPitch = kQBK + 8;
 // 64-row weight tiles per workgroup: with 64-token tiles 2 (their
 // accumulators would otherwise cost occupancy); with 32-token tiles 2 for
-// INT3 and 4 for INT4 (measured at 128 tokens: INT3 95.6 -> 92.9 us and bf16
-// 113.7 -> 107.9 with 2, INT4 98.3 -> 103.4)
+// INT3 and 4 for INT4 (measured at 128 tokens against four tiles: INT3
+// 95.6 -> 92.9 us and bf16 113.7 -> 107.9 with two; INT4 with two 103.4 us,
+// with four 98.3, so INT4 keeps four)
 template <int BM, int BITS>
 constexpr int ntg_of() { return BM == 32 ? (BITS == 3 ? 2 : 4) : 2; }
 int ntg_for(int bm, int bits) {
@@ -1070,6 +1072,12 @@ void by_kind(int64_t bits, bool bf, F&& f) {
   }
 }
 
+// An asynchronous device-to-device copy that keeps the first failure.
+hipError_t copy_d2d(hipError_t prev, void* dst, const void* src, int64_t bytes, hipStream_t st) {
+  const hipError_t e = hipMemcpyAsync(dst, src, (size_t)bytes, hipMemcpyDeviceToDevice, st);
+  return prev != hipSuccess ? prev : e;
+}
+
 void launch_route(const float* logits, int64_t T, int E, int k, int32_t* ids, float* wts,
                   hipStream_t st) {
   const dim3 grid((unsigned)((T + 3) / 4)), block(256);
@@ -1084,6 +1092,13 @@ void launch_route(const float* logits, int64_t T, int E, int k, int32_t* ids, fl
 
 }  // namespace
 
+bool qmoe_supported(const Sizes& s1, const Sizes& s2, int top_k) {
+  // the grouping kernel's per-expert histograms and the routing kernels'
+  // register-held top-k bound E and k; in-expert code offsets are 32-bit
+  return s1.E <= kMaxE && top_k <= kMaxTopK && s1.N * s1.row_bytes < (int64_t(1) << 31) &&
+         s2.N * s2.row_bytes < (int64_t(1) << 31);
+}
+
 uint64_t qmoe_ws_bytes(const Sizes& s1, const Sizes& s2, int top_k, int64_t T) {
   if (T <= 0) return 0;
   return ws_layout(s1, s2, top_k, T).total;
@@ -1095,11 +1110,8 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
                        hipStream_t st, const QmoeDebug* dbg) {
   const int64_t E = s1.E, H = s1.K, I = s2.K;
   const int k = top_k;
-  // limits of these kernels (checked before any launch)
-  if (E > kMaxE || k > 16 || H % 32 || I % 32) return hipErrorNotSupported;
-  // in-expert code offsets are 32-bit
-  if (s1.N * s1.row_bytes >= (int64_t(1) << 31) || s2.N * s2.row_bytes >= (int64_t(1) << 31))
-    return hipErrorNotSupported;
+  // the C ABI rejects these as unsupported before calling; kept as a guard
+  if (!qmoe_supported(s1, s2, k)) return hipErrorNotSupported;
   const Ws L = ws_layout(s1, s2, k, T);
   uint8_t* w = static_cast<uint8_t*>(ws);
   int32_t* ids = reinterpret_cast<int32_t*>(w + L.ids);
@@ -1148,9 +1160,11 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
                          dbg ? dbg->slot : nullptr);
     });
     if (dbg) {
-      if (dbg->ids) (void)hipMemcpyAsync(dbg->ids, ids, S * 4, hipMemcpyDeviceToDevice, st);
-      if (dbg->w) (void)hipMemcpyAsync(dbg->w, wts, S * 4, hipMemcpyDeviceToDevice, st);
-      if (dbg->h) (void)hipMemcpyAsync(dbg->h, hbuf, S * I * 2, hipMemcpyDeviceToDevice, st);
+      hipError_t e = hipSuccess;
+      if (dbg->ids) e = copy_d2d(e, dbg->ids, ids, S * 4, st);
+      if (dbg->w) e = copy_d2d(e, dbg->w, wts, S * 4, st);
+      if (dbg->h) e = copy_d2d(e, dbg->h, hbuf, S * I * 2, st);
+      if (e != hipSuccess) return e;
     }
     return hipGetLastError();
   }
@@ -1198,11 +1212,11 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
     else
       hipLaunchKernelGGL(qmoe_combine<false>, gridc, dim3(256), 0, st, slots, Tt, k, H, out + t0 * H);
     if (dbg) {
-      if (dbg->ids)
-        (void)hipMemcpyAsync(dbg->ids + t0 * k, ids, S * 4, hipMemcpyDeviceToDevice, st);
-      if (dbg->w) (void)hipMemcpyAsync(dbg->w + t0 * k, wts, S * 4, hipMemcpyDeviceToDevice, st);
-      if (dbg->slot)
-        (void)hipMemcpyAsync(dbg->slot + t0 * k * H, slots, S * H * 4, hipMemcpyDeviceToDevice, st);
+      hipError_t e = hipSuccess;
+      if (dbg->ids) e = copy_d2d(e, dbg->ids + t0 * k, ids, S * 4, st);
+      if (dbg->w) e = copy_d2d(e, dbg->w + t0 * k, wts, S * 4, st);
+      if (dbg->slot) e = copy_d2d(e, dbg->slot + t0 * k * H, slots, S * H * 4, st);
+      if (e != hipSuccess) return e;
       if (dbg->h)
         hipLaunchKernelGGL(qmoe_gather_h, dim3((unsigned)((S * I + 255) / 256)), dim3(256), 0, st,
                            hbuf, go.inv, S, I, dbg->h + t0 * k * I);

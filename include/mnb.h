@@ -207,8 +207,14 @@ int32_t mnb_gemm_workspace_size(const mnb_plan* plan, int64_t M, uint64_t* bytes
  *   Y[m,n] = sum_{k<K} A[m,k] * (q[n,k] - z) * s,  m < M, n < N.
  * A_dev fp32 [M, K] row-major (lda = K); Y_dev fp32 [M, N] row-major.  A and
  * the dequantized weights are rounded to fp16 at the matrix-core inputs and
- * accumulated in fp32.  M = 0 is a no-op.  ws_dev as for mnb_gemv (may be
- * NULL when the required size is 0).  Errors as for mnb_gemv. */
+ * accumulated in fp32.  Valid range, as for any fp16-input product: |A| and
+ * |(q - z) * s| must stay below 65520 (larger values round to +-Inf, and the
+ * outputs they reach become Inf or NaN), and weights below 2^-14 in magnitude
+ * become fp16 subnormals with absolute error up to 2^-25 each, so the error
+ * bound 4e-3 * sum|a w| holds only for scales with |(q - z) * s| >= 2^-14 or
+ * zero (the GEMV, in fp32, has neither limit).  M = 0 is a no-op.  ws_dev as
+ * for mnb_gemv (may be NULL when the required size is 0).  Errors as for
+ * mnb_gemv. */
 int32_t mnb_gemm(const mnb_plan* plan, int64_t M, const float* A_dev,
                  float* Y_dev, void* ws_dev, uint64_t ws_bytes, void* stream);
 
@@ -221,7 +227,8 @@ enum { QMOE_QUANT_INT = 0 };
 
 typedef struct qmoe_desc {
   int32_t abi_version;               /* MNB_ABI_VERSION                      */
-  int32_t top_k;                     /* 1..num_experts (8 for the configs)   */
+  int32_t top_k;                     /* 1..num_experts (8 for the configs);
+                                        more than 16: UNSUPPORTED            */
   int32_t normalize_routing_weights; /* must be 1 (renormalized top-k)       */
   int32_t activation;                /* must be QMOE_ACT_SWIGLU              */
   int32_t gate_up;                   /* must be QMOE_GATE_UP_INTERLEAVED     */
@@ -230,7 +237,9 @@ typedef struct qmoe_desc {
   int32_t reserved;                  /* must be 0                            */
 } qmoe_desc;
 
-/* Workspace bytes for qmoe_forward with T tokens. */
+/* Limits of the built kernels (beyond them: UNSUPPORTED, from both calls
+ * below): num_experts <= 1024, top_k <= 16, and each expert's packed codes
+ * below 2 GiB.  Workspace bytes for qmoe_forward with T tokens. */
 int32_t qmoe_workspace_size(const mnb_plan* fc1, const mnb_plan* fc2,
                             const qmoe_desc* q, int64_t T, uint64_t* bytes);
 

@@ -180,6 +180,24 @@ def test_int4_moe_host_prepack_round_trip(orc, E, N, K, bs):
 
 
 @pytest.mark.parametrize("bits", [3, 4])
+def test_moe_host_prepack_threaded_stack(bits):
+    """A stack above 8 MB is repacked tile by tile on several host threads;
+    whole experts (first, middle, last; N = 1000 leaves an 8-row last tile)
+    read back as numpy's LSB-first unpack of the contract rows."""
+    E, N, K, bs = 16, 1000, 2048, 64
+    W = synth.packed_rows(900 + bits, E * N, K, bits)
+    assert W.nbytes > (8 << 20)
+    s = synth.scales_f16(901, (E * N, K // bs))
+    plan, _, _keep = host_prepare(mnb.qmoe_proj_desc(K, N, E, bs, bits=bits), W, s, None)
+    weights = (1 << np.arange(bits)).astype(np.int64)
+    for e in (0, 7, 15):
+        codes, _, _ = mnb.mnb_debug_unpack_host(plan, e, 0, N, want_scales=False)
+        rows = W[e * N:(e + 1) * N]
+        ref = np.unpackbits(rows, axis=1, bitorder="little")[:, :K * bits].reshape(N, K, bits) @ weights
+        assert np.array_equal(codes, ref)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
 @pytest.mark.parametrize("bad", [np.inf, -np.inf, np.nan, -0.5, -65504.0])
 def test_moe_scale_content_rejected(bad, bits):
     E, N, K, bs = 2, 4, 128, 64
@@ -287,6 +305,35 @@ def test_qmoe_descriptor_and_shape_checks():
     pd, _, _k3 = host_prepare(mnb.dense_desc(64, 8), B, s, None)
     assert status_of(mnb.qmoe_workspace_size, pd, p2, q, 4) == UNSUP
     assert lib.mnb_gemv(ctypes.byref(p1), 1, 1, 256, 1 << 20, None) == UNSUP
+
+
+def test_qmoe_kernel_limits_are_unsupported():
+    """More than 1024 experts or top_k above 16 are valid requests that the
+    built kernels do not run: both qmoe_workspace_size and qmoe_forward
+    report UNSUPPORTED before any device call."""
+    H, I, bs = 32, 32, 32
+
+    def plans(E):
+        W1 = synth.int3_rows(11, E * 2 * I, H)
+        s1 = synth.scales_f16(12, (E * 2 * I, H // bs))
+        W2 = synth.int3_rows(13, E * H, I)
+        s2 = synth.scales_f16(14, (E * H, I // bs))
+        p1, _, k1 = host_prepare(mnb.qmoe_proj_desc(H, 2 * I, E, bs), W1, s1, None)
+        p2, _, k2 = host_prepare(mnb.qmoe_proj_desc(I, H, E, bs), W2, s2, None)
+        return p1, p2, (k1, k2)
+
+    lib = mnb.lib()
+    for E, k, want in ((1024, 16, OK), (1025, 8, UNSUP), (32, 17, UNSUP), (32, 16, OK)):
+        p1, p2, keep = plans(E)
+        q = mnb.make_qmoe_desc(k)
+        got = status_of(mnb.qmoe_workspace_size, p1, p2, q, 4) if want else 0
+        if want:
+            assert got == want, (E, k)
+        else:
+            assert mnb.qmoe_workspace_size(p1, p2, q, 4) > 0
+        if want:
+            assert lib.qmoe_forward(ctypes.byref(p1), ctypes.byref(p2), ctypes.byref(q), 4, 16, 16,
+                                    16, 256, 1 << 30, None) == want, (E, k)
 
 
 def test_gemv_multi_argument_checks_before_any_device_call():

@@ -219,3 +219,32 @@ def test_gemm_small_m_exact_integer_and_zero_cases(orc):
     Bz = np.full((N, K // 32, 16), 0x88, np.uint8)
     wz = mnb.PreparedWeight(mnb.dense_desc(K, N), Bz, synth.scales_f32(33, (N, K // 32)), None)
     assert (run_gemm(wz, synth.activations_f32(34, M, K)) == 0).all()
+
+
+@pytest.mark.parametrize("M,K,N", [(2, 256, 64), (20, 256, 96), (160, 256, 160)])
+def test_gemm_fp16_input_range(orc, M, K, N):
+    """The documented range of the fp16-input GEMM, on each kernel regime
+    (single-launch small M, register-staged, LDS-streaming): an |A| past the
+    fp16 range turns its output row non-finite while the other rows stay
+    within the bound; |A| just inside it stays finite and within the bound;
+    scales small enough that every weight is an fp16 subnormal add at most
+    2^-25 |a| per product to the bound."""
+    say(f"gemm fp16 range M={M} K={K} N={N}")
+    bs = 32
+    w, B, s, Z = prepare(K, N, bs, False, seed=M + 7)
+    a = synth.activations_f32(synth.seed_for(M, 77), M, K)
+    a[0, 5] = 1.0e5          # rounds to +Inf in fp16
+    a[1, 9] = -65000.0       # finite in fp16 (max 65504)
+    y = run_gemm(w, a)
+    assert not np.isfinite(y[0]).any()
+    check(orc, y[1:], a[1:], B, s, Z, K, N, bs)
+    # subnormal weights: |(q - 8) s| <= 8 * 2^-20 = 2^-17 < 2^-14
+    s_tiny = np.full_like(s, 2.0 ** -20)
+    wt = mnb.PreparedWeight(mnb.dense_desc(K, N, bs, False), B, s_tiny, None)
+    a2 = synth.activations_f32(synth.seed_for(M, 78), M, K)
+    y2 = run_gemm(wt, a2)
+    _, y64, S = orc.mnb_gemm(a2, B, s_tiny, None, K, N, bs=bs, nthreads=8)
+    extra = 2.0 ** -25 * np.abs(a2.astype(np.float64)).sum(axis=1, keepdims=True) * 1.001
+    err = np.abs(y2.astype(np.float64) - y64)
+    assert np.isfinite(y2).all()
+    assert (err <= TOL * S + extra).all()

@@ -499,3 +499,57 @@ def test_qmoe_bf16_no_tokens_is_a_no_op():
     assert lib.qmoe_forward_biased(ctypes.byref(m.p1.plan), ctypes.byref(m.p2.plan),
                                    ctypes.byref(m.q), 0, None, None, None, None, None, None, 0,
                                    None) == 0
+
+
+# 32-token work items (T k <= 24 E) whose 64-row weight tiles do not fill the
+# last tile group: FC1 (2I = 320 rows) and FC2 (H = 320 rows) have 5 tiles
+# each, so groups of two (INT3) end with one tile and groups of four (INT4)
+# end with one as well.
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("bits1,bits2", [(3, 3), (4, 4), (3, 4), (4, 3)])
+def test_qmoe_partial_last_tile_group(orc, bits1, bits2, dtype):
+    T, H, I, E, k, bs = 17, 320, 160, 16, 4, 32
+    say(f"qmoe partial tile group ({bits1},{bits2}) {dtype} T={T} H={H} I={I} E={E} k={k}")
+    x, logits, m = random_moe(T * 5 + bits1 * 3 + bits2, T, H, I, E, k, bs, bits1, bits2,
+                              dtype=dtype)
+    res = m.run(x, logits, debug=True)
+    o = m.oracle(orc, x, logits)
+    check_end_to_end(res["out"], o, dtype)
+    check_stages(orc, m, res, o)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bs", [32, 64, 128])
+def test_debug_unpack_and_dequant_qmoe_plans_bit_exact(orc, bits, bs, dtype):
+    """The tile-major QMoE layout read back on the device: every code equals
+    the oracle's row-local LSB-first unpack of the contract bytes, and the
+    dequantized weight equals (q - 2^(bits-1)) * s rounded once to the plan's
+    16-bit type (INT3 QMoE page, P0 section: (code - 4) * scale; P1: FP16 or
+    BF16 scales).  N = 37 leaves a 5-row last tile; K = 10 blocks of 32 (or 3
+    of 128) leaves a short last chunk."""
+    E, N = 3, 37
+    K = {32: 320, 64: 384, 128: 384}[bs]
+    say(f"debug unpack/dequant qmoe bits={bits} bs={bs} {dtype} E={E} N={N} K={K}")
+    W = synth.packed_rows(synth.seed_for(bits * 10 + bs, 1), E * N, K, bits)
+    if dtype == "bf16":
+        s = synth.scales_bf16(synth.seed_for(bits * 10 + bs, 2), (E * N, K // bs))
+        sd, s64 = mnb.MNB_DTYPE_BF16, bf16_f64(s)
+        to16 = orc.f64_to_bf16
+    else:
+        s = synth.scales_f16(synth.seed_for(bits * 10 + bs, 2), (E * N, K // bs))
+        sd, s64 = mnb.MNB_DTYPE_F16, s.astype(np.float64)
+        to16 = orc.f64_to_f16
+    w = mnb.PreparedWeight(mnb.qmoe_proj_desc(K, N, E, bs, bits, sd), W, s)
+    for e, row0, nrows in ((0, 0, N), (1, 3, 30), (2, 16, 21)):
+        codes = torch.empty((nrows, K), dtype=torch.uint8, device="cuda")
+        mnb.mnb_debug_unpack(w.plan, e, row0, nrows, codes)
+        deq = torch.empty((nrows, K), dtype=torch.int16, device="cuda")
+        mnb.mnb_debug_dequant_f16(w.plan, e, row0, nrows, deq)
+        torch.cuda.synchronize()
+        rows = range(e * N + row0, e * N + row0 + nrows)
+        want = np.stack([orc.unpack_bits(W[r], K, bits) for r in rows])
+        assert np.array_equal(codes.cpu().numpy(), want)
+        q = want.astype(np.float64) - (1 << (bits - 1))
+        ref = to16(q * np.repeat(s64[e * N + row0:e * N + row0 + nrows], bs, axis=1))
+        assert np.array_equal(deq.cpu().numpy().view(np.uint16), ref)
