@@ -97,6 +97,14 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        # torch ships its own HIP runtime under the same soname; loading torch
+        # first makes libmnb.so bind to that one.  Loaded the other way round,
+        # the process holds two HIP runtimes and the library cannot use device
+        # pointers or streams that torch created (every device call fails).
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         for name, args in SIGNATURES.items():
             fn = getattr(L, name)

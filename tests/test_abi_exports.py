@@ -43,3 +43,16 @@ def test_status_strings():
     for code, text in mnb.STATUS.items():
         assert mnb.mnb_status_string(code) == text
     assert mnb.mnb_status_string(-99) == "MNB_ERR_UNKNOWN"
+
+
+def test_library_binds_to_torchs_hip_runtime():
+    """Loading the library before torch must not leave two HIP runtimes in
+    the process (torch bundles its own under the same soname; pointers and
+    streams of one are unknown to the other)."""
+    import subprocess
+    import sys
+    code = ("import block_quantized_weight_03_amd as m; m.lib(); import torch; "
+            "print(len({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         check=True, timeout=300)
+    assert out.stdout.strip().splitlines()[-1] == "1"
