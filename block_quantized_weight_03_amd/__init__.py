@@ -23,6 +23,7 @@ MNB_ROWS_BLOCKED, MNB_ROWS_ROW_LOCAL = 0, 1
 QMOE_ACT_SWIGLU = 1
 QMOE_GATE_UP_INTERLEAVED = 1
 QMOE_QUANT_INT = 0
+MNB_NOALLOC_SCRATCH_BYTES = 64 << 20  # the static workspace of qmoe_forward_noalloc
 
 STATUS = {0: "MNB_OK", -1: "MNB_ERR_INVALID_ARG", -2: "MNB_ERR_UNSUPPORTED",
           -3: "MNB_ERR_SIZE_OVERFLOW", -4: "MNB_ERR_CONTENT", -5: "MNB_ERR_WORKSPACE_TOO_SMALL",
@@ -78,6 +79,7 @@ SIGNATURES = {
     "qmoe_workspace_size": [_PPLAN, _PPLAN, _PQ, _I64, _PU64],
     "qmoe_forward": [_PPLAN, _PPLAN, _PQ, _I64, _P, _P, _P, _P, _U64, _P],
     "qmoe_forward_biased": [_PPLAN, _PPLAN, _PQ, _I64, _P, _P, _P, _P, _P, _P, _U64, _P],
+    "qmoe_forward_noalloc": [_PPLAN, _PPLAN, _PQ, _I64, _P, _P, _P, _P],
     "mnb_quantize_int3_rtn": [_P, _I64, _I64, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P],
     # include/mnb_debug.h
     "mnb_prepare_host": [_PD, _P, _P, _P, _P, _U64, _PPLAN],
@@ -245,6 +247,13 @@ def qmoe_forward(fc1: mnb_plan, fc2: mnb_plan, q: qmoe_desc, T: int, x_dev, logi
     _check(lib().qmoe_forward(ctypes.byref(fc1), ctypes.byref(fc2), ctypes.byref(q), T, _ptr(x_dev),
                               _ptr(logits_dev), _ptr(out_dev), _ptr(ws_dev), ws_bytes,
                               _stream(stream)), "qmoe_forward")
+
+
+def qmoe_forward_noalloc(fc1: mnb_plan, fc2: mnb_plan, q: qmoe_desc, T: int, x_dev, logits_dev,
+                         out_dev, stream=None):
+    _check(lib().qmoe_forward_noalloc(ctypes.byref(fc1), ctypes.byref(fc2), ctypes.byref(q), T,
+                                      _ptr(x_dev), _ptr(logits_dev), _ptr(out_dev),
+                                      _stream(stream)), "qmoe_forward_noalloc")
 
 
 def mnb_quantize_int3_rtn(W_dev, rows: int, K: int, block_size: int, B_dev, scales_dev,

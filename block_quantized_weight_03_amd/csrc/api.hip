@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -18,6 +19,11 @@
 #include "kernels.h"
 
 using namespace mnb;
+
+// Workspace array of qmoe_forward_noalloc (see scratch_for_current_device).
+constexpr uint64_t kScratchBytes = uint64_t(64) << 20;
+static_assert(kScratchBytes == MNB_NOALLOC_SCRATCH_BYTES, "header and library must agree");
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -90,6 +96,29 @@ int32_t check_qmoe(const mnb_plan* fc1, const mnb_plan* fc2, const qmoe_desc* q,
   if (fc1->desc.scale_dtype != fc2->desc.scale_dtype) return MNB_ERR_UNSUPPORTED;
   if (q->top_k < 1 || q->top_k > s1->E) return MNB_ERR_INVALID_ARG;
   if (!qmoe_supported(*s1, *s2, q->top_k)) return MNB_ERR_UNSUPPORTED;
+  return MNB_OK;
+}
+
+// Workspace of qmoe_forward_noalloc: one array per GPU, held from the first
+// use on that GPU until the process ends.  Its address is taken once per
+// device with hipGetSymbolAddress (host code never passes the array's name
+// to a kernel: on the host it is only a stand-in, not the device address).
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+// The device address of the current device's scratch array.
+int32_t scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MNB_ERR_DEVICE;
+  if (dev < 0 || dev >= kScratchDevices) return MNB_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MNB_ERR_DEVICE;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return MNB_OK;
 }
 
@@ -287,6 +316,26 @@ int32_t qmoe_forward(const mnb_plan* fc1, const mnb_plan* fc2, const qmoe_desc* 
   MNB_GUARD({
     return qmoe_common(fc1, fc2, q, T, x_dev, logits_dev, nullptr, nullptr, out_dev, ws_dev,
                        ws_bytes, stream, nullptr);
+  })
+}
+
+int32_t qmoe_forward_noalloc(const mnb_plan* fc1, const mnb_plan* fc2, const qmoe_desc* q,
+                             int64_t T, const uint16_t* x_dev, const float* logits_dev,
+                             uint16_t* out_dev, void* stream) {
+  MNB_GUARD({
+    Sizes s1, s2;
+    int32_t rc = check_qmoe(fc1, fc2, q, T, &s1, &s2);
+    if (rc != MNB_OK) return rc;
+    if (T == 0) return MNB_OK;
+    // the size limit is checked on the host before any HIP call
+    if (qmoe_ws_bytes(s1, s2, q->top_k, T) > kScratchBytes) return MNB_ERR_WORKSPACE_TOO_SMALL;
+    void* ws = nullptr;
+    if ((rc = check_device(fc1)) != MNB_OK) return rc;
+    if ((rc = scratch_for_current_device(&ws)) != MNB_OK) return rc;
+    // nothing in the workspace needs to start at zero: every kernel writes
+    // what a later one reads before it is read
+    return qmoe_common(fc1, fc2, q, T, x_dev, logits_dev, nullptr, nullptr, out_dev, ws,
+                       kScratchBytes, stream, nullptr);
   })
 }
 

@@ -48,7 +48,8 @@
  *    before any launch; a failed check launches nothing and writes nothing.
  *  - Device pointers ("_dev") are caller-owned device memory on the device
  *    that was current when the plan was prepared.  The library never
- *    allocates device memory and keeps no state between calls.
+ *    allocates device memory and keeps no state between calls, except the
+ *    static workspace array of qmoe_forward_noalloc (one per GPU).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Every compute call only enqueues work on `stream` and returns; only
  *    mnb_prepare waits (for its own upload).
@@ -284,6 +285,24 @@ int32_t qmoe_forward_biased(const mnb_plan* fc1, const mnb_plan* fc2,
                             const uint16_t* fc1_bias_dev,
                             const uint16_t* fc2_bias_dev, uint16_t* out_dev,
                             void* ws_dev, uint64_t ws_bytes, void* stream);
+
+/* qmoe_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is a static device array of
+ * MNB_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, created when the
+ * library's code is loaded on that GPU and held until the process ends; its
+ * address is looked up on the first call on each device.  No call allocates.
+ * Every call on a GPU shares that GPU's array and leaves its contents behind:
+ * calls that overlap on one GPU (other streams, other host threads) race and
+ * must be serialized by the caller.  Requests whose qmoe_workspace_size
+ * exceeds MNB_NOALLOC_SCRATCH_BYTES return WORKSPACE_TOO_SMALL before any
+ * device work (the workspace grows with min(T, 512) * top_k * (4H + 2I) bytes
+ * plus small tables; the 128-expert, H = 2048, I = 768, top-8 layer needs
+ * about 40 MB).  Arguments, results and all other errors as for qmoe_forward. */
+#define MNB_NOALLOC_SCRATCH_BYTES (64ull << 20)
+int32_t qmoe_forward_noalloc(const mnb_plan* fc1, const mnb_plan* fc2,
+                             const qmoe_desc* q, int64_t T, const uint16_t* x_dev,
+                             const float* logits_dev, uint16_t* out_dev, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Producer-side INT3 round-to-nearest quantizer [P0][OLIVE]: fp32 weights to
