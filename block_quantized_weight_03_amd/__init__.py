@@ -88,6 +88,7 @@ SIGNATURES = {
     "mnb_debug_dequant_f16": [_PPLAN, _I64, _I64, _I64, _P, _P],
     "qmoe_forward_debug": [_PPLAN, _PPLAN, _PQ, _I64, _P, _P, _P, _P, _P, _P, _U64, _P, _P, _P, _P,
                            _P],
+    "mnb_debug_stream_read": [_P, _P, _I32, _P, _P],
 }
 
 _lib = None
@@ -310,6 +311,15 @@ def mnb_debug_unpack_host(plan: mnb_plan, expert: int, row0: int, nrows: int, wa
     _check(lib().mnb_debug_unpack_host(ctypes.byref(plan), expert, row0, nrows, _ptr(codes),
                                        _ptr(zeros), _ptr(scales)), "mnb_debug_unpack_host")
     return codes, zeros, scales
+
+
+def mnb_debug_stream_read(buffers, sink_dev, stream=None):
+    """buffers: list of (device pointer or tensor, bytes) pairs, 1 to 4."""
+    n = len(buffers)
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[_ptr(b) for b, _ in buffers])
+    sizes = (ctypes.c_uint64 * max(n, 1))(*[int(nb) for _, nb in buffers])
+    _check(lib().mnb_debug_stream_read(ptrs, sizes, n, _ptr(sink_dev), _stream(stream)),
+           "mnb_debug_stream_read")
 
 
 def mnb_debug_unpack(plan: mnb_plan, expert: int, row0: int, nrows: int, codes_dev, stream=None):

@@ -387,6 +387,22 @@ int32_t mnb_quantize_int3_rtn(const float* W_dev, int64_t rows, int64_t K, int32
   })
 }
 
+int32_t mnb_debug_stream_read(const void* const* src_dev, const uint64_t* bytes, int32_t count,
+                              uint32_t* sink_dev, void* stream) {
+  MNB_GUARD({
+    if (!src_dev || !bytes || !sink_dev || count < 1 || count > kMaxSegs) return MNB_ERR_INVALID_ARG;
+    for (int i = 0; i < count; ++i) {
+      if (!src_dev[i] || (reinterpret_cast<uintptr_t>(src_dev[i]) & 15) || (bytes[i] & 15))
+        return MNB_ERR_INVALID_ARG;
+      if (bytes[i] / 16 / 1024 >= (uint64_t)UINT32_MAX / kMaxSegs) return MNB_ERR_UNSUPPORTED;
+    }
+    if (launch_stream_read(src_dev, bytes, count, sink_dev, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+      return MNB_ERR_DEVICE;
+    return MNB_OK;
+  })
+}
+
 int32_t mnb_debug_unpack_host(const mnb_plan* plan, int64_t expert, int64_t row0, int64_t nrows,
                               uint8_t* codes, uint8_t* zeros, void* scales) {
   MNB_GUARD({

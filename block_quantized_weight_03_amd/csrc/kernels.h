@@ -71,6 +71,12 @@ hipError_t launch_debug_dequant_f16(const Sizes& s, const mnb_plan& p, int64_t e
                                     int64_t row0, int64_t nrows, uint16_t* out,
                                     hipStream_t st);
 
+// plain 16-byte nontemporal read of count (<= kMaxSegs) buffers in one launch
+// (16-byte aligned, bytes multiples of 16); sink is written only for an
+// improbable value, so that the loads are not removed
+hipError_t launch_stream_read(const void* const* src, const uint64_t* bytes, int count,
+                              uint32_t* sink, hipStream_t st);
+
 inline uint64_t align256(uint64_t v) { return (v + 255) / 256 * 256; }
 
 }  // namespace mnb

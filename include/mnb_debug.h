@@ -67,6 +67,19 @@ int32_t qmoe_forward_debug(const mnb_plan* fc1, const mnb_plan* fc2,
                            int32_t* ids_dev, float* w_dev,
                            uint16_t* h_dev, float* slot_dev);
 
+/* Measurement aid: a plain streaming read of count (1..4) device buffers in
+ * one launch, the ceiling against which the GEMV's achieved bandwidth is
+ * reported.  Each thread issues four 16-byte nontemporal loads (16 KiB per
+ * workgroup of 256), so bytes[i] / 16 KiB workgroups per buffer; the loaded
+ * words are folded together and sink_dev (one uint32) is written only when the
+ * fold equals a fixed improbable value, which keeps the loads from being
+ * removed.  src_dev: host array of device pointers, each 16-byte aligned;
+ * bytes: host array, multiples of 16 (0 allowed).  Asynchronous on `stream`.
+ * Errors: INVALID_ARG (count, NULL or misaligned pointers, sizes), UNSUPPORTED
+ * (grid too large), DEVICE. */
+int32_t mnb_debug_stream_read(const void* const* src_dev, const uint64_t* bytes,
+                              int32_t count, uint32_t* sink_dev, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -463,3 +463,16 @@ def test_biased_qmoe_pointer_checks_before_any_device_call():
     assert f(*args(None, None, None, 8192)) == INVALID       # no activations
     assert f(ctypes.byref(p1), ctypes.byref(p2), ctypes.byref(q), 0, None, None, None, None, None,
              None, 0, None) == OK                            # T = 0: no-op
+
+
+def test_stream_read_argument_checks_before_any_device_call():
+    lib = mnb.lib()
+    P = ctypes.c_void_p * 2
+    U = ctypes.c_uint64 * 2
+    sink = ctypes.c_void_p(256)
+    assert lib.mnb_debug_stream_read(P(256, 512), U(16, 32), 0, sink, None) == INVALID
+    assert lib.mnb_debug_stream_read(P(256, 512), U(16, 32), 5, sink, None) == INVALID
+    assert lib.mnb_debug_stream_read(P(256, 520), U(16, 32), 2, sink, None) == INVALID  # misaligned
+    assert lib.mnb_debug_stream_read(P(256, 512), U(16, 33), 2, sink, None) == INVALID  # size
+    assert lib.mnb_debug_stream_read(P(256, None), U(16, 32), 2, sink, None) == INVALID
+    assert lib.mnb_debug_stream_read(P(256, 512), U(16, 32), 2, None, None) == INVALID

@@ -256,3 +256,22 @@ def test_debug_unpack_and_dequant_bit_exact(orc):
         if Z is None:  # implicit zero point 8: the chain is fp32((q - 8) * s)
             W = orc.mnb_dequant(B, s, Z, K, N, bs=bs)
             assert np.array_equal(ref, orc.f64_to_f16(W.astype(np.float32).astype(np.float64)))
+
+
+def test_stream_read_ceiling_kernel_reads_its_buffers():
+    """The measurement read kernel loads every segment: a buffer whose fold
+    equals the kernel's sentinel makes it write the sink, others leave it."""
+    say("stream read kernel")
+    sent = np.zeros(16, np.uint32)                 # 4 chunks of 16 bytes
+    sent[0], sent[1] = 0x7F4A7C15, 0x7F4A7C15 ^ 0x9E3779B9
+    hit = torch.from_numpy(sent.view(np.int32)).cuda()
+    big = torch.zeros(1 << 20, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    mnb.mnb_debug_stream_read([(big, big.numel() * 4)], sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
+    mnb.mnb_debug_stream_read([(big, big.numel() * 4), (hit, 64), (big, 16 * 1000)], sink)
+    torch.cuda.synchronize()
+    assert int(sink.cpu().numpy().view(np.uint32)[0]) == 0x9E3779B9
+    with pytest.raises(mnb.MnbError):
+        mnb.mnb_debug_stream_read([(big, 20)], sink)
