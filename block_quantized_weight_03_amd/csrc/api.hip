@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -57,15 +58,13 @@ int32_t prepare_common(const mnb_desc* desc, const uint8_t* B, const void* scale
   if (rc != MNB_OK) return rc;
   int dev = -1;
   if (device) {
-    std::vector<uint8_t> host;
-    try {
-      host.resize(s.total);
-    } catch (const std::bad_alloc&) {
-      return MNB_ERR_HOST_MEMORY;
-    }
-    prepack(s, B, scales, zp, host.data());
+    // staging for the repacked bytes (left uninitialised: prepack writes
+    // every byte)
+    std::unique_ptr<uint8_t[]> host(new (std::nothrow) uint8_t[s.total]);
+    if (!host) return MNB_ERR_HOST_MEMORY;
+    prepack(s, B, scales, zp, host.get());
     if (hipGetDevice(&dev) != hipSuccess) return MNB_ERR_DEVICE;
-    if (hipMemcpyAsync(dst, host.data(), s.total, hipMemcpyHostToDevice, st) != hipSuccess)
+    if (hipMemcpyAsync(dst, host.get(), s.total, hipMemcpyHostToDevice, st) != hipSuccess)
       return MNB_ERR_DEVICE;
     if (hipStreamSynchronize(st) != hipSuccess) return MNB_ERR_DEVICE;
   } else {

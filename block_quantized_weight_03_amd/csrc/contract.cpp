@@ -254,27 +254,33 @@ void pack_moe_tile(const Sizes& s, const uint8_t* B, uint8_t* codes, int64_t e, 
 
 void prepack(const Sizes& s, const uint8_t* B, const void* scales,
              const uint8_t* zp, uint8_t* dst) {
-  std::memset(dst, 0, s.total);
+  // every byte of the sections is written below; only the alignment gaps
+  // between and after them are cleared here
+  std::memset(dst + s.codes, 0, s.off_scales - s.codes);
+  std::memset(dst + s.off_scales + s.scales, 0, s.off_zeros - s.off_scales - s.scales);
+  std::memset(dst + s.off_zeros + s.zeros, 0, s.total - s.off_zeros - s.zeros);
   uint8_t* codes = dst;
   if (s.kind == kDenseInt4) {
     // Store each code as (q - 8) in 4-bit two's complement: nibble XOR 8.
     // Pad positions k >= K of the last block are written as 0.
     const int64_t half = s.bs / 2;
     const int64_t valid_last = s.K - (s.nb - 1) * s.bs;
-    for (int64_t n = 0; n < s.N; ++n) {
-      const uint8_t* src = B + (uint64_t)n * (uint64_t)s.row_bytes;
-      uint8_t* out = codes + (uint64_t)n * (uint64_t)s.row_bytes;
-      for (int64_t i = 0; i < s.row_bytes; ++i) out[i] = (uint8_t)(src[i] ^ 0x88u);
-      if (valid_last < s.bs) {
-        uint8_t* last = out + (s.nb - 1) * half;
-        for (int64_t j = valid_last; j < s.bs; ++j) {
-          if (j & 1)
-            last[j >> 1] &= 0x0Fu;
-          else
-            last[j >> 1] &= 0xF0u;
+    parallel_items(s.N, s.codes, [&](int64_t lo, int64_t hi) {
+      for (int64_t n = lo; n < hi; ++n) {
+        const uint8_t* src = B + (uint64_t)n * (uint64_t)s.row_bytes;
+        uint8_t* out = codes + (uint64_t)n * (uint64_t)s.row_bytes;
+        for (int64_t i = 0; i < s.row_bytes; ++i) out[i] = (uint8_t)(src[i] ^ 0x88u);
+        if (valid_last < s.bs) {
+          uint8_t* last = out + (s.nb - 1) * half;
+          for (int64_t j = valid_last; j < s.bs; ++j) {
+            if (j & 1)
+              last[j >> 1] &= 0x0Fu;
+            else
+              last[j >> 1] &= 0xF0u;
+          }
         }
       }
-    }
+    });
   } else {
     // contract rows are LSB-first bit streams; regroup every 32 codes into
     // the pair-interleaved words, stored tile-major (same byte count).  Each
@@ -285,26 +291,31 @@ void prepack(const Sizes& s, const uint8_t* B, const void* scales,
       for (int64_t it = lo; it < hi; ++it) pack_moe_tile(s, B, codes, it / tiles, it % tiles);
     });
   }
-  std::memcpy(dst + s.off_scales, scales, s.scales);
+  parallel_items(64, s.scales, [&](int64_t lo, int64_t hi) {
+    const uint64_t a = s.scales * (uint64_t)lo / 64, b = s.scales * (uint64_t)hi / 64;
+    std::memcpy(dst + s.off_scales + a, static_cast<const uint8_t*>(scales) + a, b - a);
+  });
   if (s.zeros) {
     // word (g, b): nibble r = zero point of row 8g + r, block b; rows past N
     // hold 8 (never read)
-    const uint64_t groups = (uint64_t)s.N / 8 + (s.N % 8 ? 1 : 0);
-    for (uint64_t g = 0; g < groups; ++g) {
-      for (int64_t b = 0; b < s.nb; ++b) {
-        uint32_t w = 0;
-        for (int r = 0; r < 8; ++r) {
-          const uint64_t n = 8 * g + (uint64_t)r;
-          uint32_t z = 8;
-          if (n < (uint64_t)s.N) {
-            const uint8_t byte = zp[n * s.zrow + (uint64_t)(b / 2)];
-            z = (b & 1) ? (byte >> 4) : (byte & 15u);
+    const int64_t groups = s.N / 8 + (s.N % 8 ? 1 : 0);
+    parallel_items(groups, s.zeros, [&](int64_t lo, int64_t hi) {
+      for (int64_t g = lo; g < hi; ++g) {
+        for (int64_t b = 0; b < s.nb; ++b) {
+          uint32_t w = 0;
+          for (int r = 0; r < 8; ++r) {
+            const uint64_t n = 8 * (uint64_t)g + (uint64_t)r;
+            uint32_t z = 8;
+            if (n < (uint64_t)s.N) {
+              const uint8_t byte = zp[n * s.zrow + (uint64_t)(b / 2)];
+              z = (b & 1) ? (byte >> 4) : (byte & 15u);
+            }
+            w |= z << (4 * r);
           }
-          w |= z << (4 * r);
+          std::memcpy(dst + s.off_zeros + ((uint64_t)g * (uint64_t)s.nb + (uint64_t)b) * 4, &w, 4);
         }
-        std::memcpy(dst + s.off_zeros + (g * (uint64_t)s.nb + (uint64_t)b) * 4, &w, 4);
       }
-    }
+    });
   }
 }
 
