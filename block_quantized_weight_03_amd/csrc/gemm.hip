@@ -431,6 +431,7 @@ bool fast_ok(const Sizes& s, int64_t M, const void* A) {
 struct Plan {
   bool lds;         // the LDS-streaming kernel (gemm_lds.hip), bm x bm tiles
   int bm;
+  int64_t n_split;  // > 0: 256 x 256 tiles below this column, 256 x 128 above
   int cfg;          // else: index into the configuration table below
   int64_t tiles_n, tiles;
   int32_t splits;
@@ -468,6 +469,21 @@ void split_k(Plan& p, const Sizes& s, int64_t M, int64_t step) {
 constexpr int64_t kLdsMinM = 128;
 constexpr int64_t kLds128MaxTiles = 384;
 
+// Columns covered by 256 x 256 tiles when the rest take 256 x 128 ones, so
+// that the wide tiles number at most one per CU and the narrow ones fill the
+// second round (0: one tile shape).  Used when 256 x 256 tiles alone would
+// need between one and two rounds with an idle remainder: at M = 4096, K =
+// 2048, N = 6144 (384 such tiles) 256 wide tiles plus 256 narrow ones took
+// 127 against 135 us.
+int64_t mixed_split(const Sizes& s, int64_t M) {
+  const int64_t rows = (M + 255) / 256, cols = (s.N + 255) / 256;
+  const int64_t tiles = rows * cols;
+  if (tiles <= kTargetWork || tiles >= 2 * kTargetWork) return 0;
+  const int64_t wide = kTargetWork / rows;  // 256-column blocks in the first round
+  if (wide < 1 || wide >= cols) return 0;
+  return wide * 256;
+}
+
 Plan choose(const Sizes& s, int64_t M, bool fast) {
   const int64_t N = s.N, K = s.K;
   (void)K;
@@ -478,6 +494,12 @@ Plan choose(const Sizes& s, int64_t M, bool fast) {
     p.cfg = -1;
     p.tiles_n = (N + p.bm - 1) / p.bm;
     p.tiles = ((M + p.bm - 1) / p.bm) * p.tiles_n;
+    p.n_split = p.bm == 256 ? mixed_split(s, M) : 0;
+    if (p.n_split > 0) {  // no split of K: the tiles already fill the chip
+      p.splits = 1;
+      p.kc = s.K;
+      return p;
+    }
     split_k(p, s, M, 64);
     return p;
   }
@@ -502,6 +524,7 @@ Plan choose(const Sizes& s, int64_t M, bool fast) {
   Plan p;
   p.lds = false;
   p.bm = 0;
+  p.n_split = 0;
   p.cfg = c;
   p.tiles_n = (N + kCfgs[c].bn - 1) / kCfgs[c].bn;
   p.tiles = tiles_of(c);
@@ -573,7 +596,7 @@ hipError_t launch_gemm(const Sizes& s, const mnb_plan& p, int64_t M, const float
                       ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
                                                  gemm_lds_a16_bytes(s, M))
                       : nullptr;
-    e = launch_gemm_lds(s, p, M, A, ws, Y, part, pl.splits, pl.kc, pl.bm, st);
+    e = launch_gemm_lds(s, p, M, A, ws, Y, part, pl.splits, pl.kc, pl.bm, pl.n_split, st);
     if (e != hipSuccess || pl.splits == 1) return e;
     const int64_t MN = M * s.N;
     hipLaunchKernelGGL(gemm_splitk_reduce, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, st,

@@ -47,14 +47,15 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 constexpr int kBK = 64;
 constexpr int kXcds = 8;
 
-// Tile BM x BM: wave w computes all BM rows of columns [w BM/4, (w+1) BM/4)
-// as TM x TN tiles of 32 x 32.  BM = 256 (TM 8, TN 2) for large M, 128 (TM 4,
-// TN 1) below.
-template <int BM>
+// Tile BM x BN (BN = 128 TN): wave w computes all BM rows of columns
+// [32 TN w, 32 TN (w + 1)) as TM x TN tiles of 32 x 32.  The shapes used are
+// 256 x 256, 256 x 128 and 128 x 128 (128 x 256, 128 x 384 and 256 x 128 on
+// their own measured no faster than these at the prefill shapes).
+template <int BM, int TN_>
 struct Tile {
-  static constexpr int TM = BM / 32, TN = BM / 128, BN = BM;
+  static constexpr int TM = BM / 32, TN = TN_, BN = 128 * TN_;
   static constexpr int ABytes = BM * kBK * 2;     // fp16 A per stage (32 / 16 KiB)
-  static constexpr int WBytes = BN * kBK / 2;     // packed codes per stage (8 / 4 KiB)
+  static constexpr int WBytes = BN * kBK / 2;     // packed codes per stage (4 KiB per TN)
   static constexpr int SBytes = 4 * TN * 64 * 4;  // one scale per lane and weight tile
   static constexpr int ACopies = BM / 32;         // 1 KiB A copies per wave and stage
   // LDS stages in flight (for 128-row tiles, 4 and 6 stages measured no
@@ -110,66 +111,69 @@ __global__ void __launch_bounds__(256) round_a_f16(const float* __restrict__ A,
       u32x4{cvt_pk_rn(a.x, a.y), cvt_pk_rn(a.z, a.w), cvt_pk_rn(b.x, b.y), cvt_pk_rn(b.z, b.w)};
 }
 
-template <bool HAS_ZP, int BM>
-__global__ void __launch_bounds__(256) gemm_int4_lds(
-    const _Float16* __restrict__ A16, const uint8_t* __restrict__ codes,
-    const float* __restrict__ scales, const uint32_t* __restrict__ zeros, float* __restrict__ Y,
-    float* __restrict__ part, int64_t M, int64_t N, int64_t K, int64_t row_bytes, int64_t nb,
-    int32_t bs_shift, int64_t tiles_n, int64_t work, int32_t splits, int64_t kc) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  using T_ = Tile<BM>;
-  constexpr int kBM = BM, kBN = T_::BN, kTM = T_::TM, kTN = T_::TN;
+// One BM x (128 TN) output tile over the K range [kbeg, kbeg + 64 steps),
+// written to out (Y or a split's partial buffer, row stride N), by 4 waves:
+// wave w owns the 32 TN columns [32 TN w, 32 TN (w + 1)) of the tile over all
+// BM rows.  (Eight waves, two per SIMD, each owning half the rows, measured
+// slower: 144 against 135 us at M = 4096, K = 2048, N = 6144, every weight
+// then being dequantized by two waves.)
+template <bool HAS_ZP, int BM, int TN, int WM = 1>
+__device__ __forceinline__ void lds_tile(
+    uint8_t* smem, const _Float16* __restrict__ A16, const uint8_t* __restrict__ codes,
+    const float* __restrict__ scales, const uint32_t* __restrict__ zeros, float* __restrict__ out,
+    int64_t M, int64_t N, int64_t K, int64_t row_bytes, int64_t nb, int32_t bs_shift, int64_t m0,
+    int64_t n0, int64_t kbeg, int steps) {
+  using T_ = Tile<BM, TN>;
+  constexpr int kBM = BM, kBN = T_::BN, kTN = T_::TN;
+  constexpr int kTM = T_::TM / WM;          // 32-row tiles per wave
   constexpr int kABytes = T_::ABytes, kWBytes = T_::WBytes, kSBytes = T_::SBytes;
-  constexpr int kAC = T_::ACopies;
+  constexpr int kAC = T_::ACopies / WM;     // 1 KiB A copies per wave and stage
+  constexpr int kWC = kTN / WM;             // code (and scale) copies per wave and stage
+  static_assert(kTN % WM == 0 && T_::ACopies % WM == 0, "copy split");
   // per stage: [A][codes][scales][zero-point words]
   constexpr int kStageBytes = T_::template stage_bytes<HAS_ZP>();
-  constexpr int kGroup = kAC + kTN * (HAS_ZP ? 3 : 2);  // vector-memory ops per stage and wave
-
-  // XCD x (= blockIdx % 8) takes work items [x * per, (x + 1) * per)
-  const int64_t per = (work + kXcds - 1) / kXcds;
-  const int64_t L = (int64_t)(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-  if (L >= work) return;  // whole workgroup
-  const int split = (int)(L % splits);
-  const int64_t tile = L / splits;
-  const int64_t m0 = (tile / tiles_n) * kBM;
-  const int64_t n0 = (tile % tiles_n) * kBN;
-  const int64_t kbeg = split * kc;
-  const int64_t kend = kbeg + kc < K ? kbeg + kc : K;
-  const int steps = (int)((kend - kbeg) / kBK);
+  constexpr int kGroup = kAC + kWC * (HAS_ZP ? 3 : 2);  // vector-memory ops per stage and wave
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave & 3, wm = wave >> 2;
 
-  // A copies: this wave fills rows [BM/4 * wave, BM/4 * (wave + 1)) of a
-  // stage, 8 rows (1 KiB) per instruction; lane l writes physical chunk l & 7
-  // of row 8u + (l >> 3), which holds logical chunk (l & 7) ^ ((row >> 1) & 7).
+  // A copies: wave w fills rows [w BM/(4 WM), (w + 1) BM/(4 WM)) of a stage,
+  // 8 rows (1 KiB) per instruction; lane l writes physical chunk l & 7 of row
+  // 8u + (l >> 3), which holds logical chunk (l & 7) ^ ((row >> 1) & 7).
   // Rows past M are clamped (their results are never stored).
   uint32_t a_off[kAC];  // element offsets into A16; the launcher checks M * K < 2^31
 #pragma unroll
   for (int u = 0; u < kAC; ++u) {
     const int r = u * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
-    int64_t m = m0 + wave * (kBM / 4) + r;
+    int64_t m = m0 + wave * (kBM / (4 * WM)) + r;
     m = m < M ? m : M - 1;
     a_off[u] = (uint32_t)(m * K + 8 * c);
   }
-  // Codes, scales and zero points of this wave's own BM/4 weight rows (rows past
-  // N clamped).  Codes: two instructions of 32 rows x 32 bytes, stored
-  // chunk-major (lane l: row l & 31, 16-byte half l >> 5), the order of the
-  // operand reads; scale and zero-point word: one dword per lane, for the
+  // Codes, scales and zero points of column group wn (rows past N clamped):
+  // this wave copies chunks j = wm kWC .. wm kWC + kWC - 1 of the group's kTN
+  // chunks of 32 weight rows.  Codes: 32 rows x 32 bytes per instruction,
+  // stored chunk-major (lane l: row l & 31, 16-byte half l >> 5), the order of
+  // the operand reads; scale and zero-point word: one dword per lane, for the
   // lane's row and sub-block.
   const int wl_n = lane & 31, wl_g = lane >> 5;
-  const uint8_t* w_src[kTN];
-  const float* s_row[kTN];
-  const uint32_t* z_row[kTN];
-  int z_sh[kTN];
+  const uint8_t* w_src[kWC];
+  const float* s_row[kWC];
+  const uint32_t* z_row[kWC];
+#pragma unroll
+  for (int jj = 0; jj < kWC; ++jj) {
+    int64_t n = n0 + wn * (kBN / 4) + (wm * kWC + jj) * 32 + wl_n;
+    n = n < N ? n : N - 1;
+    w_src[jj] = codes + n * row_bytes + 16 * wl_g;
+    s_row[jj] = scales + n * nb;
+    z_row[jj] = HAS_ZP ? zeros + (n >> 3) * nb : nullptr;
+  }
+  int z_sh[kTN];  // nibble of the zero-point word of this lane's row in chunk j
 #pragma unroll
   for (int j = 0; j < kTN; ++j) {
-    int64_t n = n0 + wave * (kBN / 4) + j * 32 + wl_n;
+    int64_t n = n0 + wn * (kBN / 4) + j * 32 + wl_n;
     n = n < N ? n : N - 1;
-    w_src[j] = codes + n * row_bytes + 16 * wl_g;
-    s_row[j] = scales + n * nb;
-    z_row[j] = HAS_ZP ? zeros + (n >> 3) * nb : nullptr;
     z_sh[j] = 4 * (int)(n & 7);
   }
 
@@ -182,16 +186,17 @@ __global__ void __launch_bounds__(256) gemm_int4_lds(
 #pragma unroll
     for (int u = 0; u < kAC; ++u) copy16(A16 + a_off[u] + k0, base + (wave * kAC + u) * 1024);
     base += kABytes;
+    const int chunk0 = wn * kTN + wm * kWC;
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) copy16(w_src[j] + (k0 >> 1), base + (wave * kTN + j) * 1024);
+    for (int jj = 0; jj < kWC; ++jj) copy16(w_src[jj] + (k0 >> 1), base + (chunk0 + jj) * 1024);
     base += kWBytes;
     const int64_t blk = ((k0 >> 5) + wl_g) >> bs_shift;
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) copy4(s_row[j] + blk, base + (wave * kTN + j) * 256);
+    for (int jj = 0; jj < kWC; ++jj) copy4(s_row[jj] + blk, base + (chunk0 + jj) * 256);
     if (HAS_ZP) {
       base += kSBytes;
 #pragma unroll
-      for (int j = 0; j < kTN; ++j) copy4(z_row[j] + blk, base + (wave * kTN + j) * 256);
+      for (int jj = 0; jj < kWC; ++jj) copy4(z_row[jj] + blk, base + (chunk0 + jj) * 256);
     }
   };
 
@@ -203,10 +208,10 @@ __global__ void __launch_bounds__(256) gemm_int4_lds(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // operand read offsets: A row (lane & 31) of each 32-row tile, chunk
-  // (4 * (lane >> 5) + t) ^ ((row >> 1) & 7); per-lane words at lane * 16 /
-  // lane * 4
-  const int a_rd = (lane & 31) * 128;
+  // operand read offsets: A row (lane & 31) of each of this wave's 32-row
+  // tiles, chunk (4 * (lane >> 5) + t) ^ ((row >> 1) & 7); per-lane words at
+  // lane * 16 / lane * 4
+  const int a_rd = (wm * (kBM / WM) + (lane & 31)) * 128;
   const int a_cx = (lane >> 1) & 7, a_cg = 4 * (lane >> 5);
 
   auto read_a = [&](half8 (&af)[kTM], const uint8_t* abase, int t) {
@@ -216,12 +221,12 @@ __global__ void __launch_bounds__(256) gemm_int4_lds(
       af[i] = *reinterpret_cast<const half8*>(abase + i * 32 * 128 + a_rd + coff);
   };
 
-  // Slices are software-pipelined: while the 16 MFMAs of slice t run, the A
+  // Slices are software-pipelined: while the MFMAs of slice t run, the A
   // operands of slice t + 1 are read from LDS and its weights dequantized.
   auto compute = [&](int b) {
     const uint8_t* abase = smem + b * kStageBytes;
-    const uint8_t* wbase = abase + kABytes + wave * (kTN * 1024) + lane * 16;
-    const uint8_t* sbase = abase + kABytes + kWBytes + wave * (kTN * 256) + lane * 4;
+    const uint8_t* wbase = abase + kABytes + wn * (kTN * 1024) + lane * 16;
+    const uint8_t* sbase = abase + kABytes + kWBytes + wn * (kTN * 256) + lane * 4;
     u32x4 wc[kTN];
     float sc[kTN], nzs[kTN];
     half8 af[2][kTM], bf[2][kTN];
@@ -255,7 +260,7 @@ __global__ void __launch_bounds__(256) gemm_int4_lds(
 #pragma unroll
         for (int q = 0; q < kTM * kTN; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 24 / kTM, 0);  // VALU
+          __builtin_amdgcn_sched_group_barrier(0x002, (24 * kTN + kTM * kTN - 1) / (kTM * kTN), 0);  // VALU
           if ((q % kTN) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
         }
       }
@@ -285,19 +290,131 @@ __global__ void __launch_bounds__(256) gemm_int4_lds(
   // drain the copies still in flight before the workgroup's LDS is released
   wait_vm_lgkm0<0>();
 
-  float* out = splits > 1 ? part + (int64_t)split * M * N : Y;
+  // streamed out once (nontemporal: measured 2-5% faster than plain stores);
+  // tiles wholly inside Y store without per-element bounds checks
+  const int64_t mw = m0 + wm * (kBM / WM);  // this wave's first row
+  const bool whole = m0 + kBM <= M && n0 + kBN <= N;  // uniform
+  float* tile_out = out + (mw + 4 * (lane >> 5)) * N + n0 + wn * (kBN / 4) + (lane & 31);
+  if (whole) {
 #pragma unroll
-  for (int i = 0; i < kTM; ++i)
+    for (int i = 0; i < kTM; ++i)
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) {
-      const int64_t col = n0 + wave * (kBN / 4) + j * 32 + (lane & 31);
+      for (int j = 0; j < kTN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        // streamed out once (nontemporal: measured 2-5% faster than plain stores)
-        if (row < M && col < N) __builtin_nontemporal_store(acc[i][j][r], out + row * N + col);
+        for (int r = 0; r < 16; ++r)
+          __builtin_nontemporal_store(
+              acc[i][j][r], tile_out + (int64_t)(i * 32 + 8 * (r >> 2) + (r & 3)) * N + j * 32);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) {
+        const int64_t col = n0 + wn * (kBN / 4) + j * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = mw + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (row < M && col < N) __builtin_nontemporal_store(acc[i][j][r], out + row * N + col);
+        }
       }
-    }
+  }
+}
+
+// One tile shape over the whole of Y, K split `splits` ways: XCD x (=
+// blockIdx % 8) takes work items [x * per, (x + 1) * per).
+template <bool HAS_ZP, int BM, int TN>
+__global__ void __launch_bounds__(256) gemm_int4_lds(
+    const _Float16* __restrict__ A16, const uint8_t* __restrict__ codes,
+    const float* __restrict__ scales, const uint32_t* __restrict__ zeros, float* __restrict__ Y,
+    float* __restrict__ part, int64_t M, int64_t N, int64_t K, int64_t row_bytes, int64_t nb,
+    int32_t bs_shift, int64_t tiles_n, int64_t work, int32_t splits, int64_t kc) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int64_t per = (work + kXcds - 1) / kXcds;
+  const int64_t L = (int64_t)(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+  if (L >= work) return;  // whole workgroup
+  const int split = (int)(L % splits);
+  const int64_t tile = L / splits;
+  const int64_t kbeg = split * kc;
+  const int64_t kend = kbeg + kc < K ? kbeg + kc : K;
+  float* out = splits > 1 ? part + (int64_t)split * M * N : Y;
+  lds_tile<HAS_ZP, BM, TN>(smem, A16, codes, scales, zeros, out, M, N, K, row_bytes, nb, bs_shift,
+                           (tile / tiles_n) * BM, (tile % tiles_n) * (128 * TN), kbeg,
+                           (int)((kend - kbeg) / kBK));
+}
+
+// Two tile widths in one launch, whole K: columns [0, n_split) in BM x (128
+// TN0) tiles (the first work0 workgroups, dispatched first), the rest in
+// BM x (128 TN1) tiles.  With as many wide tiles as CUs, the narrow ones fill
+// the second round, which then takes about half as long instead of leaving
+// CUs idle.  Within each class XCD x takes a contiguous range of its tiles.
+template <bool HAS_ZP, int BM, int TN0, int TN1>
+__global__ void __launch_bounds__(256) gemm_int4_lds_mix(
+    const _Float16* __restrict__ A16, const uint8_t* __restrict__ codes,
+    const float* __restrict__ scales, const uint32_t* __restrict__ zeros, float* __restrict__ Y,
+    int64_t M, int64_t N, int64_t K, int64_t row_bytes, int64_t nb, int32_t bs_shift,
+    int64_t n_split, int64_t tiles_n0, int64_t work0, int64_t blocks0, int64_t tiles_n1,
+    int64_t work1) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int steps = (int)(K / kBK);
+  const int64_t b = blockIdx.x;
+  if (b < blocks0) {
+    const int64_t per = blocks0 / kXcds;
+    const int64_t L = (b % kXcds) * per + b / kXcds;
+    if (L >= work0) return;
+    lds_tile<HAS_ZP, BM, TN0>(smem, A16, codes, scales, zeros, Y, M, N, K, row_bytes, nb, bs_shift,
+                              (L / tiles_n0) * BM, (L % tiles_n0) * (128 * TN0), 0, steps);
+  } else {
+    const int64_t b1 = b - blocks0;
+    const int64_t per = (work1 + kXcds - 1) / kXcds;
+    const int64_t L = (b1 % kXcds) * per + b1 / kXcds;
+    if (L >= work1) return;
+    lds_tile<HAS_ZP, BM, TN1>(smem, A16, codes, scales, zeros, Y, M, N, K, row_bytes, nb, bs_shift,
+                              (L / tiles_n1) * BM, n_split + (L % tiles_n1) * (128 * TN1), 0, steps);
+  }
+}
+
+template <bool HAS_ZP, int BM, int TN0, int TN1>
+hipError_t launch_mix(const Sizes& s, const mnb_plan& p, int64_t M, const _Float16* A16, float* Y,
+                      int64_t n_split, hipStream_t st) {
+  using T0 = Tile<BM, TN0>;
+  using T1 = Tile<BM, TN1>;
+  const int64_t rows = (M + BM - 1) / BM;
+  const int64_t tiles_n0 = n_split / T0::BN, work0 = rows * tiles_n0;
+  const int64_t blocks0 = (work0 + kXcds - 1) / kXcds * kXcds;
+  const int64_t tiles_n1 = (s.N - n_split + T1::BN - 1) / T1::BN, work1 = rows * tiles_n1;
+  const int64_t blocks = blocks0 + (work1 + kXcds - 1) / kXcds * kXcds;
+  if (blocks > 0x7FFFFFFF || n_split % T0::BN || n_split >= s.N) return hipErrorInvalidValue;
+  const size_t l0 = (size_t)T0::Stages * T0::template stage_bytes<HAS_ZP>();
+  const size_t l1 = (size_t)T1::Stages * T1::template stage_bytes<HAS_ZP>();
+  hipLaunchKernelGGL((gemm_int4_lds_mix<HAS_ZP, BM, TN0, TN1>), dim3((unsigned)blocks), dim3(256),
+                     l0 > l1 ? l0 : l1, st, A16, static_cast<const uint8_t*>(p.codes),
+                     static_cast<const float*>(p.scales), static_cast<const uint32_t*>(p.zeros), Y,
+                     M, s.N, s.K, s.row_bytes, s.nb, s.bs == 32 ? 0 : (s.bs == 64 ? 1 : 2), n_split,
+                     tiles_n0, work0, blocks0, tiles_n1, work1);
+  return hipGetLastError();
+}
+
+template <bool HAS_ZP, int BM, int TN>
+hipError_t launch_tile(const Sizes& s, const mnb_plan& p, int64_t M, const _Float16* A16, float* Y,
+                       float* part, int32_t splits, int64_t kc, hipStream_t st) {
+  using T_ = Tile<BM, TN>;
+  const int64_t tiles_n = (s.N + T_::BN - 1) / T_::BN;
+  const int64_t work = ((M + BM - 1) / BM) * tiles_n * splits;
+  const int64_t blocks = (work + kXcds - 1) / kXcds * kXcds;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const size_t lds = (size_t)T_::Stages * T_::template stage_bytes<HAS_ZP>();
+  hipLaunchKernelGGL((gemm_int4_lds<HAS_ZP, BM, TN>), dim3((unsigned)blocks), dim3(256), lds, st,
+                     A16, static_cast<const uint8_t*>(p.codes),
+                     static_cast<const float*>(p.scales), static_cast<const uint32_t*>(p.zeros), Y,
+                     part, M, s.N, s.K, s.row_bytes, s.nb, s.bs == 32 ? 0 : (s.bs == 64 ? 1 : 2),
+                     tiles_n, work, splits, kc);
+  return hipGetLastError();
+}
+
+template <int BM, int TN>
+hipError_t launch_tile_zp(const Sizes& s, const mnb_plan& p, int64_t M, const _Float16* A16, float* Y,
+                          float* part, int32_t splits, int64_t kc, hipStream_t st) {
+  return s.zeros ? launch_tile<true, BM, TN>(s, p, M, A16, Y, part, splits, kc, st)
+                 : launch_tile<false, BM, TN>(s, p, M, A16, Y, part, splits, kc, st);
 }
 
 }  // namespace
@@ -310,34 +427,19 @@ uint64_t gemm_lds_a16_bytes(const Sizes& s, int64_t M) {
   return align256((uint64_t)M * (uint64_t)s.K * 2);
 }
 
-template <bool HAS_ZP, int BM>
-hipError_t launch_tile(const Sizes& s, const mnb_plan& p, int64_t M, const _Float16* A16, float* Y,
-                       float* part, int32_t splits, int64_t kc, hipStream_t st) {
-  using T_ = Tile<BM>;
-  const int64_t tiles_n = (s.N + T_::BN - 1) / T_::BN;
-  const int64_t work = ((M + BM - 1) / BM) * tiles_n * splits;
-  const int64_t blocks = (work + kXcds - 1) / kXcds * kXcds;
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const size_t lds = (size_t)T_::Stages * T_::template stage_bytes<HAS_ZP>();
-  hipLaunchKernelGGL((gemm_int4_lds<HAS_ZP, BM>), dim3((unsigned)blocks), dim3(256), lds, st, A16,
-                     static_cast<const uint8_t*>(p.codes), static_cast<const float*>(p.scales),
-                     static_cast<const uint32_t*>(p.zeros), Y, part, M, s.N, s.K, s.row_bytes, s.nb,
-                     s.bs == 32 ? 0 : (s.bs == 64 ? 1 : 2), tiles_n, work, splits, kc);
-  return hipGetLastError();
-}
-
 hipError_t launch_gemm_lds(const Sizes& s, const mnb_plan& p, int64_t M, const float* A,
                            void* ws, float* Y, float* part, int32_t splits, int64_t kc, int bm,
-                           hipStream_t st) {
+                           int64_t n_split, hipStream_t st) {
   _Float16* A16 = static_cast<_Float16*>(ws);
   const int64_t n8 = M * s.K / 8;
   hipLaunchKernelGGL(round_a_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, A, A16,
                      n8);
-  if (bm == 128)
-    return s.zeros ? launch_tile<true, 128>(s, p, M, A16, Y, part, splits, kc, st)
-                   : launch_tile<false, 128>(s, p, M, A16, Y, part, splits, kc, st);
-  return s.zeros ? launch_tile<true, 256>(s, p, M, A16, Y, part, splits, kc, st)
-                 : launch_tile<false, 256>(s, p, M, A16, Y, part, splits, kc, st);
+  if (n_split > 0)  // 256 x 256 tiles up to column n_split, then 256 x 128
+    return s.zeros ? launch_mix<true, 256, 2, 1>(s, p, M, A16, Y, n_split, st)
+                   : launch_mix<false, 256, 2, 1>(s, p, M, A16, Y, n_split, st);
+  if (bm == 128) return launch_tile_zp<128, 1>(s, p, M, A16, Y, part, splits, kc, st);
+  if (bm == 256) return launch_tile_zp<256, 2>(s, p, M, A16, Y, part, splits, kc, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace mnb

@@ -248,3 +248,16 @@ def test_gemm_fp16_input_range(orc, M, K, N):
     err = np.abs(y2.astype(np.float64) - y64)
     assert np.isfinite(y2).all()
     assert (err <= TOL * S + extra).all()
+
+
+@pytest.mark.parametrize("zp", [False, True])
+def test_gemm_mixed_tile_widths_every_element(orc, zp):
+    """Shapes whose 256 x 256 tiles would need between one and two rounds run
+    256-wide tiles on the first columns and 256 x 128 tiles on the rest, in
+    one launch; ragged M and N put partial tiles at the end of both widths."""
+    M, K, N, bs = 2011, 256, 10163, 32
+    say(f"gemm mixed tile widths M={M} K={K} N={N} zp={zp}")
+    w, B, s, Z = prepare(K, N, bs, zp, seed=91 + zp)
+    a = synth.activations_f32(synth.seed_for(M, 5), M, K)
+    y = run_gemm(w, a)
+    check(orc, y, a, B, s, Z, K, N, bs)
