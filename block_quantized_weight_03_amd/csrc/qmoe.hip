@@ -17,8 +17,8 @@
 //              equals an fp32 softmax over all experts renormalized over the
 //              selected ones.
 //  2. group:   one workgroup; per-expert counts, offsets, a permutation of the
-//              T*k slots into expert-grouped order that is stable in (token,
-//              rank) order, and the list of (expert, row-tile) work items.
+//              T*k slots into expert-grouped order, and the list of (expert,
+//              row-tile) work items.
 //  3. fc1:     per work item, G = X_e W1_e^T on the matrix cores (gathered
 //              token rows in LDS; INT3 / INT4 weights dequantized in
 //              registers as fp16((q - z) * s), z = 4 / 8, once per item);
@@ -152,7 +152,7 @@ __global__ void __launch_bounds__(256) qmoe_route(const float* __restrict__ logi
 }
 
 // ---------------------------------------------------------------------------
-// 2. grouping: counts, offsets, stable permutation, work items
+// 2. grouping: counts, offsets, permutation, work items
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int clamp_id(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
 
@@ -172,9 +172,12 @@ struct GroupOut {
 //            thread writes its own work items;
 //  ranks:    the base of wave w in expert e is offsets[e] plus the counts of
 //            waves 0 .. w-1; a wave walks its slots in order, 64 at a time,
-//            and a slot's rank inside the batch is the number of lower lanes
-//            with the same expert.  The permutation is therefore stable in
-//            slot (token, rank) order.
+//            and takes each slot's position with an LDS fetch-and-add on its
+//            expert's base.  Slots of different waves are ordered by wave;
+//            within a wave the order of the lanes' atomics is the hardware's.
+//            No result depends on this order: each token's rows go through
+//            the same per-row arithmetic wherever they sit in a work item,
+//            and the combine sums a token's ranks in rank order.
 __global__ void __launch_bounds__(kGroupThreads) qmoe_group(const int32_t* __restrict__ ids,
                                                             int64_t T, int k, int E, int64_t max_items,
                                                             int bm, GroupOut o) {
@@ -267,24 +270,11 @@ __global__ void __launch_bounds__(kGroupThreads) qmoe_group(const int32_t* __res
   }
   __syncthreads();
   int32_t* base = hist + wave * E;
-  for (int64_t b0 = s_lo; b0 < s_hi; b0 += 64) {
-    const int64_t sl = b0 + lane;
-    const bool valid = sl < s_hi;
-    const int e = valid ? clamp_id(ids[sl], E) : -1;
-    int32_t r = 0;
-    for (int j = 0; j < 64; ++j) {
-      const int ej = __builtin_amdgcn_readlane(e, j);
-      r += (j < lane && ej == e) ? 1 : 0;
-    }
-    int32_t pos = 0;
-    if (valid) {
-      pos = base[e] + r;
-      o.perm[pos] = (int32_t)sl;
-      o.inv[sl] = pos;
-    }
-    __builtin_amdgcn_wave_barrier();
-    if (valid) atomicMax(&base[e], pos + 1);
-    __builtin_amdgcn_wave_barrier();
+  for (int64_t sl = s_lo + lane; sl < s_hi; sl += 64) {
+    const int e = clamp_id(ids[sl], E);
+    const int32_t pos = atomicAdd(&base[e], 1);
+    o.perm[pos] = (int32_t)sl;
+    o.inv[sl] = pos;
   }
 }
 
