@@ -105,8 +105,10 @@ __device__ __forceinline__ void route_token(const float* __restrict__ l, int E, 
     const int e = i * 64 + lane;
     key[i] = (i < nper && e < E) ? logit_key(l[e]) : 0u;
   }
-  float lmax = 0.0f, den = 0.0f, sel_v[16];
-  int sel_i[16];
+  // lane j keeps the j-th selection (no register array indexed by the round,
+  // which compiled to dozens of register moves per round)
+  float lmax = 0.0f, den = 0.0f, my_v = 0.0f;
+  int my_i = 0;
   for (int j = 0; j < k; ++j) {  // k <= 16 (checked by the launcher)
     // this lane's best: largest key, lowest i on ties (= lowest expert)
     uint32_t bk = 0;
@@ -130,14 +132,14 @@ __device__ __forceinline__ void route_token(const float* __restrict__ l, int E, 
     if (j == 0) lmax = v;
     const float ex = expf(v - lmax);
     den += ex;
-    sel_v[j] = ex;
-    sel_i[j] = win;
-  }
-  if (lane == 0) {
-    for (int j = 0; j < k; ++j) {
-      ids[j] = sel_i[j];
-      wts[j] = sel_v[j] / den;
+    if (lane == j) {
+      my_v = ex;
+      my_i = win;
     }
+  }
+  if (lane < k) {
+    ids[lane] = my_i;
+    wts[lane] = my_v / den;
   }
 }
 
