@@ -299,7 +299,9 @@ void prepack(const Sizes& s, const uint8_t* B, const void* scales,
     // word (g, b): nibble r = zero point of row 8g + r, block b; rows past N
     // hold 8 (never read)
     const int64_t groups = s.N / 8 + (s.N % 8 ? 1 : 0);
-    parallel_items(groups, s.zeros, [&](int64_t lo, int64_t hi) {
+    // (8 strided byte reads and a word write per (group, block): weighed as
+    // 64 bytes of streaming work each when choosing the thread count)
+    parallel_items(groups, s.zeros * 16, [&](int64_t lo, int64_t hi) {
       for (int64_t g = lo; g < hi; ++g) {
         for (int64_t b = 0; b < s.nb; ++b) {
           uint32_t w = 0;
