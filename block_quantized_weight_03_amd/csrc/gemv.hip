@@ -150,7 +150,7 @@ __global__ void __launch_bounds__(256) gemv_prep_a(const float* __restrict__ A, 
 
 struct Digits {
   uint32_t d[kDig][4];
-  int32_t se[kDig / 2];
+  int32_t sf[2];  // digit sums weighted as in F0 and F1 below (planes 0-3, 4-7)
   int32_t ne;
   float poison;
 };
@@ -162,40 +162,56 @@ __device__ __forceinline__ void load_digits(Digits& g, const P* dig, const int32
   for (int p = 0; p < kDig; ++p)
 #pragma unroll
     for (int w = 0; w < 4; ++w) g.d[p][w] = dig[((c * kDig + p) * 4 + w) * 64 + lane];
+  int32_t se[kDig / 2];
 #pragma unroll
-  for (int j = 0; j < kDig / 2; ++j) g.se[j] = sums[(c * (kDig / 2) + j) * 64 + lane];
+  for (int j = 0; j < kDig / 2; ++j) se[j] = sums[(c * (kDig / 2) + j) * 64 + lane];
+  // |se| <= 256 + 16 * 256, so |sf| < 2^21 (exact 24-bit multiplies below)
+  g.sf[0] = se[0] + 256 * se[1];
+  g.sf[1] = se[2] + 256 * se[3];
   const int32_t ne = nexp[c * 64 + lane];
   g.poison = ne == kBadExp ? __builtin_nanf("") : 0.0f;
   g.ne = ne == kBadExp ? 0 : ne;
 }
 
 // Partial of one 32-code sub-block: sum_k (q_k - z) * a_k * s (fp32).
+// F0 = D0 + 16 D1 + 256 D2 + 4096 D3 (D_p = the codes' dot product with digit
+// plane p) is built by Horner's rule, each plane's four v_dot8 accumulating
+// onto 16 times the planes above it, likewise F1 over planes 4..7; |D_p| <=
+// 32 * 8 * 8, so |F| < 2^25 and nothing overflows.
 template <bool HAS_ZP>
 __device__ __forceinline__ float subblock_dot(const u32x4 q, const Digits& g, float s, int z) {
-  int D[kDig];
+  int F[2];
 #pragma unroll
-  for (int p = 0; p < kDig; ++p) {
-    int acc = __builtin_amdgcn_sdot8((int)q.x, (int)g.d[p][0], 0, false);
-    acc = __builtin_amdgcn_sdot8((int)q.y, (int)g.d[p][1], acc, false);
-    acc = __builtin_amdgcn_sdot8((int)q.z, (int)g.d[p][2], acc, false);
-    acc = __builtin_amdgcn_sdot8((int)q.w, (int)g.d[p][3], acc, false);
-    D[p] = acc;  // |D| <= 32 * 8 * 8
+  for (int h = 0; h < 2; ++h) {
+    int acc = 0;
+#pragma unroll
+    for (int p = 4 * h + 3; p >= 4 * h; --p) {
+      acc *= 16;
+      acc = __builtin_amdgcn_sdot8((int)q.x, (int)g.d[p][0], acc, false);
+      acc = __builtin_amdgcn_sdot8((int)q.y, (int)g.d[p][1], acc, false);
+      acc = __builtin_amdgcn_sdot8((int)q.z, (int)g.d[p][2], acc, false);
+      acc = __builtin_amdgcn_sdot8((int)q.w, (int)g.d[p][3], acc, false);
+    }
+    F[h] = acc;
   }
-  int E0 = D[0] + 16 * D[1], E1 = D[2] + 16 * D[3];
-  int E2 = D[4] + 16 * D[5], E3 = D[6] + 16 * D[7];
   if (HAS_ZP) {
-    // |8 - z| <= 8 and |digit sums| < 2^13: 24-bit multiplies are exact
+    // |8 - z| <= 8 and |sf| < 2^21: 24-bit multiplies are exact
     const int zc = 8 - z;
-    E0 = __mul24(zc, g.se[0]) + E0;
-    E1 = __mul24(zc, g.se[1]) + E1;
-    E2 = __mul24(zc, g.se[2]) + E2;
-    E3 = __mul24(zc, g.se[3]) + E3;
+    F[0] = __mul24(zc, g.sf[0]) + F[0];
+    F[1] = __mul24(zc, g.sf[1]) + F[1];
   }
-  const int F0 = E0 + 256 * E1;  // |E| < 2^16 so |F| < 2^25
-  const int F1 = E2 + 256 * E3;
-  const float f = fmaf((float)F1, 65536.0f, (float)F0);
+  const float f = fmaf((float)F[1], 65536.0f, (float)F[0]);
   return ldexpf(f * s, g.ne) + g.poison;
 }
+
+// Raw buffer resource over `bytes` bytes at p: a load whose dwords lie past
+// the end returns 0 for them, so clamps and tail branches are not needed.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past every resource used here
+constexpr int kNT = 2;                          // cache policy: nontemporal (streamed once)
 
 template <int R, bool HAS_ZP>
 struct RowTile {
@@ -234,6 +250,27 @@ __device__ __forceinline__ void load_rows(RowTile<R, HAS_ZP>& t, const uint8_t* 
     t.zpk = __builtin_nontemporal_load(zeros + (n0 >> 3) * nb + b) >> (4 * (n0 & 7));
 }
 
+// The same loads through buffer resources over the codes, scales and zero
+// points: rows past N lie past the end of each resource and inactive lanes
+// add an out-of-range offset, so every load returns zeros for them without
+// a branch.  lq, ls and lz are the lane terms (kOutOfRange for inactive
+// lanes); the launcher checks that the offsets of the rows a wave can touch
+// stay below 2^31.
+template <int R, bool HAS_ZP>
+__device__ __forceinline__ void load_rows_buf(RowTile<R, HAS_ZP>& t, __amdgpu_buffer_rsrc_t rc,
+                                              __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rz,
+                                              uint32_t n0, uint32_t row_bytes, uint32_t nb4,
+                                              uint32_t lq, uint32_t ls, uint32_t lz) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t n = n0 + r;
+    t.q[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, n * row_bytes + lq, 0, kNT));
+    t.s[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, n * nb4 + ls, 0, kNT));
+  }
+  t.zpk = 0;
+  if (HAS_ZP) t.zpk = __builtin_amdgcn_raw_buffer_load_b32(rz, (n0 >> 3) * nb4 + lz, 0, kNT) >> (4 * (n0 & 7));
+}
+
 // Reduces part[r] over the 64 lanes of the wave in a fixed order and returns,
 // in lane r*(64/R) for each r < R, the total of row r (other lanes: garbage).
 template <int R>
@@ -263,7 +300,7 @@ constexpr int lds_red_floats() {
 }
 
 // Fused kernel: in-kernel digits, K <= 8192 (team = nchunk waves, one chunk each).
-template <int R, bool HAS_ZP>
+template <int R, bool HAS_ZP, bool BUF>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) gemv_int4_fused(
     const float* __restrict__ A, const uint8_t* __restrict__ codes,
     const float* __restrict__ scales, const uint32_t* __restrict__ zeros, float* __restrict__ Y,
@@ -294,8 +331,22 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) g
   const int64_t iters = base0 < nrg ? (nrg - base0 + stride - 1) / stride : 0;
   int64_t rg = base0 + tm;
 
+  // buffer path: resources over the codes, scales and zero-point words
+  const __amdgpu_buffer_rsrc_t rc = buffer_over(codes, BUF ? (uint32_t)(N * row_bytes) : 0u);
+  const __amdgpu_buffer_rsrc_t rs = buffer_over(scales, BUF ? (uint32_t)(N * nb * 4) : 0u);
+  const __amdgpu_buffer_rsrc_t rz =
+      buffer_over(zeros, BUF && HAS_ZP ? (uint32_t)(((N + 7) >> 3) * nb * 4) : 0u);
+  const uint32_t lq = act ? qoff : kOutOfRange, ls = act ? 4u * b : kOutOfRange;
+  const uint32_t rb32 = (uint32_t)row_bytes, nb4 = 4u * (uint32_t)nb;
+  auto load = [&](RowTile<R, HAS_ZP>& t, int64_t g) {
+    if constexpr (BUF)
+      load_rows_buf<R, HAS_ZP>(t, rc, rs, rz, (uint32_t)(g * R), rb32, nb4, lq, ls, ls);
+    else
+      load_rows<R, HAS_ZP>(t, codes, scales, zeros, g * R, g < nrg ? N : 0, row_bytes, nb, zrow, qoff, b, act);
+  };
+
   RowTile<R, HAS_ZP> t0, t1;
-  if (iters > 0) load_rows<R, HAS_ZP>(t0, codes, scales, zeros, rg * R, rg < nrg ? N : 0, row_bytes, nb, zrow, qoff, b, act);
+  if (iters > 0) load(t0, rg);
 
   // digits of this workgroup's chunks, computed by all threads
   const int64_t tasks = (int64_t)nchunk * 64 * 4;
@@ -308,8 +359,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) g
 
   auto step = [&](RowTile<R, HAS_ZP>& cur, RowTile<R, HAS_ZP>& nxt, int64_t it) {
     const int64_t rgn = rg + stride;
-    if (it + 1 < iters)
-      load_rows<R, HAS_ZP>(nxt, codes, scales, zeros, rgn * R, rgn < nrg ? N : 0, row_bytes, nb, zrow, qoff, b, act);
+    if (it + 1 < iters) load(nxt, rgn);
     float part[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) part[r] = subblock_dot<HAS_ZP>(cur.q[r], g, cur.s[r], (int)((cur.zpk >> (4 * r)) & 15u));
@@ -380,14 +430,6 @@ __device__ __forceinline__ float subblock_dot_f32(const u32x4 q, const Acts& x, 
   return ((acc[0] + acc[1]) + (acc[2] + acc[3])) * s + x.poison;
 }
 
-// Raw buffer resource over `bytes` bytes at p: a load whose dwords lie past
-// the end returns 0 for them, so clamps and tail branches are not needed.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-
-constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past every resource used here
-constexpr int kNT = 2;                          // cache policy: nontemporal (streamed once)
 
 // Sum over the 64 lanes of a wave with DPP moves (no LDS round trip); the
 // total lands in lane 63.  Fixed order, so the result is deterministic.
@@ -614,6 +656,10 @@ int cu_count() {
 template <int R, bool HAS_ZP>
 hipError_t launch_fused(const Sizes& s, const mnb_plan& p, const float* A, float* Y, int64_t nsb,
                         int64_t nchunk, hipStream_t st) {
+  // 32-bit buffer offsets for every row a wave can touch (row groups past the
+  // last one, up to R * 64 rows past N, read zeros)
+  const int64_t rows = s.N + (int64_t)R * 64;
+  const bool buf = rows * s.row_bytes < (int64_t(1) << 31) && rows * s.nb * 4 < (int64_t(1) << 31);
   const int team = (int)nchunk;
   const int teams = kMaxTeam / team;
   const int threads = 64 * team * teams;
@@ -624,7 +670,8 @@ hipError_t launch_fused(const Sizes& s, const mnb_plan& p, const float* A, float
   const int64_t cap = (int64_t)cu_count() * 4;
   if (blocks > cap) blocks = cap;
   const size_t lds = (size_t)lds_red_floats<R>() * 4 + (size_t)nchunk * (kDig * 4 * 64 + (kDig / 2) * 64 + 64) * 4;
-  hipLaunchKernelGGL((gemv_int4_fused<R, HAS_ZP>), dim3((unsigned)blocks), dim3(threads), lds, st,
+  auto kern = buf ? gemv_int4_fused<R, HAS_ZP, true> : gemv_int4_fused<R, HAS_ZP, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(threads), lds, st,
                      A, static_cast<const uint8_t*>(p.codes), static_cast<const float*>(p.scales),
                      static_cast<const uint32_t*>(p.zeros), Y, s.K, s.N, s.row_bytes, s.nb,
                      (int32_t)nsb, (int32_t)nchunk, bs_shift_of(s), (int64_t)s.zrow);

@@ -125,6 +125,22 @@ def test_gemv_vocabulary_head_sampled(orc):
     check(orc, y, a, B, s, Z, K, N, 32, rows=rows)
 
 
+@pytest.mark.parametrize("K,N,zp", [(4096, 40000, False), (2050, 35001, True), (1024, 33000, False)])
+def test_gemv_long_row_streams_sampled(orc, K, N, zp):
+    """N > 32768: the in-kernel digit path with buffer-resource row loads (rows
+    past N and lanes past the last sub-block read zeros); first and last rows
+    plus a random sample against the oracle."""
+    say(f"gemv long rows K={K} N={N} zp={zp}")
+    w, B, s, Z = prepare(K, N, zp=zp, seed=K + N)
+    a = synth.activations_f32(synth.seed_for(K, N), 1, K)
+    y = run_gemv(w, a)
+    assert np.isfinite(y).all()
+    rng = np.random.default_rng(N)
+    rows = np.unique(np.concatenate([np.arange(40), np.arange(N - 40, N),
+                                     rng.choice(N, 2048, replace=False)]))
+    check(orc, y, a, B, s, Z, K, N, 32, rows=rows)
+
+
 def test_gemv_exact_integer_case_bit_exact(orc):
     say("gemv exact integer")
     K, N = 4096, 256
