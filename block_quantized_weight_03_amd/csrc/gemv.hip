@@ -413,21 +413,54 @@ struct Acts {
   float poison;
 };
 
+// (q - 8) / 16 of the low nibble of byte B of x: v_cvt_off_f32_i4 converts
+// the signed 4-bit value in bits [3:0] of its source to float and divides by
+// 16 (exact), and the byte is taken by an SDWA source select (the compiler
+// folds the shift and mask).  The stored nibble is q ^ 8, i.e. q - 8 in 4-bit
+// two's complement.
+template <int B>
+__device__ __forceinline__ float nib16(uint32_t x) {
+  return __builtin_amdgcn_cvt_off_f32_i4(B == 3 ? x >> 24 : (x >> (8 * B)) & 0xFFu);
+}
+
 template <bool HAS_ZP>
 __device__ __forceinline__ float subblock_dot_f32(const u32x4 q, const Acts& x, float s, int z) {
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
   float acc[4];
+  if constexpr (HAS_ZP) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    acc[i] = 0.0f;
+    for (int i = 0; i < 4; ++i) {
+      acc[i] = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      int v = (int)(w[i] << (28 - 4 * e)) >> 28;  // stored nibble = q - 8, sign-extended
-      if (HAS_ZP) v += 8 - z;
-      acc[i] = fmaf((float)v, x.a[8 * i + e], acc[i]);
+      for (int e = 0; e < 8; ++e) {
+        const int v = ((int)(w[i] << (28 - 4 * e)) >> 28) + 8 - z;  // stored nibble = q - 8
+        acc[i] = fmaf((float)v, x.a[8 * i + e], acc[i]);
+      }
     }
+    return ((acc[0] + acc[1]) + (acc[2] + acc[3])) * s + x.poison;
+  } else {
+    // z = 8: the chains add (q - 8) a / 16 (every product and partial sum is
+    // 2^-4 times the one of (q - 8) a, so the rounding is the same) and the
+    // sub-block sum is scaled back by 16 exactly; codes in even and odd
+    // nibble positions come from the word and the word shifted by 4
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = w[i];
+      uint32_t hi = w[i] >> 4;
+      asm("" : "+v"(hi));  // one shift, then byte selects (not a bit-field extract per code)
+      float c = 0.0f;
+      c = fmaf(nib16<0>(lo), x.a[8 * i + 0], c);
+      c = fmaf(nib16<0>(hi), x.a[8 * i + 1], c);
+      c = fmaf(nib16<1>(lo), x.a[8 * i + 2], c);
+      c = fmaf(nib16<1>(hi), x.a[8 * i + 3], c);
+      c = fmaf(nib16<2>(lo), x.a[8 * i + 4], c);
+      c = fmaf(nib16<2>(hi), x.a[8 * i + 5], c);
+      c = fmaf(nib16<3>(lo), x.a[8 * i + 6], c);
+      c = fmaf(nib16<3>(hi), x.a[8 * i + 7], c);
+      acc[i] = c;
+    }
+    return ldexpf((acc[0] + acc[1]) + (acc[2] + acc[3]), 4) * s + x.poison;
   }
-  return ((acc[0] + acc[1]) + (acc[2] + acc[3])) * s + x.poison;
 }
 
 
