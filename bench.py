@@ -16,7 +16,9 @@ bracketed by torch.cuda.synchronize() on both sides.
 Exactly `--warmup` untimed steps precede the `--steps` timed ones; the
 other workloads (vocabulary head, prefill GEMM, QMoE layers, quantizer) are
 measured first, each from graph replays of its own launches, so the short
-headline region starts at sustained clocks.  The roofline's average launch
+headline region starts at sustained clocks.  For context, `extra` also times
+the vendor BLAS (torch.matmul) on the prefill shapes with dense fp16 weights,
+after the headline region.  The roofline's average launch
 duration comes from HIP events recorded on the launch stream around the same
 timed graph replays (five GEMV kernel launches per step, back to back, so the
 average includes the short gaps between kernels); its ceiling is a plain
@@ -236,6 +238,25 @@ def cpu_oracle_configs(threads):
     return res
 
 
+def vendor_dense_gemm(torch, dev):
+    """Context only (not this library): the vendor BLAS (torch.matmul) on the
+    prefill shapes with the weights already dense fp16, fp16 A and fp16 output
+    (no dequantization, no rounding pass, half the output bytes), graph-replayed
+    like the library's calls.  Run after the headline region."""
+    dense = {}
+    for (K, N) in ((2048, 6144), (6144, 2048)):
+        wd = (torch.rand(K, N, device=dev, generator=torch.Generator(device=dev).manual_seed(K)) * 2 - 1).half()
+        for M in (512, 2048, 4096):
+            ad = (torch.rand(M, K, device=dev, generator=torch.Generator(device=dev).manual_seed(M)) * 2 - 1).half()
+            od = torch.empty((M, N), dtype=torch.float16, device=dev)
+            us = 1e3 * graph_time(torch, [lambda ad=ad, wd=wd, od=od: torch.matmul(ad, wd, out=od)] * 4, 5)
+            tf = 2.0 * M * N * K / us / 1e6
+            dense[f"M{M}_K{K}_N{N}"] = {"us": round(us, 2), "TFLOP/s": round(tf, 1),
+                                         "frac_of_fp16_peak": round(tf / PEAK_FP16_TFLOPS, 4)}
+        del wd
+    return dense
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -415,6 +436,8 @@ def main():
 
     extra = {"per_projection": per_proj, "step_spread": spread, "single_call_latency": single,
              "hot_cache_gemv": hot, **extra}
+    if not args.no_extras:
+        extra["prefill_gemm_vendor_dense_fp16"] = vendor_dense_gemm(torch, dev)
     info = host_info()
     base = None
     if not args.no_cpu:
