@@ -359,7 +359,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) g
 
   auto step = [&](RowTile<R, HAS_ZP>& cur, RowTile<R, HAS_ZP>& nxt, int64_t it) {
     const int64_t rgn = rg + stride;
-    if (it + 1 < iters) load(nxt, rgn);
+    // Buffer path: the next group's loads are issued unconditionally (past the
+    // last group they read zeros), so no branch joins the loop body and the
+    // compiler waits only for this group's loads, not for every load in flight.
+    if constexpr (BUF)
+      load(nxt, rgn < nrg ? rgn : nrg);
+    else if (it + 1 < iters)
+      load(nxt, rgn);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of this group's arithmetic
     float part[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) part[r] = subblock_dot<HAS_ZP>(cur.q[r], g, cur.s[r], (int)((cur.zpk >> (4 * r)) & 15u));
