@@ -100,10 +100,18 @@ __device__ __forceinline__ void route_token(const float* __restrict__ l, int E, 
                                             int32_t* ids, float* wts) {
   const int nper = (E + 63) >> 6;
   uint32_t key[kPer];
+  // all logit loads first (clamped to a valid expert, then masked): a
+  // guarded load per slot compiled to a branch and a full wait each
+  float lv[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int e = i * 64 + lane;
-    key[i] = (i < nper && e < E) ? logit_key(l[e]) : 0u;
+    lv[i] = l[e < E ? e : E - 1];
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = i * 64 + lane;
+    key[i] = (i < nper && e < E) ? logit_key(lv[i]) : 0u;
   }
   // lane j keeps the j-th selection (no register array indexed by the round,
   // which compiled to dozens of register moves per round)
