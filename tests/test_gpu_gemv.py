@@ -195,12 +195,16 @@ def test_gemv_scale_invariance_power_of_two():
         assert np.array_equal(ys, (y.astype(np.float64) * 2.0 ** p).astype(np.float32))
 
 
-def test_gemv_non_finite_activation_poisons_output():
-    say("gemv non-finite A")
-    K, N = 256, 64
-    w, *_ = prepare(K, N, seed=17)
+@pytest.mark.parametrize("K,N,zp", [(256, 64, False), (2050, 300, True), (6144, 128, False),
+                                    (2048, 33000, False), (1024, 40000, True)])
+@pytest.mark.parametrize("bad", [np.inf, -np.inf, np.nan])
+def test_gemv_non_finite_activation_poisons_output(K, N, zp, bad):
+    """Any non-finite activation makes every output NaN, on the short-row and
+    the long-row (digit) paths, with and without zero points."""
+    say(f"gemv non-finite A K={K} N={N} zp={zp} bad={bad}")
+    w, *_ = prepare(K, N, zp=zp, seed=17)
     a = synth.activations_f32(18, 1, K)
-    a[0, 77] = np.inf
+    a[0, K // 3] = bad
     assert np.isnan(run_gemv(w, a)).all()
 
 
