@@ -491,16 +491,20 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 constexpr int kTeams = 4;  // row groups (teams of waves) per workgroup of the fp32 path
 constexpr int kNPT = 8 / kTeams;  // 16-byte pieces of A per thread
 
-// Up to kMaxSegs weight matrices with the same K, block size and zero-point
-// kind, multiplied by the same A in one launch: segment i owns workgroups
-// [first[i], first[i + 1]).
+// Up to NS weight matrices with the same K, block size and zero-point kind,
+// multiplied by the same A in one launch: segment i owns workgroups
+// [first[i], first[i + 1]).  NS is the segment count rounded up to 1, 2 or
+// 4, so a single-matrix launch passes 80 bytes of kernel arguments instead
+// of 200: the first replay of a graph of these launches (a short timed run)
+// measured 1.1 us less per five-launch step with the smaller arguments.
+template <int NS>
 struct GemvSegs {
-  const uint8_t* codes[kMaxSegs];
-  const float* scales[kMaxSegs];
-  const uint32_t* zeros[kMaxSegs];
-  float* Y[kMaxSegs];
-  int32_t N[kMaxSegs];
-  int32_t first[kMaxSegs + 1];
+  const uint8_t* codes[NS];
+  const float* scales[NS];
+  const uint32_t* zeros[NS];
+  float* Y[NS];
+  int32_t N[NS];
+  int32_t first[NS + 1];
   int32_t count;
 };
 
@@ -514,9 +518,9 @@ struct GemvSegs {
 // sub-block's 128 bytes, so the 16 lanes served per LDS cycle hit 64
 // distinct banks.  The A loads are issued before the weight loads; loads
 // complete in order, so waiting for A does not wait for the weights.
-template <int R, bool HAS_ZP>
+template <int R, bool HAS_ZP, int NS>
 __global__ void __launch_bounds__(1024) gemv_int4_f32(
-    const float* __restrict__ A, const GemvSegs sg, int32_t K, int32_t row_bytes, int32_t nb,
+    const float* __restrict__ A, const GemvSegs<NS> sg, int32_t K, int32_t row_bytes, int32_t nb,
     int32_t nsb, int32_t team, int32_t bs_shift) {
   // A: 64 * team sub-blocks of 128 bytes (the launcher sizes it), then the
   // team partials
@@ -526,7 +530,7 @@ __global__ void __launch_bounds__(1024) gemv_int4_f32(
   // this workgroup's segment (uniform)
   int seg = 0;
 #pragma unroll
-  for (int i = 1; i < kMaxSegs; ++i)
+  for (int i = 1; i < NS; ++i)
     if (i < sg.count && (int)blockIdx.x >= sg.first[i]) seg = i;
   const uint8_t* __restrict__ codes = sg.codes[seg];
   const float* __restrict__ scales = sg.scales[seg];
@@ -720,12 +724,12 @@ hipError_t launch_fused(const Sizes& s, const mnb_plan& p, const float* A, float
 
 // s: the shape shared by the segments (K, block size, zero-point kind);
 // segment i multiplies plan p[i] (N = N[i]) into Y[i]
-template <int R, bool HAS_ZP>
-hipError_t launch_f32_segs(const Sizes& s, const mnb_plan* const* p, const int64_t* N, int count,
-                           const float* A, float* const* Y, int64_t nsb, int64_t nchunk,
-                           hipStream_t st) {
+template <int R, bool HAS_ZP, int NS>
+hipError_t launch_f32_segs_n(const Sizes& s, const mnb_plan* const* p, const int64_t* N, int count,
+                             const float* A, float* const* Y, int64_t nsb, int64_t nchunk,
+                             hipStream_t st) {
   const int team = (int)nchunk;
-  GemvSegs sg{};
+  GemvSegs<NS> sg{};
   sg.count = count;
   int64_t blocks = 0;
   for (int i = 0; i < count; ++i) {
@@ -739,10 +743,19 @@ hipError_t launch_f32_segs(const Sizes& s, const mnb_plan* const* p, const int64
   }
   sg.first[count] = (int32_t)blocks;
   const size_t lds = (size_t)team * 8192 + (size_t)kTeams * team * R * 4;
-  hipLaunchKernelGGL((gemv_int4_f32<R, HAS_ZP>), dim3((unsigned)blocks), dim3(64 * kTeams * team),
+  hipLaunchKernelGGL((gemv_int4_f32<R, HAS_ZP, NS>), dim3((unsigned)blocks), dim3(64 * kTeams * team),
                      lds, st, A, sg, (int32_t)s.K, (int32_t)s.row_bytes, (int32_t)s.nb,
                      (int32_t)nsb, team, bs_shift_of(s));
   return hipGetLastError();
+}
+
+template <int R, bool HAS_ZP>
+hipError_t launch_f32_segs(const Sizes& s, const mnb_plan* const* p, const int64_t* N, int count,
+                           const float* A, float* const* Y, int64_t nsb, int64_t nchunk,
+                           hipStream_t st) {
+  if (count == 1) return launch_f32_segs_n<R, HAS_ZP, 1>(s, p, N, count, A, Y, nsb, nchunk, st);
+  if (count == 2) return launch_f32_segs_n<R, HAS_ZP, 2>(s, p, N, count, A, Y, nsb, nchunk, st);
+  return launch_f32_segs_n<R, HAS_ZP, kMaxSegs>(s, p, N, count, A, Y, nsb, nchunk, st);
 }
 
 template <int R, bool HAS_ZP>
