@@ -114,6 +114,8 @@ Rows make_rows(const Sizes& s, const mnb_plan& p, int64_t expert, int64_t row0) 
 // thread issues four 16-byte nontemporal loads (1024 lanes' worth per
 // workgroup, 16 KiB) and folds them together; the result is stored only if it
 // equals a value no realistic input produces, which keeps the loads live.
+// One or two buffers take flat arguments (preloaded into SGPRs, like the
+// short-row GEMV's), more a segment table.
 struct ReadSegs {
   const u32x4* ptr[kMaxSegs];
   int64_t n16[kMaxSegs];       // 16-byte chunks per segment
@@ -121,12 +123,9 @@ struct ReadSegs {
   int count;
 };
 
-__global__ void __launch_bounds__(256) stream_read_kernel(ReadSegs r, uint32_t* __restrict__ sink) {
-  int seg = 0;
-  while (seg + 1 < r.count && (int64_t)blockIdx.x >= r.first[seg + 1]) ++seg;
-  const int64_t base = ((int64_t)blockIdx.x - r.first[seg]) * 1024 + threadIdx.x;
-  const u32x4* p = r.ptr[seg];
-  const int64_t n = r.n16[seg];
+__device__ __forceinline__ void stream_read_body(const u32x4* p, int64_t n, int64_t blk,
+                                                 uint32_t* __restrict__ sink) {
+  const int64_t base = blk * 1024 + threadIdx.x;
   u32x4 v[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -136,6 +135,25 @@ __global__ void __launch_bounds__(256) stream_read_kernel(ReadSegs r, uint32_t* 
   const u32x4 x = (v[0] ^ v[1]) ^ (v[2] ^ v[3]);
   const uint32_t f = x.x ^ x.y ^ x.z ^ x.w;
   if (f == 0x9E3779B9u && x.x == 0x7F4A7C15u) sink[0] = f;
+}
+
+__global__ void __launch_bounds__(256) stream_read_kernel(ReadSegs r, uint32_t* __restrict__ sink) {
+  int seg = 0;
+  while (seg + 1 < r.count && (int64_t)blockIdx.x >= r.first[seg + 1]) ++seg;
+  stream_read_body(r.ptr[seg], r.n16[seg], (int64_t)blockIdx.x - r.first[seg], sink);
+}
+
+__global__ void __launch_bounds__(256) stream_read_1(const u32x4* p, int64_t n, uint32_t* __restrict__ sink) {
+  stream_read_body(p, n, (int64_t)blockIdx.x, sink);
+}
+
+// the second buffer owns the workgroups from first1 on
+__global__ void __launch_bounds__(256) stream_read_2(const u32x4* p0, const u32x4* p1, int64_t n0,
+                                                     int64_t n1, int64_t first1,
+                                                     uint32_t* __restrict__ sink) {
+  const bool second = (int64_t)blockIdx.x >= first1;
+  stream_read_body(second ? p1 : p0, second ? n1 : n0, (int64_t)blockIdx.x - (second ? first1 : 0),
+                   sink);
 }
 
 }  // namespace
@@ -151,7 +169,14 @@ hipError_t launch_stream_read(const void* const* src, const uint64_t* bytes, int
     r.first[i + 1] = r.first[i] + (r.n16[i] + 1023) / 1024;
   }
   if (r.first[count] == 0) return hipSuccess;
-  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)r.first[count]), dim3(256), 0, st, r, sink);
+  const dim3 grid((unsigned)r.first[count]);
+  if (count == 1)
+    hipLaunchKernelGGL(stream_read_1, grid, dim3(256), 0, st, r.ptr[0], r.n16[0], sink);
+  else if (count == 2 && r.n16[0] > 0 && r.n16[1] > 0)
+    hipLaunchKernelGGL(stream_read_2, grid, dim3(256), 0, st, r.ptr[0], r.ptr[1], r.n16[0], r.n16[1],
+                       r.first[1], sink);
+  else
+    hipLaunchKernelGGL(stream_read_kernel, grid, dim3(256), 0, st, r, sink);
   return hipGetLastError();
 }
 

@@ -491,22 +491,39 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 constexpr int kTeams = 4;  // row groups (teams of waves) per workgroup of the fp32 path
 constexpr int kNPT = 8 / kTeams;  // 16-byte pieces of A per thread
 
-// Up to NS weight matrices with the same K, block size and zero-point kind,
-// multiplied by the same A in one launch: segment i owns workgroups
-// [first[i], first[i + 1]).  NS is the segment count rounded up to 1, 2 or
-// 4, so a single-matrix launch passes 80 bytes of kernel arguments instead
-// of 200: the first replay of a graph of these launches (a short timed run)
-// measured 1.1 us less per five-launch step with the smaller arguments.
-template <int NS>
+// Up to kMaxSegs weight matrices with the same K, block size and zero-point
+// kind, multiplied by the same A in one launch: segment i owns workgroups
+// [first[i], first[i + 1]).  Used when the matrices differ in N or in the
+// placement of their sections; the common one- and two-matrix launches take
+// flat arguments instead (below).
 struct GemvSegs {
-  const uint8_t* codes[NS];
-  const float* scales[NS];
-  const uint32_t* zeros[NS];
-  float* Y[NS];
-  int32_t N[NS];
-  int32_t first[NS + 1];
+  const uint8_t* codes[kMaxSegs];
+  const float* scales[kMaxSegs];
+  const uint32_t* zeros[kMaxSegs];
+  float* Y[kMaxSegs];
+  int32_t N[kMaxSegs];
+  int32_t first[kMaxSegs + 1];
   int32_t count;
 };
+
+// Shape terms of the short-row kernels.  The launch passes K and the
+// block-size shift packed in one word (K < 2^16 on this path) and the
+// kernel derives the rest on the scalar unit: nb blocks, nsb = nb * bs / 32
+// sub-blocks, row_bytes = 16 * nsb (blocked rows), team = ceil(nsb / 64).
+struct F32Shape {
+  int K, nb, nsb, row_bytes, team, bs_shift;
+};
+
+__device__ __forceinline__ F32Shape f32_shape(uint32_t meta) {
+  F32Shape h;
+  h.K = (int)(meta & 0xFFFFu);
+  h.bs_shift = (int)(meta >> 16);
+  h.nb = (h.K + (32 << h.bs_shift) - 1) >> (5 + h.bs_shift);
+  h.nsb = h.nb << h.bs_shift;
+  h.row_bytes = h.nsb * 16;
+  h.team = (h.nsb + 63) >> 6;
+  return h;
+}
 
 // One-shot: every wave takes R consecutive rows of one K chunk, with 32-bit
 // index math throughout (the launcher checks that the codes of the matrix
@@ -518,26 +535,19 @@ struct GemvSegs {
 // sub-block's 128 bytes, so the 16 lanes served per LDS cycle hit 64
 // distinct banks.  The A loads are issued before the weight loads; loads
 // complete in order, so waiting for A does not wait for the weights.
-template <int R, bool HAS_ZP, int NS>
-__global__ void __launch_bounds__(1024) gemv_int4_f32(
-    const float* __restrict__ A, const GemvSegs<NS> sg, int32_t K, int32_t row_bytes, int32_t nb,
-    int32_t nsb, int32_t team, int32_t bs_shift) {
+// blk is the workgroup's index within its matrix.
+template <int R, bool HAS_ZP>
+__device__ __forceinline__ void gemv_f32_body(const float* __restrict__ A,
+                                              const uint8_t* __restrict__ codes,
+                                              const float* __restrict__ scales,
+                                              const uint32_t* __restrict__ zeros,
+                                              float* __restrict__ Y, const int N, const int blk,
+                                              const F32Shape h) {
   // A: 64 * team sub-blocks of 128 bytes (the launcher sizes it), then the
   // team partials
   extern __shared__ __align__(16) u32x4 as[];
+  const int team = h.team;
   float* tot = reinterpret_cast<float*>(as + 512 * team);
-
-  // this workgroup's segment (uniform)
-  int seg = 0;
-#pragma unroll
-  for (int i = 1; i < NS; ++i)
-    if (i < sg.count && (int)blockIdx.x >= sg.first[i]) seg = i;
-  const uint8_t* __restrict__ codes = sg.codes[seg];
-  const float* __restrict__ scales = sg.scales[seg];
-  const uint32_t* __restrict__ zeros = sg.zeros[seg];
-  float* __restrict__ Y = sg.Y[seg];
-  const int N = sg.N[seg];
-  const int blk = (int)blockIdx.x - sg.first[seg];
 
   const int tid = (int)threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -550,17 +560,18 @@ __global__ void __launch_bounds__(1024) gemv_int4_f32(
   // A pieces of this thread: tid + nt * u (past K: zeros); the workgroup's
   // nt = 256 team threads hold all 8 * 64 * team pieces of its K chunks
   const int nt = 64 * kTeams * team;
-  const __amdgpu_buffer_rsrc_t ra = buffer_over(A, (uint32_t)K * 4u);
+  const __amdgpu_buffer_rsrc_t ra = buffer_over(A, (uint32_t)h.K * 4u);
   u32x4 ap[kNPT];
 #pragma unroll
   for (int u = 0; u < kNPT; ++u)
     ap[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, 16u * (uint32_t)(tid + nt * u), 0, 0));
 
   const int sb = wit * 64 + lane;
-  const bool act = sb < nsb;
-  const uint32_t b = (uint32_t)sb >> bs_shift;
-  const __amdgpu_buffer_rsrc_t rc = buffer_over(codes, (uint32_t)N * (uint32_t)row_bytes);
-  const __amdgpu_buffer_rsrc_t rs = buffer_over(scales, (uint32_t)N * (uint32_t)nb * 4u);
+  const bool act = sb < h.nsb;
+  const uint32_t b = (uint32_t)sb >> h.bs_shift;
+  const uint32_t row_bytes = (uint32_t)h.row_bytes, nb = (uint32_t)h.nb;
+  const __amdgpu_buffer_rsrc_t rc = buffer_over(codes, (uint32_t)N * row_bytes);
+  const __amdgpu_buffer_rsrc_t rs = buffer_over(scales, (uint32_t)N * nb * 4u);
   u32x4 q[R];
   float s[R];
 #pragma unroll
@@ -573,7 +584,7 @@ __global__ void __launch_bounds__(1024) gemv_int4_f32(
   }
   uint32_t zpk = 0;  // zero point of row n0 + r in bits [4r, 4r + 4)
   if (HAS_ZP) {
-    const uint32_t zbytes = (uint32_t)((N + 7) >> 3) * (uint32_t)nb * 4u;
+    const uint32_t zbytes = (uint32_t)((N + 7) >> 3) * nb * 4u;
     zpk = __builtin_amdgcn_raw_buffer_load_b32(buffer_over(zeros, zbytes),
                                                act ? ((n0 >> 3) * nb + b) * 4u : kOutOfRange, 0, kNT) >>
           (4 * (n0 & 7));
@@ -625,6 +636,47 @@ __global__ void __launch_bounds__(1024) gemv_int4_f32(
       if (n0 + lane < N) Y[n0 + lane] = out;
     }
   }
+}
+
+// Workgroups per matrix of N rows.
+__host__ __device__ constexpr int f32_blocks(int N, int R) { return ((N + R - 1) / R + kTeams - 1) / kTeams; }
+
+// One or two matrices with flat arguments, at most 14 dwords, so that a
+// kernel built with kernel-argument preloading receives all of them in
+// SGPRs at wave launch instead of loading them first.  The sections of a
+// matrix are addressed from its codes: scales at codes + off_s, zero points
+// at codes + off_z.  With two matrices (same N, same section offsets), the
+// second owns the workgroups from f32_blocks(N) on.
+template <int R, bool HAS_ZP>
+__global__ void __launch_bounds__(1024) gemv_int4_f32(
+    const float* __restrict__ A, const uint8_t* __restrict__ codes, float* __restrict__ Y,
+    int32_t N, uint32_t meta, uint32_t off_s, uint32_t off_z) {
+  gemv_f32_body<R, HAS_ZP>(A, codes, reinterpret_cast<const float*>(codes + off_s),
+                           reinterpret_cast<const uint32_t*>(codes + off_z), Y, N,
+                           (int)blockIdx.x, f32_shape(meta));
+}
+
+template <int R, bool HAS_ZP>
+__global__ void __launch_bounds__(1024) gemv_int4_f32_pair(
+    const float* __restrict__ A, const uint8_t* codes0, const uint8_t* codes1, float* Y0,
+    float* Y1, int32_t N, uint32_t meta, uint32_t off_s, uint32_t off_z) {
+  const int per = f32_blocks(N, R);
+  const bool second = (int)blockIdx.x >= per;
+  const uint8_t* codes = second ? codes1 : codes0;
+  gemv_f32_body<R, HAS_ZP>(A, codes, reinterpret_cast<const float*>(codes + off_s),
+                           reinterpret_cast<const uint32_t*>(codes + off_z), second ? Y1 : Y0, N,
+                           (int)blockIdx.x - (second ? per : 0), f32_shape(meta));
+}
+
+template <int R, bool HAS_ZP>
+__global__ void __launch_bounds__(1024) gemv_int4_f32_segs(const float* __restrict__ A,
+                                                           const GemvSegs sg, uint32_t meta) {
+  int seg = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxSegs; ++i)
+    if (i < sg.count && (int)blockIdx.x >= sg.first[i]) seg = i;
+  gemv_f32_body<R, HAS_ZP>(A, sg.codes[seg], sg.scales[seg], sg.zeros[seg], sg.Y[seg], sg.N[seg],
+                           (int)blockIdx.x - sg.first[seg], f32_shape(meta));
 }
 
 // K > 8192: digits precomputed in the workspace, each wave walks its chunks.
@@ -722,14 +774,49 @@ hipError_t launch_fused(const Sizes& s, const mnb_plan& p, const float* A, float
   return hipGetLastError();
 }
 
-// s: the shape shared by the segments (K, block size, zero-point kind);
-// segment i multiplies plan p[i] (N = N[i]) into Y[i]
-template <int R, bool HAS_ZP, int NS>
-hipError_t launch_f32_segs_n(const Sizes& s, const mnb_plan* const* p, const int64_t* N, int count,
-                             const float* A, float* const* Y, int64_t nsb, int64_t nchunk,
-                             hipStream_t st) {
+// Byte offset of section `sec` from the codes of plan p, if it fits the
+// 32-bit offset of the flat launches (always, for plans made by
+// mnb_prepare: the sections follow the codes, 256-byte aligned).
+bool section_offset(const mnb_plan& p, const void* sec, uint32_t* off) {
+  if (!sec) {
+    *off = 0;
+    return true;
+  }
+  const uintptr_t c = reinterpret_cast<uintptr_t>(p.codes), v = reinterpret_cast<uintptr_t>(sec);
+  if (v < c || v - c > 0xFFFFFF00u || (v - c) % 4) return false;
+  *off = (uint32_t)(v - c);
+  return true;
+}
+
+// s: the shape shared by the matrices (K, block size, zero-point kind);
+// matrix i multiplies plan p[i] (N = N[i]) into Y[i]
+template <int R, bool HAS_ZP>
+hipError_t launch_f32_segs(const Sizes& s, const mnb_plan* const* p, const int64_t* N, int count,
+                           const float* A, float* const* Y, int64_t nsb, int64_t nchunk,
+                           hipStream_t st) {
   const int team = (int)nchunk;
-  GemvSegs<NS> sg{};
+  const uint32_t meta = (uint32_t)s.K | ((uint32_t)bs_shift_of(s) << 16);
+  const size_t lds = (size_t)team * 8192 + (size_t)kTeams * team * R * 4;
+  const dim3 threads(64 * kTeams * team);
+  (void)nsb;
+  uint32_t os[2], oz[2];
+  bool flat = count <= 2;
+  for (int i = 0; i < count && flat; ++i)
+    flat = section_offset(*p[i], p[i]->scales, &os[i]) && section_offset(*p[i], HAS_ZP ? p[i]->zeros : nullptr, &oz[i]);
+  if (flat && count == 1) {
+    hipLaunchKernelGGL((gemv_int4_f32<R, HAS_ZP>), dim3((unsigned)f32_blocks((int)N[0], R)), threads, lds,
+                       st, A, static_cast<const uint8_t*>(p[0]->codes), Y[0], (int32_t)N[0], meta,
+                       os[0], oz[0]);
+    return hipGetLastError();
+  }
+  if (flat && count == 2 && N[0] == N[1] && os[0] == os[1] && oz[0] == oz[1]) {
+    hipLaunchKernelGGL((gemv_int4_f32_pair<R, HAS_ZP>), dim3((unsigned)(2 * f32_blocks((int)N[0], R))),
+                       threads, lds, st, A, static_cast<const uint8_t*>(p[0]->codes),
+                       static_cast<const uint8_t*>(p[1]->codes), Y[0], Y[1], (int32_t)N[0], meta,
+                       os[0], oz[0]);
+    return hipGetLastError();
+  }
+  GemvSegs sg{};
   sg.count = count;
   int64_t blocks = 0;
   for (int i = 0; i < count; ++i) {
@@ -739,23 +826,12 @@ hipError_t launch_f32_segs_n(const Sizes& s, const mnb_plan* const* p, const int
     sg.Y[i] = Y[i];
     sg.N[i] = (int32_t)N[i];
     sg.first[i] = (int32_t)blocks;
-    blocks += ((N[i] + R - 1) / R + kTeams - 1) / kTeams;
+    blocks += f32_blocks((int)N[i], R);
   }
   sg.first[count] = (int32_t)blocks;
-  const size_t lds = (size_t)team * 8192 + (size_t)kTeams * team * R * 4;
-  hipLaunchKernelGGL((gemv_int4_f32<R, HAS_ZP, NS>), dim3((unsigned)blocks), dim3(64 * kTeams * team),
-                     lds, st, A, sg, (int32_t)s.K, (int32_t)s.row_bytes, (int32_t)s.nb,
-                     (int32_t)nsb, team, bs_shift_of(s));
+  hipLaunchKernelGGL((gemv_int4_f32_segs<R, HAS_ZP>), dim3((unsigned)blocks), threads, lds, st, A, sg,
+                     meta);
   return hipGetLastError();
-}
-
-template <int R, bool HAS_ZP>
-hipError_t launch_f32_segs(const Sizes& s, const mnb_plan* const* p, const int64_t* N, int count,
-                           const float* A, float* const* Y, int64_t nsb, int64_t nchunk,
-                           hipStream_t st) {
-  if (count == 1) return launch_f32_segs_n<R, HAS_ZP, 1>(s, p, N, count, A, Y, nsb, nchunk, st);
-  if (count == 2) return launch_f32_segs_n<R, HAS_ZP, 2>(s, p, N, count, A, Y, nsb, nchunk, st);
-  return launch_f32_segs_n<R, HAS_ZP, kMaxSegs>(s, p, N, count, A, Y, nsb, nchunk, st);
 }
 
 template <int R, bool HAS_ZP>

@@ -215,7 +215,7 @@ def test_gemv_non_finite_activation_poisons_output(K, N, zp, bad):
 @pytest.mark.parametrize("K,Ns,bs,zp", [
     (2048, (6144, 6144), 32, False), (2050, (1024, 37, 300), 32, True),
     (6144, (2048, 100), 64, False), (4096, (7, 513, 64, 2000), 128, True),
-    (256, (40000, 33), 32, False)])
+    (256, (40000, 33), 32, False), (2050, (300, 300), 32, True), (6144, (2048, 2048), 64, True)])
 def test_gemv_multi_matches_separate_calls(orc, K, Ns, bs, zp):
     say(f"gemv multi K={K} Ns={Ns} bs={bs} zp={zp}")
     ws_, hosts = [], []
@@ -293,5 +293,15 @@ def test_stream_read_ceiling_kernel_reads_its_buffers():
     mnb.mnb_debug_stream_read([(big, big.numel() * 4), (hit, 64), (big, 16 * 1000)], sink)
     torch.cuda.synchronize()
     assert int(sink.cpu().numpy().view(np.uint32)[0]) == 0x9E3779B9
+    # two buffers (the flat two-segment launch): the sentinel in either one,
+    # and an empty first buffer (segment table launch)
+    for pair in ([(big, 16 * 3000), (hit, 64)], [(hit, 64), (big, 16 * 3000)], [(big, 0), (hit, 64)]):
+        sink.zero_()
+        mnb.mnb_debug_stream_read([(big, big.numel() * 4), (big, 16 * 1000)], sink)
+        torch.cuda.synchronize()
+        assert int(sink.item()) == 0
+        mnb.mnb_debug_stream_read(pair, sink)
+        torch.cuda.synchronize()
+        assert int(sink.cpu().numpy().view(np.uint32)[0]) == 0x9E3779B9
     with pytest.raises(mnb.MnbError):
         mnb.mnb_debug_stream_read([(big, 20)], sink)
