@@ -429,8 +429,8 @@ bool fast_ok(const Sizes& s, int64_t M, const void* A) {
 }
 
 struct Plan {
-  bool lds;         // the LDS-streaming kernel (gemm_lds.hip), bm x bm tiles
-  int bm;
+  bool lds;         // the LDS-streaming kernel (gemm_lds.hip), bm x (128 tn) tiles
+  int bm, tn;
   int64_t n_split;  // > 0: 256 x 256 tiles below this column, 256 x 128 above
   int cfg;          // else: index into the configuration table below
   int64_t tiles_n, tiles;
@@ -491,11 +491,25 @@ Plan choose(const Sizes& s, int64_t M, bool fast) {
     Plan p;
     p.lds = true;
     p.bm = ((M + 127) / 128) * ((N + 127) / 128) <= kLds128MaxTiles ? 128 : 256;
+    p.tn = p.bm / 128;
     p.cfg = -1;
     p.tiles_n = (N + p.bm - 1) / p.bm;
     p.tiles = ((M + p.bm - 1) / p.bm) * p.tiles_n;
     p.n_split = p.bm == 256 ? mixed_split(s, M) : 0;
     if (p.n_split > 0) {  // no split of K: the tiles already fill the chip
+      p.splits = 1;
+      p.kc = s.K;
+      return p;
+    }
+    // too few 256 x 256 tiles for the chip, enough 256 x 128 ones: those,
+    // over the whole of K, instead of splitting K (no partials, no reduce;
+    // at M = 4096, K = 6144, N = 2048: 256 narrow tiles against 128 wide
+    // tiles split in two)
+    const int64_t narrow = ((M + 255) / 256) * ((N + 127) / 128);
+    if (p.bm == 256 && p.tiles < kTargetWork * 3 / 4 && narrow >= kTargetWork * 3 / 4) {
+      p.tn = 1;
+      p.tiles_n = (N + 127) / 128;
+      p.tiles = narrow;
       p.splits = 1;
       p.kc = s.K;
       return p;
@@ -524,6 +538,7 @@ Plan choose(const Sizes& s, int64_t M, bool fast) {
   Plan p;
   p.lds = false;
   p.bm = 0;
+  p.tn = 0;
   p.n_split = 0;
   p.cfg = c;
   p.tiles_n = (N + kCfgs[c].bn - 1) / kCfgs[c].bn;
@@ -596,7 +611,7 @@ hipError_t launch_gemm(const Sizes& s, const mnb_plan& p, int64_t M, const float
                       ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
                                                  gemm_lds_a16_bytes(s, M))
                       : nullptr;
-    e = launch_gemm_lds(s, p, M, A, ws, Y, part, pl.splits, pl.kc, pl.bm, pl.n_split, st);
+    e = launch_gemm_lds(s, p, M, A, ws, Y, part, pl.splits, pl.kc, pl.bm, pl.tn, pl.n_split, st);
     if (e != hipSuccess || pl.splits == 1) return e;
     const int64_t MN = M * s.N;
     hipLaunchKernelGGL(gemm_splitk_reduce, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, st,

@@ -429,7 +429,7 @@ uint64_t gemm_lds_a16_bytes(const Sizes& s, int64_t M) {
 
 hipError_t launch_gemm_lds(const Sizes& s, const mnb_plan& p, int64_t M, const float* A,
                            void* ws, float* Y, float* part, int32_t splits, int64_t kc, int bm,
-                           int64_t n_split, hipStream_t st) {
+                           int tn, int64_t n_split, hipStream_t st) {
   _Float16* A16 = static_cast<_Float16*>(ws);
   const int64_t n8 = M * s.K / 8;
   hipLaunchKernelGGL(round_a_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, A, A16,
@@ -438,6 +438,7 @@ hipError_t launch_gemm_lds(const Sizes& s, const mnb_plan& p, int64_t M, const f
     return s.zeros ? launch_mix<true, 256, 2, 1>(s, p, M, A16, Y, n_split, st)
                    : launch_mix<false, 256, 2, 1>(s, p, M, A16, Y, n_split, st);
   if (bm == 128) return launch_tile_zp<128, 1>(s, p, M, A16, Y, part, splits, kc, st);
+  if (bm == 256 && tn == 1) return launch_tile_zp<256, 1>(s, p, M, A16, Y, part, splits, kc, st);
   if (bm == 256) return launch_tile_zp<256, 2>(s, p, M, A16, Y, part, splits, kc, st);
   return hipErrorInvalidValue;
 }

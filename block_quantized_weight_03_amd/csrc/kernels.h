@@ -35,12 +35,12 @@ hipError_t launch_gemm_small(const Sizes& s, const mnb_plan& p, int64_t M, const
 // its workspace starts with an fp16 copy of A, then the split partials
 bool gemm_lds_supported(const Sizes& s, int64_t M);
 uint64_t gemm_lds_a16_bytes(const Sizes& s, int64_t M);
-// (bm x bm tiles, 256 or 128; with n_split > 0, which requires bm = 256 and
-// splits = 1, 256 x 256 tiles over columns [0, n_split) and 256 x 128 tiles
-// over the rest, in one launch)
+// (bm x (128 tn) tiles: 128 x 128, 256 x 256 or 256 x 128; with n_split > 0,
+// which requires bm = 256 and splits = 1, 256 x 256 tiles over columns
+// [0, n_split) and 256 x 128 tiles over the rest, in one launch)
 hipError_t launch_gemm_lds(const Sizes& s, const mnb_plan& p, int64_t M, const float* A,
                            void* ws, float* Y, float* part, int32_t splits, int64_t kc, int bm,
-                           int64_t n_split, hipStream_t st);
+                           int tn, int64_t n_split, hipStream_t st);
 
 // ---- QMoE with INT3 / INT4 projections, fp16 or bf16 (qmoe.hip) ----------
 struct QmoeDebug {

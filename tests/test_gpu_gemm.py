@@ -134,14 +134,16 @@ def test_gemm_rows_are_independent(M, lo, hi):
 
 
 # M >= 128 with K a multiple of 64 takes the LDS-streaming kernel (128 x 128
-# tiles while there are at most 384 of them, else 256 x 256): ragged M and N
-# tails, one-stage K, every block size, zero points, split K, on both tile
-# sizes (the last three cases have more than 384 tiles of 128 x 128).
+# tiles while there are at most 384 of them, else 256 x 256, or 256 x 128
+# over the whole of K where too few 256 x 256 tiles would need split K):
+# ragged M and N tails, one-stage K, every block size, zero points, split K,
+# on every tile shape (the last four cases have more than 384 tiles of
+# 128 x 128 and take the 256 x 128 tiles).
 @pytest.mark.parametrize("M,K,N,bs,zp", [
     (1100, 320, 700, 64, True), (1025, 64, 33, 32, False), (1030, 384, 257, 128, True),
     (1300, 192, 1000, 32, False), (1040, 4096, 300, 128, True), (600, 320, 700, 64, True),
     (2048, 4096, 130, 128, False), (2100, 64, 3000, 32, True), (2600, 128, 2500, 64, False),
-    (4100, 320, 1600, 128, True)])
+    (4100, 320, 1600, 128, True), (4000, 320, 1900, 64, True)])
 def test_gemm_large_m_ragged_elementwise(orc, M, K, N, bs, zp):
     say(f"gemm large-M M={M} K={K} N={N} bs={bs} zp={zp}")
     w, B, s, Z = prepare(K, N, bs, zp, seed=M * 7 + K + N)
@@ -151,7 +153,7 @@ def test_gemm_large_m_ragged_elementwise(orc, M, K, N, bs, zp):
 
 
 @pytest.mark.parametrize("M,K,N,zp", [(128, 6144, 2048, False), (512, 6144, 2048, True),
-                                       (4096, 6144, 2048, False)])
+                                       (1024, 6144, 2048, False)])
 def test_gemm_split_k_reuses_a_dirty_workspace(orc, M, K, N, zp):
     """Split K on the LDS-streaming kernel (12, 4 and 2 splits here): one
     workspace, filled with 0xFF before the first call, serves three calls;
