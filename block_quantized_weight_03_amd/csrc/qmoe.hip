@@ -850,6 +850,29 @@ struct Stage2 {
   }
 };
 
+// The decode launches pass flat arguments (their leading ones, at most 14
+// dwords, arrive preloaded in SGPRs): the codes pointer with the scales at
+// codes + off_s, and the shape packed in two words, kn = K | N << 16 and
+// ek = E | top_k << 16 | bs_shift << 24 (bs = 32 << bs_shift; K, N and E below
+// 2^16 on this path).  The blocked row of BITS-bit codes holds K BITS / 8
+// bytes (K is a multiple of the block size).
+template <int BITS>
+__device__ __forceinline__ MoeGemmArgs decode_args(const uint8_t* codes, uint32_t off_s,
+                                                   const void* act, uint32_t kn, uint32_t ek) {
+  MoeGemmArgs g{};
+  g.codes = codes;
+  g.scales = reinterpret_cast<const uint16_t*>(codes + off_s);
+  g.act = act;
+  g.K = kn & 0xFFFFu;
+  g.N = kn >> 16;
+  g.E = (int)(ek & 0xFFFFu);
+  g.top_k = (int)((ek >> 16) & 0xFFu);
+  g.bs = 32 << (ek >> 24);
+  g.row_bytes = g.K * BITS / 8;
+  g.nblk = g.K / g.bs;
+  return g;
+}
+
 __device__ __forceinline__ TileRef tile_ref(const MoeGemmArgs& g, int e, int row0, int lane) {
   TileRef t;
   t.N = (int)g.N;
@@ -875,10 +898,17 @@ __device__ __forceinline__ TileRef tile_ref(const MoeGemmArgs& g, int e, int row
 // fixed order and h[slot I + 8 tile + m] = fp16(silu(g_m) u_m) for gate row
 // 2m, up row 2m + 1.
 template <int kPer, bool ROUTE, int BITS, bool BF>
-__global__ void __launch_bounds__(256) qmoe_fc1_decode(MoeGemmArgs g, int64_t T,
+__global__ void __launch_bounds__(256) qmoe_fc1_decode(const void* __restrict__ act,
                                                        const float* __restrict__ logits,
+                                                       const uint8_t* __restrict__ codes,
+                                                       uint16_t* __restrict__ h_out, uint32_t off_s,
+                                                       uint32_t kn, uint32_t ek,
                                                        int32_t* __restrict__ ids,
-                                                       float* __restrict__ wts) {
+                                                       float* __restrict__ wts,
+                                                       const uint16_t* __restrict__ bias) {
+  MoeGemmArgs g = decode_args<BITS>(codes, off_s, act, kn, ek);
+  g.h_out = h_out;
+  g.bias = bias;
   extern __shared__ __align__(16) uint8_t sm[];
   const int K = (int)g.K, N = (int)g.N, I = N / 2, ntile = N >> 4, k = g.top_k;
   _Float16* xs = reinterpret_cast<_Float16*>(sm);
@@ -940,8 +970,18 @@ __global__ void __launch_bounds__(256) qmoe_fc1_decode(MoeGemmArgs g, int64_t T,
 // expert ids[t, j]'s tile rows, then out[t, n] = fp16(sum_j r_j y_j[n]) with
 // y_j and the rank sum in fixed orders.
 template <int BITS, bool BF>
-__global__ void __launch_bounds__(1024) qmoe_fc2_decode(MoeGemmArgs g, int64_t T, uint16_t* out,
-                                                        float* slot_dbg) {
+__global__ void __launch_bounds__(1024) qmoe_fc2_decode(const void* __restrict__ act,
+                                                        const int32_t* __restrict__ ids,
+                                                        const uint8_t* __restrict__ codes,
+                                                        const float* __restrict__ wts,
+                                                        uint16_t* __restrict__ out, uint32_t off_s,
+                                                        uint32_t kn, uint32_t ek,
+                                                        const uint16_t* __restrict__ bias,
+                                                        float* __restrict__ slot_dbg) {
+  MoeGemmArgs g = decode_args<BITS>(codes, off_s, act, kn, ek);
+  g.perm = ids;
+  g.wts = wts;
+  g.bias = bias;
   extern __shared__ __align__(16) uint8_t sm[];
   const int H = (int)g.N, I = (int)g.K, k = g.top_k, ntile = H >> 3;  // 8-row tiles
   _Float16* hs = reinterpret_cast<_Float16*>(sm);
@@ -1092,6 +1132,15 @@ void launch_route(const float* logits, int64_t T, int E, int k, int32_t* ids, fl
 
 }  // namespace
 
+// Byte offset of a plan's scales from its codes for the flat decode
+// launches (the sections of a plan made by mnb_prepare follow the codes).
+bool scales_offset(const mnb_plan& p, uint32_t* off) {
+  const uintptr_t c = reinterpret_cast<uintptr_t>(p.codes), v = reinterpret_cast<uintptr_t>(p.scales);
+  if (v < c || v - c > 0xFFFFFF00u || (v - c) % 2) return false;
+  *off = (uint32_t)(v - c);
+  return true;
+}
+
 bool qmoe_supported(const Sizes& s1, const Sizes& s2, int top_k) {
   // the grouping kernel's per-expert histograms and the routing kernels'
   // register-held top-k bound E and k; in-expert code offsets are 32-bit
@@ -1127,12 +1176,16 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
 
   // few tokens: per-slot GEMVs, no grouping (every slot reads its expert once);
   // the activation rows they stage in LDS bound H and k * I
-  if (T * k <= kDecodeSlots && H <= 16384 && k * I <= 16384) {
+  uint32_t os1, os2;
+  if (T * k <= kDecodeSlots && H <= 16384 && k * I <= 16384 &&
+      scales_offset(p1, &os1) && scales_offset(p2, &os2)) {
     const int64_t S = T * k;
-    MoeGemmArgs a1{static_cast<const uint8_t*>(p1.codes), static_cast<const uint16_t*>(p1.scales),
-                   x, s1.N, s1.K, s1.row_bytes, s1.nb, s1.bs, k, (int)E,
-                   nullptr, nullptr, ids, nullptr, nullptr, wts, hbuf, nullptr,
-                   b1};
+    const uint32_t ek = (uint32_t)E | ((uint32_t)k << 16);
+    const uint32_t kn1 = (uint32_t)s1.K | ((uint32_t)s1.N << 16), kn2 = (uint32_t)s2.K | ((uint32_t)s2.N << 16);
+    const uint32_t ek1 = ek | ((uint32_t)(s1.bs == 32 ? 0 : (s1.bs == 64 ? 1 : 2)) << 24);
+    const uint32_t ek2 = ek | ((uint32_t)(s2.bs == 32 ? 0 : (s2.bs == 64 ? 1 : 2)) << 24);
+    const uint8_t* c1 = static_cast<const uint8_t*>(p1.codes);
+    const uint8_t* c2 = static_cast<const uint8_t*>(p2.codes);
     const dim3 g1((unsigned)(S * (s1.N / 16))), wg1(256);
     const size_t l1 = (size_t)(2 * H + 4 * 256 + 128);
     if (S > kFusedRouteSlots) launch_route(logits, T, (int)E, k, ids, wts, st);
@@ -1140,24 +1193,20 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
       constexpr int B = decltype(bits)::value;
       constexpr bool BF = decltype(bfc)::value;
       if (S > kFusedRouteSlots)
-        hipLaunchKernelGGL((qmoe_fc1_decode<2, false, B, BF>), g1, wg1, l1, st, a1, T, logits, ids, wts);
+        hipLaunchKernelGGL((qmoe_fc1_decode<2, false, B, BF>), g1, wg1, l1, st, x, logits, c1, hbuf, os1, kn1, ek1, ids, wts, b1);
       else if (E <= 128)
-        hipLaunchKernelGGL((qmoe_fc1_decode<2, true, B, BF>), g1, wg1, l1, st, a1, T, logits, ids, wts);
+        hipLaunchKernelGGL((qmoe_fc1_decode<2, true, B, BF>), g1, wg1, l1, st, x, logits, c1, hbuf, os1, kn1, ek1, ids, wts, b1);
       else if (E <= 256)
-        hipLaunchKernelGGL((qmoe_fc1_decode<4, true, B, BF>), g1, wg1, l1, st, a1, T, logits, ids, wts);
+        hipLaunchKernelGGL((qmoe_fc1_decode<4, true, B, BF>), g1, wg1, l1, st, x, logits, c1, hbuf, os1, kn1, ek1, ids, wts, b1);
       else
-        hipLaunchKernelGGL((qmoe_fc1_decode<kMaxE / 64, true, B, BF>), g1, wg1, l1, st, a1, T, logits, ids, wts);
+        hipLaunchKernelGGL((qmoe_fc1_decode<kMaxE / 64, true, B, BF>), g1, wg1, l1, st, x, logits, c1, hbuf, os1, kn1, ek1, ids, wts, b1);
     });
-    MoeGemmArgs a2{static_cast<const uint8_t*>(p2.codes), static_cast<const uint16_t*>(p2.scales),
-                   hbuf, s2.N, s2.K, s2.row_bytes, s2.nb, s2.bs, k, (int)E,
-                   nullptr, nullptr, ids, nullptr, nullptr, wts, nullptr, nullptr,
-                   b2};
     by_kind(s2.bits, bf, [&](auto bits, auto bfc) {
       constexpr int B = decltype(bits)::value;
       constexpr bool BF = decltype(bfc)::value;
       hipLaunchKernelGGL((qmoe_fc2_decode<B, BF>), dim3((unsigned)(T * (H / 8))), dim3(64 * k),
-                         (size_t)(2 * k * I + 4 * 64 * k), st, a2, T, out,
-                         dbg ? dbg->slot : nullptr);
+                         (size_t)(2 * k * I + 4 * 64 * k), st, hbuf, ids, c2, wts, out, os2, kn2, ek2,
+                         b2, dbg ? dbg->slot : nullptr);
     });
     if (dbg) {
       hipError_t e = hipSuccess;
