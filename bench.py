@@ -13,12 +13,14 @@ them from HBM rather than from the 256 MB Infinity Cache.  The timed steps are
 replayed from a HIP graph (launch overhead of the Python binding excluded) and
 bracketed by torch.cuda.synchronize() on both sides.
 
-Exactly `--warmup` untimed steps precede the `--steps` timed ones; the
-other workloads (vocabulary head, prefill GEMM, QMoE layers, quantizer) are
-measured first, each from graph replays of its own launches, so the short
-headline region starts at sustained clocks.  For context, `extra` also times
-the vendor BLAS (torch.matmul) on the prefill shapes with dense fp16 weights,
-after the headline region.  The roofline's average launch
+The other workloads (vocabulary head, prefill GEMM, QMoE layers, quantizer)
+are measured first, each from graph replays of its own launches; then the
+headline's weight copies are prepared (host repack and upload) and its graphs
+captured, and exactly `--warmup` untimed steps precede the `--steps` timed
+ones.  The timed steps continue the weight rotation where the warm-up
+stopped, so no timed step reads a copy that a warm-up step has just read.
+For context, `extra` also times the vendor BLAS (torch.matmul) on the prefill
+shapes with dense fp16 weights, after the headline region.  The roofline's average launch
 duration comes from HIP events recorded on the launch stream around the same
 timed graph replays (five GEMV kernel launches per step, back to back, so the
 average includes the short gaps between kernels); its ceiling is a plain
@@ -274,8 +276,7 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
 
-    # ---- the other workloads first (their own graphs; the GPU is then at its
-    # sustained clocks when the short headline region is timed) -------------
+    # ---- the other workloads first, each from its own graphs ----------------
     extra = {}
     if not args.no_extras:
         extra.update(bench_extras(torch, mnb, dev))
@@ -323,16 +324,19 @@ def main():
                 mnb.mnb_gemv(w.plan, acts[i][1], outs[i], gemv_ws, gemv_ws.numel())
 
     # captured without running: every step executes only as a warm-up or a
-    # timed step
-    full = Graph(torch, lambda: [step(c) for c in range(copies)], warm=False)
-    rem = args.steps % copies
-    part = Graph(torch, lambda: [step(c) for c in range(rem)], warm=False) if rem else None
+    # timed step.  The timed steps continue the rotation where the warm-up
+    # stopped (copy W mod copies), so no timed step reads a copy that a warm-up
+    # step has just read.
     wrem = args.warmup % copies
+    rem = args.steps % copies
     wpart = Graph(torch, lambda: [step(c) for c in range(wrem)], warm=False) if wrem else None
+    wfull = Graph(torch, lambda: [step(c) for c in range(copies)], warm=False)
+    full = Graph(torch, lambda: [step((wrem + c) % copies) for c in range(copies)], warm=False)
+    part = Graph(torch, lambda: [step((wrem + c) % copies) for c in range(rem)], warm=False) if rem else None
 
     # ---- exactly W warm-up steps, then exactly K timed steps ---------------
     for _ in range(args.warmup // copies):
-        full.replay()
+        wfull.replay()
     if wpart:
         wpart.replay()
     torch.cuda.synchronize()
@@ -431,7 +435,7 @@ def main():
            "GB/s": round(gemv_bytes(LAYER[o][1], LAYER[o][2]) / hot_us / 1e3, 1),
            "note": "one weight copy replayed, cache-resident: not an HBM figure"}
 
-    del full, part, wpart
+    del full, part, wpart, wfull
     torch.cuda.synchronize()
 
     extra = {"per_projection": per_proj, "step_spread": spread, "single_call_latency": single,
