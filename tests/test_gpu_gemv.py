@@ -305,3 +305,56 @@ def test_stream_read_ceiling_kernel_reads_its_buffers():
         assert int(sink.cpu().numpy().view(np.uint32)[0]) == 0x9E3779B9
     with pytest.raises(mnb.MnbError):
         mnb.mnb_debug_stream_read([(big, 20)], sink)
+
+
+def _relocated_plan(w):
+    """A copy of w's plan whose codes and scales sit in separate device
+    buffers with the scales below the codes, so the scales cannot be
+    addressed as an offset from the codes; returns (plan, buffers to keep),
+    or None if no arrangement of the copies gives that order."""
+    p = w.plan
+    cb, sb = p.codes_bytes, p.scales_bytes
+    base = w.buffer
+    off_s = p.scales - p.codes
+    codes_copy = base[:cb].clone()
+    scales_copy = base[off_s:off_s + sb].clone()
+    c_opts = [(p.codes, None), (codes_copy.data_ptr(), codes_copy)]
+    s_opts = [(p.scales, None), (scales_copy.data_ptr(), scales_copy)]
+    for c, ckeep in c_opts:
+        for s, skeep in s_opts:
+            if s < c:
+                q = mnb.mnb_plan.from_buffer_copy(p)
+                q.codes, q.scales = c, s
+                return q, [codes_copy, scales_copy]
+    return None
+
+
+@pytest.mark.parametrize("K,N,zp", [(2048, 300, False), (2050, 300, True), (6144, 128, False)])
+def test_gemv_plan_with_relocated_sections(K, N, zp):
+    """The short-row launches address a plan's scales and zero points as
+    offsets from its codes when they can; a plan whose sections lie
+    elsewhere (here: scales below the codes) takes the segment-table launch,
+    which computes the same bits, alone and as one matrix of a pair."""
+    say(f"gemv relocated plan sections K={K} N={N} zp={zp}")
+    w, *_ = prepare(K, N, zp=zp, seed=K + 7 * N)
+    r = _relocated_plan(w)
+    if r is None:
+        pytest.skip("the allocator placed every copy above the codes")
+    plan2, keep = r
+    a = synth.activations_f32(synth.seed_for(K, 77), 1, K)
+    A = torch.from_numpy(a.reshape(-1)).cuda()
+    ws = torch.empty(mnb.mnb_gemv_workspace_size(w.plan) + 256, dtype=torch.uint8, device="cuda")
+    y1 = torch.empty(N, dtype=torch.float32, device="cuda")
+    y2 = torch.empty(N, dtype=torch.float32, device="cuda")
+    mnb.mnb_gemv(w.plan, A, y1, ws, ws.numel())
+    mnb.mnb_gemv(plan2, A, y2, ws, ws.numel())
+    torch.cuda.synchronize()
+    assert np.array_equal(y1.cpu().numpy().view(np.uint32), y2.cpu().numpy().view(np.uint32))
+    # as one matrix of a same-shape pair (the pair launch needs equal offsets)
+    y3 = torch.empty(N, dtype=torch.float32, device="cuda")
+    y4 = torch.empty(N, dtype=torch.float32, device="cuda")
+    mnb.mnb_gemv_multi([w.plan, plan2], A, [y3, y4], ws, ws.numel())
+    torch.cuda.synchronize()
+    assert np.array_equal(y3.cpu().numpy().view(np.uint32), y1.cpu().numpy().view(np.uint32))
+    assert np.array_equal(y4.cpu().numpy().view(np.uint32), y1.cpu().numpy().view(np.uint32))
+    del keep

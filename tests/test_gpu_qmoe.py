@@ -553,3 +553,46 @@ def test_debug_unpack_and_dequant_qmoe_plans_bit_exact(orc, bits, bs, dtype):
         q = want.astype(np.float64) - (1 << (bits - 1))
         ref = to16(q * np.repeat(s64[e * N + row0:e * N + row0 + nrows], bs, axis=1))
         assert np.array_equal(deq.cpu().numpy().view(np.uint16), ref)
+
+
+class _PlanOnly:
+    def __init__(self, plan):
+        self.plan = plan
+
+
+def _relocated(pw):
+    """A copy of pw's plan with its codes and scales in separate device
+    buffers, the scales below the codes (so the flat decode launches cannot
+    address them from the codes); None if the allocator gives no such order."""
+    p = pw.plan
+    off_s = p.scales - p.codes
+    codes_copy = pw.buffer[:p.codes_bytes].clone()
+    scales_copy = pw.buffer[off_s:off_s + p.scales_bytes].clone()
+    for c in (p.codes, codes_copy.data_ptr()):
+        for s in (p.scales, scales_copy.data_ptr()):
+            if s < c:
+                q = mnb.mnb_plan.from_buffer_copy(p)
+                q.codes, q.scales = c, s
+                return q, [codes_copy, scales_copy]
+    return None
+
+
+@pytest.mark.parametrize("bits1,bits2", [(3, 3), (4, 4)])
+def test_qmoe_decode_with_relocated_plan_sections(orc, bits1, bits2):
+    """The decode launches address each plan's scales as an offset from its
+    codes; plans whose scales lie below their codes take the grouped path,
+    which matches the oracle as well."""
+    T, H, I, E, k, bs = 1, 256, 128, 16, 4, 32
+    say(f"qmoe relocated plan sections ({bits1},{bits2}) T={T}")
+    x, logits, m = random_moe(91 + bits1, T, H, I, E, k, bs, bits1, bits2)
+    r1, r2 = _relocated(m.p1), _relocated(m.p2)
+    if r1 is None or r2 is None:
+        pytest.skip("the allocator placed every copy above the codes")
+    keep = r1[1] + r2[1]
+    base = m.run(x, logits)
+    m.p1, m.p2 = _PlanOnly(r1[0]), _PlanOnly(r2[0])
+    res = m.run(x, logits)
+    o = m.oracle(orc, x, logits)
+    check_end_to_end(base["out"], o)
+    check_end_to_end(res["out"], o)
+    del keep
