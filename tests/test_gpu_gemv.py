@@ -125,11 +125,14 @@ def test_gemv_vocabulary_head_sampled(orc):
     check(orc, y, a, B, s, Z, K, N, 32, rows=rows)
 
 
-@pytest.mark.parametrize("K,N,zp", [(4096, 40000, False), (2050, 35001, True), (1024, 33000, False)])
+@pytest.mark.parametrize("K,N,zp", [(4096, 40000, False), (2050, 35001, True), (1024, 33000, False),
+                                    (2048, 32768, False), (2048, 32769, True), (8192, 32768, True)])
 def test_gemv_long_row_streams_sampled(orc, K, N, zp):
     """N > 32768: the in-kernel digit path with buffer-resource row loads (rows
-    past N and lanes past the last sub-block read zeros); first and last rows
-    plus a random sample against the oracle."""
+    past N and lanes past the last sub-block read zeros); N = 32768, the
+    largest short-row launch (also at K = 8192, four waves per row group),
+    and N = 32769, the smallest digit-path one; first and last rows plus a
+    random sample against the oracle."""
     say(f"gemv long rows K={K} N={N} zp={zp}")
     w, B, s, Z = prepare(K, N, zp=zp, seed=K + N)
     a = synth.activations_f32(synth.seed_for(K, N), 1, K)
