@@ -299,13 +299,14 @@ constexpr int lds_red_floats() {
   return kMaxTeam * R * 64 + kMaxTeam * R;
 }
 
-// Fused kernel: in-kernel digits, K <= 8192 (team = nchunk waves, one chunk each).
+// Fused kernel: in-kernel digits, K <= 8192 (team = nchunk waves, one chunk
+// each), workgroups of nwaves waves, grid workgroups.
 template <int R, bool HAS_ZP, bool BUF>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) gemv_int4_fused(
+__device__ __forceinline__ void gemv_fused_body(
     const float* __restrict__ A, const uint8_t* __restrict__ codes,
     const float* __restrict__ scales, const uint32_t* __restrict__ zeros, float* __restrict__ Y,
     int64_t K, int64_t N, int64_t row_bytes, int64_t nb, int32_t nsb, int32_t nchunk,
-    int32_t bs_shift, int64_t zrow) {
+    int32_t bs_shift, int64_t zrow, int nwaves, int64_t grid) {
   extern __shared__ __align__(16) uint32_t smem[];
   float* red_all = reinterpret_cast<float*>(smem);          // [4 waves][R][64]
   float* tot = red_all + kMaxTeam * R * 64;                  // [4 waves][R]
@@ -314,7 +315,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) g
   int32_t* nexp = sums + nchunk * (kDig / 2) * 64;           // [nchunk][64]
 
   const int team = nchunk;
-  const int nwaves = (int)(blockDim.x >> 6);
   const int teams = nwaves / team;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = (int)(threadIdx.x & 63);
@@ -326,7 +326,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) g
   const uint32_t b = (uint32_t)sb >> bs_shift;
 
   const int64_t nrg = (N + R - 1) / R;
-  const int64_t stride = (int64_t)gridDim.x * teams;
+  const int64_t stride = grid * teams;
   const int64_t base0 = (int64_t)blockIdx.x * teams;
   const int64_t iters = base0 < nrg ? (nrg - base0 + stride - 1) / stride : 0;
   int64_t rg = base0 + tm;
@@ -350,7 +350,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) g
 
   // digits of this workgroup's chunks, computed by all threads
   const int64_t tasks = (int64_t)nchunk * 64 * 4;
-  for (int64_t i = threadIdx.x; i < tasks; i += blockDim.x)
+  for (int64_t i = threadIdx.x; i < tasks; i += 64 * nwaves)
     make_digits(A, K, i >> 2, (int)(i & 3), dig, sums, nexp);
   __syncthreads();
   Digits g;
@@ -395,6 +395,34 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) g
     step(t0, t1, it);
     if (it + 1 < iters) step(t1, t0, it + 1);
   }
+}
+
+template <int R, bool HAS_ZP, bool BUF>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) gemv_int4_fused(
+    const float* __restrict__ A, const uint8_t* __restrict__ codes,
+    const float* __restrict__ scales, const uint32_t* __restrict__ zeros, float* __restrict__ Y,
+    int64_t K, int64_t N, int64_t row_bytes, int64_t nb, int32_t nsb, int32_t nchunk,
+    int32_t bs_shift, int64_t zrow) {
+  gemv_fused_body<R, HAS_ZP, BUF>(A, codes, scales, zeros, Y, K, N, row_bytes, nb, nsb, nchunk,
+                                  bs_shift, zrow, (int)(blockDim.x >> 6), (int64_t)gridDim.x);
+}
+
+// The same with flat arguments, all preloaded into SGPRs (10 dwords; the
+// block size follows from K as in the launcher and the grid size is an argument,
+// so no implicit argument is read either): scales and zero points at
+// codes + off_s and codes + off_z, meta = K | bs_shift << 16, blocked rows.
+// Used where 32-bit offsets cover the matrix (the buffer path).
+template <int R, bool HAS_ZP>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) gemv_int4_fused_flat(
+    const float* __restrict__ A, const uint8_t* __restrict__ codes, float* __restrict__ Y,
+    int32_t N, uint32_t meta, uint32_t off_s, uint32_t off_z, int32_t grid) {
+  const int K = (int)(meta & 0xFFFFu), bs_shift = (int)(meta >> 16);
+  const int nb = (K + (32 << bs_shift) - 1) >> (5 + bs_shift);
+  const int nsb = nb << bs_shift;
+  gemv_fused_body<R, HAS_ZP, true>(A, codes, reinterpret_cast<const float*>(codes + off_s),
+                                   reinterpret_cast<const uint32_t*>(codes + off_z), Y, K, N,
+                                   16 * nsb, nb, nsb, (nsb + 63) >> 6, bs_shift, 0,
+                                   kMaxTeam / ((nsb + 63) >> 6) * ((nsb + 63) >> 6), grid);
 }
 
 // ---- plain fp32 path for small N ----------------------------------------
@@ -749,6 +777,20 @@ int cu_count() {
   return cus;
 }
 
+// Byte offset of section `sec` from the codes of plan p, if it fits the
+// 32-bit offset of the flat launches (always, for plans made by
+// mnb_prepare: the sections follow the codes, 256-byte aligned).
+bool section_offset(const mnb_plan& p, const void* sec, uint32_t* off) {
+  if (!sec) {
+    *off = 0;
+    return true;
+  }
+  const uintptr_t c = reinterpret_cast<uintptr_t>(p.codes), v = reinterpret_cast<uintptr_t>(sec);
+  if (v < c || v - c > 0xFFFFFF00u || (v - c) % 4) return false;
+  *off = (uint32_t)(v - c);
+  return true;
+}
+
 template <int R, bool HAS_ZP>
 hipError_t launch_fused(const Sizes& s, const mnb_plan& p, const float* A, float* Y, int64_t nsb,
                         int64_t nchunk, hipStream_t st) {
@@ -766,26 +808,19 @@ hipError_t launch_fused(const Sizes& s, const mnb_plan& p, const float* A, float
   const int64_t cap = (int64_t)cu_count() * 4;
   if (blocks > cap) blocks = cap;
   const size_t lds = (size_t)lds_red_floats<R>() * 4 + (size_t)nchunk * (kDig * 4 * 64 + (kDig / 2) * 64 + 64) * 4;
+  uint32_t os, oz;
+  if (buf && section_offset(p, p.scales, &os) && section_offset(p, HAS_ZP ? p.zeros : nullptr, &oz)) {
+    hipLaunchKernelGGL((gemv_int4_fused_flat<R, HAS_ZP>), dim3((unsigned)blocks), dim3(threads), lds, st,
+                       A, static_cast<const uint8_t*>(p.codes), Y, (int32_t)s.N,
+                       (uint32_t)s.K | ((uint32_t)bs_shift_of(s) << 16), os, oz, (int32_t)blocks);
+    return hipGetLastError();
+  }
   auto kern = buf ? gemv_int4_fused<R, HAS_ZP, true> : gemv_int4_fused<R, HAS_ZP, false>;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(threads), lds, st,
                      A, static_cast<const uint8_t*>(p.codes), static_cast<const float*>(p.scales),
                      static_cast<const uint32_t*>(p.zeros), Y, s.K, s.N, s.row_bytes, s.nb,
                      (int32_t)nsb, (int32_t)nchunk, bs_shift_of(s), (int64_t)s.zrow);
   return hipGetLastError();
-}
-
-// Byte offset of section `sec` from the codes of plan p, if it fits the
-// 32-bit offset of the flat launches (always, for plans made by
-// mnb_prepare: the sections follow the codes, 256-byte aligned).
-bool section_offset(const mnb_plan& p, const void* sec, uint32_t* off) {
-  if (!sec) {
-    *off = 0;
-    return true;
-  }
-  const uintptr_t c = reinterpret_cast<uintptr_t>(p.codes), v = reinterpret_cast<uintptr_t>(sec);
-  if (v < c || v - c > 0xFFFFFF00u || (v - c) % 4) return false;
-  *off = (uint32_t)(v - c);
-  return true;
 }
 
 // s: the shape shared by the matrices (K, block size, zero-point kind);
