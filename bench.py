@@ -561,7 +561,12 @@ def bench_extras(torch, mnb, dev):
 def qmoe_extra(torch, mnb, dev, bits1, bits2, bf16=False, prep=None):
     """QMoE layer (hidden 2048, 128 experts, intermediate 768, top-8, block 64)
     at T = 1, 128, 512 tokens, from graph replays over 4 weight copies; fp16
-    or bfloat16 activations and scales."""
+    or bfloat16 activations and scales.  At T >= 128 every call routes to all
+    128 experts (about 1 GB over the copies); at T = 1 each copy is paired
+    with 8 router-logit sets, so that the 32 calls route to 52 distinct experts
+    per copy, 400 MB (INT3) to 520 MB (INT4), more than the 256 MB Infinity
+    Cache (the same 8 experts per copy would be 60 / 80 MB, which the cache
+    could hold across replays)."""
     H, I, E, k, bs = 2048, 768, 128, 8, 64
     scales = synth.scales_bf16 if bf16 else synth.scales_f16
     W1 = synth.packed_rows(synth.seed_for(5, 3), E * 2 * I, H, bits1)
@@ -589,14 +594,17 @@ def qmoe_extra(torch, mnb, dev, bits1, bits2, bf16=False, prep=None):
         else:
             xa = synth.activations_f16(synth.seed_for(5, 1), T, H)
         x = torch.from_numpy(xa).to(dev)
-        lg = torch.from_numpy(synth.router_logits(synth.seed_for(5, 2), T, E)).to(dev)
+        nlg = 8 if T == 1 else 1
+        lgs = [torch.from_numpy(synth.router_logits(synth.seed_for(5, 2 + 1000 * j), T, E)).to(dev)
+               for j in range(nlg)]
         o = torch.empty((T, H), dtype=torch.int16 if bf16 else torch.float16, device=dev)
         need = mnb.qmoe_workspace_size(experts[0][0].plan, experts[0][1].plan, q, T)
         qws = torch.empty(need, dtype=torch.uint8, device=dev)
         calls = [lambda p=p, x=x, lg=lg, o=o, qws=qws, T=T: mnb.qmoe_forward(
-            p[0].plan, p[1].plan, q, T, x, lg, o, qws, qws.numel()) for p in experts]
+            p[0].plan, p[1].plan, q, T, x, lg, o, qws, qws.numel()) for lg in lgs for p in experts]
         us = 1e3 * graph_time(torch, calls, 5)
-        ids = torch.topk(lg.float(), k, dim=1).indices.unique().numel()  # distinct experts routed
+        # distinct experts routed per call (averaged over the logit sets)
+        ids = sum(torch.topk(lg.float(), k, dim=1).indices.unique().numel() for lg in lgs) / nlg
         byts = ids * per_expert
         moe[f"T{T}"] = {"us": round(us, 2), "distinct_experts": ids,
                         "weight_GB/s": round(byts / us / 1e3, 1),
