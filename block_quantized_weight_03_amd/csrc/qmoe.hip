@@ -458,8 +458,10 @@ struct MoeGemmArgs {
 constexpr int kQBN = 64;         // weight rows per workgroup
 constexpr int kQBK = 128;        // K per chunk
 constexpr int kQPitch = kQBK + 8;
-// 64-row weight tiles per workgroup: with 64-token tiles 2 (their
-// accumulators would otherwise cost occupancy); with 32-token tiles 2 for
+// 64-row weight tiles per workgroup: with 48- and 64-token tiles 2 (their
+// accumulators would otherwise cost occupancy; 48-token tiles measured at 512
+// tokens with three: INT3 unchanged, INT4 13% slower; with four: 5% slower);
+// with 32-token tiles 2 for
 // INT3 and 4 for INT4 (measured at 128 tokens against four tiles: INT3
 // 95.6 -> 92.9 us and bf16 113.7 -> 107.9 with two; INT4 with two 103.4 us,
 // with four 98.3, so INT4 keeps four)
@@ -625,7 +627,7 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
   };
 
   // kWS register stages of weights: chunk c is dequantized from stage
-  // c % kWS, which then takes chunk c + kWS.  With 64-token items (many
+  // c % kWS, which then takes chunk c + kWS.  With 48- and 64-token items (many
   // workgroups per CU, each weight feeding more MFMAs) two stages keep two
   // chunks of the HBM stream in flight per wave (measured 3-4% faster at 512
   // tokens); with 32-token items one stage is faster (measured 3-12% at 128
@@ -634,7 +636,7 @@ __global__ void __launch_bounds__(256) qmoe_gemm(MoeGemmArgs g, int64_t groups_n
   // For two stages the chunk loop is unrolled by two so that each stage keeps
   // its registers (moving a register whose load is in flight would wait for
   // it).
-  constexpr int kWS = BM == 64 ? 2 : 1;
+  constexpr int kWS = BM >= 48 ? 2 : 1;
   WStage w0[kNTG], w1[kNTG];
 #pragma unroll
   for (int t = 0; t < kNTG; ++t) load_w(w0[t], t, 0);
@@ -1068,8 +1070,11 @@ int64_t max_items(int64_t Tt, int k, int64_t E, int bm) {
 }
 
 // Token tile of the work items: about the expected tokens per expert, so a
-// weight tile is dequantized once for all of an expert's tokens.
-int pick_bm(int64_t Tt, int k, int64_t E) { return Tt * k <= 24 * E ? 32 : kMaxBM; }
+// weight tile is dequantized once for all of an expert's tokens, with as few
+// padding rows as the 16-token MFMA tiles allow (at 512 tokens, top-8 of 128
+// experts, about 32 tokens per expert: 48-token items measured 4% faster than
+// 64-token ones, INT3 and INT4).
+int pick_bm(int64_t Tt, int k, int64_t E) { return Tt * k <= 24 * E ? 32 : (Tt * k <= 40 * E ? 48 : kMaxBM); }
 
 Ws ws_layout(const Sizes& s1, const Sizes& s2, int k, int64_t T) {
   const int64_t Tt = T < kTokTile ? T : kTokTile;
@@ -1238,6 +1243,8 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
       constexpr bool BF = decltype(bfc)::value;
       if (bm == 32)
         hipLaunchKernelGGL((qmoe_gemm<true, 32, B, BF>), grid1, dim3(256), 0, st, a1, ng1, nt1);
+      else if (bm == 48)
+        hipLaunchKernelGGL((qmoe_gemm<true, 48, B, BF>), grid1, dim3(256), 0, st, a1, ng1, nt1);
       else
         hipLaunchKernelGGL((qmoe_gemm<true, kMaxBM, B, BF>), grid1, dim3(256), 0, st, a1, ng1, nt1);
     });
@@ -1252,6 +1259,8 @@ hipError_t launch_qmoe(const Sizes& s1, const mnb_plan& p1, const Sizes& s2, con
       constexpr bool BF = decltype(bfc)::value;
       if (bm == 32)
         hipLaunchKernelGGL((qmoe_gemm<false, 32, B, BF>), grid2, dim3(256), 0, st, a2, ng2, nt2);
+      else if (bm == 48)
+        hipLaunchKernelGGL((qmoe_gemm<false, 48, B, BF>), grid2, dim3(256), 0, st, a2, ng2, nt2);
       else
         hipLaunchKernelGGL((qmoe_gemm<false, kMaxBM, B, BF>), grid2, dim3(256), 0, st, a2, ng2, nt2);
     });

@@ -518,6 +518,28 @@ def test_qmoe_partial_last_tile_group(orc, bits1, bits2, dtype):
     check_stages(orc, m, res, o)
 
 
+# 48-token work items (24 E < T k <= 40 E).  The router logits favour expert 0
+# for two thirds of the tokens, so its tokens span three items (the last one
+# partial) next to single items of the others; H = 384 gives FC1 three K
+# chunks, so the two-stage weight loop ends on its first half, and I = 160
+# gives FC2 a partial last chunk.
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("bits1,bits2", [(3, 3), (4, 4), (3, 4)])
+def test_qmoe_48_token_items_with_a_hot_expert(orc, bits1, bits2, dtype):
+    T, H, I, E, k, bs = 150, 384, 160, 4, 1, 32
+    say(f"qmoe 48-token items ({bits1},{bits2}) {dtype} T={T} H={H} I={I} E={E} k={k}")
+    x, logits, m = random_moe(T + 3 * bits1 + bits2, T, H, I, E, k, bs, bits1, bits2,
+                              bias=(bits1 == 3), dtype=dtype)
+    logits = logits.copy()
+    logits[: 2 * T // 3, 0] += 8.0
+    res = m.run(x, logits, debug=True)
+    hot = int((res["ids"][:, 0] == 0).sum())
+    assert 96 < hot <= T, hot  # three items of expert 0
+    o = m.oracle(orc, x, logits)
+    check_end_to_end(res["out"], o, dtype)
+    check_stages(orc, m, res, o)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("bits", [3, 4])
 @pytest.mark.parametrize("bs", [32, 64, 128])
