@@ -143,7 +143,12 @@ def test_gemm_rows_are_independent(M, lo, hi):
     (1100, 320, 700, 64, True), (1025, 64, 33, 32, False), (1030, 384, 257, 128, True),
     (1300, 192, 1000, 32, False), (1040, 4096, 300, 128, True), (600, 320, 700, 64, True),
     (2048, 4096, 130, 128, False), (2100, 64, 3000, 32, True), (2600, 128, 2500, 64, False),
-    (4100, 320, 1600, 128, True), (4000, 320, 1900, 64, True)])
+    (4100, 320, 1600, 128, True), (4000, 320, 1900, 64, True),
+    # 256 x 256 tiles alone would need between one and two rounds: one launch of
+    # 256 x 256 tiles up to a column split and 256 x 128 tiles beyond it, here
+    # with zero points, a ragged last row block and (N = 4000) a partial last
+    # narrow column tile
+    (4100, 192, 4000, 64, True), (4500, 128, 4096, 32, True)])
 def test_gemm_large_m_ragged_elementwise(orc, M, K, N, bs, zp):
     say(f"gemm large-M M={M} K={K} N={N} bs={bs} zp={zp}")
     w, B, s, Z = prepare(K, N, bs, zp, seed=M * 7 + K + N)
