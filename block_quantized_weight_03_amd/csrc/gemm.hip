@@ -470,8 +470,9 @@ constexpr int64_t kLdsMinM = 128;
 constexpr int64_t kLds128MaxTiles = 384;
 
 // Columns covered by 256 x 256 tiles when the rest take 256 x 128 ones, so
-// that the wide tiles number at most one per CU and the narrow ones fill the
-// second round (0: one tile shape).  Used when 256 x 256 tiles alone would
+// that the wide tiles number at most one per CU and the two widths together
+// take about two rounds (the launch interleaves them in its dispatch order;
+// 0: one tile shape).  Used when 256 x 256 tiles alone would
 // need between one and two rounds with an idle remainder: at M = 4096, K =
 // 2048, N = 6144 (384 such tiles) 256 wide tiles plus 256 narrow ones took
 // 127 against 135 us.

@@ -46,6 +46,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 
 constexpr int kBK = 64;
 constexpr int kXcds = 8;
+constexpr int64_t kMixChunk = 128;  // blocks per class chunk in the mixed-width dispatch order
 
 // Tile BM x BN (BN = 128 TN): wave w computes all BM rows of columns
 // [32 TN w, 32 TN (w + 1)) as TM x TN tiles of 32 x 32.  The shapes used are
@@ -355,7 +356,25 @@ __global__ void __launch_bounds__(256) gemm_int4_lds_mix(
     int64_t work1) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int steps = (int)(K / kBK);
-  const int64_t b = blockIdx.x;
+  // Dispatch order: chunks of kMixChunk blocks of the two classes alternate
+  // while both last, then the rest of each class, so that a round holds both
+  // tile widths and the narrow tiles' outputs leave while wide tiles still
+  // compute (measured at M = 4096, K = 2048, N = 6144: 125.4/126.6 ->
+  // 123.4/123.8 us against all wide tiles first).  The chunk is a multiple
+  // of the XCD count, so a block keeps its XCD (b mod 8) and each class still
+  // reaches every XCD in contiguous runs.
+  int64_t b = blockIdx.x;
+  {
+    const int64_t blocks1 = (work1 + kXcds - 1) / kXcds * kXcds;
+    const int64_t mq = ((blocks0 < blocks1 ? blocks0 : blocks1) / kMixChunk) * kMixChunk;
+    if (b < 2 * mq) {
+      const int64_t c = (b / (2 * kMixChunk)) * kMixChunk + b % kMixChunk;
+      b = (b / kMixChunk) % 2 == 0 ? c : blocks0 + c;
+    } else {
+      const int64_t r = b - 2 * mq;
+      b = r < blocks0 - mq ? mq + r : blocks0 + mq + (r - (blocks0 - mq));
+    }
+  }
   if (b < blocks0) {
     const int64_t per = blocks0 / kXcds;
     const int64_t L = (b % kXcds) * per + b / kXcds;
