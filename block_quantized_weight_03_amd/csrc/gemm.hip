@@ -479,6 +479,14 @@ constexpr int64_t kLds128MaxTiles = 384;
 int64_t mixed_split(const Sizes& s, int64_t M) {
   const int64_t rows = (M + 255) / 256, cols = (s.N + 255) / 256;
   const int64_t tiles = rows * cols;
+  // Too few 256 x 256 tiles for one per CU, and 256 x 128 tiles alone would
+  // need a second, mostly idle round: as many wide column blocks as make
+  // both widths fit one round (M = 1536, N = 6144: 36 wide and 216 narrow
+  // tiles, 65.6 us against 82.1 us for 288 narrow ones).
+  if (tiles < kTargetWork * 3 / 4 && 2 * tiles > kTargetWork) {
+    const int64_t w = 2 * cols - kTargetWork / rows;
+    return w >= 1 && w < cols ? w * 256 : 0;
+  }
   if (tiles <= kTargetWork || tiles >= 2 * kTargetWork) return 0;
   const int64_t wide = kTargetWork / rows;  // 256-column blocks in the first round
   if (wide < 1 || wide >= cols) return 0;
