@@ -448,11 +448,21 @@ constexpr uint64_t kMaxPartialBytes = 64ull << 20;  // split-K workspace bound
 
 // Splits K so that tiles * splits reaches about one workgroup per CU, with at
 // least 8 steps of `step` codes per split and a bounded partial workspace.
-void split_k(Plan& p, const Sizes& s, int64_t M, int64_t step) {
+// With `fit` (the LDS-streaming kernel) tiles * splits stays within one
+// workgroup per CU, except that a long K (each of two splits keeping at least
+// 32 steps) is split in two even where that exceeds it: measured on the K =
+// 2048 / 6144 prefill shapes, rounding the split count up put a second
+// workgroup on some CUs and cost 13-17% at M = 384 and 9-13% at M = 640-896
+// (K = 6144), while no split at M = 1152-1280, K = 6144 cost 3-5%.
+void split_k(Plan& p, const Sizes& s, int64_t M, int64_t step, bool fit = false) {
   const int64_t ksteps = (s.K + step - 1) / step;
   int64_t S = 1;
   if (p.tiles < kTargetWork * 3 / 4) {
     S = (kTargetWork + p.tiles - 1) / p.tiles;
+    if (fit) {
+      S = kTargetWork / p.tiles;
+      if (S == 1 && ksteps >= 64) S = 2;
+    }
     const int64_t max_by_k = ksteps / 8 > 1 ? ksteps / 8 : 1;
     if (S > max_by_k) S = max_by_k;
     while (S > 1 && (uint64_t)S * (uint64_t)M * (uint64_t)s.N * 4 > kMaxPartialBytes) --S;
@@ -523,7 +533,7 @@ Plan choose(const Sizes& s, int64_t M, bool fast) {
       p.kc = s.K;
       return p;
     }
-    split_k(p, s, M, 64);
+    split_k(p, s, M, 64, true);
     return p;
   }
   auto tiles_of = [&](int c) {
