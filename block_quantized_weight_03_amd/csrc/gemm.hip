@@ -509,7 +509,14 @@ Plan choose(const Sizes& s, int64_t M, bool fast) {
   if (fast && M >= kLdsMinM && gemm_lds_supported(s, M)) {
     Plan p;
     p.lds = true;
-    p.bm = ((M + 127) / 128) * ((N + 127) / 128) <= kLds128MaxTiles ? 128 : 256;
+    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+    const int64_t narrow1 = ((M + 255) / 256) * ((N + 127) / 128);
+    // 128 x 128 tiles up to kLds128MaxTiles, except where they would exceed
+    // one per CU while 256 x 128 tiles fill three quarters of the chip or
+    // more in one round (M = 1024, K = 2048, N = 6144: 43.8 -> 41.3 us;
+    // M = 3072, K = 6144, N = 2048: 128.3 -> 117.5 us)
+    const bool narrow_round = t128 > kTargetWork && narrow1 >= kTargetWork * 3 / 4 && narrow1 <= kTargetWork;
+    p.bm = t128 <= kLds128MaxTiles && !narrow_round ? 128 : 256;
     p.tn = p.bm / 128;
     p.cfg = -1;
     p.tiles_n = (N + p.bm - 1) / p.bm;
