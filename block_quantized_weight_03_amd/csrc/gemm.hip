@@ -472,11 +472,15 @@ void split_k(Plan& p, const Sizes& s, int64_t M, int64_t step, bool fit = false)
   p.kc = steps_per * step;
 }
 
-// rows of A from which the LDS-streaming kernel is used; it takes 128 x 128
+// rows of A from which the LDS-streaming kernel is used (its 128-row tiles
+// clamp the rows past M; from M = 64 it measured faster than the register-
+// staged kernels: M = 64 / 96 / 127 at K = 2048, N = 6144 19.4 / 23.8 / 25.1
+// -> 16.7 / 19.0 / 20.5 us, at K = 6144, N = 2048 17.6 / 19.1 / 20.7 -> 15.6 /
+// 16.1 / 21.0 us; below 64 it was slower at K = 6144); it takes 128 x 128
 // tiles while they number at most kLds128MaxTiles (one and a half rounds of
 // two workgroups per CU: measured faster than 256 x 256 tiles up to there),
 // else 256 x 256 tiles
-constexpr int64_t kLdsMinM = 128;
+constexpr int64_t kLdsMinM = 64;
 constexpr int64_t kLds128MaxTiles = 384;
 
 // Columns covered by 256 x 256 tiles when the rest take 256 x 128 ones, so

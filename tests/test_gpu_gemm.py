@@ -63,7 +63,12 @@ def check(orc, y, a, B, s, Z, K, N, bs):
     (300, 2048, 260, 32, False), (2, 1, 3, 32, False),
     # M <= 32 with K % 32 == 0
     (1, 2048, 300, 32, False), (16, 2048, 1000, 64, True), (17, 4096, 129, 128, False),
-    (32, 96, 33, 32, True), (5, 6144, 64, 32, False), (31, 160, 257, 32, True)])
+    (32, 96, 33, 32, True), (5, 6144, 64, 32, False), (31, 160, 257, 32, True),
+    # the register-staged kernels between the small-M and the LDS-streaming
+    # ranges (M < 64, or K not a multiple of 64), and the LDS-streaming kernel
+    # from M = 64
+    (48, 2048, 300, 32, False), (100, 2080, 500, 32, True), (64, 128, 1000, 64, True),
+    (127, 192, 333, 32, False)])
 def test_gemm_small_shapes_elementwise(orc, M, K, N, bs, zp):
     say(f"gemm small M={M} K={K} N={N} bs={bs} zp={zp}")
     w, B, s, Z = prepare(K, N, bs, zp, seed=M * 31 + K + N)
@@ -118,12 +123,13 @@ def test_gemm_deterministic():
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
 
 
-@pytest.mark.parametrize("M,lo,hi", [(32, 3, 20), (100, 30, 90), (700, 100, 400)])
+@pytest.mark.parametrize("M,lo,hi", [(32, 3, 20), (100, 20, 90), (700, 100, 400)])
 def test_gemm_rows_are_independent(M, lo, hi):
     """Row m of the output depends only on row m of A (no cross-row mixing in
     the tiling): a sub-batch that takes the same kernel (the register-staged
-    one below 128 rows, here the 128 x 128 LDS-streaming one above) gives the
-    same bits.  Different kernels sum K in different orders."""
+    one below 64 rows, here the 128 x 128 LDS-streaming one from 64, with K
+    unsplit) gives the same bits.  Different kernels sum K in different
+    orders."""
     say(f"gemm row independence M={M}")
     K, N = 512, 384
     w, *_ = prepare(K, N, seed=27)
