@@ -14,7 +14,9 @@ replayed from a HIP graph (launch overhead of the Python binding excluded) and
 bracketed by torch.cuda.synchronize() on both sides.
 
 The other workloads (vocabulary head, prefill GEMM, QMoE layers, quantizer)
-are measured first, each from graph replays of its own launches; then the
+are measured first, each from graph replays of its own launches (the median
+per call over 20 back-to-back replays, with the 10th and 90th percentiles in
+its `spread`); then the
 headline's weight copies are prepared (host repack and upload) and its graphs
 captured, and exactly `--warmup` untimed steps precede the `--steps` timed
 ones.  The timed steps continue the weight rotation where the warm-up
@@ -85,11 +87,13 @@ class Graph:
         self.g.replay()
 
 
-def graph_time(torch, calls, reps, min_calls=24):
+def graph_time(torch, calls, reps, min_calls=24, spread=None):
     """Captures `calls` (repeated to at least `min_calls` launches, so that the
-    graph launch itself is amortised) in one graph and returns the average per
-    call in ms over `reps` replays, timed with an event pair on the launch
-    stream."""
+    graph launch itself is amortised) in one graph and, after about 20 ms of
+    warm-up replays, times `reps` back-to-back replays with one event between
+    each two on the launch stream; returns the median per call in ms.  If
+    `spread` is a dict it receives the 10th and 90th percentiles per call (us)
+    and the replay count."""
     calls = list(calls) * max(1, -(-min_calls // len(calls)))
     g = Graph(torch, lambda: [c() for c in calls])
     # warm-up: about 20 ms of replays, so that clocks are at their sustained
@@ -103,12 +107,18 @@ def graph_time(torch, calls, reps, min_calls=24):
     for _ in range(max(2, int(20.0 / max(e0.elapsed_time(e1), 1e-3)))):
         g.replay()
     torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
         g.replay()
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / (reps * len(calls))
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) / len(calls) for i in range(reps)])
+    p10, p50, p90 = np.percentile(per, [10, 50, 90])
+    if spread is not None:
+        spread.update({"p10_us": round(1e3 * float(p10), 3), "p90_us": round(1e3 * float(p90), 3),
+                       "replays": reps, "calls_per_replay": len(calls)})
+    return float(p50)
 
 
 def source_hash(*names):
@@ -511,7 +521,8 @@ def bench_extras(torch, mnb, dev):
     Y = torch.empty(N, dtype=torch.float32, device=dev)
     ws = torch.empty(256, dtype=torch.uint8, device=dev)
     calls = [lambda w=w: mnb.mnb_gemv(w.plan, A, Y, ws, 256) for w in vw]
-    us = 1e3 * graph_time(torch, calls, 10)
+    sp = {}
+    us = 1e3 * graph_time(torch, calls, 20, spread=sp)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     reads = [lambda w=w: mnb.mnb_debug_stream_read([(w.buffer, (w.plan.total_bytes // 16) * 16)], sink)
              for w in vw]
@@ -522,7 +533,7 @@ def bench_extras(torch, mnb, dev):
                               "frac_of_hbm_peak": round(vb / us / 1e3 / PEAK_HBM_GBS, 4),
                               "read_ceiling_us": round(rus, 3),
                               "read_ceiling_GB/s": round(vb / rus / 1e3, 1),
-                              "frac_of_ceiling": round(rus / us, 4)}
+                              "frac_of_ceiling": round(rus / us, 4), "spread": sp}
     del vw
     log("extras: vocabulary head done")
     # prefill GEMM at M = 16 .. 4096 on both shapes
@@ -537,10 +548,12 @@ def bench_extras(torch, mnb, dev):
             need = mnb.mnb_gemm_workspace_size(w.plan, M)
             gws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
             call = lambda w=w, M=M, a=a, y=y, gws=gws: mnb.mnb_gemm(w.plan, M, a, y, gws, gws.numel())
-            us = 1e3 * graph_time(torch, [call] * 4, 5)
+            sp = {}
+            us = 1e3 * graph_time(torch, [call] * 4, 20, spread=sp)
             tf = 2.0 * M * N * K / us / 1e6
             pre[f"M{M}_K{K}_N{N}"] = {"us": round(us, 2), "TFLOP/s": round(tf, 1),
-                                       "frac_of_fp16_peak": round(tf / PEAK_FP16_TFLOPS, 4)}
+                                       "frac_of_fp16_peak": round(tf / PEAK_FP16_TFLOPS, 4),
+                                       "spread": sp}
         del w
     out["prefill_gemm"] = pre
     log("extras: prefill GEMM done")
@@ -602,14 +615,16 @@ def qmoe_extra(torch, mnb, dev, bits1, bits2, bf16=False, prep=None):
         qws = torch.empty(need, dtype=torch.uint8, device=dev)
         calls = [lambda p=p, x=x, lg=lg, o=o, qws=qws, T=T: mnb.qmoe_forward(
             p[0].plan, p[1].plan, q, T, x, lg, o, qws, qws.numel()) for lg in lgs for p in experts]
-        us = 1e3 * graph_time(torch, calls, 5)
+        sp = {}
+        us = 1e3 * graph_time(torch, calls, 20, spread=sp)
         # distinct experts routed per call (averaged over the logit sets)
         ids = sum(torch.topk(lg.float(), k, dim=1).indices.unique().numel() for lg in lgs) / nlg
         byts = ids * per_expert
         moe[f"T{T}"] = {"us": round(us, 2), "distinct_experts": ids,
                         "weight_GB/s": round(byts / us / 1e3, 1),
                         "frac_of_hbm_peak": round(byts / us / 1e3 / PEAK_HBM_GBS, 4),
-                        "TFLOP/s": round(2.0 * T * k * (2 * I * H + H * I) / us / 1e6, 2)}
+                        "TFLOP/s": round(2.0 * T * k * (2 * I * H + H * I) / us / 1e6, 2),
+                        "spread": sp}
     del experts
     return moe
 
@@ -625,10 +640,12 @@ def rtn_extra(torch, mnb, dev):
     s = torch.empty((rows, K // bs), dtype=torch.float16, device=dev)
     st = torch.empty((rows, K // bs), dtype=torch.uint8, device=dev)
     call = lambda: mnb.mnb_quantize_int3_rtn(W, rows, K, bs, B, s, st, None, mnb.MNB_DTYPE_F16)
-    us = 1e3 * graph_time(torch, [call], 3, min_calls=8)
+    sp = {}
+    us = 1e3 * graph_time(torch, [call], 20, min_calls=8, spread=sp)
     byts = rows * K * 4 + rows * 3 * K // 8 + rows * (K // bs) * 3
     res = {"rows": rows, "K": K, "block_size": bs, "us": round(us, 2),
-           "GB/s": round(byts / us / 1e3, 1), "frac_of_hbm_peak": round(byts / us / 1e3 / PEAK_HBM_GBS, 4)}
+           "GB/s": round(byts / us / 1e3, 1), "frac_of_hbm_peak": round(byts / us / 1e3 / PEAK_HBM_GBS, 4),
+           "spread": sp}
     del W, B, s, st
     return res
 
