@@ -1,5 +1,5 @@
-// Small-M GEMM (M <= 16) on dense INT4 weights for gfx950: one launch, no
-// workspace (used for M <= 4, or M <= 16 with N >= 4096; see
+// Small-M GEMM (M <= 32) on dense INT4 weights for gfx950: one launch, no
+// workspace (used for M <= 4, or M <= 32 with N >= 4096; see
 // gemm_small_supported).
 //
 // Operation ("Qwen3 Missing-Kernel Implementation Plan", section "PR
@@ -9,7 +9,7 @@
 // each weight rounded once as fp16(fma(q, s, -(z*s))) from fp32, products
 // accumulated in fp32.
 //
-// At M <= 16 the product is a stream over the weights that must keep enough
+// At M <= 32 the product is a stream over the weights that must keep enough
 // bytes in flight to cover HBM latency.  A workgroup owns one 16-row weight
 // tile; its W waves split the 128-code K chunks into contiguous ranges, and
 // each wave issues the 16-byte loads of all its chunks before it uses the
@@ -60,13 +60,14 @@ __device__ __forceinline__ half8 w_operand(uint32_t word, float s, float nzs) {
 // CPW: chunks per wave (at least ceil(nch / W); extra slots reload the last
 // chunk of the range and are not used); RT: 16-row weight tiles per
 // workgroup, each wave computing all of them so that one A load feeds RT
-// MFMAs.  M <= 16, K % 128 == 0.
-template <int CPW, int W, int RT, bool HAS_ZP>
+// MFMAs; TT: 16-token tiles (M <= 16 TT), each dequantized weight operand
+// feeding TT MFMAs.  K % 128 == 0.
+template <int CPW, int W, int RT, bool HAS_ZP, int TT>
 __global__ void __launch_bounds__(64 * W) gemm_int4_small(
     const float* __restrict__ A, const uint8_t* __restrict__ codes,
     const float* __restrict__ scales, const uint32_t* __restrict__ zeros, float* __restrict__ Y,
     int32_t M, int32_t N, int32_t K, int64_t row_bytes, int64_t nb, int32_t bs_shift) {
-  __shared__ f32x4 red[W][RT][64];
+  __shared__ f32x4 red[W][TT * RT][64];
   const int lane = (int)(threadIdx.x & 63);
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int n0 = (int)blockIdx.x * 16 * RT;
@@ -74,7 +75,6 @@ __global__ void __launch_bounds__(64 * W) gemm_int4_small(
   const int c_beg = nch * wave / W, c_end = nch * (wave + 1) / W;
   const int cnt = c_end - c_beg;  // wave-uniform, <= CPW
   const int r = lane & 15, g = lane >> 4;
-  const int tok = min(r, M - 1);  // tokens past M compute a copy of the last one (not stored)
 
   // every chunk of the range in flight before the first is used (clamped:
   // a wave with no chunk reloads chunk 0 and adds nothing); rows past N
@@ -100,32 +100,47 @@ __global__ void __launch_bounds__(64 * W) gemm_int4_small(
       nz[t][u] = HAS_ZP ? (float)((__builtin_nontemporal_load(zrow + b) >> zsh) & 15u) : 8.0f;
     }
   }
-  const float* arow = A + (int64_t)tok * K + 32 * g;
-  f32x4 a0[8], a1[8];
-  auto load_a = [&](f32x4 (&a)[8], int u) {
+  // token row of lane r in token tile tt (tokens past M compute a copy of
+  // the last one, not stored)
+  const float* arow[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) arow[tt] = A + (int64_t)min(16 * tt + r, M - 1) * K + 32 * g;
+  f32x4 a0[TT][8], a1[TT][8];
+  auto load_a = [&](f32x4 (&a)[TT][8], int u) {
     int c = c_beg + u;
     c = c < c_end ? c : c_end - 1;
     c = c < 0 ? 0 : c;
-    const f32x4* src = reinterpret_cast<const f32x4*>(arow + 128 * c);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = src[i];
+    for (int tt = 0; tt < TT; ++tt) {
+      const f32x4* src = reinterpret_cast<const f32x4*>(arow[tt] + 128 * c);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a[tt][i] = src[i];
+    }
   };
-  f32x4 acc[RT];
+  f32x4 acc[TT][RT];
 #pragma unroll
-  for (int t = 0; t < RT; ++t) acc[t] = f32x4{0, 0, 0, 0};
-  auto chunk = [&](const f32x4 (&a)[8], int u) {
-    const half8 a0 = a_operand(a[0], a[1]), a1 = a_operand(a[2], a[3]);
-    const half8 a2 = a_operand(a[4], a[5]), a3 = a_operand(a[6], a[7]);
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int t = 0; t < RT; ++t) acc[tt][t] = f32x4{0, 0, 0, 0};
+  auto chunk = [&](const f32x4 (&a)[TT][8], int u) {
+    half8 ao[TT][4];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ao[tt][i] = a_operand(a[tt][2 * i], a[tt][2 * i + 1]);
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const float s = sc[t][u], nzs = -(nz[t][u] * s);
       const u32x4 w = wq[t][u];
-      const uint32_t w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
+      const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
       // MFMA i takes k = 32 g + 8 i + [0, 8) in lane group g on both sides
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, w_operand(w0, s, nzs), acc[t], 0, 0, 0);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, w_operand(w1, s, nzs), acc[t], 0, 0, 0);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2, w_operand(w2, s, nzs), acc[t], 0, 0, 0);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a3, w_operand(w3, s, nzs), acc[t], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const half8 wo = w_operand(wv[i], s, nzs);
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+          acc[tt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao[tt][i], wo, acc[tt][t], 0, 0, 0);
+      }
     }
   };
   load_a(a0, 0);
@@ -140,44 +155,54 @@ __global__ void __launch_bounds__(64 * W) gemm_int4_small(
       chunk(a1, u + 1);
     }
   }
-  // lane l holds tokens 4 (l >> 4) + i of weight row n0 + 16 t + (l & 15)
+  // lane l holds tokens 16 tt + 4 (l >> 4) + i of weight row n0 + 16 t + (l & 15)
 #pragma unroll
-  for (int t = 0; t < RT; ++t) red[wave][t][lane] = acc[t];
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int t = 0; t < RT; ++t) red[wave][tt * RT + t][lane] = acc[tt][t];
   __syncthreads();
-  if (wave < RT) {  // wave t sums tile t over the waves, in wave order
-    const int t = wave;
-    f32x4 o = red[0][t][lane];
+  if (wave < TT * RT) {  // wave j sums tile j = (tt, t) over the waves, in wave order
+    const int j = wave, tt = j / RT, t = j % RT;
+    f32x4 o = red[0][j][lane];
 #pragma unroll
     for (int w = 1; w < W; ++w) {
-      const f32x4 v = red[w][t][lane];
+      const f32x4 v = red[w][j][lane];
       o = f32x4{o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w};
     }
     const int n = n0 + 16 * t + r;
     if (n < N) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int m = 4 * g + i;
+        const int m = 16 * tt + 4 * g + i;
         if (m < M) Y[(int64_t)m * N + n] = o[i];
       }
     }
   }
 }
 
-template <int CPW, int W, int RT = 1>
-hipError_t launch_cw(const Sizes& s, const mnb_plan& p, int64_t M, const float* A, float* Y,
-                     int bs_shift, hipStream_t st) {
+template <int CPW, int W, int RT, int TT>
+hipError_t launch_cwt(const Sizes& s, const mnb_plan& p, int64_t M, const float* A, float* Y,
+                      int bs_shift, hipStream_t st) {
   const dim3 grid((unsigned)((s.N + 16 * RT - 1) / (16 * RT))), block(64 * W);
   if (s.zeros)
-    hipLaunchKernelGGL((gemm_int4_small<CPW, W, RT, true>), grid, block, 0, st, A,
+    hipLaunchKernelGGL((gemm_int4_small<CPW, W, RT, true, TT>), grid, block, 0, st, A,
                        static_cast<const uint8_t*>(p.codes), static_cast<const float*>(p.scales),
                        static_cast<const uint32_t*>(p.zeros), Y, (int32_t)M, (int32_t)s.N,
                        (int32_t)s.K, s.row_bytes, s.nb, bs_shift);
   else
-    hipLaunchKernelGGL((gemm_int4_small<CPW, W, RT, false>), grid, block, 0, st, A,
+    hipLaunchKernelGGL((gemm_int4_small<CPW, W, RT, false, TT>), grid, block, 0, st, A,
                        static_cast<const uint8_t*>(p.codes), static_cast<const float*>(p.scales),
                        nullptr, Y, (int32_t)M, (int32_t)s.N, (int32_t)s.K, s.row_bytes, s.nb,
                        bs_shift);
   return hipGetLastError();
+}
+
+// one 16-token tile up to M = 16, two up to 32
+template <int CPW, int W, int RT = 1>
+hipError_t launch_cw(const Sizes& s, const mnb_plan& p, int64_t M, const float* A, float* Y,
+                     int bs_shift, hipStream_t st) {
+  return M <= 16 ? launch_cwt<CPW, W, RT, 1>(s, p, M, A, Y, bs_shift, st)
+                 : launch_cwt<CPW, W, RT, 2>(s, p, M, A, Y, bs_shift, st);
 }
 
 int cus() {
@@ -200,9 +225,11 @@ int cus() {
 // (graph replays): K = 2048, N = 6144, M = 1/4/8/16: 5.6-6.0/6.7/7.3/8.2 us
 // (32-row tiles) against 10.9/11.6/11.8/12.4 us for the split-K kernel;
 // K = 6144, N = 2048 (128 tiles): M = 1/4 9.2/10.6 against 11.4/11.5 us, but
-// M = 8/16 12.6/16.4 against 11.5/12.0 us.
+// M = 8/16 12.6/16.4 against 11.5/12.0 us.  With two 16-token tiles sharing
+// each dequantized weight operand (M = 17..32), K = 2048, N = 6144, M =
+// 17/24/32: 9.4/10.6/12.0 against 12.5/13.3/14.0 us for the next kernel.
 bool gemm_small_supported(const Sizes& s, int64_t M, const void* A) {
-  const bool shape = M >= 1 && M <= 16 && s.K % 128 == 0 && s.K <= 8192 &&
+  const bool shape = M >= 1 && M <= 32 && s.K % 128 == 0 && s.K <= 8192 &&
                      s.N <= (int64_t(1) << 30) && (reinterpret_cast<uintptr_t>(A) & 15) == 0;
   return shape && (M <= 4 || (s.N + 15) / 16 >= 256);
 }

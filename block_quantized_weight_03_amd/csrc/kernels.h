@@ -25,7 +25,7 @@ uint64_t gemm_ws_bytes(const Sizes& s, int64_t M);
 hipError_t launch_gemm(const Sizes& s, const mnb_plan& p, int64_t M, const float* A,
                        float* Y, void* ws, hipStream_t st);
 
-// single-launch small-M kernel (gemm_small.hip): M <= 4, or M <= 16 with
+// single-launch small-M kernel (gemm_small.hip): M <= 4, or M <= 32 with
 // N >= 4096; K % 128 == 0, K <= 8192, A 16-byte aligned; needs no workspace
 bool gemm_small_supported(const Sizes& s, int64_t M, const void* A);
 hipError_t launch_gemm_small(const Sizes& s, const mnb_plan& p, int64_t M, const float* A,

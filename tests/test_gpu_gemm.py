@@ -205,18 +205,21 @@ def test_gemm_large_m_rows_are_independent():
     assert np.array_equal(y[100:2300], y_sub)
 
 
-# The single-launch small-M kernel (M <= 4, or M <= 16 with N >= 4096; K a
+# The single-launch small-M kernel (M <= 4, or M <= 32 with N >= 4096; K a
 # multiple of 128 up to 8192): one 16-row weight tile per workgroup, K chunks
 # split over 4 or 8 waves (with waves that get no chunk when K is short),
-# rows of N past the last whole tile, every block size, zero points; then
-# the limits beside it (K = 8320, M = 17, M = 8 with N = 2048) that take the
-# other kernels.
+# rows of N past the last whole tile, every block size, zero points, one
+# 16-token tile up to M = 16 and two above (a partial second one at M = 17,
+# 25); then the limits beside it (K = 8320, M = 17 with N = 70, M = 8 with
+# N = 2048, M = 33) that take the other kernels.
 @pytest.mark.parametrize("M,K,N,bs,zp", [
     (1, 128, 17, 32, True), (16, 8192, 4112, 128, True), (7, 384, 4100, 64, False),
     (16, 1024, 4144, 64, True), (5, 2048, 6160, 32, False), (9, 128, 8200, 128, True),
     (16, 2176, 4096, 32, True), (12, 6272, 4128, 64, False), (2, 256, 5, 128, True),
     (16, 2048, 6144, 32, False), (4, 6144, 2048, 64, True), (3, 8192, 33, 32, False),
-    (16, 8320, 40, 32, False), (17, 2048, 70, 32, True), (8, 2048, 2048, 32, False)])
+    (16, 8320, 40, 32, False), (17, 2048, 70, 32, True), (8, 2048, 2048, 32, False),
+    (17, 4096, 4112, 128, True), (20, 2048, 6144, 32, False), (25, 8192, 4096, 32, True),
+    (32, 1024, 4144, 64, False), (32, 6272, 4128, 64, True), (33, 2048, 4096, 32, False)])
 def test_gemm_single_launch_small_m(orc, M, K, N, bs, zp):
     say(f"gemm single-launch small M={M} K={K} N={N} bs={bs} zp={zp}")
     w, B, s, Z = prepare(K, N, bs, zp, seed=M * 7 + K + N)
