@@ -476,11 +476,14 @@ void split_k(Plan& p, const Sizes& s, int64_t M, int64_t step, bool fit = false)
 // clamp the rows past M; from M = 64 it measured faster than the register-
 // staged kernels: M = 64 / 96 / 127 at K = 2048, N = 6144 19.4 / 23.8 / 25.1
 // -> 16.7 / 19.0 / 20.5 us, at K = 6144, N = 2048 17.6 / 19.1 / 20.7 -> 15.6 /
-// 16.1 / 21.0 us; below 64 it was slower at K = 6144); it takes 128 x 128
+// 16.1 / 21.0 us; below 64 it was slower at K = 6144, but from M = 40 faster
+// at K = 2048: M = 40 / 48 / 56 16.6 / 17.3 / 19.1 -> 15.9 / 16.2 / 16.5 us,
+// so K <= 2048 takes it from kLdsMinShortK); it takes 128 x 128
 // tiles while they number at most kLds128MaxTiles (one and a half rounds of
 // two workgroups per CU: measured faster than 256 x 256 tiles up to there),
 // else 256 x 256 tiles
 constexpr int64_t kLdsMinM = 64;
+constexpr int64_t kLdsMinShortK = 40;
 constexpr int64_t kLds128MaxTiles = 384;
 
 // Columns covered by 256 x 256 tiles when the rest take 256 x 128 ones, so
@@ -510,7 +513,7 @@ int64_t mixed_split(const Sizes& s, int64_t M) {
 Plan choose(const Sizes& s, int64_t M, bool fast) {
   const int64_t N = s.N, K = s.K;
   (void)K;
-  if (fast && M >= kLdsMinM && gemm_lds_supported(s, M)) {
+  if (fast && M >= (s.K <= 2048 ? kLdsMinShortK : kLdsMinM) && gemm_lds_supported(s, M)) {
     Plan p;
     p.lds = true;
     const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);

@@ -65,10 +65,11 @@ def check(orc, y, a, B, s, Z, K, N, bs):
     (1, 2048, 300, 32, False), (16, 2048, 1000, 64, True), (17, 4096, 129, 128, False),
     (32, 96, 33, 32, True), (5, 6144, 64, 32, False), (31, 160, 257, 32, True),
     # the register-staged kernels between the small-M and the LDS-streaming
-    # ranges (M < 64, or K not a multiple of 64), and the LDS-streaming kernel
-    # from M = 64
-    (48, 2048, 300, 32, False), (100, 2080, 500, 32, True), (64, 128, 1000, 64, True),
-    (127, 192, 333, 32, False)])
+    # ranges (M < 64, or M < 40 with K <= 2048, or K not a multiple of 64),
+    # and the LDS-streaming kernel from M = 64 (from 40 with K <= 2048)
+    (48, 4096, 300, 32, False), (39, 2048, 300, 32, True), (100, 2080, 500, 32, True),
+    (64, 128, 1000, 64, True), (127, 192, 333, 32, False), (40, 2048, 333, 32, False),
+    (57, 1024, 500, 64, True)])
 def test_gemm_small_shapes_elementwise(orc, M, K, N, bs, zp):
     say(f"gemm small M={M} K={K} N={N} bs={bs} zp={zp}")
     w, B, s, Z = prepare(K, N, bs, zp, seed=M * 31 + K + N)
