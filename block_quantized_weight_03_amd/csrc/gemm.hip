@@ -538,11 +538,10 @@ Plan choose(const Sizes& s, int64_t M, bool fast) {
     // over the whole of K, instead of splitting K (no partials, no reduce;
     // at M = 4096, K = 6144, N = 2048: 256 narrow tiles against 128 wide
     // tiles split in two)
-    const int64_t narrow = ((M + 255) / 256) * ((N + 127) / 128);
-    if (p.bm == 256 && p.tiles < kTargetWork * 3 / 4 && narrow >= kTargetWork * 3 / 4) {
+    if (p.bm == 256 && p.tiles < kTargetWork * 3 / 4 && narrow1 >= kTargetWork * 3 / 4) {
       p.tn = 1;
       p.tiles_n = (N + 127) / 128;
-      p.tiles = narrow;
+      p.tiles = narrow1;
       p.splits = 1;
       p.kc = s.K;
       return p;
