@@ -523,7 +523,13 @@ Plan choose(const Sizes& s, int64_t M, bool fast) {
     // more in one round (M = 1024, K = 2048, N = 6144: 43.8 -> 41.3 us;
     // M = 3072, K = 6144, N = 2048: 128.3 -> 117.5 us)
     const bool narrow_round = t128 > kTargetWork && narrow1 >= kTargetWork * 3 / 4 && narrow1 <= kTargetWork;
-    p.bm = t128 <= kLds128MaxTiles && !narrow_round ? 128 : 256;
+    // 256 x 256 tiles just over one per CU (by at most an eighth) leave the
+    // rest for a second, mostly idle round whatever the mix; 128 x 128 tiles
+    // spread it finer (M = 2688 / 2816, K = 2048, N = 6144, 264 such tiles:
+    // 119.9 / 118.5 -> 97.1 / 113.0 us; 288 tiles at M = 3072: equal)
+    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+    const bool wide_spill = t256 > kTargetWork && t256 <= kTargetWork * 9 / 8;
+    p.bm = (t128 <= kLds128MaxTiles && !narrow_round) || wide_spill ? 128 : 256;
     p.tn = p.bm / 128;
     p.cfg = -1;
     p.tiles_n = (N + p.bm - 1) / p.bm;

@@ -161,7 +161,10 @@ def test_gemm_rows_are_independent(M, lo, hi):
     (1400, 192, 6100, 64, False), (1536, 128, 6144, 32, True),
     # 128 x 128 tiles would exceed one per CU (384) while 192 tiles of 256 x 128
     # cover the output in one round: those
-    (1000, 192, 6100, 64, True)])
+    (1000, 192, 6100, 64, True),
+    # 256 x 256 tiles just over one per CU (264): 128 x 128 tiles (1008, two
+    # workgroups per CU) instead
+    (2688, 128, 6100, 32, True)])
 def test_gemm_large_m_ragged_elementwise(orc, M, K, N, bs, zp):
     say(f"gemm large-M M={M} K={K} N={N} bs={bs} zp={zp}")
     w, B, s, Z = prepare(K, N, bs, zp, seed=M * 7 + K + N)
