@@ -748,10 +748,15 @@ __device__ __forceinline__ float group_dot_unscaled(const typename Group<BITS>::
 // lane >> 4) takes group 4c + g of row row0 + n for the chunks c = c0,
 // c0 + cstep, ... (one 768-byte (INT3) or 1024-byte (INT4) load per wave and
 // chunk in the tile-major layout).  Loads
-// are issued in batches of kDecBatch chunks before any is used, the first
+// are issued in batches of kDecFc1Batch chunks before any is used, the first
 // batch before the activations are staged; groups past K read a valid group
-// with scale 0.
+// with scale 0.  Four chunks per wave cover a K = 2048 row with the FC1
+// workgroup's four waves, so no slot of the batch reloads a clamped chunk
+// (eight measured slower at T = 1: INT3 13.05 -> 12.1 us, INT4 13.95 ->
+// 12.6 us with four); the FC2 half tiles below take two halves of
+// kDecBatch / 2 chunks (three per half at I = 768 measured the same).
 constexpr int kDecBatch = 8;
+constexpr int kDecFc1Batch = 4;
 
 struct TileRef {
   const uint8_t* codes;     // this expert's codes
@@ -761,9 +766,9 @@ struct TileRef {
 
 template <int BITS, bool BF>
 struct TileBatch {
-  typename Group<BITS>::W w[kDecBatch];
-  uint16_t s[kDecBatch];
-  int G[kDecBatch];
+  typename Group<BITS>::W w[kDecFc1Batch];
+  uint16_t s[kDecFc1Batch];
+  int G[kDecFc1Batch];
   uint32_t ok;  // bit u: group G[u] lies inside K (the loaded scale is used as is)
   int cnt;      // chunks of this batch inside K (wave-uniform)
 
@@ -773,7 +778,7 @@ struct TileBatch {
     cnt = c0 < t.nch ? (t.nch - c0 + cstep - 1) / cstep : 0;
     ok = 0;
 #pragma unroll
-    for (int u = 0; u < kDecBatch; ++u) {
+    for (int u = 0; u < kDecFc1Batch; ++u) {
       const int Gr = 4 * (c0 + u * cstep) + t.g;
       ok |= (Gr < t.ng ? 1u : 0u) << u;
       G[u] = Gr < t.ng ? Gr : t.ng - 1;
@@ -784,7 +789,7 @@ struct TileBatch {
   __device__ __forceinline__ float dot(const _Float16* xs, uint32_t magic) const {
     float acc = 0.0f;
 #pragma unroll
-    for (int u = 0; u < kDecBatch; ++u)
+    for (int u = 0; u < kDecFc1Batch; ++u)
       if (u < cnt) {
         const uint16_t sc = (ok >> u) & 1u ? s[u] : (uint16_t)0;
         acc += group_dot_unscaled<BITS, BF>(w[u], Dt<BF>::to_f32(sc), magic,
@@ -945,7 +950,7 @@ __global__ void __launch_bounds__(256) qmoe_fc1_decode(const void* __restrict__ 
   __syncthreads();
   const uint32_t magic = opaque_magic<BF>();
   float acc = b.dot(xs, magic);
-  for (int c = wave + 4 * kDecBatch; c < tr.nch; c += 4 * kDecBatch) {
+  for (int c = wave + 4 * kDecFc1Batch; c < tr.nch; c += 4 * kDecFc1Batch) {
     b.load(tr, c, 4);
     acc += b.dot(xs, magic);
   }

@@ -491,6 +491,23 @@ def test_qmoe_variant_path_boundaries(orc, dtype, bits1, bits2, T, E, k):
     check_stages(orc, m, res, o)
 
 
+# Decode path (T k <= 32) with a hidden size past one batch of FC1 chunks per
+# wave: H = 4160 gives 130 groups, 33 K chunks of four groups (the last one
+# partial), so the FC1 waves take three batches of their chunks.
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("bits1,bits2", [(3, 3), (4, 4)])
+@pytest.mark.parametrize("T,k", [(1, 3), (3, 8)])
+def test_qmoe_decode_long_hidden(orc, dtype, bits1, bits2, T, k):
+    H, I, E, bs = 4160, 128, 6 if k < 8 else 10, 64
+    say(f"qmoe decode long hidden {dtype} ({bits1},{bits2}) T={T} H={H} I={I} E={E} k={k}")
+    x, logits, m = random_moe(T * 17 + k + bits1, T, H, I, E, k, bs, bits1, bits2,
+                              bias=(T == 1), dtype=dtype)
+    res = m.run(x, logits, debug=True)
+    o = m.oracle(orc, x, logits)
+    check_end_to_end(res["out"], o, dtype)
+    check_stages(orc, m, res, o)
+
+
 def test_qmoe_bf16_no_tokens_is_a_no_op():
     say("qmoe bf16 T=0")
     _, _, m = random_moe(5, 1, 64, 32, 4, 2, 32, dtype="bf16")
